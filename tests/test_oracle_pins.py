@@ -1,0 +1,347 @@
+"""Pins for the CPU oracle: results the mathematics fixes, reached by a route
+other than the oracle's own code (closed forms, exact rational arithmetic,
+torch's decoders, brute force).  CPU only.
+
+Passage followed by the oracle: "sglang PR #30117" page, key source snippet
+(out = x @ weight.T + bias, bf16 in/out, fp32 accumulation).
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import exact
+from workloads import inputs as gen
+
+KS = (2048, 2880, 4096, 6144, 7168)
+
+
+# ------------------------------------------------------------------ decoders
+
+def test_decode_bf16_all_codes_match_torch():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.decode_bf16(c) for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_decode_e4m3_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.decode_e4m3(c) for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # the format's landmarks, from its bit-field definition
+    assert oracle.decode_e4m3(0x7E) == 448.0
+    assert oracle.decode_e4m3(0x01) == 2.0 ** -9
+    assert oracle.decode_e4m3(0x08) == 2.0 ** -6
+    assert math.isnan(oracle.decode_e4m3(0x7F)) and math.isnan(oracle.decode_e4m3(0xFF))
+    for c in range(256):
+        e = exact.e4m3_code_to_fraction(c)
+        g = oracle.decode_e4m3(c)
+        assert exact.same(e if isinstance(e, float) else e, g if math.isnan(g) else Fraction(g))
+
+
+def test_decode_e8m0_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = np.array([oracle.decode_e8m0(c) for c in codes])
+    assert math.isnan(got[255]) and math.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert oracle.decode_e8m0(127) == 1.0 and oracle.decode_e8m0(0) == 2.0 ** -127
+
+
+# ------------------------------------------------------------------ rounding
+
+def _exact_bf16(v: float):
+    return exact.round_fraction(Fraction(v), **exact.BF16)
+
+
+def _check_round(v):
+    code = oracle.round_bf16(v)
+    got = exact.bf16_code_to_fraction(code)
+    want = _exact_bf16(v)
+    assert exact.same(got, want), (v, hex(code), want)
+    if v == 0:
+        assert (code & 0x8000) == (0x8000 if math.copysign(1, v) < 0 else 0)
+
+
+def test_round_bf16_double_rounding_case():
+    # 1 + 2^-8 + 2^-40 lies above the tie 1 + 2^-8: nearest bf16 is 1 + 2^-7.
+    assert oracle.round_bf16(1 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81
+    # the tie itself goes to even (1.0)
+    assert oracle.round_bf16(1 + 2.0 ** -8) == 0x3F80
+    assert oracle.round_bf16(1 + 3 * 2.0 ** -8) == 0x3F82
+
+
+def test_round_bf16_against_exact_fractions():
+    rng = np.random.default_rng(1234)
+    vals = []
+    # random magnitudes over the whole range, both signs
+    for e in range(-140, 129, 3):
+        for _ in range(6):
+            vals.append(float(rng.uniform(1, 2)) * 2.0 ** e * (1 if rng.random() < .5 else -1))
+    # exact ties and near-ties in several binades, incl. the subnormal range
+    for e in (-133, -130, -127, -126, -100, -8, 0, 7, 100, 126, 127):
+        q = 2.0 ** (max(e, -126) - 7)
+        for k in (1, 2, 3, 255):
+            base = k * q if e <= -126 else (2.0 ** e) + k * q
+            vals += [base + q / 2, base - q / 2, base + q / 2 + q / 64, base + q / 2 - q / 64]
+    # overflow boundary: max finite, the midpoint to 2^128 and just below it
+    mf = (2 - 2.0 ** -7) * 2.0 ** 127
+    vals += [mf, mf + 2.0 ** 119, mf + 2.0 ** 119 - 2.0 ** 100, 2.0 ** 128, -mf - 2.0 ** 119]
+    vals += [0.0, -0.0, 2.0 ** -134, 2.0 ** -134 * 1.0000001, 2.0 ** -135, 3 * 2.0 ** -134]
+    for v in vals:
+        _check_round(v)
+
+
+def test_round_bf16_matches_torch_for_fp32_values():
+    # torch's fp32 -> bf16 conversion is a single RNE; for values that are
+    # exactly binary32 the oracle's fp64 -> bf16 rounding must agree with it.
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.round_bf16(float(v)) for v in f[:50000]], dtype=np.uint16)
+    assert np.array_equal(got, ref[:50000])
+
+
+def test_round_nan_inf():
+    assert oracle.round_bf16(float("inf")) == 0x7F80
+    assert oracle.round_bf16(float("-inf")) == 0xFF80
+    c = oracle.round_bf16(float("nan"))
+    assert (c & 0x7F80) == 0x7F80 and (c & 0x7F) != 0
+
+
+# ------------------------------------------------------------------ GEMM pins
+
+def _decode(out16):
+    return torch.from_numpy(out16.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("K", KS)
+def test_all_ones_gives_K(K):
+    x, w = gen.ones(3, 5, K)
+    out = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w))
+    assert np.all(_decode(out) == K)  # every configured K is exact in bf16
+
+
+@pytest.mark.parametrize("K", KS)
+def test_all_ones_plus_bias_rounds_back_to_K(K):
+    # K + 1 lies strictly below the midpoint between K and the next bf16
+    # (spacing 16 in [2048, 4096), 32 in [4096, 8192)): rounds back to K.
+    x, w = gen.ones(2, 3, K)
+    bias = torch.ones(3, dtype=torch.bfloat16)
+    out = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w), gen.bits16(bias))
+    assert np.all(_decode(out) == K)
+    # bias = 8 in [2048,4096) (half the spacing 16) is a tie: K is even -> K,
+    # while bias = 24 lands at 1.5 spacings -> K + 32 (tie to even 2*16).
+    if K < 4096:
+        for b, want in ((8.0, K if (K // 16) % 2 == 0 else K + 16), (24.0, K + 32)):
+            out = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w),
+                                   gen.bits16(torch.full((3,), b, dtype=torch.bfloat16)))
+            assert np.all(_decode(out) == want), (K, b)
+
+
+@pytest.mark.parametrize("K", (8, 2880, 7168))
+def test_sign_alternating_gives_zero(K):
+    x, w = gen.alternating(2, 4, K)
+    out = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w))
+    assert np.all(_decode(out) == 0.0)
+
+
+@pytest.mark.parametrize("K,N", ((2880, 128), (2048, 256), (64, 48)))
+def test_one_hot_selects_x(K, N):
+    x, w, pi = gen.one_hot(4, N, K, seed=11)
+    out = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w))
+    xb = gen.bits16(x)
+    assert np.array_equal(out, xb[:, pi.numpy()])
+    # with bias: RNE(x + b), computed exactly
+    b = (torch.randn(N, generator=torch.Generator().manual_seed(5)) * 0.3).to(torch.bfloat16)
+    outb = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w), gen.bits16(b))
+    bb = gen.bits16(b)
+    for m in range(4):
+        for n in range(N):
+            want = exact.round_fraction(exact.bf16_code_to_fraction(xb[m, pi[n]])
+                                        + exact.bf16_code_to_fraction(bb[n]), **exact.BF16)
+            assert exact.bf16_code_to_fraction(outb[m, n]) == want
+
+
+@pytest.mark.parametrize("M,N,K,bias", ((5, 7, 2880, True), (16, 9, 7168, False), (3, 4, 8, True)))
+def test_small_integer_regime_exact(M, N, K, bias):
+    x, w, b = gen.small_integers(M, N, K, bias, seed=M * 1000 + K)
+    xi = x.to(torch.int64).numpy()
+    wi = w.to(torch.int64).numpy()
+    acc = xi @ wi.T
+    if bias:
+        acc = acc + b.to(torch.int64).numpy()[None, :]
+    out = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w), None if b is None else gen.bits16(b))
+    for m in range(M):
+        for n in range(N):
+            want = exact.round_fraction(Fraction(int(acc[m, n])), **exact.BF16)
+            assert exact.bf16_code_to_fraction(out[m, n]) == want
+
+
+def test_brute_force_tiny():
+    x, w = gen.brute_force_set()
+    out = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w))
+    xb, wb = gen.bits16(x), gen.bits16(w)
+    # The oracle accumulates in fp64.  Its result must be the exactly
+    # rounded one wherever fp64 summation cannot move the sum across a bf16
+    # rounding boundary; inside that error bound either neighbour is right.
+    near_tie = 0
+    for r in range(x.shape[0]):
+        a = [exact.bf16_code_to_fraction(c) for c in xb[r]]
+        for c in range(w.shape[0]):
+            prods = [ai * exact.bf16_code_to_fraction(bj) for ai, bj in zip(a, wb[c])]
+            s = sum(prods, Fraction(0))
+            want = exact.round_fraction(s, **exact.BF16)
+            got = exact.bf16_code_to_fraction(out[r, c])
+            lo, hi = exact.round_range(s, exact.fp64_sum_bound(prods), exact.BF16)
+            if lo == hi:
+                assert exact.same(got, want), (r, c, s, hex(out[r, c]))
+            else:
+                near_tie += 1
+                assert lo <= got <= hi, (r, c, s, hex(out[r, c]))
+    # Only a product exactly on a bf16 tie plus a product below fp64's reach
+    # (e.g. 1.5 * (1 + 2^-7) + 2^-133 * 2^-133) is ambiguous: 140 of the
+    # 20736 combinations of this set; every other one is checked exactly.
+    assert near_tie <= x.shape[0] * w.shape[0] // 100, near_tie
+
+
+def test_numpy_fp64_cross_check():
+    M, N, K = 8, 64, 2880
+    x, w, b = gen.bf16_inputs(M, N, K, True, seed=99)
+    out = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w), gen.bits16(b))
+    ref = x.double().numpy() @ w.double().numpy().T + b.double().numpy()[None, :]
+    got = _decode(out)
+    # one bf16 rounding of nearly the same fp64 value: within half an ulp
+    # (at most 2^-8 of the value) plus the fp64 summation-order noise.
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-12)
+    # the roundings agree except at (practically never met) near-ties
+    again = np.array([[oracle.round_bf16(v) for v in row] for row in ref], dtype=np.uint16)
+    assert (again != out).sum() <= 1
+
+
+def test_thread_count_does_not_change_bits():
+    x, w, b = gen.bf16_inputs(7, 96, 2048, True, seed=3)
+    a = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w), gen.bits16(b), threads=1)
+    c = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w), gen.bits16(b), threads=8)
+    assert np.array_equal(a, c)
+
+
+def test_transposed_operand_would_be_seen():
+    # x[M,K] and W[N,K] differ in role: out[m, n] uses row m of x and row n
+    # of W.  A one-hot x picks columns of W: out[m, n] = W[n, m].
+    K, N, M = 16, 5, 4
+    x = torch.zeros(M, K, dtype=torch.bfloat16)
+    x[torch.arange(M), torch.arange(M)] = 1.0
+    w = torch.arange(N * K, dtype=torch.float32).reshape(N, K).to(torch.bfloat16)
+    out = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w))
+    assert np.array_equal(_decode(out), w.double().numpy()[:, :M].T)
+
+
+def test_empty_K_is_bias_only():
+    x = torch.zeros(2, 0, dtype=torch.bfloat16)
+    w = torch.zeros(3, 0, dtype=torch.bfloat16)
+    b = torch.tensor([1.5, -2.0, 0.25], dtype=torch.bfloat16)
+    out = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w), gen.bits16(b))
+    assert np.array_equal(_decode(out), np.tile([1.5, -2.0, 0.25], (2, 1)))
+
+
+def test_fp32_output_rounds_once_from_exact():
+    M, N, K = 4, 6, 64
+    x, w, _ = gen.bf16_inputs(M, N, K, False, seed=21)
+    out = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w), out_f32=True)
+    xb, wb = gen.bits16(x), gen.bits16(w)
+    for m in range(M):
+        for n in range(N):
+            s = sum((exact.bf16_code_to_fraction(xb[m, k]) * exact.bf16_code_to_fraction(wb[n, k])
+                     for k in range(K)), Fraction(0))
+            assert exact.f32_to_fraction(out[m, n]) == exact.round_fraction(s, **exact.F32)
+
+
+def test_nan_and_inf_propagate():
+    x = torch.ones(2, 8, dtype=torch.bfloat16)
+    w = torch.ones(3, 8, dtype=torch.bfloat16)
+    x[0, 3] = float("nan")
+    w[2, 0] = float("inf")
+    out = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w))
+    d = _decode(out)
+    assert np.all(np.isnan(d[0]))
+    assert d[1, 2] == math.inf and d[1, 0] == 8.0
+
+
+# ------------------------------------------------------------------ FP8 pins
+
+def _e4m3_int(q):
+    """e4m3 bytes -> exact integers in units of 2^-9 (every e4m3 value is a
+    multiple of the smallest subnormal 2^-9)."""
+    return np.array([[int(exact.e4m3_code_to_fraction(c) * 512) for c in row] for row in q],
+                    dtype=np.int64)
+
+
+def test_fp8_per_tensor_exact():
+    M, N, K = 3, 5, 256
+    xq, wq, sx, sw = gen.fp8_inputs(M, N, K, "fp8_tensor", seed=17)
+    xb, wb = gen.bits8(xq), gen.bits8(wq)
+    acc = _e4m3_int(xb) @ _e4m3_int(wb).T   # exact, units of 2^-18
+    for scales in ((1.0, 1.0), (float(sx), float(sw))):
+        out = oracle.gemm_fp8_tensor(xb, wb, *scales)
+        s = Fraction(float(np.float32(scales[0]))) * Fraction(float(np.float32(scales[1])))
+        for m in range(M):
+            for n in range(N):
+                want = exact.round_fraction(Fraction(int(acc[m, n]), 2 ** 18) * s, **exact.BF16)
+                assert exact.bf16_code_to_fraction(out[m, n]) == want
+
+
+def test_fp8_mx_exact_and_invariants():
+    M, N, K = 3, 4, 128
+    xq, wq, xe, we = gen.fp8_inputs(M, N, K, "fp8_mx", seed=23)
+    rng = np.random.default_rng(5)
+    xe = torch.from_numpy(rng.integers(120, 135, size=(M, K // 32)).astype(np.uint8))
+    we = torch.from_numpy(rng.integers(118, 131, size=(N, K // 32)).astype(np.uint8))
+    xb, wb, xeb, web = gen.bits8(xq), gen.bits8(wq), gen.bits8(xe), gen.bits8(we)
+    xi, wi = _e4m3_int(xb), _e4m3_int(wb)
+    out = oracle.gemm_fp8_mx(xb, wb, xeb, web)
+    for m in range(M):
+        for n in range(N):
+            s = Fraction(0)
+            for blk in range(K // 32):
+                part = int(np.dot(xi[m, blk * 32:(blk + 1) * 32], wi[n, blk * 32:(blk + 1) * 32]))
+                s += Fraction(part, 2 ** 18) * Fraction(2) ** (int(xeb[m, blk]) - 127) \
+                    * Fraction(2) ** (int(web[n, blk]) - 127)
+            want = exact.round_fraction(s, **exact.BF16)
+            assert exact.bf16_code_to_fraction(out[m, n]) == want
+    # raising every x-block exponent of row m by j scales row m by exactly 2^j
+    xe2 = xeb.copy()
+    xe2[1] += 3
+    out2 = oracle.gemm_fp8_mx(xb, wb, xe2, web)
+    d, d2 = _decode(out), _decode(out2)
+    assert np.array_equal(d2[1], d[1] * 8) and np.array_equal(d2[[0, 2]], d[[0, 2]])
+    # all exponents 127 is per-tensor with unit scales
+    ones_x = np.full_like(xeb, 127)
+    ones_w = np.full_like(web, 127)
+    assert np.array_equal(oracle.gemm_fp8_mx(xb, wb, ones_x, ones_w),
+                          oracle.gemm_fp8_tensor(xb, wb, 1.0, 1.0))
+
+
+def test_no_intermediate_fp32_rounding():
+    # 1.5 * (1 + 2^-7) = 1.51171875 is exactly the midpoint of the bf16
+    # neighbours 1.5078125 and 1.515625.  Subtracting 2^-30 (from
+    # 2^-15 * -2^-15) puts the exact sum just below it, so one correct
+    # rounding gives 1.5078125.  An fp32 intermediate would snap the sum
+    # back onto the midpoint and the tie would go to 1.515625.
+    x = torch.tensor([[1.5, 2.0 ** -15]], dtype=torch.bfloat16)
+    w = torch.tensor([[1.0078125, -(2.0 ** -15)]], dtype=torch.bfloat16)
+    out = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w))
+    assert out[0, 0] == 0x3FC1
+    w2 = torch.tensor([[1.0078125, 2.0 ** -15]], dtype=torch.bfloat16)
+    assert oracle.gemm_bf16(gen.bits16(x), gen.bits16(w2))[0, 0] == 0x3FC2
