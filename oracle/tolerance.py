@@ -42,8 +42,8 @@ def check(gpu, ref, K, out_f32=False):
         return False, f"shape {g.shape} != {r.shape}"
     nan_r, nan_g = np.isnan(r), np.isnan(g)
     if not np.array_equal(nan_r, nan_g):
-        i = np.argwhere(nan_r != nan_g)[0]
-        return False, f"NaN mismatch at {tuple(i)}: gpu={g[tuple(i)]} ref={r[tuple(i)]}"
+        i = tuple(int(v) for v in np.argwhere(nan_r != nan_g)[0])
+        return False, f"NaN mismatch at {i}: gpu={g[i]} ref={r[i]}"
     inf_r = np.isinf(r)
     if not np.array_equal(inf_r, np.isinf(g)) or not np.array_equal(r[inf_r], g[inf_r]):
         return False, "Inf mismatch"
@@ -52,7 +52,7 @@ def check(gpu, ref, K, out_f32=False):
     err = np.abs(g - r)
     bad = fin & ~(err <= b)
     if bad.any():
-        i = tuple(np.argwhere(bad)[0])
+        i = tuple(int(v) for v in np.argwhere(bad)[0])
         return False, (f"{int(bad.sum())} of {r.size} elements out of tolerance; first at {i}: "
                        f"gpu={g[i]!r} ref={r[i]!r} err={err[i]:.3e} bound={b[i]:.3e}")
     worst = float(np.max(err[fin] / np.maximum(b[fin], 1e-300))) if fin.any() else 0.0
