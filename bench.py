@@ -1,0 +1,245 @@
+"""Benchmark of the small-M bf16 GEMM on one MI355X.
+
+Workload (one "step"): the router GEMM out[M,256] = x[M,7168] @ W[256,7168]^T
+for M = 1, 2, ..., 16, one call each, back to back on one stream.  bf16 in
+and out, fp32 accumulation, no bias.  Inputs are seeded synthetic data
+(x ~ N(0,1), W ~ N(0,1/K), drawn by torch's device generator) resident in
+HBM before timing starts.
+
+Cold weights: every call reads a different W from a pool of distinct
+(x, W, out) sets whose W bytes total >= 1 GiB (> 4x the 256 MB Infinity
+Cache), so no call finds its W in any cache.  The calls of a step are
+captured in HIP graphs (one per step of the pool's rotation) and replayed;
+HIP events on the launch stream bracket the timed replays.
+
+value = algorithmic bytes of the step / time of the step, in GB/s, with
+bytes per call = N*K*2 + M*K*2 + M*N*2 (W, x, out).
+
+Also reported: per-M microseconds per call (graphs of one M over the whole
+pool), the empty-kernel and read-stream floors at the same shape, the
+roofline line of the dominant kernel, and the CPU oracle's time on a
+bounded sample of the same workload (its outputs also checked against the
+GPU's).
+
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu]
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/call and achieved HBM GB/s (% of peak), bf16 M=1–16, K=7168, N=256"
+PEAK_GBS = 8000.0
+K_DIM, N_DIM, M_VALUES = 7168, 256, list(range(1, 17))
+POOL_BYTES = 1 << 30
+
+
+def call_bytes(M, N=N_DIM, K=K_DIM):
+    return N * K * 2 + M * K * 2 + M * N * 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the GEMM is replicated or sharded per GPU with no collective; see the design notes)",
+              file=sys.stderr)
+        return 2
+    import torch
+
+    import latency_skinny_gemm_amd as skg
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    floors = ctypes.CDLL(os.path.join(ROOT, "latency_skinny_gemm_amd", "libskinny_floors.so"))
+    floors.skinny_floor_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    floors.skinny_floor_read.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.Stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    # ---------------------------------------------------------------- pool
+    w_bytes = N_DIM * K_DIM * 2
+    calls = len(M_VALUES)
+    n_slots = -(-POOL_BYTES // w_bytes)
+    n_slots = -(-n_slots // calls) * calls  # whole steps
+    g = torch.Generator(device=dev)
+    g.manual_seed(20261202)
+    Ms = max(M_VALUES)
+    W = torch.empty((n_slots, N_DIM, K_DIM), dtype=torch.bfloat16, device=dev)
+    X = torch.empty((n_slots, Ms, K_DIM), dtype=torch.bfloat16, device=dev)
+    OUT = torch.zeros((n_slots, Ms, N_DIM), dtype=torch.bfloat16, device=dev)
+    for i in range(n_slots):
+        W[i].copy_(torch.randn((N_DIM, K_DIM), generator=g, device=dev) * (K_DIM ** -0.5))
+        X[i].copy_(torch.randn((Ms, K_DIM), generator=g, device=dev))
+    torch.cuda.synchronize()
+
+    plans = {M: skg.plan(M, N_DIM, K_DIM) for M in M_VALUES}
+    kind_name = {skg.KIND_DOT: "dot", skg.KIND_SPLITK: "splitk"}
+
+    def launch(slot, M):
+        rc = skg.lib().skinny_gemm_bf16(X[slot].data_ptr(), W[slot].data_ptr(), None, None,
+                                        OUT[slot].data_ptr(), M, N_DIM, K_DIM, sptr)
+        if rc != 0:
+            raise skg.SkinnyGemmError(rc, f"skinny_gemm_bf16 M={M}")
+
+    def capture(fn):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            fn()
+        return gr
+
+    def time_graphs(graphs, reps, warm):
+        with torch.cuda.stream(stream):
+            for i in range(warm):
+                graphs[i % len(graphs)].replay()
+            stream.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                graphs[i % len(graphs)].replay()
+            e1.record(stream)
+            e1.synchronize()
+        return e0.elapsed_time(e1) / 1e3  # seconds
+
+    with torch.cuda.stream(stream):
+        skg.reserve(Ms, N_DIM, 256)
+        # eager warm-up of every plan (and a first correctness sample below)
+        for M in M_VALUES:
+            launch(0, M)
+    stream.synchronize()
+
+    # ---------------------------------------------------------------- headline
+    n_step_graphs = n_slots // calls
+    step_graphs = []
+    for gi in range(n_step_graphs):
+        step_graphs.append(capture(lambda gi=gi: [launch(gi * calls + j, M)
+                                                  for j, M in enumerate(M_VALUES)]))
+    torch.cuda.synchronize()
+    t_steps = time_graphs(step_graphs, args.steps, args.warmup)
+    ms_per_step = t_steps / args.steps * 1e3
+    step_bytes = sum(call_bytes(M) for M in M_VALUES)
+    value = step_bytes / (t_steps / args.steps) / 1e9
+
+    # ---------------------------------------------------------------- per M
+    per_m = {}
+    for M in M_VALUES:
+        gr = capture(lambda M=M: [launch(s, M) for s in range(n_slots)])
+        t = time_graphs([gr], 3, 1)
+        us = t / (3 * n_slots) * 1e6
+        per_m[M] = {"us_per_call": round(us, 3), "GBps": round(call_bytes(M) / (us * 1e-6) / 1e9, 1),
+                    "kernel": kind_name[plans[M].kind], "plan": {k: v for k, v in plans[M].as_dict().items()
+                                                                if k in ("threads", "cols", "splits", "depth", "reduce", "grid")}}
+        del gr
+
+    # ---------------------------------------------------------------- floors
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+
+    def floor_empty():
+        for _ in range(n_slots):
+            floors.skinny_floor_empty(256, 256, sptr)
+
+    def floor_read():
+        for s in range(n_slots):
+            floors.skinny_floor_read(ctypes.c_void_p(W[s].data_ptr()), N_DIM, K_DIM * 2, 256,
+                                     ctypes.c_void_p(sink.data_ptr()), sptr)
+
+    t_empty = time_graphs([capture(floor_empty)], 3, 1) / (3 * n_slots) * 1e6
+    t_read = time_graphs([capture(floor_read)], 3, 1) / (3 * n_slots) * 1e6
+
+    # ---------------------------------------------------------------- roofline
+    by_kind = {}
+    for M in M_VALUES:
+        k = per_m[M]["kernel"]
+        b, t, n = by_kind.get(k, (0, 0.0, 0))
+        by_kind[k] = (b + call_bytes(M), t + per_m[M]["us_per_call"], n + 1)
+    dom = max(by_kind, key=lambda k: by_kind[k][1])
+    b, t, n = by_kind[dom]
+    achieved = b / (t * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                "kernel": dom, "launches_per_step": n,
+                "avg_launch_us": round(t / n, 3),
+                "algorithmic_bytes_per_launch": round(b / n)}
+
+    # ---------------------------------------------------------------- CPU oracle
+    cpu = None
+    parity = None
+    if not args.no_cpu:
+        import oracle
+        from oracle import tolerance
+
+        threads = min(16, len(os.sched_getaffinity(0)))
+        x0 = X[0].cpu()
+        w0 = W[0].cpu()
+        with torch.cuda.stream(stream):
+            for M in M_VALUES:
+                launch(0, M)  # leaves out[0] = the M = 16 result for slot 0
+        stream.synchronize()
+        xb = x0.view(torch.int16).numpy().view("uint16")
+        wb = w0.view(torch.int16).numpy().view("uint16")
+        worst = "ok"
+        reps, t_cpu, done_bytes = 0, 0.0, 0
+        while t_cpu < args.cpu_seconds or reps == 0:
+            for M in M_VALUES:
+                t0 = time.perf_counter()
+                ref = oracle.gemm_bf16(xb[:M], wb, threads=threads)
+                t_cpu += time.perf_counter() - t0
+                done_bytes += call_bytes(M)
+                if reps == 0:
+                    with torch.cuda.stream(stream):
+                        launch(0, M)
+                    stream.synchronize()
+                    ok, msg = tolerance.check(OUT[0, :M].cpu(), ref, K_DIM)
+                    if not ok:
+                        worst = f"M={M}: {msg}"
+            reps += 1
+        parity = worst
+        cpu = {"value": round(done_bytes / t_cpu / 1e9, 4), "unit": "GB/s",
+               "cores": oracle.threads_used(threads), "kind": "oracle",
+               "sample": f"{reps} pass(es) over M=1..16 at K=7168, N=256 (pool slot 0); "
+                         f"{t_cpu:.1f} s of oracle time; us/call at M=1: "
+                         f"{t_cpu / reps / len(M_VALUES) * 1e6:.0f} (mean over M)"}
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16 router GEMM out[M,256]=x[M,7168]@W[256,7168]^T, "
+                               "M=1..16 one call each per step, cold W (pool >= 1 GiB)",
+                   "K": K_DIM, "N": N_DIM, "M": "1-16", "calls_per_step": calls,
+                   "pool_slots": n_slots, "pool_W_bytes": n_slots * w_bytes},
+        "us_per_call_mean": round(ms_per_step * 1e3 / calls, 3),
+        "frac_of_peak": round(value / PEAK_GBS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "floors": {"empty_kernel_us": round(t_empty, 3), "read_stream_us": round(t_read, 3),
+                   "read_stream_GBps": round(w_bytes / (t_read * 1e-6) / 1e9, 1),
+                   "shape": "256 workgroups x 256 threads; read: 256 rows x 14336 B"},
+        "per_m": per_m,
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

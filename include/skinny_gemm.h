@@ -1,0 +1,176 @@
+/*
+ * skinny_gemm.h -- C ABI of the small-M ("skinny") GEMM library for AMD
+ * MI355X (gfx950).
+ *
+ * The operation (every entry point):
+ *
+ *     out[m, n] = bf16( sum_k x[m, k] * W[n, k]  (+ bias[n]) )
+ *
+ * with fp32 accumulation and one rounding (round-to-nearest-even) of the
+ * fp32 result to bf16, the bias added in fp32 before that rounding.
+ * Defined on the "sglang PR #30117" page, key source snippet (kernel header
+ * comment: x[M,K] times weight[N,K] transposed, optional bias[N], bf16
+ * in/out, fp32 accumulation) and used as the MoE router GEMM on the
+ * "vllm PR #42562" page (summary and impl. items 1-3).
+ *
+ * Layouts.  Every tensor is dense and row-major with no strides:
+ *   x[M, K], W[N, K], bias[N], out[M, N].
+ * W[N, K] row-major is the same memory as the column-major [K, N] weight of
+ * the "sglang PR #28333" page's FP8 snippet.  Callers make tensors
+ * contiguous; the library never reads strides (the "sglang PR #30117"
+ * review found leading-dimension detection error-prone).
+ *
+ * Domain.  1 <= M <= 128, N >= 1, K >= 8 and K % 8 == 0 (bf16) so every row
+ * starts 16-byte aligned (the "vllm PR #48774" page keeps only router shapes
+ * with K a multiple of 8; the "vllm PR #42562" review settles on 16-byte
+ * alignment for 128-bit loads).  M == 0 or N == 0 is a successful no-op.
+ * Anything else out of domain returns SKG_ERR_UNSUPPORTED: there is no
+ * silent fallback (the "sglang PR #34042" page: an explicit request errors
+ * instead of falling back).
+ *
+ * Pointers.  All tensor pointers are DEVICE pointers on the current HIP
+ * device.  x and W must be 16-byte aligned; bias and out 2-byte aligned.
+ * out must not overlap x, W or bias.  The caller owns every tensor; the
+ * library never frees or retains them past the call.
+ *
+ * Streams.  Work is enqueued on `stream` (0 = the null stream) and the call
+ * returns without synchronising.  Completion follows stream order.  A call
+ * allocates nothing once workspace is reserved (skinny_gemm_reserve), so it
+ * may be captured into a HIP graph.
+ *
+ * Errors.  Every entry point returns SKG_OK (0) or a negative SKG_ERR_*.
+ * Arguments are validated on the host before any HIP call, so a rejected
+ * call touches no device state.  SKG_ERR_HIP reports a launch failure
+ * (hipGetLastError after the launch).
+ *
+ * Threads.  The planner and its table are immutable; calls from several
+ * host threads are safe.  Split-K calls use a workspace owned per (device,
+ * stream): calls that overlap in time on the same stream's workspace race,
+ * calls on different streams do not.
+ */
+#ifndef SKINNY_GEMM_H
+#define SKINNY_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ status codes */
+#define SKG_OK 0
+#define SKG_ERR_INVALID_ARG (-1) /* NULL pointer, negative size, overlap, bad plan */
+#define SKG_ERR_ALIGNMENT (-2)   /* pointer not aligned as required above */
+#define SKG_ERR_UNSUPPORTED (-3) /* outside the domain, or a mode not built */
+#define SKG_ERR_WORKSPACE (-4)   /* split-K workspace too small during graph capture */
+#define SKG_ERR_HIP (-5)         /* HIP reported an error */
+
+/* ------------------------------------------------------------ enums */
+#define SKG_DTYPE_BF16 0
+#define SKG_DTYPE_FP8 1
+
+#define SKG_FP8_PER_TENSOR 1
+#define SKG_FP8_MX32 2
+
+#define SKG_KIND_DOT 1    /* dot-product kernel: whole K per workgroup */
+#define SKG_KIND_SPLITK 2 /* MFMA kernel, K split over workgroups */
+
+#define SKG_REDUCE_NONE 0  /* splits == 1: no cross-workgroup reduction */
+#define SKG_REDUCE_LAST 1  /* the last workgroup to finish a tile reduces it */
+#define SKG_REDUCE_KERNEL 2 /* a second kernel reduces every tile */
+
+#define SKG_MAX_M 128
+
+/* FP8 scales (host struct; its pointers are DEVICE pointers).
+ *  mode SKG_FP8_PER_TENSOR: sx, sw -> one fp32 each (the "sglang PR #28333"
+ *    page's bmm_fp8 call: x_scale and weight_scale as one-element tensors);
+ *    out = bf16(sx * sw * sum(xq * wq) + bias), the scale product applied once.
+ *  mode SKG_FP8_MX32: x_e8m0[M, K/32], w_e8m0[N, K/32], row-major, one e8m0
+ *    exponent per 32 consecutive K of a row (the MX block scaling of the
+ *    "sglang PR #34042" page, stored plainly instead of swizzled). */
+typedef struct skinny_fp8_scales {
+    int mode;
+    const float *sx;
+    const float *sw;
+    const uint8_t *x_e8m0;
+    const uint8_t *w_e8m0;
+} skinny_fp8_scales;
+
+/* A launch plan: what the dispatcher chose for one (M, N, K, dtype).
+ * The "vllm PR #42562" and "vllm PR #48774" pages key their compiled
+ * kernels by (backend, M, K, block size, split_k, stages); this is the same
+ * idea as a plain struct.  Fields marked (derived) are filled in by the
+ * library from the others. */
+typedef struct SkgPlan {
+    int kind;     /* SKG_KIND_DOT or SKG_KIND_SPLITK */
+    int threads;  /* workgroup size, a multiple of 64, <= 1024 */
+    int cols;     /* DOT: output columns per workgroup (1, 2);
+                     SPLITK: 16-column blocks per workgroup (1, 2, 4) */
+    int splits;   /* SPLITK: number of K chunks S (>= 1); DOT: 1 */
+    int depth;    /* SPLITK: 32-wide K steps a wave keeps in flight (1, 2, 4, 8);
+                     DOT: 16-byte vectors per thread per column (derived) */
+    int reduce;   /* SKG_REDUCE_*; NONE iff splits == 1 */
+    int k_chunk;  /* (derived) SPLITK: K elements per split, multiple of 32 */
+    int m_tiles;  /* (derived) SPLITK: ceil(M / 16) */
+    int grid;     /* (derived) workgroups in the main launch */
+    int from_table; /* (derived) 1 when the tuned table supplied the plan */
+} SkgPlan;
+
+/* bf16 GEMM.  `scales` must be NULL (it exists so both entry points share one
+ * argument order).  Picks a plan with skinny_gemm_plan and launches it. */
+int skinny_gemm_bf16(const void *x, const void *W, const void *bias, const void *scales,
+                     void *out, int M, int N, int K, hipStream_t stream);
+
+/* FP8 e4m3fn GEMM with bf16 bias and output; `scales` is a HOST pointer to
+ * the struct above.  K % 16 == 0 (per-tensor) or K % 32 == 0 (MX).
+ * Returns SKG_ERR_UNSUPPORTED for a mode this build does not implement. */
+int skinny_gemm_fp8(const void *x, const void *W, const void *bias,
+                    const skinny_fp8_scales *scales, void *out, int M, int N, int K,
+                    hipStream_t stream);
+
+/* The dispatcher's decision for (M, N, K, dtype), written to *plan; no HIP
+ * call.  The "vllm PR #48774" page's rule: a tuned (K, N) -> {M: config}
+ * table first, else the default (dot product when M <= 4 or K < 2048, else
+ * split-K).  Our table comes from a sweep on MI355X.  Returns SKG_OK, or the
+ * error the GEMM call would return for these sizes. */
+int skinny_gemm_plan(int M, int N, int K, int dtype, SkgPlan *plan);
+
+/* Checks a caller-made plan for (M, N, K, dtype) and fills its derived
+ * fields.  SKG_ERR_INVALID_ARG if the plan cannot cover the problem or
+ * exceeds a kernel limit.  No HIP call. */
+int skinny_gemm_plan_complete(int M, int N, int K, int dtype, SkgPlan *plan);
+
+/* bf16 GEMM with a caller-made plan (completed as above): for sweeps and
+ * tests that must exercise a given kernel.  Same contract otherwise. */
+int skinny_gemm_bf16_planned(const void *x, const void *W, const void *bias, void *out,
+                             int M, int N, int K, const SkgPlan *plan, hipStream_t stream);
+
+/* Reserves split-K workspace for `stream` on the current device, large
+ * enough for any plan with M <= max_M, N <= max_N and splits <= max_S.
+ * Allocates (hipMalloc) and zeroes the tile counters; call it before graph
+ * capture.  Outside capture a call that needs more grows the workspace
+ * itself; during capture it returns SKG_ERR_WORKSPACE instead. */
+int skinny_gemm_reserve(int max_M, int max_N, int max_S, hipStream_t stream);
+
+/* Frees every workspace of every device after a device synchronisation.
+ * No call may be in flight. */
+int skinny_gemm_release_all(void);
+
+/* Human-readable name of a status code (static storage). */
+const char *skinny_gemm_status_string(int status);
+
+/* skinny_gemm_plan for a device with `num_cus` compute units, without
+ * touching any device: the dispatch logic as a pure function, for tests
+ * with a made-up device.  The tuned table applies only when num_cus is the
+ * MI355X's 256; other counts take the default rule, sized to num_cus.
+ * skinny_gemm_plan is this function at 256 CUs. */
+int skinny_gemm_plan_on(int M, int N, int K, int dtype, int num_cus, SkgPlan *plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKINNY_GEMM_H */

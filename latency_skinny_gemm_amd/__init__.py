@@ -1,0 +1,203 @@
+"""Python binding of the small-M GEMM library (libskinny_gemm.so).
+
+Argument marshalling only: every step of the GEMM runs in the library's HIP
+kernels.  torch supplies device memory and the current stream.  When the
+library is not built, every call raises: there is no fallback.
+
+    out[M, N] = bf16( x[M, K] @ W[N, K]^T (+ bias[N]) ), fp32 accumulation.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = ["SkgPlan", "SkinnyGemmError", "gemm_bf16", "gemm_bf16_planned", "plan", "plan_on",
+           "plan_complete", "reserve", "release_all", "status_string", "library_path",
+           "KIND_DOT", "KIND_SPLITK", "REDUCE_NONE", "REDUCE_LAST", "REDUCE_KERNEL",
+           "DTYPE_BF16", "DTYPE_FP8"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libskinny_gemm.so")
+
+# mirrors of include/skinny_gemm.h
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_ALIGNMENT = -2
+ERR_UNSUPPORTED = -3
+ERR_WORKSPACE = -4
+ERR_HIP = -5
+DTYPE_BF16 = 0
+DTYPE_FP8 = 1
+FP8_PER_TENSOR = 1
+FP8_MX32 = 2
+KIND_DOT = 1
+KIND_SPLITK = 2
+REDUCE_NONE = 0
+REDUCE_LAST = 1
+REDUCE_KERNEL = 2
+MAX_M = 128
+
+
+class SkgPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in
+                ("kind", "threads", "cols", "splits", "depth", "reduce",
+                 "k_chunk", "m_tiles", "grid", "from_table")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+    def __repr__(self):
+        return "SkgPlan(" + ", ".join(f"{k}={v}" for k, v in self.as_dict().items()) + ")"
+
+
+class SkinnyGemmError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class Fp8Scales(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int), ("sx", ctypes.c_void_p), ("sw", ctypes.c_void_p),
+                ("x_e8m0", ctypes.c_void_p), ("w_e8m0", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(hipcc for gfx950).  There is no fallback implementation.")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    PP = ctypes.POINTER(SkgPlan)
+    L.skinny_gemm_bf16.argtypes = [P, P, P, P, P, I, I, I, P]
+    L.skinny_gemm_bf16.restype = I
+    L.skinny_gemm_bf16_planned.argtypes = [P, P, P, P, I, I, I, PP, P]
+    L.skinny_gemm_bf16_planned.restype = I
+    L.skinny_gemm_fp8.argtypes = [P, P, P, ctypes.POINTER(Fp8Scales), P, I, I, I, P]
+    L.skinny_gemm_fp8.restype = I
+    L.skinny_gemm_plan.argtypes = [I, I, I, I, PP]
+    L.skinny_gemm_plan.restype = I
+    L.skinny_gemm_plan_on.argtypes = [I, I, I, I, I, PP]
+    L.skinny_gemm_plan_on.restype = I
+    L.skinny_gemm_plan_complete.argtypes = [I, I, I, I, PP]
+    L.skinny_gemm_plan_complete.restype = I
+    L.skinny_gemm_reserve.argtypes = [I, I, I, P]
+    L.skinny_gemm_reserve.restype = I
+    L.skinny_gemm_release_all.argtypes = []
+    L.skinny_gemm_release_all.restype = I
+    L.skinny_gemm_status_string.argtypes = [I]
+    L.skinny_gemm_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def lib():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _load()
+
+
+def status_string(status):
+    return _load().skinny_gemm_status_string(int(status)).decode()
+
+
+def _check(status, what):
+    if status != OK:
+        raise SkinnyGemmError(status, what)
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_tensors(x, W, bias, out, dtype):
+    if x.dim() != 2 or W.dim() != 2 or x.shape[1] != W.shape[1]:
+        raise ValueError(f"x[M,K] and W[N,K] expected, got {tuple(x.shape)} and {tuple(W.shape)}")
+    M, K = x.shape
+    N = W.shape[0]
+    for name, t in (("x", x), ("W", W), ("bias", bias), ("out", out)):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (the library takes no strides)")
+    if x.dtype != dtype or W.dtype != dtype:
+        raise TypeError(f"x and W must be {dtype}, got {x.dtype} and {W.dtype}")
+    if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (N,)):
+        raise TypeError("bias must be bf16 [N]")
+    if out is not None and (out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N)):
+        raise TypeError("out must be bf16 [M, N]")
+    return M, N, K
+
+
+def gemm_bf16(x, W, bias=None, out=None, stream=None):
+    """out[M,N] = x[M,K] @ W[N,K]^T (+ bias), bf16, on the library's plan."""
+    M, N, K = _check_tensors(x, W, bias, out, torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    rc = _load().skinny_gemm_bf16(_ptr(x), _ptr(W), _ptr(bias), None, _ptr(out), M, N, K,
+                                  _stream_ptr(stream))
+    _check(rc, f"skinny_gemm_bf16(M={M}, N={N}, K={K})")
+    return out
+
+
+def gemm_bf16_planned(x, W, p, bias=None, out=None, stream=None):
+    """As gemm_bf16, with a caller-made SkgPlan (completed by the library)."""
+    M, N, K = _check_tensors(x, W, bias, out, torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    rc = _load().skinny_gemm_bf16_planned(_ptr(x), _ptr(W), _ptr(bias), _ptr(out), M, N, K,
+                                          ctypes.byref(p), _stream_ptr(stream))
+    _check(rc, f"skinny_gemm_bf16_planned(M={M}, N={N}, K={K}, {p})")
+    return out
+
+
+def make_plan(kind, threads, cols=1, splits=1, depth=0, reduce=REDUCE_NONE):
+    p = SkgPlan()
+    p.kind, p.threads, p.cols, p.splits, p.depth, p.reduce = kind, threads, cols, splits, depth, reduce
+    return p
+
+
+def plan(M, N, K, dtype=DTYPE_BF16):
+    p = SkgPlan()
+    _check(_load().skinny_gemm_plan(M, N, K, dtype, ctypes.byref(p)), "skinny_gemm_plan")
+    return p
+
+
+def plan_on(M, N, K, num_cus, dtype=DTYPE_BF16):
+    p = SkgPlan()
+    _check(_load().skinny_gemm_plan_on(M, N, K, dtype, num_cus, ctypes.byref(p)),
+           "skinny_gemm_plan_on")
+    return p
+
+
+def plan_complete(M, N, K, p, dtype=DTYPE_BF16):
+    """Completes a copy of p; raises SkinnyGemmError if it is not valid."""
+    q = SkgPlan.from_buffer_copy(p)
+    _check(_load().skinny_gemm_plan_complete(M, N, K, dtype, ctypes.byref(q)),
+           "skinny_gemm_plan_complete")
+    return q
+
+
+def reserve(max_M, max_N, max_S, stream=None):
+    _check(_load().skinny_gemm_reserve(max_M, max_N, max_S, _stream_ptr(stream)),
+           "skinny_gemm_reserve")
+
+
+def release_all():
+    _check(_load().skinny_gemm_release_all(), "skinny_gemm_release_all")

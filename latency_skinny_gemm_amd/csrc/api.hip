@@ -1,0 +1,230 @@
+// api.hip -- the C ABI: argument checks, workspace, and launches.
+//
+// Checks run on the host before any HIP call, so a rejected call changes no
+// device state (and the checks run on machines without a GPU).  The dtype
+// guards follow the "vllm PR #42562" review (bf16 weights and activations
+// only on the bf16 path); the "sglang PR #34042" page's rule that an
+// explicit request errors rather than falling back is why every unsupported
+// case returns a status instead of routing elsewhere.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "internal.h"
+
+namespace skg {
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlap(const void *a, size_t abytes, const void *b, size_t bbytes) {
+    if (!a || !b) return false;
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+// Pointer checks shared by the bf16 entry points (sizes already checked and
+// M, N > 0).
+int check_pointers_bf16(const void *x, const void *W, const void *bias, void *out, int M, int N,
+                        int K) {
+    if (!x || !W || !out) return SKG_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(W, 16)) return SKG_ERR_ALIGNMENT;
+    if (!aligned(out, 2) || (bias && !aligned(bias, 2))) return SKG_ERR_ALIGNMENT;
+    const size_t ob = (size_t)M * N * 2;
+    if (overlap(out, ob, x, (size_t)M * K * 2) || overlap(out, ob, W, (size_t)N * K * 2) ||
+        overlap(out, ob, bias, (size_t)N * 2))
+        return SKG_ERR_INVALID_ARG;
+    return SKG_OK;
+}
+
+// ---------------------------------------------------------------- workspace
+// Split-K partials (fp32 [S][M][N]) and one ticket counter per output tile,
+// owned per (device, stream).  Counters are zero at rest: the workgroup that
+// reduces a tile sets its counter back to zero.
+struct Workspace {
+    int device;
+    hipStream_t stream;
+    float *ws;
+    size_t ws_floats;
+    unsigned *tickets;
+    size_t n_tickets;
+};
+
+std::mutex g_mu;
+std::vector<Workspace> g_ws;
+std::vector<void *> g_retired;  // replaced buffers, freed by release_all
+
+int grow(Workspace &w, size_t floats, size_t tickets) {
+    if (floats > w.ws_floats) {
+        float *p = nullptr;
+        if (hipMalloc((void **)&p, floats * sizeof(float)) != hipSuccess) return SKG_ERR_HIP;
+        if (w.ws) g_retired.push_back(w.ws);
+        w.ws = p;
+        w.ws_floats = floats;
+    }
+    if (tickets > w.n_tickets) {
+        unsigned *t = nullptr;
+        if (hipMalloc((void **)&t, tickets * sizeof(unsigned)) != hipSuccess) return SKG_ERR_HIP;
+        if (hipMemset(t, 0, tickets * sizeof(unsigned)) != hipSuccess) return SKG_ERR_HIP;
+        if (w.tickets) g_retired.push_back(w.tickets);
+        w.tickets = t;
+        w.n_tickets = tickets;
+    }
+    return SKG_OK;
+}
+
+Workspace *find(int device, hipStream_t stream) {
+    for (auto &w : g_ws)
+        if (w.device == device && w.stream == stream) return &w;
+    return nullptr;
+}
+
+// Workspace for this (device, stream) with room for the request.  Grows it
+// outside graph capture; during capture a short workspace is an error.
+int acquire(hipStream_t stream, size_t floats, size_t tickets, float **ws, unsigned **tk) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SKG_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    Workspace *w = find(dev, stream);
+    if (!w || w->ws_floats < floats || w->n_tickets < tickets) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return SKG_ERR_HIP;
+        if (cs != hipStreamCaptureStatusNone) return SKG_ERR_WORKSPACE;
+        if (!w) {
+            g_ws.push_back(Workspace{dev, stream, nullptr, 0, nullptr, 0});
+            w = &g_ws.back();
+        }
+        // no kernel of this stream may still use a buffer we retire
+        if (hipStreamSynchronize(stream) != hipSuccess) return SKG_ERR_HIP;
+        int rc = grow(*w, floats, tickets);
+        if (rc != SKG_OK) return rc;
+    }
+    *ws = w->ws;
+    *tk = w->tickets;
+    return SKG_OK;
+}
+
+int run_bf16(const void *x, const void *W, const void *bias, void *out, int M, int N, int K,
+             const SkgPlan &p, hipStream_t stream) {
+    if (p.kind == SKG_KIND_DOT) {
+        int e = launch_dot(p, x, W, bias, out, M, N, K, stream);
+        return e == (int)hipSuccess ? SKG_OK : SKG_ERR_HIP;
+    }
+    float *ws = nullptr;
+    unsigned *tk = nullptr;
+    if (p.splits > 1) {
+        int rc = acquire(stream, workspace_floats(p, M, N), (size_t)tile_count(p, N), &ws, &tk);
+        if (rc != SKG_OK) return rc;
+    }
+    int e = launch_splitk(p, x, W, bias, out, ws, tk, M, N, K, stream);
+    return e == (int)hipSuccess ? SKG_OK : SKG_ERR_HIP;
+}
+
+}  // namespace
+
+size_t workspace_floats(const SkgPlan &p, int M, int N) {
+    return p.splits > 1 ? (size_t)p.splits * M * N : 0;
+}
+
+int tile_count(const SkgPlan &p, int N) {
+    return p.kind == SKG_KIND_SPLITK ? (N + 16 * p.cols - 1) / (16 * p.cols) : 0;
+}
+
+}  // namespace skg
+
+using namespace skg;
+
+extern "C" int skinny_gemm_bf16(const void *x, const void *W, const void *bias,
+                                const void *scales, void *out, int M, int N, int K,
+                                hipStream_t stream) {
+    int rc = check_sizes(M, N, K, SKG_DTYPE_BF16);
+    if (rc != SKG_OK) return rc;
+    if (M == 0 || N == 0) return SKG_OK;
+    if (scales) return SKG_ERR_INVALID_ARG;
+    rc = check_pointers_bf16(x, W, bias, out, M, N, K);
+    if (rc != SKG_OK) return rc;
+    SkgPlan p;
+    rc = skinny_gemm_plan(M, N, K, SKG_DTYPE_BF16, &p);
+    if (rc != SKG_OK) return rc;
+    return run_bf16(x, W, bias, out, M, N, K, p, stream);
+}
+
+extern "C" int skinny_gemm_bf16_planned(const void *x, const void *W, const void *bias, void *out,
+                                        int M, int N, int K, const SkgPlan *plan,
+                                        hipStream_t stream) {
+    int rc = check_sizes(M, N, K, SKG_DTYPE_BF16);
+    if (rc != SKG_OK) return rc;
+    if (M == 0 || N == 0) return SKG_OK;
+    if (!plan) return SKG_ERR_INVALID_ARG;
+    rc = check_pointers_bf16(x, W, bias, out, M, N, K);
+    if (rc != SKG_OK) return rc;
+    SkgPlan p = *plan;
+    rc = complete_plan(M, N, K, SKG_DTYPE_BF16, &p);
+    if (rc != SKG_OK) return rc;
+    return run_bf16(x, W, bias, out, M, N, K, p, stream);
+}
+
+extern "C" int skinny_gemm_fp8(const void *x, const void *W, const void *bias,
+                               const skinny_fp8_scales *scales, void *out, int M, int N, int K,
+                               hipStream_t stream) {
+    (void)stream;
+    int rc = check_sizes(M, N, K, SKG_DTYPE_FP8);
+    if (rc != SKG_OK) return rc;
+    if (M == 0 || N == 0) return SKG_OK;
+    if (!scales || !x || !W || !out) return SKG_ERR_INVALID_ARG;
+    if (scales->mode != SKG_FP8_PER_TENSOR && scales->mode != SKG_FP8_MX32)
+        return SKG_ERR_INVALID_ARG;
+    if (scales->mode == SKG_FP8_MX32 && K % 32 != 0) return SKG_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(out, 2) || (bias && !aligned(bias, 2)))
+        return SKG_ERR_ALIGNMENT;
+    (void)bias;
+    return SKG_ERR_UNSUPPORTED;  // the FP8 kernels are not part of this build yet
+}
+
+extern "C" int skinny_gemm_reserve(int max_M, int max_N, int max_S, hipStream_t stream) {
+    if (max_M < 1 || max_N < 1 || max_S < 1 || max_M > SKG_MAX_M || max_S > kMaxSplits)
+        return SKG_ERR_INVALID_ARG;
+    float *ws = nullptr;
+    unsigned *tk = nullptr;
+    // the most tiles any plan can have: 16-column blocks of max_N
+    return acquire(stream, (size_t)max_S * max_M * max_N, (size_t)(max_N + 15) / 16, &ws, &tk);
+}
+
+extern "C" int skinny_gemm_release_all(void) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    int rc = SKG_OK;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) == hipSuccess) {
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        for (int d = 0; d < ndev; ++d)
+            if (hipSetDevice(d) == hipSuccess && hipDeviceSynchronize() != hipSuccess)
+                rc = SKG_ERR_HIP;
+        (void)hipSetDevice(cur);
+    }
+    for (auto &w : g_ws) {
+        (void)hipSetDevice(w.device);
+        if (w.ws && hipFree(w.ws) != hipSuccess) rc = SKG_ERR_HIP;
+        if (w.tickets && hipFree(w.tickets) != hipSuccess) rc = SKG_ERR_HIP;
+    }
+    for (void *p : g_retired)
+        if (hipFree(p) != hipSuccess) rc = SKG_ERR_HIP;
+    g_ws.clear();
+    g_retired.clear();
+    return rc;
+}
+
+extern "C" const char *skinny_gemm_status_string(int status) {
+    switch (status) {
+    case SKG_OK: return "SKG_OK";
+    case SKG_ERR_INVALID_ARG: return "SKG_ERR_INVALID_ARG";
+    case SKG_ERR_ALIGNMENT: return "SKG_ERR_ALIGNMENT";
+    case SKG_ERR_UNSUPPORTED: return "SKG_ERR_UNSUPPORTED";
+    case SKG_ERR_WORKSPACE: return "SKG_ERR_WORKSPACE";
+    case SKG_ERR_HIP: return "SKG_ERR_HIP";
+    default: return "SKG_ERR_UNKNOWN";
+    }
+}

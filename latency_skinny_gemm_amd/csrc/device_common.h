@@ -1,0 +1,89 @@
+// device_common.h -- small device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skg {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- buffers
+// A raw buffer resource (gfx9 descriptor word 3 = 0x00020000: 32-bit
+// dwords, no swizzle).  A load whose byte offset is at or past num_records
+// returns zeros and touches no memory; kOOB is such an offset for every
+// buffer the planner admits (all are < 2^31 bytes, and offsets added to kOOB
+// stay below 2^32).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr unsigned kOOB = 0x80000000u;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// cache-policy bits of the buffer instruction: bit 1 = nt (streaming)
+constexpr int kCacheDefault = 0;
+constexpr int kCacheStream = 2;
+
+template <int POLICY>
+__device__ __forceinline__ u32x4 load16(Rsrc r, unsigned byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, POLICY);
+}
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_lo(unsigned v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned v) { return __uint_as_float(v & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((unsigned)b << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even.  NaN stays NaN (quiet bit
+// set); overflow carries into the exponent and gives +-inf.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    unsigned u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// acc + sum of the 8 products of two 16-byte bf16 vectors, k ascending,
+// each product exact in fp32 and each addition rounded once (fused).
+__device__ __forceinline__ float dot8_fma(u32x4 a, u32x4 b, float acc) {
+    acc = __builtin_fmaf(bf16_lo(a.x), bf16_lo(b.x), acc);
+    acc = __builtin_fmaf(bf16_hi(a.x), bf16_hi(b.x), acc);
+    acc = __builtin_fmaf(bf16_lo(a.y), bf16_lo(b.y), acc);
+    acc = __builtin_fmaf(bf16_hi(a.y), bf16_hi(b.y), acc);
+    acc = __builtin_fmaf(bf16_lo(a.z), bf16_lo(b.z), acc);
+    acc = __builtin_fmaf(bf16_hi(a.z), bf16_hi(b.z), acc);
+    acc = __builtin_fmaf(bf16_lo(a.w), bf16_lo(b.w), acc);
+    acc = __builtin_fmaf(bf16_hi(a.w), bf16_hi(b.w), acc);
+    return acc;
+}
+
+// ---------------------------------------------------------------- reductions
+// DPP lane moves within a 16-lane row (gfx9 dpp_ctrl encodings).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror: lane 7-i within 8
+constexpr int kDppMirror = 0x140;     // row_mirror: lane 15-i within 16
+
+// Sum over the 64 lanes of a wave, returned in every lane.  A fixed tree:
+// pairs, quads, 8-lane halves and 16-lane rows by DPP, then the four rows
+// by two butterfly shuffles.  Every lane ends with the same bits (each step
+// adds the same two values in either order, and fp addition commutes).
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_mov<kDppQuadSwap1>(v);
+    v += dpp_mov<kDppQuadSwap2>(v);
+    v += dpp_mov<kDppHalfMirror>(v);
+    v += dpp_mov<kDppMirror>(v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+}  // namespace skg

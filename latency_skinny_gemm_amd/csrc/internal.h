@@ -1,0 +1,61 @@
+// internal.h -- declarations shared by the library's translation units.
+// Not installed; the public ABI is include/skinny_gemm.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "skinny_gemm.h"
+
+namespace skg {
+
+// Limits of the kernels as built.
+constexpr int kMaxThreads = 1024;
+constexpr int kDotMaxM = 16;          // dot kernel is instantiated for M = 1..16
+constexpr int kSplitKMaxThreads = 512;
+constexpr int kSplitKMaxLdsFloats = 16384;  // 64 KB of LDS for the wave reduction
+constexpr int kMaxSplits = 256;
+constexpr int kNumCusMI355X = 256;
+constexpr long kMaxBufferBytes = 0x7FFFFFFFL;  // one buffer resource covers < 2 GiB
+
+// DOT: vectors (16 B) per thread per column that the kernel is built for.
+constexpr int kDotVecs[] = {1, 2, 3, 4, 6, 8};
+// Registers a DOT thread holds: C rows of W and M rows of x, V 16-byte
+// vectors each, x counted twice (the compiler widens x to fp32 ahead of
+// use), and C*M accumulators.  Only the 256 architectural VGPRs feed VALU
+// work: a kernel is built only when this is <= 224 and may run 1024-thread
+// workgroups (4 waves per SIMD, 128 VGPRs each) only when it is <= 96.
+// (Checked against the compiler's resource report: no kernel spills.)
+constexpr int dot_regs(int M, int C, int V) { return (2 * M + C) * V * 4 + C * M; }
+constexpr int kDotRegsMax = 224;
+constexpr int dot_max_threads(int M, int C, int V) { return dot_regs(M, C, V) <= 96 ? 1024 : 512; }
+
+// SPLITK per-lane registers: two stages of D steps of (NB + MT) vectors and
+// NB*MT accumulators of 4 (those may live in AGPRs).  Above 224 the kernel
+// is bounded to 256 threads (one wave per SIMD), else 512.
+constexpr int splitk_regs(int MT, int NB, int D) { return 2 * D * (NB + MT) * 4 + NB * MT * 4; }
+constexpr int splitk_max_threads(int MT, int NB, int D) {
+    return splitk_regs(MT, NB, D) > 224 ? 256 : kSplitKMaxThreads;
+}
+constexpr bool splitk_built(int MT, int NB, int D) { return NB * MT <= 32 && D * (NB + MT) <= 40; }
+
+// SPLITK: K steps (32 wide) in flight per wave per stage.
+constexpr int kSplitKDepths[] = {1, 2, 4, 8};
+
+// Host-side validation and planning (plan.cpp).  No HIP calls.
+int check_sizes(int M, int N, int K, int dtype);
+int complete_plan(int M, int N, int K, int dtype, SkgPlan *p);
+int default_plan(int M, int N, int K, int dtype, int num_cus, SkgPlan *p);
+bool table_plan(int M, int N, int K, int dtype, SkgPlan *p);
+
+// Workspace needed by a completed plan (api.cpp).
+size_t workspace_floats(const SkgPlan &p, int M, int N);
+int tile_count(const SkgPlan &p, int N);
+
+// Launchers (kernels_*.hip).  Return a hipError_t as int.
+int launch_dot(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
+               int M, int N, int K, hipStream_t stream);
+int launch_splitk(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
+                  float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream);
+
+}  // namespace skg

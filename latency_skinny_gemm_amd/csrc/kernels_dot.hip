@@ -1,0 +1,165 @@
+// kernels_dot.hip -- dot-product kernel for tiny M (gfx950).
+//
+// The "vllm PR #42562" page (impl. item 1 and the LLBf16Dotprod snippet)
+// gives the idea: one workgroup per output column (expert), the whole K
+// loop unrolled at compile time, 128-bit vector loads of W, a per-token fp32
+// multiply-add, and a shuffle + shared-memory reduction.  Here, on 64-wide
+// waves:
+//  * workgroup b owns C consecutive columns n0 = b*C ...; thread t owns the
+//    16-byte vectors t, t+T, t+2T, ... of K (V of them), so each wave-wide
+//    load instruction covers 1 KB of one W row, coalesced;
+//  * every load of W (streaming, non-temporal) and of x is issued before
+//    the first multiply: the whole per-workgroup slice is in flight at once;
+//  * vectors past K read as zeros through the buffer resource's range
+//    check, so there is no scalar tail loop (K % 8 == 0 always holds);
+//  * the per-thread sums are reduced over the wave by DPP row moves and two
+//    shuffles, then over the waves through LDS in wave order, then bias is
+//    added in fp32 and the sum is rounded once to bf16.
+// Every reduction order is fixed: the result is bitwise reproducible for a
+// given plan and input.
+#include "device_common.h"
+#include "internal.h"
+
+namespace skg {
+
+template <int M, int C, int V>
+__global__ void __launch_bounds__((dot_max_threads(M, C, V)))
+    dot_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
+               const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int N, int K) {
+    const int T = blockDim.x;
+    const int t = threadIdx.x;
+    const int n0 = blockIdx.x * C;
+    const int ncols = min(C, N - n0);
+    const unsigned rowb = (unsigned)K * 2u;
+    const Rsrc wr = make_rsrc(W + (size_t)n0 * K, (unsigned)ncols * rowb);
+    const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
+    const int K8 = K >> 3;
+
+    u32x4 wv[C][V];
+    u32x4 xv[M][V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int v = t + i * T;
+        const unsigned off = v < K8 ? (unsigned)v * 16u : kOOB;
+#pragma unroll
+        for (int c = 0; c < C; ++c) wv[c][i] = load16<kCacheStream>(wr, off + (unsigned)c * rowb);
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int v = t + i * T;
+        const unsigned off = v < K8 ? (unsigned)v * 16u : kOOB;
+#pragma unroll
+        for (int m = 0; m < M; ++m) xv[m][i] = load16<kCacheDefault>(xr, off + (unsigned)m * rowb);
+    }
+
+    float acc[C][M];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[c][m] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[c][m] = dot8_fma(xv[m][i], wv[c][i], acc[c][m]);
+
+    __shared__ float red[kMaxThreads / 64][C * M];
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
+    const int lane = t & 63;
+    const int nw = T >> 6;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float s = wave_sum(acc[c][m]);
+            if (lane == 0) red[wave][c * M + m] = s;
+        }
+    __syncthreads();
+    if (t < C * M) {
+        const int c = t / M;
+        const int m = t - c * M;
+        const int n = n0 + c;
+        float s = red[0][t];
+        for (int w = 1; w < nw; ++w) s += red[w][t];
+        if (n < N) {
+            if (bias) s += bf16_to_f32(bias[n]);
+            out[(size_t)m * N + n] = f32_to_bf16_rne(s);
+        }
+    }
+}
+
+namespace {
+
+typedef int (*DotLaunch)(const SkgPlan &, const void *, const void *, const void *, void *, int,
+                         int, hipStream_t);
+
+template <int M, int C, int V>
+int launch_dot_t(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
+                 int N, int K, hipStream_t stream) {
+    hipLaunchKernelGGL((dot_kernel<M, C, V>), dim3(p.grid), dim3(p.threads), 0, stream,
+                       (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)bias,
+                       (uint16_t *)out, N, K);
+    return (int)hipGetLastError();
+}
+
+// Instantiated only where the per-thread registers fit (the planner applies
+// the same bound and never asks for the others).
+template <int M, int C, int V>
+constexpr DotLaunch dot_entry() {
+    if constexpr (dot_regs(M, C, V) <= kDotRegsMax)
+        return &launch_dot_t<M, C, V>;
+    else
+        return nullptr;
+}
+
+template <int M, int C>
+DotLaunch pick_v(int V) {
+    switch (V) {
+    case 1: return dot_entry<M, C, 1>();
+    case 2: return dot_entry<M, C, 2>();
+    case 3: return dot_entry<M, C, 3>();
+    case 4: return dot_entry<M, C, 4>();
+    case 6: return dot_entry<M, C, 6>();
+    case 8: return dot_entry<M, C, 8>();
+    default: return nullptr;
+    }
+}
+
+template <int M>
+DotLaunch pick_c(int C, int V) {
+    return C == 1 ? pick_v<M, 1>(V) : C == 2 ? pick_v<M, 2>(V) : nullptr;
+}
+
+DotLaunch pick(int M, int C, int V) {
+    switch (M) {
+    case 1: return pick_c<1>(C, V);
+    case 2: return pick_c<2>(C, V);
+    case 3: return pick_c<3>(C, V);
+    case 4: return pick_c<4>(C, V);
+    case 5: return pick_c<5>(C, V);
+    case 6: return pick_c<6>(C, V);
+    case 7: return pick_c<7>(C, V);
+    case 8: return pick_c<8>(C, V);
+    case 9: return pick_c<9>(C, V);
+    case 10: return pick_c<10>(C, V);
+    case 11: return pick_c<11>(C, V);
+    case 12: return pick_c<12>(C, V);
+    case 13: return pick_c<13>(C, V);
+    case 14: return pick_c<14>(C, V);
+    case 15: return pick_c<15>(C, V);
+    case 16: return pick_c<16>(C, V);
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+int launch_dot(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
+               int M, int N, int K, hipStream_t stream) {
+    DotLaunch f = pick(M, p.cols, p.depth);
+    if (!f) return (int)hipErrorInvalidConfiguration;
+    return f(p, x, W, bias, out, N, K, stream);
+}
+
+}  // namespace skg

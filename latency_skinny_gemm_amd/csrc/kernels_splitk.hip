@@ -1,0 +1,246 @@
+// kernels_splitk.hip -- split-K MFMA kernel and its ordered reduction (gfx950).
+//
+// The "vllm PR #42562" page (impl. item 2, the LLBf16SplitK snippet and the
+// review notes) splits K over the CTAs of a cluster, pads M to a 16-row MMA
+// tile, accumulates in fp32 and reduces the partials through distributed
+// shared memory after a cluster barrier.  gfx950 has no clusters and no
+// DSMEM; here:
+//  * workgroup (j, s) owns columns [16*NB*j, 16*NB*(j+1)) and the K chunk
+//    [s*k_chunk, (s+1)*k_chunk); its waves take the chunk's 32-wide K steps
+//    round-robin (step = wave + nwaves*i);
+//  * each step is one v_mfma_f32_16x16x32_bf16 per (m-tile, column block):
+//    A = x rows (M padded to 16 with zeros), B = W rows.  A lane's 8-element
+//    B operand is 16 contiguous bytes of one W row, so W goes from HBM
+//    straight into the MFMA operand registers with coalesced 16-byte loads
+//    (64 contiguous bytes per row per step);
+//  * a wave keeps 2 x D steps of loads in flight (two register stages used
+//    alternately), so the W stream never waits on an MFMA;
+//  * rows past M, columns past N and K past the chunk read as zeros through
+//    the buffer resources' range check;
+//  * the waves' 16x16 fp32 tiles are summed through LDS in wave order;
+//  * with S > 1 each workgroup writes its fp32 partial to the workspace
+//    ws[s][m][n]; the partials are then summed in ascending s by either the
+//    last workgroup of the tile to finish (a device-scope ticket counter,
+//    release/acquire fences; no workgroup ever waits on another) or by a
+//    second kernel.  Both add the same numbers in the same order, so the
+//    output does not depend on which workgroup finishes last.
+#include "device_common.h"
+#include "internal.h"
+
+namespace skg {
+
+template <int MT, int NB, int D>
+__global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
+    splitk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
+                  const uint16_t *__restrict__ bias, uint16_t *__restrict__ out,
+                  float *__restrict__ ws, unsigned *__restrict__ tickets, int M, int N, int K,
+                  int S, int k_chunk, int reduce) {
+    extern __shared__ float lds[];
+    __shared__ unsigned is_last;
+
+    const int nw = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int lane = threadIdx.x & 63;
+    const int s = blockIdx.x % S;  // split index fastest: the S workgroups of
+    const int j = blockIdx.x / S;  // a tile share one x chunk per XCD
+    const int col0 = j * NB * 16;
+    const int ncols = min(NB * 16, N - col0);
+    const unsigned rowb = (unsigned)K * 2u;
+    const Rsrc wr = make_rsrc(W + (size_t)col0 * K, (unsigned)ncols * rowb);
+    const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
+    const int kbeg = s * k_chunk;
+    const int kend = min(K, kbeg + k_chunk);
+    const int nsteps = (kend - kbeg + 31) >> 5;
+    const int my_steps = nsteps > wave ? (nsteps - wave + nw - 1) / nw : 0;
+    const int nchunks = (my_steps + D - 1) / D;
+    const unsigned r16 = (unsigned)(lane & 15);
+    const int kq = (lane >> 4) * 8;
+
+    f32x4 acc[NB][MT];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 wa[D][NB], xa[D][MT], wb[D][NB], xb[D][MT];
+
+    auto load_stage = [&](u32x4(&wbuf)[D][NB], u32x4(&xbuf)[D][MT], int chunk) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int i = chunk * D + d;
+            const int k = kbeg + (wave + nw * i) * 32 + kq;
+            const unsigned koff = ((i < my_steps) & (k < kend)) ? (unsigned)k * 2u : kOOB;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                wbuf[d][nb] = load16<kCacheStream>(wr, koff + ((unsigned)nb * 16u + r16) * rowb);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                xbuf[d][mt] = load16<kCacheDefault>(xr, koff + ((unsigned)mt * 16u + r16) * rowb);
+        }
+    };
+    auto mma_stage = [&](u32x4(&wbuf)[D][NB], u32x4(&xbuf)[D][MT]) {
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, xbuf[d][mt]),
+                        __builtin_bit_cast(bf16x8, wbuf[d][nb]), acc[nb][mt], 0, 0, 0);
+    };
+
+    if (nchunks <= 1) {
+        load_stage(wa, xa, 0);
+        mma_stage(wa, xa);
+    } else {
+        load_stage(wa, xa, 0);
+        for (int c = 0; c < nchunks; c += 2) {
+            load_stage(wb, xb, c + 1);  // past the end: all zeros, no traffic
+            mma_stage(wa, xa);
+            load_stage(wa, xa, c + 2);
+            mma_stage(wb, xb);
+        }
+    }
+
+    // ---- sum the waves' tiles through LDS, in wave order
+    // layout: [wave][q = (nb*MT + mt)*4 + i][lane]
+    constexpr int Q = NB * MT * 4;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                lds[(wave * Q + (nb * MT + mt) * 4 + i) * 64 + lane] = acc[nb][mt][i];
+    __syncthreads();
+
+    // MFMA 16x16 output layout: lane l, register i holds row 4*(l/16)+i,
+    // column l%16 of the tile; rows are m (from x), columns n (from W).
+    for (int q = wave; q < Q; q += nw) {
+        float v = lds[q * 64 + lane];
+        for (int w = 1; w < nw; ++w) v += lds[(w * Q + q) * 64 + lane];
+        const int nb = q / (MT * 4);
+        const int mt = (q >> 2) % MT;
+        const int i = q & 3;
+        const int n = col0 + nb * 16 + (lane & 15);
+        const int m = mt * 16 + (lane >> 4) * 4 + i;
+        if (m < M && n < N) {
+            if (S == 1) {
+                if (bias) v += bf16_to_f32(bias[n]);
+                out[(size_t)m * N + n] = f32_to_bf16_rne(v);
+            } else {
+                ws[((size_t)s * M + m) * N + n] = v;
+            }
+        }
+    }
+    if (S == 1 || reduce != SKG_REDUCE_LAST) return;
+
+    // ---- last workgroup of tile j sums the S partials in ascending s
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this wave's partials
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned prev =
+            __hip_atomic_fetch_add(&tickets[j], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = (prev == (unsigned)S - 1u) ? 1u : 0u;
+        if (is_last)  // every partial of tile j has arrived: rearm for the next call
+            __hip_atomic_store(&tickets[j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!is_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const int elems = M * ncols;
+    for (int e = threadIdx.x; e < elems; e += blockDim.x) {
+        const int m = e / ncols;
+        const int n = col0 + (e - m * ncols);
+        float v = 0.0f;
+        for (int ss = 0; ss < S; ++ss) v += ws[((size_t)ss * M + m) * N + n];
+        if (bias) v += bf16_to_f32(bias[n]);
+        out[(size_t)m * N + n] = f32_to_bf16_rne(v);
+    }
+}
+
+// Second-pass reduction: the same sum in the same order as the in-kernel
+// one, one output element per thread.
+__global__ void __launch_bounds__(256)
+    splitk_reduce_kernel(const float *__restrict__ ws, const uint16_t *__restrict__ bias,
+                         uint16_t *__restrict__ out, int M, int N, int S) {
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= M * N) return;
+    const int m = e / N;
+    const int n = e - m * N;
+    float v = 0.0f;
+    for (int ss = 0; ss < S; ++ss) v += ws[((size_t)ss * M + m) * N + n];
+    if (bias) v += bf16_to_f32(bias[n]);
+    out[e] = f32_to_bf16_rne(v);
+}
+
+namespace {
+
+typedef int (*SplitKLaunch)(const SkgPlan &, const void *, const void *, const void *, void *,
+                            float *, unsigned *, int, int, int, hipStream_t);
+
+template <int MT, int NB, int D>
+int launch_splitk_t(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
+                    float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream) {
+    const size_t lds_bytes = (size_t)(p.threads / 64) * NB * MT * 4 * 64 * sizeof(float);
+    hipLaunchKernelGGL((splitk_kernel<MT, NB, D>), dim3(p.grid), dim3(p.threads), lds_bytes,
+                       stream, (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)bias,
+                       (uint16_t *)out, ws, tickets, M, N, K, p.splits, p.k_chunk, p.reduce);
+    return (int)hipGetLastError();
+}
+
+template <int MT, int NB, int D>
+constexpr SplitKLaunch splitk_entry() {
+    if constexpr (splitk_built(MT, NB, D))
+        return &launch_splitk_t<MT, NB, D>;
+    else
+        return nullptr;
+}
+
+template <int MT, int NB>
+SplitKLaunch pick_d(int D) {
+    switch (D) {
+    case 1: return splitk_entry<MT, NB, 1>();
+    case 2: return splitk_entry<MT, NB, 2>();
+    case 4: return splitk_entry<MT, NB, 4>();
+    case 8: return splitk_entry<MT, NB, 8>();
+    default: return nullptr;
+    }
+}
+
+template <int MT>
+SplitKLaunch pick_nb(int NB, int D) {
+    return NB == 1 ? pick_d<MT, 1>(D) : NB == 2 ? pick_d<MT, 2>(D) : NB == 4 ? pick_d<MT, 4>(D)
+                                                                              : nullptr;
+}
+
+SplitKLaunch pick(int MT, int NB, int D) {
+    switch (MT) {
+    case 1: return pick_nb<1>(NB, D);
+    case 2: return pick_nb<2>(NB, D);
+    case 3: return pick_nb<3>(NB, D);
+    case 4: return pick_nb<4>(NB, D);
+    case 5: return pick_nb<5>(NB, D);
+    case 6: return pick_nb<6>(NB, D);
+    case 7: return pick_nb<7>(NB, D);
+    case 8: return pick_nb<8>(NB, D);
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+int launch_splitk(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
+                  float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream) {
+    SplitKLaunch f = pick(p.m_tiles, p.cols, p.depth);
+    if (!f) return (int)hipErrorInvalidConfiguration;
+    int rc = f(p, x, W, bias, out, ws, tickets, M, N, K, stream);
+    if (rc != (int)hipSuccess || p.splits == 1 || p.reduce != SKG_REDUCE_KERNEL) return rc;
+    const int elems = M * N;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((elems + 255) / 256), dim3(256), 0, stream, ws,
+                       (const uint16_t *)bias, (uint16_t *)out, M, N, p.splits);
+    return (int)hipGetLastError();
+}
+
+}  // namespace skg

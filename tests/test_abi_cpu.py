@@ -1,0 +1,199 @@
+"""The C ABI on the CPU: the library loads, exports everything its headers
+declare, rejects bad arguments before any HIP call, and plans exactly.
+No call here reaches the GPU (every GEMM call is one the library must
+reject during host-side validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import latency_skinny_gemm_amd as skg
+from latency_skinny_gemm_amd import build as lib_build
+from workloads import configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(skg.library_path()):
+        lib_build.build()
+    return skg.lib()
+
+
+def _declared(header):
+    txt = open(os.path.join(ROOT, "include", header)).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(skinny_\w+)\s*\(", txt, flags=re.M))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared("skinny_gemm.h")
+    assert {"skinny_gemm_bf16", "skinny_gemm_fp8", "skinny_gemm_plan", "skinny_gemm_reserve",
+            "skinny_gemm_release_all", "skinny_gemm_status_string"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+    floors = ctypes.CDLL(os.path.join(os.path.dirname(skg.library_path()), "libskinny_floors.so"))
+    for n in _declared("skinny_floors.h"):
+        assert hasattr(floors, n), n
+
+
+# fake, never dereferenced device addresses (validation rejects first)
+X, W, OUT, B = 0x10000, 0x200000, 0x4000000, 0x8000000
+
+
+@pytest.mark.parametrize("args,status", [
+    ((X, W, 0, 0, OUT, -1, 8, 64), skg.ERR_INVALID_ARG),
+    ((X, W, 0, 0, OUT, 2, -8, 64), skg.ERR_INVALID_ARG),
+    ((X, W, 0, 0, OUT, 2, 8, -64), skg.ERR_INVALID_ARG),
+    ((X, W, 0, 0, OUT, 0, 8, 64), skg.OK),          # empty: no launch
+    ((0, 0, 0, 0, 0, 5, 0, 64), skg.OK),            # empty: no launch
+    ((X, W, 0, 0, OUT, 129, 8, 64), skg.ERR_UNSUPPORTED),
+    ((X, W, 0, 0, OUT, 2, 8, 60), skg.ERR_UNSUPPORTED),
+    ((X, W, 0, 0, OUT, 2, 8, 0), skg.ERR_UNSUPPORTED),
+    ((X, W, 0, 0, OUT, 2, 8, 4), skg.ERR_UNSUPPORTED),
+    ((0, W, 0, 0, OUT, 2, 8, 64), skg.ERR_INVALID_ARG),
+    ((X, 0, 0, 0, OUT, 2, 8, 64), skg.ERR_INVALID_ARG),
+    ((X, W, 0, 0, 0, 2, 8, 64), skg.ERR_INVALID_ARG),
+    ((X, W, 0, 0x1234, OUT, 2, 8, 64), skg.ERR_INVALID_ARG),  # scales must be NULL
+    ((X + 2, W, 0, 0, OUT, 2, 8, 64), skg.ERR_ALIGNMENT),
+    ((X, W + 8, 0, 0, OUT, 2, 8, 64), skg.ERR_ALIGNMENT),
+    ((X, W, 0, 0, OUT + 1, 2, 8, 64), skg.ERR_ALIGNMENT),
+    ((X, W, B + 1, 0, OUT, 2, 8, 64), skg.ERR_ALIGNMENT),
+    ((X, W, 0, 0, X + 64, 2, 8, 64), skg.ERR_INVALID_ARG),   # out overlaps x
+    ((X, W, 0, 0, W + 1000, 2, 8, 64), skg.ERR_INVALID_ARG), # out overlaps W
+    ((X, W, B, 0, B - 2, 2, 8, 64), skg.ERR_INVALID_ARG),    # out overlaps bias
+])
+def test_bf16_validation_before_any_device_call(lib, args, status):
+    x, w, b, sc, o, M, N, K = args
+    assert lib.skinny_gemm_bf16(x or None, w or None, b or None, sc or None, o or None,
+                                M, N, K, None) == status
+
+
+def test_fp8_validation(lib):
+    sc = skg.Fp8Scales()
+    sc.mode = 7
+    assert lib.skinny_gemm_fp8(X, W, None, ctypes.byref(sc), OUT, 2, 8, 64, None) == skg.ERR_INVALID_ARG
+    assert lib.skinny_gemm_fp8(X, W, None, None, OUT, 2, 8, 64, None) == skg.ERR_INVALID_ARG
+    sc.mode = skg.FP8_MX32
+    assert lib.skinny_gemm_fp8(X, W, None, ctypes.byref(sc), OUT, 2, 8, 48, None) == skg.ERR_UNSUPPORTED
+    assert lib.skinny_gemm_fp8(X, W, None, ctypes.byref(sc), OUT, 2, 8, 40, None) == skg.ERR_UNSUPPORTED
+    assert lib.skinny_gemm_fp8(X + 8, W, None, ctypes.byref(sc), OUT, 2, 8, 64, None) == skg.ERR_ALIGNMENT
+
+
+def test_status_strings(lib):
+    for st in (skg.OK, skg.ERR_INVALID_ARG, skg.ERR_ALIGNMENT, skg.ERR_UNSUPPORTED,
+               skg.ERR_WORKSPACE, skg.ERR_HIP):
+        assert skg.status_string(st).startswith("SKG_")
+    assert skg.status_string(-99) == "SKG_ERR_UNKNOWN"
+
+
+def test_reserve_rejects_bad_sizes(lib):
+    assert lib.skinny_gemm_reserve(0, 10, 1, None) == skg.ERR_INVALID_ARG
+    assert lib.skinny_gemm_reserve(129, 10, 1, None) == skg.ERR_INVALID_ARG
+    assert lib.skinny_gemm_reserve(4, 10, 10000, None) == skg.ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ planner
+
+BF16 = [p for p in configs.all_points() if p.dtype == "bf16"]
+
+
+@pytest.mark.parametrize("p", BF16, ids=lambda p: p.key())
+def test_default_rule_without_table(lib, p):
+    # a made-up 200-CU device never uses the MI355X table: the pages' rule
+    q = skg.plan_on(p.M, p.N, p.K, 200)
+    want = skg.KIND_DOT if (p.M <= 4 or p.K < 2048) else skg.KIND_SPLITK
+    assert q.kind == want and q.from_table == 0
+    _check_coverage(q, p.M, p.N, p.K)
+
+
+@pytest.mark.parametrize("p", BF16, ids=lambda p: p.key())
+def test_library_plan_is_valid_and_covers(lib, p):
+    q = skg.plan(p.M, p.N, p.K)
+    again = skg.plan_complete(p.M, p.N, p.K, q)
+    for f in ("kind", "threads", "cols", "splits", "depth", "reduce", "k_chunk", "grid"):
+        assert getattr(again, f) == getattr(q, f), f
+    _check_coverage(q, p.M, p.N, p.K)
+
+
+def test_split_count_follows_cu_count(lib):
+    small = skg.plan_on(8, 256, 7168, 64)
+    big = skg.plan_on(8, 256, 7168, 256)
+    assert small.kind == big.kind == skg.KIND_SPLITK
+    assert small.splits * small.grid // small.splits <= big.grid
+    assert small.grid >= 64 and big.grid >= 256
+
+
+@pytest.mark.parametrize("plan,M,N,K", [
+    (dict(kind=9, threads=256), 4, 256, 2048),
+    (dict(kind=skg.KIND_DOT, threads=100), 4, 256, 2048),
+    (dict(kind=skg.KIND_DOT, threads=2048), 4, 256, 2048),
+    (dict(kind=skg.KIND_DOT, threads=256, cols=3), 4, 256, 2048),
+    (dict(kind=skg.KIND_DOT, threads=64), 4, 256, 7168),        # > 8 vectors a thread
+    (dict(kind=skg.KIND_DOT, threads=256), 17, 256, 2048),      # DOT is built for M <= 16
+    (dict(kind=skg.KIND_DOT, threads=1024), 16, 256, 7168),     # registers at 1024 threads
+    (dict(kind=skg.KIND_SPLITK, threads=256, cols=3, splits=2, depth=2), 4, 256, 2048),
+    (dict(kind=skg.KIND_SPLITK, threads=256, cols=1, splits=2, depth=3), 4, 256, 2048),
+    (dict(kind=skg.KIND_SPLITK, threads=256, cols=1, splits=0, depth=2), 4, 256, 2048),
+    (dict(kind=skg.KIND_SPLITK, threads=256, cols=1, splits=300, depth=2), 4, 256, 2048),
+    (dict(kind=skg.KIND_SPLITK, threads=512, cols=4, splits=2, depth=2), 128, 256, 2048),
+    (dict(kind=skg.KIND_SPLITK, threads=256, cols=1, splits=2, depth=2, reduce=5), 4, 256, 2048),
+])
+def test_complete_rejects_invalid_plans(lib, plan, M, N, K):
+    p = skg.make_plan(**plan)
+    with pytest.raises(skg.SkinnyGemmError) as e:
+        skg.plan_complete(M, N, K, p)
+    assert e.value.status == skg.ERR_INVALID_ARG
+
+
+def test_complete_drops_empty_splits(lib):
+    # K = 2880 has 90 steps of 32; 64 splits of ceil(90/64) = 2 steps leave
+    # only 45 non-empty splits
+    q = skg.plan_complete(16, 128, 2880, skg.make_plan(skg.KIND_SPLITK, 256, 1, 64, 2, skg.REDUCE_LAST))
+    assert q.splits == 45 and q.k_chunk == 64 and q.grid == 8 * 45
+    q = skg.plan_complete(16, 128, 2880, skg.make_plan(skg.KIND_SPLITK, 256, 1, 1, 2, skg.REDUCE_LAST))
+    assert q.reduce == skg.REDUCE_NONE
+
+
+# ------------------------------------------------------------------ coverage
+# A model of the kernels' index arithmetic: every output written exactly
+# once, and every k of every output accumulated exactly once.
+
+def _check_coverage(p, M, N, K):
+    if p.kind == skg.KIND_DOT:
+        T, C, V = p.threads, p.cols, p.depth
+        K8 = K // 8
+        cols = [n for b in range(p.grid) for c in range(C) if (n := b * C + c) < N]
+        assert sorted(cols) == list(range(N))
+        vecs = sorted(t + i * T for t in range(T) for i in range(V) if t + i * T < K8)
+        assert vecs == list(range(K8))
+        assert T % 64 == 0 and T <= 1024 and p.grid == -(-N // C)
+        return
+    assert p.kind == skg.KIND_SPLITK
+    S, NB, D, kc = p.splits, p.cols, p.depth, p.k_chunk
+    nw = p.threads // 64
+    groups = -(-N // (16 * NB))
+    assert p.grid == groups * S and kc % 32 == 0 and (S - 1) * kc < K <= S * kc
+    # columns: tile j covers [16*NB*j, 16*NB*(j+1)) clipped to N
+    cols = sorted(n for j in range(groups) for c in range(16 * NB) if (n := 16 * NB * j + c) < N)
+    assert cols == list(range(N))
+    # K: per split, the waves' steps, the two-stage chunk schedule, lane groups
+    seen = [0] * K
+    for s in range(S):
+        kbeg, kend = s * kc, min(K, (s + 1) * kc)
+        nsteps = -(-(kend - kbeg) // 32)
+        for w in range(nw):
+            my = -(-(nsteps - w) // nw) if nsteps > w else 0
+            nch = -(-my // D)
+            consumed = [0] if nch <= 1 else [c for c0 in range(0, nch, 2) for c in (c0, c0 + 1)]
+            for ch in consumed:
+                for d in range(D):
+                    i = ch * D + d
+                    for g in range(4):  # lane groups of 16: k offset 8*g
+                        k = kbeg + (w + nw * i) * 32 + 8 * g
+                        if i < my and k < kend:
+                            for kk in range(k, k + 8):
+                                seen[kk] += 1
+    assert seen == [1] * K

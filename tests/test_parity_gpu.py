@@ -1,0 +1,231 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Every configured workload point runs on the plan the library picks, and on
+each kernel explicitly (dot product where M <= 16, split-K with both
+reductions).  Random inputs must meet the elementwise bound
+|gpu - ref| <= 2^-7 |ref| + 1e-3 sqrt(K) rms(ref); inputs whose every fp32
+partial sum is exact (small integers, one-hot, all-ones) must match the
+oracle bit for bit.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import tolerance
+from workloads import configs
+from workloads import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def skg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import latency_skinny_gemm_amd as m
+    m.lib()
+    return m
+
+
+@functools.lru_cache(maxsize=None)
+def _ref_point(p):
+    x, w, b = gen.point_inputs(p)
+    ref = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w), None if b is None else gen.bits16(b),
+                           threads=16)
+    return x, w, b, ref
+
+
+def _dev(*ts):
+    return [None if t is None else t.to(DEV) for t in ts]
+
+
+def _kernel_plans(skg, M, N, K):
+    """The library's plan plus one explicit plan per kernel / reduction."""
+    plans = [("default", None)]
+    if M <= 16:
+        for cols in (1, 2):
+            for threads in range(256, 1025, 64):  # the smallest workgroup that fits
+                p = skg.make_plan(skg.KIND_DOT, threads, cols=cols)
+                try:
+                    skg.plan_complete(M, N, K, p)
+                except skg.SkinnyGemmError:
+                    continue
+                plans.append((f"dot_c{cols}_t{threads}", p))
+                break
+    mt = (M + 15) // 16
+    nb = 4 if mt >= 4 else (2 if mt >= 2 else 1)
+    threads = 128 if nb * mt > 16 else 256
+    plans.append(("splitk_last", skg.make_plan(skg.KIND_SPLITK, threads, cols=nb, splits=8,
+                                               depth=2, reduce=skg.REDUCE_LAST)))
+    plans.append(("splitk_kernel", skg.make_plan(skg.KIND_SPLITK, threads, cols=nb, splits=5,
+                                                 depth=1, reduce=skg.REDUCE_KERNEL)))
+    plans.append(("splitk_s1", skg.make_plan(skg.KIND_SPLITK, threads, cols=nb, splits=1,
+                                             depth=4 if nb * mt <= 8 else 2)))
+    return plans
+
+
+def _run(skg, x, w, b, p):
+    out = skg.gemm_bf16(x, w, b) if p is None else skg.gemm_bf16_planned(x, w, p, b)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+BF16_POINTS = [p for p in configs.all_points() if p.dtype == "bf16"]
+
+
+@pytest.mark.parametrize("p", BF16_POINTS, ids=lambda p: p.key())
+def test_point_within_tolerance(skg, p):
+    x, w, b, ref = _ref_point(p)
+    xd, wd, bd = _dev(x, w, b)
+    for name, plan in _kernel_plans(skg, p.M, p.N, p.K):
+        if plan is not None:
+            try:
+                skg.plan_complete(p.M, p.N, p.K, plan)
+            except skg.SkinnyGemmError:
+                continue  # this explicit shape does not fit the problem
+        out = _run(skg, xd, wd, bd, plan)
+        ok, msg = tolerance.check(out, ref, p.K)
+        assert ok, f"{p.key()} [{name}]: {msg}"
+
+
+EXACT_SHAPES = [(1, 256, 2048), (3, 100, 2880), (4, 128, 2880), (5, 384, 7168), (9, 256, 4096),
+                (16, 256, 6144), (16, 37, 8), (33, 72, 264), (64, 576, 7168), (128, 200, 2056)]
+
+
+@pytest.mark.parametrize("M,N,K", EXACT_SHAPES)
+def test_small_integers_bitwise(skg, M, N, K):
+    x, w, b = gen.small_integers(M, N, K, True, seed=M * 7919 + N * 31 + K)
+    ref = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w), gen.bits16(b), threads=16)
+    xd, wd, bd = _dev(x, w, b)
+    for name, plan in _kernel_plans(skg, M, N, K):
+        if plan is not None:
+            try:
+                skg.plan_complete(M, N, K, plan)
+            except skg.SkinnyGemmError:
+                continue
+        out = _run(skg, xd, wd, bd, plan)
+        got = gen.bits16(out)
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, f"[{name}] {len(bad)} mismatches, first {tuple(bad[0])}"
+
+
+@pytest.mark.parametrize("M,N,K", [(2, 128, 2880), (16, 256, 7168), (40, 96, 4096)])
+def test_one_hot_selects_x_bitwise(skg, M, N, K):
+    x, w, pi = gen.one_hot(M, N, K, seed=N + K)
+    want = gen.bits16(x)[:, pi.numpy()]
+    xd, wd = _dev(x, w)
+    for name, plan in _kernel_plans(skg, M, N, K):
+        if plan is not None:
+            try:
+                skg.plan_complete(M, N, K, plan)
+            except skg.SkinnyGemmError:
+                continue
+        got = gen.bits16(_run(skg, xd, wd, None, plan))
+        assert np.array_equal(got, want), f"[{name}]"
+
+
+@pytest.mark.parametrize("K", (2048, 2880, 4096, 6144, 7168))
+def test_all_ones_gives_K(skg, K):
+    x, w = gen.ones(16, 256, K)
+    xd, wd = _dev(x, w)
+    for name, plan in _kernel_plans(skg, 16, 256, K):
+        out = _run(skg, xd, wd, None, plan)
+        assert torch.all(out.float() == K), f"[{name}]"
+
+
+def test_runs_are_bitwise_deterministic(skg):
+    p = configs.Point("det", "bf16", 12, 384, 7168, True)
+    x, w, b, _ = _ref_point(p)
+    xd, wd, bd = _dev(x, w, b)
+    for name, plan in _kernel_plans(skg, p.M, p.N, p.K):
+        a = _run(skg, xd, wd, bd, plan)
+        c = _run(skg, xd, wd, bd, plan)
+        assert torch.equal(a.view(torch.int16), c.view(torch.int16)), f"[{name}]"
+
+
+def test_reductions_agree_bitwise(skg):
+    # the in-kernel last-arriver sum and the second-kernel sum add the same
+    # partials in the same order
+    for (M, N, K) in ((8, 256, 7168), (64, 576, 7168), (5, 100, 2880)):
+        x, w, b = gen.bf16_inputs(M, N, K, True, seed=K + M)
+        xd, wd, bd = _dev(x, w, b)
+        mt = (M + 15) // 16
+        outs = []
+        for red in (skg.REDUCE_LAST, skg.REDUCE_KERNEL):
+            plan = skg.make_plan(skg.KIND_SPLITK, 128, cols=1, splits=7, depth=2, reduce=red)
+            outs.append(_run(skg, xd, wd, bd, plan))
+        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), (M, N, K, mt)
+
+
+def test_output_guard_bands_untouched(skg):
+    M, N, K = 7, 130, 2880
+    G = 4096
+    x, w, b = gen.bf16_inputs(M, N, K, True, seed=5)
+    ref = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w), gen.bits16(b), threads=16)
+    xd, wd, bd = _dev(x, w, b)
+    for name, plan in _kernel_plans(skg, M, N, K):
+        buf = torch.full((G + M * N + G,), -7.0, dtype=torch.bfloat16, device=DEV)
+        out = buf[G:G + M * N].view(M, N)
+        if plan is None:
+            skg.gemm_bf16(xd, wd, bd, out=out)
+        else:
+            skg.gemm_bf16_planned(xd, wd, plan, bd, out=out)
+        torch.cuda.synchronize()
+        host = buf.cpu()
+        assert torch.all(host[:G] == -7.0) and torch.all(host[G + M * N:] == -7.0), f"[{name}]"
+        ok, msg = tolerance.check(host[G:G + M * N].view(M, N), ref, K)
+        assert ok, f"[{name}] {msg}"
+
+
+def test_graph_replays_match_eager(skg):
+    shapes = [(1, 256, 7168), (8, 256, 7168), (16, 384, 7168), (64, 576, 7168)]
+    stream = torch.cuda.Stream()
+    data = []
+    for (M, N, K) in shapes:
+        x, w, b = gen.bf16_inputs(M, N, K, False, seed=M * N)
+        data.append(_dev(x, w, b))
+    with torch.cuda.stream(stream):
+        skg.reserve(128, 4096, 64)
+        eager = [skg.gemm_bf16(x, w, b) for (x, w, b) in data]
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(e) for e in eager]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for (x, w, b), o in zip(data, outs):
+            skg.gemm_bf16(x, w, b, out=o)
+    for _ in range(3):
+        for o in outs:
+            o.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, o in zip(eager, outs):
+            assert torch.equal(e.view(torch.int16), o.view(torch.int16))
+
+
+def test_error_statuses_on_device(skg):
+    x = torch.zeros(2, 64, dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros(8, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        skg.gemm_bf16(x, torch.zeros(8, 56, dtype=torch.bfloat16, device=DEV))  # K mismatch
+    with pytest.raises(skg.SkinnyGemmError) as e:
+        skg.gemm_bf16(torch.zeros(2, 60, dtype=torch.bfloat16, device=DEV),
+                      torch.zeros(8, 60, dtype=torch.bfloat16, device=DEV))
+    assert e.value.status == skg.ERR_UNSUPPORTED  # K % 8 != 0
+    with pytest.raises(skg.SkinnyGemmError) as e:
+        skg.gemm_bf16(torch.zeros(129, 64, dtype=torch.bfloat16, device=DEV), w)
+    assert e.value.status == skg.ERR_UNSUPPORTED  # M > 128
+    lib = skg.lib()
+    flat = torch.zeros(2 * 64 + 8, dtype=torch.bfloat16, device=DEV)
+    out = torch.zeros(2, 8, dtype=torch.bfloat16, device=DEV)
+    rc = lib.skinny_gemm_bf16(flat.data_ptr() + 2, w.data_ptr(), None, None, out.data_ptr(),
+                              2, 8, 64, None)
+    assert rc == skg.ERR_ALIGNMENT
+    rc = lib.skinny_gemm_bf16(x.data_ptr(), w.data_ptr(), None, None, x.data_ptr(), 2, 8, 64, None)
+    assert rc == skg.ERR_INVALID_ARG  # out overlaps x
+    torch.cuda.synchronize()
