@@ -82,6 +82,9 @@ extern "C" {
 #define SKG_REDUCE_LAST 1  /* the last workgroup to finish a tile reduces it */
 #define SKG_REDUCE_KERNEL 2 /* a second kernel reduces every tile */
 
+#define SKG_FLAG_DOT2 1 /* DOT: multiply-add with v_dot2c_f32_bf16 (bf16 pairs, fp32
+                          accumulator; not rounded per IEEE step, see DESIGN) */
+
 #define SKG_MAX_M 128
 
 /* FP8 scales (host struct; its pointers are DEVICE pointers).
@@ -113,6 +116,7 @@ typedef struct SkgPlan {
     int depth;    /* SPLITK: 32-wide K steps a wave keeps in flight (1, 2, 4, 8);
                      DOT: 16-byte vectors per thread per column (derived) */
     int reduce;   /* SKG_REDUCE_*; NONE iff splits == 1 */
+    int flags;    /* SKG_FLAG_* */
     int k_chunk;  /* (derived) SPLITK: K elements per split, multiple of 32 */
     int m_tiles;  /* (derived) SPLITK: ceil(M / 16) */
     int grid;     /* (derived) workgroups in the main launch */

@@ -61,7 +61,51 @@ __device__ __forceinline__ float dot8_fma(u32x4 a, u32x4 b, float acc) {
     return acc;
 }
 
+// acc + the same 8 products with gfx950's bf16 dot instruction (two
+// products and the accumulator per instruction, no widening).  Its
+// internal sum is not rounded per IEEE step: an accumulator far below the
+// two products can be lost (error bounded by ~2^-24 of the largest term).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot8_dot2(u32x4 a, u32x4 b, float acc) {
+    // Pairs are taken from the 8-element view with shufflevector: bit-casting
+    // the 32-bit lanes a.y/a.z/a.w one by one is folded onto a.x by this
+    // compiler (every product then uses the first pair).
+    const bf16x8 a8 = __builtin_bit_cast(bf16x8, a);
+    const bf16x8 b8 = __builtin_bit_cast(bf16x8, b);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a8, a8, 0, 1),
+                                          __builtin_shufflevector(b8, b8, 0, 1), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a8, a8, 2, 3),
+                                          __builtin_shufflevector(b8, b8, 2, 3), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a8, a8, 4, 5),
+                                          __builtin_shufflevector(b8, b8, 4, 5), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a8, a8, 6, 7),
+                                          __builtin_shufflevector(b8, b8, 6, 7), acc, false);
+    return acc;
+}
+
+// Wait until every memory operation this wave issued has completed (for a
+// store: acknowledged by the L2).  s_waitcnt with all counters zero.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
 // ---------------------------------------------------------------- reductions
+// sum_{i < n} ld(i), added in ascending i starting from 0.0f.  The loads go
+// out in groups of CH before any of them is added, so n partials cost about
+// n / CH memory latencies instead of n; the additions keep their order, so
+// the bits do not depend on CH.
+template <int CH, class Load>
+__device__ __forceinline__ float ordered_sum(int n, Load ld) {
+    float v = 0.0f;
+    for (int i0 = 0; i0 < n; i0 += CH) {
+        float t[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) t[i] = (i0 + i < n) ? ld(i0 + i) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+            if (i0 + i < n) v += t[i];
+    }
+    return v;
+}
+
 // DPP lane moves within a 16-lane row (gfx9 dpp_ctrl encodings).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {

@@ -26,9 +26,14 @@ constexpr int kDotVecs[] = {1, 2, 3, 4, 6, 8};
 // work: a kernel is built only when this is <= 224 and may run 1024-thread
 // workgroups (4 waves per SIMD, 128 VGPRs each) only when it is <= 96.
 // (Checked against the compiler's resource report: no kernel spills.)
-constexpr int dot_regs(int M, int C, int V) { return (2 * M + C) * V * 4 + C * M; }
+// With the dot2 instruction x stays packed (no widening): M + C rows.
+constexpr int dot_regs(int M, int C, int V, bool dot2) {
+    return ((dot2 ? M : 2 * M) + C) * V * 4 + C * M;
+}
 constexpr int kDotRegsMax = 224;
-constexpr int dot_max_threads(int M, int C, int V) { return dot_regs(M, C, V) <= 96 ? 1024 : 512; }
+constexpr int dot_max_threads(int M, int C, int V, bool dot2) {
+    return dot_regs(M, C, V, dot2) <= 96 ? 1024 : 512;
+}
 
 // SPLITK per-lane registers: two stages of D steps of (NB + MT) vectors and
 // NB*MT accumulators of 4 (those may live in AGPRs).  Above 224 the kernel

@@ -12,6 +12,9 @@
 //    the first multiply: the whole per-workgroup slice is in flight at once;
 //  * vectors past K read as zeros through the buffer resource's range
 //    check, so there is no scalar tail loop (K % 8 == 0 always holds);
+//  * the multiply-add is either fp32 FMA on widened bf16 (one IEEE rounding
+//    per product) or, with SKG_FLAG_DOT2, gfx950's bf16 dot instruction
+//    (two products per instruction on packed operands, no widening);
 //  * the per-thread sums are reduced over the wave by DPP row moves and two
 //    shuffles, then over the waves through LDS in wave order, then bias is
 //    added in fp32 and the sum is rounded once to bf16.
@@ -22,8 +25,8 @@
 
 namespace skg {
 
-template <int M, int C, int V>
-__global__ void __launch_bounds__((dot_max_threads(M, C, V)))
+template <int M, int C, int V, bool DOT2>
+__global__ void __launch_bounds__((dot_max_threads(M, C, V, DOT2)))
     dot_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
                const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int N, int K) {
     const int T = blockDim.x;
@@ -62,7 +65,9 @@ __global__ void __launch_bounds__((dot_max_threads(M, C, V)))
 #pragma unroll
         for (int c = 0; c < C; ++c)
 #pragma unroll
-            for (int m = 0; m < M; ++m) acc[c][m] = dot8_fma(xv[m][i], wv[c][i], acc[c][m]);
+            for (int m = 0; m < M; ++m)
+                acc[c][m] = DOT2 ? dot8_dot2(xv[m][i], wv[c][i], acc[c][m])
+                                 : dot8_fma(xv[m][i], wv[c][i], acc[c][m]);
 
     __shared__ float red[kMaxThreads / 64][C * M];
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
@@ -80,8 +85,7 @@ __global__ void __launch_bounds__((dot_max_threads(M, C, V)))
         const int c = t / M;
         const int m = t - c * M;
         const int n = n0 + c;
-        float s = red[0][t];
-        for (int w = 1; w < nw; ++w) s += red[w][t];
+        float s = ordered_sum<8>(nw, [&](int w) { return red[w][t]; });
         if (n < N) {
             if (bias) s += bf16_to_f32(bias[n]);
             out[(size_t)m * N + n] = f32_to_bf16_rne(s);
@@ -94,10 +98,10 @@ namespace {
 typedef int (*DotLaunch)(const SkgPlan &, const void *, const void *, const void *, void *, int,
                          int, hipStream_t);
 
-template <int M, int C, int V>
+template <int M, int C, int V, bool DOT2>
 int launch_dot_t(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
                  int N, int K, hipStream_t stream) {
-    hipLaunchKernelGGL((dot_kernel<M, C, V>), dim3(p.grid), dim3(p.threads), 0, stream,
+    hipLaunchKernelGGL((dot_kernel<M, C, V, DOT2>), dim3(p.grid), dim3(p.threads), 0, stream,
                        (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)bias,
                        (uint16_t *)out, N, K);
     return (int)hipGetLastError();
@@ -105,50 +109,52 @@ int launch_dot_t(const SkgPlan &p, const void *x, const void *W, const void *bia
 
 // Instantiated only where the per-thread registers fit (the planner applies
 // the same bound and never asks for the others).
-template <int M, int C, int V>
+template <int M, int C, int V, bool DOT2>
 constexpr DotLaunch dot_entry() {
-    if constexpr (dot_regs(M, C, V) <= kDotRegsMax)
-        return &launch_dot_t<M, C, V>;
+    if constexpr (dot_regs(M, C, V, DOT2) <= kDotRegsMax)
+        return &launch_dot_t<M, C, V, DOT2>;
     else
         return nullptr;
 }
 
-template <int M, int C>
+template <int M, int C, bool DOT2>
 DotLaunch pick_v(int V) {
     switch (V) {
-    case 1: return dot_entry<M, C, 1>();
-    case 2: return dot_entry<M, C, 2>();
-    case 3: return dot_entry<M, C, 3>();
-    case 4: return dot_entry<M, C, 4>();
-    case 6: return dot_entry<M, C, 6>();
-    case 8: return dot_entry<M, C, 8>();
+    case 1: return dot_entry<M, C, 1, DOT2>();
+    case 2: return dot_entry<M, C, 2, DOT2>();
+    case 3: return dot_entry<M, C, 3, DOT2>();
+    case 4: return dot_entry<M, C, 4, DOT2>();
+    case 6: return dot_entry<M, C, 6, DOT2>();
+    case 8: return dot_entry<M, C, 8, DOT2>();
     default: return nullptr;
     }
 }
 
 template <int M>
-DotLaunch pick_c(int C, int V) {
-    return C == 1 ? pick_v<M, 1>(V) : C == 2 ? pick_v<M, 2>(V) : nullptr;
+DotLaunch pick_c(int C, int V, bool dot2) {
+    if (C == 1) return dot2 ? pick_v<M, 1, true>(V) : pick_v<M, 1, false>(V);
+    if (C == 2) return dot2 ? pick_v<M, 2, true>(V) : pick_v<M, 2, false>(V);
+    return nullptr;
 }
 
-DotLaunch pick(int M, int C, int V) {
+DotLaunch pick(int M, int C, int V, bool dot2) {
     switch (M) {
-    case 1: return pick_c<1>(C, V);
-    case 2: return pick_c<2>(C, V);
-    case 3: return pick_c<3>(C, V);
-    case 4: return pick_c<4>(C, V);
-    case 5: return pick_c<5>(C, V);
-    case 6: return pick_c<6>(C, V);
-    case 7: return pick_c<7>(C, V);
-    case 8: return pick_c<8>(C, V);
-    case 9: return pick_c<9>(C, V);
-    case 10: return pick_c<10>(C, V);
-    case 11: return pick_c<11>(C, V);
-    case 12: return pick_c<12>(C, V);
-    case 13: return pick_c<13>(C, V);
-    case 14: return pick_c<14>(C, V);
-    case 15: return pick_c<15>(C, V);
-    case 16: return pick_c<16>(C, V);
+    case 1: return pick_c<1>(C, V, dot2);
+    case 2: return pick_c<2>(C, V, dot2);
+    case 3: return pick_c<3>(C, V, dot2);
+    case 4: return pick_c<4>(C, V, dot2);
+    case 5: return pick_c<5>(C, V, dot2);
+    case 6: return pick_c<6>(C, V, dot2);
+    case 7: return pick_c<7>(C, V, dot2);
+    case 8: return pick_c<8>(C, V, dot2);
+    case 9: return pick_c<9>(C, V, dot2);
+    case 10: return pick_c<10>(C, V, dot2);
+    case 11: return pick_c<11>(C, V, dot2);
+    case 12: return pick_c<12>(C, V, dot2);
+    case 13: return pick_c<13>(C, V, dot2);
+    case 14: return pick_c<14>(C, V, dot2);
+    case 15: return pick_c<15>(C, V, dot2);
+    case 16: return pick_c<16>(C, V, dot2);
     default: return nullptr;
     }
 }
@@ -157,7 +163,7 @@ DotLaunch pick(int M, int C, int V) {
 
 int launch_dot(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
                int M, int N, int K, hipStream_t stream) {
-    DotLaunch f = pick(M, p.cols, p.depth);
+    DotLaunch f = pick(M, p.cols, p.depth, (p.flags & SKG_FLAG_DOT2) != 0);
     if (!f) return (int)hipErrorInvalidConfiguration;
     return f(p, x, W, bias, out, N, K, stream);
 }

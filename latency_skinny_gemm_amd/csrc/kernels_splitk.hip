@@ -6,8 +6,8 @@
 // shared memory after a cluster barrier.  gfx950 has no clusters and no
 // DSMEM; here:
 //  * workgroup (j, s) owns columns [16*NB*j, 16*NB*(j+1)) and the K chunk
-//    [s*k_chunk, (s+1)*k_chunk); its waves take the chunk's 32-wide K steps
-//    round-robin (step = wave + nwaves*i);
+//    [s*k_chunk, (s+1)*k_chunk); each wave takes a contiguous run of the
+//    chunk's 32-wide K steps;
 //  * each step is one v_mfma_f32_16x16x32_bf16 per (m-tile, column block):
 //    A = x rows (M padded to 16 with zeros), B = W rows.  A lane's 8-element
 //    B operand is 16 contiguous bytes of one W row, so W goes from HBM
@@ -51,7 +51,11 @@ __global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
     const int kbeg = s * k_chunk;
     const int kend = min(K, kbeg + k_chunk);
     const int nsteps = (kend - kbeg + 31) >> 5;
-    const int my_steps = nsteps > wave ? (nsteps - wave + nw - 1) / nw : 0;
+    // each wave takes a contiguous run of steps, so the two 64-byte halves
+    // of a 128-byte W line are read by the same wave, back to back
+    const int spw = (nsteps + nw - 1) / nw;
+    const int first_step = wave * spw;
+    const int my_steps = max(0, min(spw, nsteps - first_step));
     const int nchunks = (my_steps + D - 1) / D;
     const unsigned r16 = (unsigned)(lane & 15);
     const int kq = (lane >> 4) * 8;
@@ -68,7 +72,7 @@ __global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int i = chunk * D + d;
-            const int k = kbeg + (wave + nw * i) * 32 + kq;
+            const int k = kbeg + (first_step + i) * 32 + kq;
             const unsigned koff = ((i < my_steps) & (k < kend)) ? (unsigned)k * 2u : kOOB;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
@@ -118,8 +122,7 @@ __global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
     // MFMA 16x16 output layout: lane l, register i holds row 4*(l/16)+i,
     // column l%16 of the tile; rows are m (from x), columns n (from W).
     for (int q = wave; q < Q; q += nw) {
-        float v = lds[q * 64 + lane];
-        for (int w = 1; w < nw; ++w) v += lds[(w * Q + q) * 64 + lane];
+        float v = ordered_sum<8>(nw, [&](int w) { return lds[(w * Q + q) * 64 + lane]; });
         const int nb = q / (MT * 4);
         const int mt = (q >> 2) % MT;
         const int i = q & 3;
@@ -137,7 +140,13 @@ __global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
     if (S == 1 || reduce != SKG_REDUCE_LAST) return;
 
     // ---- last workgroup of tile j sums the S partials in ascending s
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this wave's partials
+    // Every wave waits until its partial stores are in the L2 before the
+    // barrier; then one agent-scope acquire-release ticket increment by
+    // thread 0 publishes the whole workgroup's partials (its release writes
+    // the XCD's L2 back to memory once per workgroup, not once per wave) and,
+    // in the last workgroup, its acquire invalidates the stale L1/L2 lines
+    // before any wave of that workgroup reads the partials.
+    wait_all_memory();
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned prev =
@@ -148,13 +157,11 @@ __global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
     }
     __syncthreads();
     if (!is_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int elems = M * ncols;
     for (int e = threadIdx.x; e < elems; e += blockDim.x) {
         const int m = e / ncols;
         const int n = col0 + (e - m * ncols);
-        float v = 0.0f;
-        for (int ss = 0; ss < S; ++ss) v += ws[((size_t)ss * M + m) * N + n];
+        float v = ordered_sum<8>(S, [&](int ss) { return ws[((size_t)ss * M + m) * N + n]; });
         if (bias) v += bf16_to_f32(bias[n]);
         out[(size_t)m * N + n] = f32_to_bf16_rne(v);
     }
@@ -169,8 +176,7 @@ __global__ void __launch_bounds__(256)
     if (e >= M * N) return;
     const int m = e / N;
     const int n = e - m * N;
-    float v = 0.0f;
-    for (int ss = 0; ss < S; ++ss) v += ws[((size_t)ss * M + m) * N + n];
+    float v = ordered_sum<8>(S, [&](int ss) { return ws[((size_t)ss * M + m) * N + n]; });
     if (bias) v += bf16_to_f32(bias[n]);
     out[e] = f32_to_bf16_rne(v);
 }

@@ -1,0 +1,206 @@
+"""Offline sweep of launch plans on MI355X -> the dispatch table.
+
+The "sglang PR #30117" page (related PR) and the "vllm PR #48774" page
+(impl. items 3-4) freeze measured autotuning results into a static table
+keyed by shape; this is the same method for this library's two kernels.
+
+For each (M, N, K) point, every admissible plan is timed the way bench.py
+times the GEMM: a HIP graph of back-to-back calls, each call on a different
+W from a pool larger than the 256 MB Infinity Cache (cold weights),
+replayed several times; the median replay time / calls is the plan's
+microseconds per call.  Results are JSON lines.  --emit-table turns result
+files into csrc/dispatch_table.inc (exact (K, N, M) keys).
+
+    python -m latency_skinny_gemm_amd.sweep --points headline --out sweep.jsonl
+    python -m latency_skinny_gemm_amd.sweep --emit-table sweep.jsonl [...]
+"""
+import argparse
+import ctypes
+import datetime
+import json
+import math
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+TABLE = os.path.join(HERE, "csrc", "dispatch_table.inc")
+
+DOT_THREADS = (64, 128, 192, 256, 320, 384, 448, 512, 640, 768, 896, 1024)
+SPLITS = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64)
+
+
+def point_sets():
+    sys.path.insert(0, ROOT)
+    from workloads import configs
+
+    bf16 = [p for p in configs.all_points() if p.dtype == "bf16"]
+    uniq = lambda ps: sorted({(p.M, p.N, p.K) for p in ps}, key=lambda t: (t[2], t[1], t[0]))
+    return {
+        "headline": uniq(configs.HEADLINE),
+        "router": uniq([p for p in bf16 if p.group in ("small_bf16", "router_k7168", "router_shapes")]),
+        "decode": uniq([p for p in bf16 if p.group == "decode_linear"]),
+        "all": uniq(bf16),
+    }
+
+
+def candidates(skg, M, N, K):
+    """Every admissible plan of both kernels for (M, N, K), deduplicated on
+    the completed plan."""
+    out, seen = [], set()
+
+    def add(p):
+        try:
+            q = skg.plan_complete(M, N, K, p)
+        except skg.SkinnyGemmError:
+            return
+        key = (q.kind, q.threads, q.cols, q.splits, q.depth, q.reduce, q.flags, q.k_chunk)
+        if key not in seen:
+            seen.add(key)
+            out.append(q)
+
+    if M <= 16:
+        for flags in (0, skg.FLAG_DOT2):
+            for cols in (1, 2):
+                for T in DOT_THREADS:
+                    add(skg.make_plan(skg.KIND_DOT, T, cols, flags=flags))
+    ksteps = -(-K // 32)
+    MT = -(-M // 16)
+    for NB in (1, 2, 4):
+        if NB * MT > 32:
+            continue
+        groups = -(-N // (16 * NB))
+        for S in SPLITS:
+            if S > ksteps or groups * S > 8192:
+                continue
+            sps = -(-ksteps // S)
+            for nw in (1, 2, 4, 8):
+                spw = -(-sps // nw)
+                D = next((d for d in (1, 2, 4, 8) if d >= spw), 8)
+                for d in sorted({D, max(1, D // 2)}):
+                    for red in ((skg.REDUCE_NONE,) if S == 1 else (skg.REDUCE_LAST, skg.REDUCE_KERNEL)):
+                        add(skg.make_plan(skg.KIND_SPLITK, nw * 64, NB, S, d, red))
+    return out
+
+
+def plan_dict(p):
+    return {k: getattr(p, k) for k in ("kind", "threads", "cols", "splits", "depth", "reduce",
+                                       "flags", "k_chunk", "grid")}
+
+
+def sweep_point(skg, torch, M, N, K, pool_bytes, reps, stream, log):
+    dev = torch.device("cuda:0")
+    slots = max(4, -(-pool_bytes // (N * K * 2)))
+    g = torch.Generator(device=dev)
+    g.manual_seed(M * 1000003 + N * 1009 + K)
+    W = (torch.randn((slots, N, K), generator=g, device=dev) * K ** -0.5).to(torch.bfloat16)
+    X = torch.randn((slots, M, K), generator=g, device=dev).to(torch.bfloat16)
+    O = torch.empty((slots, M, N), dtype=torch.bfloat16, device=dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    L = skg.lib()
+    results = []
+    for p in candidates(skg, M, N, K):
+        def calls(p=p):
+            for s in range(slots):
+                rc = L.skinny_gemm_bf16_planned(X[s].data_ptr(), W[s].data_ptr(), None,
+                                                O[s].data_ptr(), M, N, K, ctypes.byref(p), sptr)
+                if rc != 0:
+                    raise skg.SkinnyGemmError(rc, f"planned {p}")
+        with torch.cuda.stream(stream):
+            calls()  # eager once: grows the workspace outside capture
+        stream.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            calls()
+        times = []
+        with torch.cuda.stream(stream):
+            gr.replay()
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                gr.replay()
+                e1.record(stream)
+                e1.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e3 / slots)
+        del gr
+        times.sort()
+        results.append((times[len(times) // 2], p))
+    results.sort(key=lambda r: r[0])
+    best_us, best = results[0]
+    rec = {"M": M, "N": N, "K": K, "slots": slots, "best_us": round(best_us, 3),
+           "best": plan_dict(best),
+           "candidates": [[round(us, 3), plan_dict(p)] for us, p in results]}
+    log.write(json.dumps(rec) + "\n")
+    log.flush()
+    kind = {1: "dot", 2: "splitk"}[best.kind]
+    print(f"M={M:3d} N={N:5d} K={K:5d}: best {best_us:7.3f} us  {kind} {plan_dict(best)} "
+          f"({len(results)} plans, slots={slots})", flush=True)
+    return rec
+
+
+def run(args):
+    import torch
+
+    import latency_skinny_gemm_amd as skg
+
+    assert torch.cuda.is_available(), "the sweep runs on the GPU"
+    pts = point_sets()[args.points]
+    if args.M:
+        pts = [p for p in pts if p[0] in args.M]
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        skg.reserve(128, 4096, 64)
+    t0 = time.time()
+    with open(args.out, "a") as log:
+        for (M, N, K) in pts:
+            sweep_point(skg, torch, M, N, K, args.pool_mb << 20, args.reps, stream, log)
+            torch.cuda.empty_cache()
+    print(f"swept {len(pts)} points in {time.time() - t0:.0f} s", flush=True)
+
+
+def emit_table(files, out_path=TABLE):
+    best = {}
+    for f in files:
+        for line in open(f):
+            r = json.loads(line)
+            key = (r["K"], r["N"], r["M"])
+            if key not in best or r["best_us"] < best[key]["best_us"]:
+                best[key] = r
+    names = {0: "SKG_REDUCE_NONE", 1: "SKG_REDUCE_LAST", 2: "SKG_REDUCE_KERNEL"}
+    kinds = {1: "SKG_KIND_DOT", 2: "SKG_KIND_SPLITK"}
+    lines = [
+        "// dispatch_table.inc -- generated by latency_skinny_gemm_amd/sweep.py --emit-table",
+        f"// from cold-weight graph-replay timings on one MI355X ({datetime.date.today()}).",
+        "// {dtype, K, N, M, {kind, threads, cols, splits, depth, reduce, flags}},  // us/call",
+    ]
+    for (K, N, M) in sorted(best):
+        b = best[(K, N, M)]["best"]
+        lines.append(
+            f"{{SKG_DTYPE_BF16, {K}, {N}, {M}, {{{kinds[b['kind']]}, {b['threads']}, {b['cols']}, "
+            f"{b['splits']}, {b['depth']}, {names[b['reduce']]}, {b['flags']}}}}},"
+            f"  // {best[(K, N, M)]['best_us']:.3f}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {len(best)} entries to {out_path}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--points", default="headline", choices=("headline", "router", "decode", "all"))
+    ap.add_argument("--M", type=int, nargs="*", help="restrict to these M")
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "sweep.jsonl"))
+    ap.add_argument("--pool-mb", type=int, default=512)
+    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--emit-table", nargs="+", metavar="JSONL")
+    args = ap.parse_args()
+    if args.emit_table:
+        emit_table(args.emit_table)
+        return 0
+    os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
+    run(args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -184,15 +184,17 @@ def _check_coverage(p, M, N, K):
     for s in range(S):
         kbeg, kend = s * kc, min(K, (s + 1) * kc)
         nsteps = -(-(kend - kbeg) // 32)
+        spw = -(-nsteps // nw)
         for w in range(nw):
-            my = -(-(nsteps - w) // nw) if nsteps > w else 0
+            first = w * spw
+            my = max(0, min(spw, nsteps - first))
             nch = -(-my // D)
             consumed = [0] if nch <= 1 else [c for c0 in range(0, nch, 2) for c in (c0, c0 + 1)]
             for ch in consumed:
                 for d in range(D):
                     i = ch * D + d
                     for g in range(4):  # lane groups of 16: k offset 8*g
-                        k = kbeg + (w + nw * i) * 32 + 8 * g
+                        k = kbeg + (first + i) * 32 + 8 * g
                         if i < my and k < kend:
                             for kk in range(k, k + 8):
                                 seen[kk] += 1

@@ -48,15 +48,16 @@ def _kernel_plans(skg, M, N, K):
     """The library's plan plus one explicit plan per kernel / reduction."""
     plans = [("default", None)]
     if M <= 16:
-        for cols in (1, 2):
-            for threads in range(256, 1025, 64):  # the smallest workgroup that fits
-                p = skg.make_plan(skg.KIND_DOT, threads, cols=cols)
-                try:
-                    skg.plan_complete(M, N, K, p)
-                except skg.SkinnyGemmError:
-                    continue
-                plans.append((f"dot_c{cols}_t{threads}", p))
-                break
+        for flags in (0, skg.FLAG_DOT2):
+            for cols in (1, 2):
+                for threads in range(256, 1025, 64):  # the smallest workgroup that fits
+                    p = skg.make_plan(skg.KIND_DOT, threads, cols=cols, flags=flags)
+                    try:
+                        skg.plan_complete(M, N, K, p)
+                    except skg.SkinnyGemmError:
+                        continue
+                    plans.append((f"dot_c{cols}_t{threads}_f{flags}", p))
+                    break
     mt = (M + 15) // 16
     nb = 4 if mt >= 4 else (2 if mt >= 2 else 1)
     threads = 128 if nb * mt > 16 else 256
