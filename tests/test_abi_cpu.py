@@ -119,11 +119,23 @@ def test_library_plan_is_valid_and_covers(lib, p):
 
 
 def test_split_count_follows_cu_count(lib):
+    # the default rule (no table below 256 CUs) sizes the grid to the device
     small = skg.plan_on(8, 256, 7168, 64)
-    big = skg.plan_on(8, 256, 7168, 256)
-    assert small.kind == big.kind == skg.KIND_SPLITK
-    assert small.splits * small.grid // small.splits <= big.grid
-    assert small.grid >= 64 and big.grid >= 256
+    big = skg.plan_on(8, 256, 7168, 200)
+    assert small.kind == big.kind == skg.KIND_SPLITK and small.from_table == big.from_table == 0
+    assert small.splits < big.splits
+    assert small.grid >= 64 and big.grid >= 200
+
+
+def test_table_entries_are_exact_and_valid(lib):
+    # every table entry is returned for its exact (M, N, K) at 256 CUs, and
+    # its completed plan covers the problem
+    for p in BF16:
+        q = skg.plan(p.M, p.N, p.K)
+        assert q.from_table == 1, p.key()
+        _check_coverage(q, p.M, p.N, p.K)
+    # a shape outside the table falls back to the rule
+    assert skg.plan(8, 320, 7168).from_table == 0
 
 
 @pytest.mark.parametrize("plan,M,N,K", [
