@@ -77,6 +77,8 @@ extern "C" {
 
 #define SKG_KIND_DOT 1    /* dot-product kernel: whole K per workgroup */
 #define SKG_KIND_SPLITK 2 /* MFMA kernel, K split over workgroups */
+#define SKG_KIND_TILED 3  /* MFMA kernel with LDS-staged x and W tiles, K split
+                             over workgroups (wide column tiles, larger M) */
 
 #define SKG_REDUCE_NONE 0  /* splits == 1: no cross-workgroup reduction */
 #define SKG_REDUCE_LAST 1  /* the last workgroup to finish a tile reduces it */
@@ -111,10 +113,14 @@ typedef struct SkgPlan {
     int kind;     /* SKG_KIND_DOT or SKG_KIND_SPLITK */
     int threads;  /* workgroup size, a multiple of 64, <= 1024 */
     int cols;     /* DOT: output columns per workgroup (1, 2);
-                     SPLITK: 16-column blocks per workgroup (1, 2, 4) */
-    int splits;   /* SPLITK: number of K chunks S (>= 1); DOT: 1 */
+                     SPLITK: 16-column blocks per workgroup (1, 2, 4);
+                     TILED: 16-column blocks per workgroup (1, 2, 4, 8, 16) */
+    int splits;   /* SPLITK, TILED: number of K chunks S (>= 1); DOT: 1 */
     int depth;    /* SPLITK: 32-wide K steps a wave keeps in flight (1, 2, 4, 8);
+                     TILED: 32-wide K steps per pipeline chunk (1, 2, 4);
                      DOT: 16-byte vectors per thread per column (derived) */
+    int waves_m;  /* TILED: waves along M (1, 2, 4; the other 4/waves_m waves
+                     split the columns); 0 = chosen by the library */
     int reduce;   /* SKG_REDUCE_*; NONE iff splits == 1 */
     int flags;    /* SKG_FLAG_* */
     int k_chunk;  /* (derived) SPLITK: K elements per split, multiple of 32 */

@@ -13,7 +13,7 @@ import torch
 
 __all__ = ["SkgPlan", "SkinnyGemmError", "gemm_bf16", "gemm_bf16_planned", "plan", "plan_on",
            "plan_complete", "reserve", "release_all", "status_string", "library_path",
-           "KIND_DOT", "KIND_SPLITK", "REDUCE_NONE", "REDUCE_LAST", "REDUCE_KERNEL", "FLAG_DOT2",
+           "KIND_DOT", "KIND_SPLITK", "KIND_TILED", "REDUCE_NONE", "REDUCE_LAST", "REDUCE_KERNEL", "FLAG_DOT2",
            "DTYPE_BF16", "DTYPE_FP8"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +32,7 @@ FP8_PER_TENSOR = 1
 FP8_MX32 = 2
 KIND_DOT = 1
 KIND_SPLITK = 2
+KIND_TILED = 3
 REDUCE_NONE = 0
 REDUCE_LAST = 1
 REDUCE_KERNEL = 2
@@ -41,7 +42,7 @@ MAX_M = 128
 
 class SkgPlan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in
-                ("kind", "threads", "cols", "splits", "depth", "reduce", "flags",
+                ("kind", "threads", "cols", "splits", "depth", "waves_m", "reduce", "flags",
                  "k_chunk", "m_tiles", "grid", "from_table")]
 
     def as_dict(self):
@@ -168,10 +169,10 @@ def gemm_bf16_planned(x, W, p, bias=None, out=None, stream=None):
     return out
 
 
-def make_plan(kind, threads, cols=1, splits=1, depth=0, reduce=REDUCE_NONE, flags=0):
+def make_plan(kind, threads, cols=1, splits=1, depth=0, reduce=REDUCE_NONE, flags=0, waves_m=0):
     p = SkgPlan()
     p.kind, p.threads, p.cols, p.splits, p.depth, p.reduce = kind, threads, cols, splits, depth, reduce
-    p.flags = flags
+    p.flags, p.waves_m = flags, waves_m
     return p
 
 

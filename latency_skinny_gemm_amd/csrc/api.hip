@@ -119,7 +119,8 @@ int run_bf16(const void *x, const void *W, const void *bias, void *out, int M, i
         int rc = acquire(stream, workspace_floats(p, M, N), (size_t)tile_count(p, N), &ws, &tk);
         if (rc != SKG_OK) return rc;
     }
-    int e = launch_splitk(p, x, W, bias, out, ws, tk, M, N, K, stream);
+    int e = p.kind == SKG_KIND_TILED ? launch_tiled(p, x, W, bias, out, ws, tk, M, N, K, stream)
+                                     : launch_splitk(p, x, W, bias, out, ws, tk, M, N, K, stream);
     return e == (int)hipSuccess ? SKG_OK : SKG_ERR_HIP;
 }
 
@@ -130,7 +131,9 @@ size_t workspace_floats(const SkgPlan &p, int M, int N) {
 }
 
 int tile_count(const SkgPlan &p, int N) {
-    return p.kind == SKG_KIND_SPLITK ? (N + 16 * p.cols - 1) / (16 * p.cols) : 0;
+    return (p.kind == SKG_KIND_SPLITK || p.kind == SKG_KIND_TILED)
+               ? (N + 16 * p.cols - 1) / (16 * p.cols)
+               : 0;
 }
 
 }  // namespace skg

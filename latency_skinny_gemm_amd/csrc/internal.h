@@ -47,6 +47,20 @@ constexpr bool splitk_built(int MT, int NB, int D) { return NB * MT <= 32 && D *
 // SPLITK: K steps (32 wide) in flight per wave per stage.
 constexpr int kSplitKDepths[] = {1, 2, 4, 8};
 
+// TILED: 4 waves as WM x WN; a wave owns MTW m-tiles x NBW column blocks.
+// Built when the accumulators fit 128 AGPRs, the two register stages plus
+// fragments fit the VGPRs, and the two LDS buffers fit 60 KB.
+constexpr int kTiledThreads = 256;
+constexpr int tiled_pairs_per_thread(int MTW, int NBW, int WM) {
+    return ((MTW * WM + NBW * (4 / WM)) * 64 + 255) / 256;
+}
+constexpr bool tiled_built(int MTW, int NBW, int WM, int D) {
+    return MTW * NBW <= 32 && 8 * D * tiled_pairs_per_thread(MTW, NBW, WM) + 4 * (MTW + NBW) <= 160 &&
+           2 * D * (MTW * WM + NBW * (4 / WM)) <= 60;
+}
+// The wave arrangement of a completed TILED plan for M rows.
+void tiled_shape(const SkgPlan &p, int M, int *MTW, int *NBW, int *WM);
+
 // Host-side validation and planning (plan.cpp).  No HIP calls.
 int check_sizes(int M, int N, int K, int dtype);
 int complete_plan(int M, int N, int K, int dtype, SkgPlan *p);
@@ -62,5 +76,9 @@ int launch_dot(const SkgPlan &p, const void *x, const void *W, const void *bias,
                int M, int N, int K, hipStream_t stream);
 int launch_splitk(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
                   float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream);
+int launch_tiled(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
+                 float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream);
+int launch_splitk_reduce(const float *ws, const void *bias, void *out, int M, int N, int S,
+                         hipStream_t stream);
 
 }  // namespace skg

@@ -26,6 +26,7 @@
 //    output does not depend on which workgroup finishes last.
 #include "device_common.h"
 #include "internal.h"
+#include "splitk_common.h"
 
 namespace skg {
 
@@ -139,32 +140,7 @@ __global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
     }
     if (S == 1 || reduce != SKG_REDUCE_LAST) return;
 
-    // ---- last workgroup of tile j sums the S partials in ascending s
-    // Every wave waits until its partial stores are in the L2 before the
-    // barrier; then one agent-scope acquire-release ticket increment by
-    // thread 0 publishes the whole workgroup's partials (its release writes
-    // the XCD's L2 back to memory once per workgroup, not once per wave) and,
-    // in the last workgroup, its acquire invalidates the stale L1/L2 lines
-    // before any wave of that workgroup reads the partials.
-    wait_all_memory();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev =
-            __hip_atomic_fetch_add(&tickets[j], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = (prev == (unsigned)S - 1u) ? 1u : 0u;
-        if (is_last)  // every partial of tile j has arrived: rearm for the next call
-            __hip_atomic_store(&tickets[j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!is_last) return;
-    const int elems = M * ncols;
-    for (int e = threadIdx.x; e < elems; e += blockDim.x) {
-        const int m = e / ncols;
-        const int n = col0 + (e - m * ncols);
-        float v = ordered_sum<8>(S, [&](int ss) { return ws[((size_t)ss * M + m) * N + n]; });
-        if (bias) v += bf16_to_f32(bias[n]);
-        out[(size_t)m * N + n] = f32_to_bf16_rne(v);
-    }
+    last_arriver_reduce(ws, tickets, bias, out, M, N, S, j, col0, ncols, &is_last);
 }
 
 // Second-pass reduction: the same sum in the same order as the in-kernel
@@ -237,16 +213,21 @@ SplitKLaunch pick(int MT, int NB, int D) {
 
 }  // namespace
 
+int launch_splitk_reduce(const float *ws, const void *bias, void *out, int M, int N, int S,
+                         hipStream_t stream) {
+    const int elems = M * N;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((elems + 255) / 256), dim3(256), 0, stream, ws,
+                       (const uint16_t *)bias, (uint16_t *)out, M, N, S);
+    return (int)hipGetLastError();
+}
+
 int launch_splitk(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
                   float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream) {
     SplitKLaunch f = pick(p.m_tiles, p.cols, p.depth);
     if (!f) return (int)hipErrorInvalidConfiguration;
     int rc = f(p, x, W, bias, out, ws, tickets, M, N, K, stream);
     if (rc != (int)hipSuccess || p.splits == 1 || p.reduce != SKG_REDUCE_KERNEL) return rc;
-    const int elems = M * N;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((elems + 255) / 256), dim3(256), 0, stream, ws,
-                       (const uint16_t *)bias, (uint16_t *)out, M, N, p.splits);
-    return (int)hipGetLastError();
+    return launch_splitk_reduce(ws, bias, out, M, N, p.splits, stream);
 }
 
 }  // namespace skg

@@ -1,0 +1,46 @@
+// splitk_common.h -- the ordered cross-workgroup reduction shared by the
+// split-K kernels (device code; included by the kernel sources only).
+#pragma once
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace skg {
+
+// Called by every thread of a workgroup that has just written its fp32
+// partial ws[s][m][n] for the columns [col0, col0 + ncols) of tile j.
+// Every wave waits until its partial stores are in the L2; then one
+// agent-scope acquire-release ticket increment by thread 0 publishes the
+// whole workgroup's partials (its release writes the XCD's L2 back to
+// memory once per workgroup) and, in the last workgroup of the tile, its
+// acquire invalidates stale L1/L2 lines before any wave reads partials.
+// That workgroup sums the S partials in ascending s, adds the bias and
+// rounds once; it re-arms the ticket.  No workgroup waits on another.
+__device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
+                                                    unsigned *__restrict__ tickets,
+                                                    const uint16_t *__restrict__ bias,
+                                                    uint16_t *__restrict__ out, int M, int N,
+                                                    int S, int j, int col0, int ncols,
+                                                    unsigned *is_last) {
+    wait_all_memory();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned prev =
+            __hip_atomic_fetch_add(&tickets[j], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        *is_last = (prev == (unsigned)S - 1u) ? 1u : 0u;
+        if (*is_last)  // every partial of tile j has arrived: rearm for the next call
+            __hip_atomic_store(&tickets[j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!*is_last) return;
+    const int elems = M * ncols;
+    for (int e = threadIdx.x; e < elems; e += blockDim.x) {
+        const int m = e / ncols;
+        const int n = col0 + (e - m * ncols);
+        float v = ordered_sum<8>(S, [&](int ss) { return ws[((size_t)ss * M + m) * N + n]; });
+        if (bias) v += bf16_to_f32(bias[n]);
+        out[(size_t)m * N + n] = f32_to_bf16_rne(v);
+    }
+}
+
+}  // namespace skg

@@ -55,7 +55,7 @@ def candidates(skg, M, N, K):
             q = skg.plan_complete(M, N, K, p)
         except skg.SkinnyGemmError:
             return
-        key = (q.kind, q.threads, q.cols, q.splits, q.depth, q.reduce, q.flags, q.k_chunk)
+        key = (q.kind, q.threads, q.cols, q.splits, q.depth, q.waves_m, q.reduce, q.flags, q.k_chunk)
         if key not in seen:
             seen.add(key)
             out.append(q)
@@ -81,12 +81,23 @@ def candidates(skg, M, N, K):
                 for d in sorted({D, max(1, D // 2)}):
                     for red in ((skg.REDUCE_NONE,) if S == 1 else (skg.REDUCE_LAST, skg.REDUCE_KERNEL)):
                         add(skg.make_plan(skg.KIND_SPLITK, nw * 64, NB, S, d, red))
+    # LDS-staged tiles: worth it once a workgroup covers many columns
+    if M > 4 or N >= 1024:
+        for NB in (2, 4, 8, 16):
+            groups = -(-N // (16 * NB))
+            for S in SPLITS:
+                if S > ksteps or not (32 <= groups * S <= 4096):
+                    continue
+                for wm in (1, 2, 4):
+                    for d in (1, 2, 4):
+                        for red in ((skg.REDUCE_NONE,) if S == 1 else (skg.REDUCE_LAST, skg.REDUCE_KERNEL)):
+                            add(skg.make_plan(skg.KIND_TILED, 256, NB, S, d, red, waves_m=wm))
     return out
 
 
 def plan_dict(p):
-    return {k: getattr(p, k) for k in ("kind", "threads", "cols", "splits", "depth", "reduce",
-                                       "flags", "k_chunk", "grid")}
+    return {k: getattr(p, k) for k in ("kind", "threads", "cols", "splits", "depth", "waves_m",
+                                       "reduce", "flags", "k_chunk", "grid")}
 
 
 def sweep_point(skg, torch, M, N, K, pool_bytes, reps, stream, log):
@@ -133,7 +144,7 @@ def sweep_point(skg, torch, M, N, K, pool_bytes, reps, stream, log):
            "candidates": [[round(us, 3), plan_dict(p)] for us, p in results]}
     log.write(json.dumps(rec) + "\n")
     log.flush()
-    kind = {1: "dot", 2: "splitk"}[best.kind]
+    kind = {1: "dot", 2: "splitk", 3: "tiled"}[best.kind]
     print(f"M={M:3d} N={N:5d} K={K:5d}: best {best_us:7.3f} us  {kind} {plan_dict(best)} "
           f"({len(results)} plans, slots={slots})", flush=True)
     return rec
@@ -168,17 +179,17 @@ def emit_table(files, out_path=TABLE):
             if key not in best or r["best_us"] < best[key]["best_us"]:
                 best[key] = r
     names = {0: "SKG_REDUCE_NONE", 1: "SKG_REDUCE_LAST", 2: "SKG_REDUCE_KERNEL"}
-    kinds = {1: "SKG_KIND_DOT", 2: "SKG_KIND_SPLITK"}
+    kinds = {1: "SKG_KIND_DOT", 2: "SKG_KIND_SPLITK", 3: "SKG_KIND_TILED"}
     lines = [
         "// dispatch_table.inc -- generated by latency_skinny_gemm_amd/sweep.py --emit-table",
         f"// from cold-weight graph-replay timings on one MI355X ({datetime.date.today()}).",
-        "// {dtype, K, N, M, {kind, threads, cols, splits, depth, reduce, flags}},  // us/call",
+        "// {dtype, K, N, M, {kind, threads, cols, splits, depth, waves_m, reduce, flags}},  // us/call",
     ]
     for (K, N, M) in sorted(best):
         b = best[(K, N, M)]["best"]
         lines.append(
             f"{{SKG_DTYPE_BF16, {K}, {N}, {M}, {{{kinds[b['kind']]}, {b['threads']}, {b['cols']}, "
-            f"{b['splits']}, {b['depth']}, {names[b['reduce']]}, {b['flags']}}}}},"
+            f"{b['splits']}, {b['depth']}, {b.get('waves_m', 0)}, {names[b['reduce']]}, {b['flags']}}}}},"
             f"  // {best[(K, N, M)]['best_us']:.3f}")
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")

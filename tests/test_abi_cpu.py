@@ -183,6 +183,9 @@ def _check_coverage(p, M, N, K):
         assert vecs == list(range(K8))
         assert T % 64 == 0 and T <= 1024 and p.grid == -(-N // C)
         return
+    if p.kind == skg.KIND_TILED:
+        _check_tiled_coverage(p, M, N, K)
+        return
     assert p.kind == skg.KIND_SPLITK
     S, NB, D, kc = p.splits, p.cols, p.depth, p.k_chunk
     nw = p.threads // 64
@@ -211,3 +214,64 @@ def _check_coverage(p, M, N, K):
                             for kk in range(k, k + 8):
                                 seen[kk] += 1
     assert seen == [1] * K
+
+
+def _check_tiled_coverage(p, M, N, K):
+    S, NB, D, kc, WM = p.splits, p.cols, p.depth, p.k_chunk, p.waves_m
+    WN = 4 // WM
+    MT = -(-M // 16)
+    MTW = {1: 1, 2: 2, 3: 4, 4: 4}[-(-MT // WM)]
+    NBW = NB // WN
+    assert p.threads == 256 and NB % WN == 0 and MTW * WM >= MT
+    groups = -(-N // (16 * NB))
+    assert p.grid == groups * S and kc % 32 == 0 and (S - 1) * kc < K <= S * kc
+    # waves partition the workgroup's (m-tile, column-block) grid
+    owned = sorted((wm * MTW + a, wn * NBW + b) for wm in range(WM) for wn in range(WN)
+                   for a in range(MTW) for b in range(NBW))
+    assert owned == sorted((a, b) for a in range(MTW * WM) for b in range(NB))
+    # load slots: every (block, lane) pair of a step exactly once
+    blk = MTW * WM + NB
+    pairs = blk * 64
+    R = -(-pairs // 256)
+    slots = sorted(t + 256 * r for t in range(256) for r in range(R) if t + 256 * r < pairs)
+    assert slots == list(range(pairs))
+    # K: every step of every split computed once (chunks alternate buffers)
+    seen = [0] * K
+    for s in range(S):
+        kbeg, kend = s * kc, min(K, (s + 1) * kc)
+        nsteps = -(-(kend - kbeg) // 32)
+        nch = -(-nsteps // D)
+        done = []
+        for c in range(0, nch, 2):
+            done.append(c)
+            if c + 1 < nch:
+                done.append(c + 1)
+        assert sorted(done) == list(range(nch))
+        for c in done:
+            for d in range(D):
+                st = c * D + d
+                for g in range(4):
+                    k = kbeg + st * 32 + 8 * g
+                    if st < nsteps and k < kend:
+                        for kk in range(k, k + 8):
+                            seen[kk] += 1
+    assert seen == [1] * K
+
+
+@pytest.mark.parametrize("M,N,K,NB,wm,D,S", [
+    (128, 4096, 7168, 16, 2, 1, 16), (64, 576, 7168, 4, 0, 2, 12), (8, 4096, 7168, 8, 1, 2, 8),
+    (33, 200, 2056, 4, 0, 2, 3), (1, 2112, 7168, 16, 0, 1, 4), (5, 100, 2880, 2, 4, 1, 5)])
+def test_tiled_plans_cover(lib, M, N, K, NB, wm, D, S):
+    q = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_TILED, 256, NB, S, D, skg.REDUCE_LAST,
+                                                 waves_m=wm))
+    assert q.kind == skg.KIND_TILED and q.waves_m in (1, 2, 4)
+    _check_coverage(q, M, N, K)
+
+
+def test_tiled_rejects_bad_plans(lib):
+    for plan in (dict(threads=128, cols=4), dict(threads=256, cols=3), dict(threads=256, cols=4, depth=8),
+                 dict(threads=256, cols=4, waves_m=3), dict(threads=256, cols=2, waves_m=1)):
+        p = skg.make_plan(skg.KIND_TILED, plan["threads"], plan["cols"], 2, plan.get("depth", 1),
+                          skg.REDUCE_LAST, waves_m=plan.get("waves_m", 0))
+        with pytest.raises(skg.SkinnyGemmError):
+            skg.plan_complete(128, 4096, 7168, p)
