@@ -135,11 +135,21 @@ int skinny_gemm_bf16(const void *x, const void *W, const void *bias, const void 
                      void *out, int M, int N, int K, hipStream_t stream);
 
 /* FP8 e4m3fn GEMM with bf16 bias and output; `scales` is a HOST pointer to
- * the struct above.  K % 16 == 0 (per-tensor) or K % 32 == 0 (MX).
- * Returns SKG_ERR_UNSUPPORTED for a mode this build does not implement. */
+ * the struct above (its pointers are device pointers; sx, sw 4-byte
+ * aligned).  x[M,K] and W[N,K] are e4m3fn bytes, row-major, 16-byte
+ * aligned.  K % 16 == 0 (per-tensor) or K % 32 == 0 (MX).  Accumulation in
+ * fp32; per-tensor mode multiplies by sx*sw once before the bias; MX mode
+ * scales every 32-element block product by its two exponents.  An e8m0 byte
+ * 0xFF (NaN) makes the outputs that use it NaN. */
 int skinny_gemm_fp8(const void *x, const void *W, const void *bias,
                     const skinny_fp8_scales *scales, void *out, int M, int N, int K,
                     hipStream_t stream);
+
+/* FP8 GEMM with a caller-made plan (kinds SKG_KIND_DOT or SKG_KIND_SPLITK;
+ * completed as by skinny_gemm_plan_complete with SKG_DTYPE_FP8). */
+int skinny_gemm_fp8_planned(const void *x, const void *W, const void *bias,
+                            const skinny_fp8_scales *scales, void *out, int M, int N, int K,
+                            const SkgPlan *plan, hipStream_t stream);
 
 /* The dispatcher's decision for (M, N, K, dtype), written to *plan; no HIP
  * call.  The "vllm PR #48774" page's rule: a tuned (K, N) -> {M: config}

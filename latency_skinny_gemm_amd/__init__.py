@@ -11,7 +11,8 @@ import os
 
 import torch
 
-__all__ = ["SkgPlan", "SkinnyGemmError", "gemm_bf16", "gemm_bf16_planned", "plan", "plan_on",
+__all__ = ["SkgPlan", "SkinnyGemmError", "gemm_bf16", "gemm_bf16_planned", "gemm_fp8",
+           "gemm_fp8_planned", "plan", "plan_on",
            "plan_complete", "reserve", "release_all", "status_string", "library_path",
            "KIND_DOT", "KIND_SPLITK", "KIND_TILED", "REDUCE_NONE", "REDUCE_LAST", "REDUCE_KERNEL", "FLAG_DOT2",
            "DTYPE_BF16", "DTYPE_FP8"]
@@ -86,6 +87,8 @@ def _load():
     L.skinny_gemm_bf16_planned.restype = I
     L.skinny_gemm_fp8.argtypes = [P, P, P, ctypes.POINTER(Fp8Scales), P, I, I, I, P]
     L.skinny_gemm_fp8.restype = I
+    L.skinny_gemm_fp8_planned.argtypes = [P, P, P, ctypes.POINTER(Fp8Scales), P, I, I, I, PP, P]
+    L.skinny_gemm_fp8_planned.restype = I
     L.skinny_gemm_plan.argtypes = [I, I, I, I, PP]
     L.skinny_gemm_plan.restype = I
     L.skinny_gemm_plan_on.argtypes = [I, I, I, I, I, PP]
@@ -166,6 +169,59 @@ def gemm_bf16_planned(x, W, p, bias=None, out=None, stream=None):
     rc = _load().skinny_gemm_bf16_planned(_ptr(x), _ptr(W), _ptr(bias), _ptr(out), M, N, K,
                                           ctypes.byref(p), _stream_ptr(stream))
     _check(rc, f"skinny_gemm_bf16_planned(M={M}, N={N}, K={K}, {p})")
+    return out
+
+
+def _fp8_args(xq, wq, sx, sw, xe, we, bias, out):
+    """Checks FP8 operands; returns (M, N, K, Fp8Scales, out)."""
+    for name, t in (("xq", xq), ("wq", wq)):
+        if t.dim() != 2 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 2-D device tensor")
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise TypeError(f"{name} must be float8_e4m3fn (or its bytes as uint8)")
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K != K2:
+        raise ValueError("xq[M,K] and wq[N,K] expected")
+    sc = Fp8Scales()
+    if sx is not None or sw is not None:
+        if xe is not None or we is not None:
+            raise ValueError("give per-tensor scales (sx, sw) or MX exponents (xe, we), not both")
+        for name, t in (("sx", sx), ("sw", sw)):
+            if t is None or t.dtype != torch.float32 or t.numel() != 1 or not t.is_cuda:
+                raise TypeError(f"{name} must be a one-element float32 device tensor")
+        sc.mode, sc.sx, sc.sw = FP8_PER_TENSOR, sx.data_ptr(), sw.data_ptr()
+    else:
+        for name, t, rows in (("xe", xe, M), ("we", we, N)):
+            if t is None or t.dtype not in (torch.uint8, torch.float8_e8m0fnu) or not t.is_cuda \
+                    or not t.is_contiguous() or tuple(t.shape) != (rows, K // 32):
+                raise TypeError(f"{name} must be a contiguous uint8 [{rows}, K/32] device tensor")
+        sc.mode, sc.x_e8m0, sc.w_e8m0 = FP8_MX32, xe.data_ptr(), we.data_ptr()
+    if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (N,)
+                             or not bias.is_cuda):
+        raise TypeError("bias must be bf16 [N] on the device")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise TypeError("out must be contiguous bf16 [M, N]")
+    return M, N, K, sc, out
+
+
+def gemm_fp8(xq, wq, sx=None, sw=None, xe=None, we=None, bias=None, out=None, stream=None):
+    """FP8 e4m3 GEMM, bf16 out: per-tensor (sx, sw) or MX (xe, we) scales."""
+    M, N, K, sc, out = _fp8_args(xq, wq, sx, sw, xe, we, bias, out)
+    rc = _load().skinny_gemm_fp8(_ptr(xq), _ptr(wq), _ptr(bias), ctypes.byref(sc), _ptr(out),
+                                 M, N, K, _stream_ptr(stream))
+    _check(rc, f"skinny_gemm_fp8(M={M}, N={N}, K={K}, mode={sc.mode})")
+    return out
+
+
+def gemm_fp8_planned(xq, wq, p, sx=None, sw=None, xe=None, we=None, bias=None, out=None,
+                     stream=None):
+    M, N, K, sc, out = _fp8_args(xq, wq, sx, sw, xe, we, bias, out)
+    rc = _load().skinny_gemm_fp8_planned(_ptr(xq), _ptr(wq), _ptr(bias), ctypes.byref(sc),
+                                         _ptr(out), M, N, K, ctypes.byref(p), _stream_ptr(stream))
+    _check(rc, f"skinny_gemm_fp8_planned(M={M}, N={N}, K={K}, {p})")
     return out
 
 

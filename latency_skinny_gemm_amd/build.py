@@ -26,7 +26,8 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
               "-I", "/opt/rocm/include", "-I", INCLUDE, "-I", CSRC]
 
-LIB_HIP = ["api.hip", "kernels_dot.hip", "kernels_splitk.hip", "kernels_tiled.hip"]
+LIB_HIP = ["api.hip", "kernels_dot.hip", "kernels_splitk.hip", "kernels_tiled.hip",
+           "kernels_fp8.hip"]
 LIB_HOST = ["plan.cpp"]
 FLOORS_HIP = ["floors.hip"]
 

@@ -124,6 +124,19 @@ int run_bf16(const void *x, const void *W, const void *bias, void *out, int M, i
     return e == (int)hipSuccess ? SKG_OK : SKG_ERR_HIP;
 }
 
+int run_fp8(const void *x, const void *W, const void *bias, const skinny_fp8_scales *sc, void *out,
+            int M, int N, int K, const SkgPlan &p, hipStream_t stream) {
+    Fp8Args a{x, W, bias, out, sc->mode, sc->sx, sc->sw, sc->x_e8m0, sc->w_e8m0};
+    float *ws = nullptr;
+    unsigned *tk = nullptr;
+    if (p.kind != SKG_KIND_DOT && p.splits > 1) {
+        int rc = acquire(stream, workspace_floats(p, M, N), (size_t)tile_count(p, N), &ws, &tk);
+        if (rc != SKG_OK) return rc;
+    }
+    int e = launch_fp8(p, a, ws, tk, M, N, K, stream);
+    return e == (int)hipSuccess ? SKG_OK : SKG_ERR_HIP;
+}
+
 }  // namespace
 
 size_t workspace_floats(const SkgPlan &p, int M, int N) {
@@ -173,18 +186,51 @@ extern "C" int skinny_gemm_bf16_planned(const void *x, const void *W, const void
 extern "C" int skinny_gemm_fp8(const void *x, const void *W, const void *bias,
                                const skinny_fp8_scales *scales, void *out, int M, int N, int K,
                                hipStream_t stream) {
-    (void)stream;
     int rc = check_sizes(M, N, K, SKG_DTYPE_FP8);
     if (rc != SKG_OK) return rc;
     if (M == 0 || N == 0) return SKG_OK;
     if (!scales || !x || !W || !out) return SKG_ERR_INVALID_ARG;
-    if (scales->mode != SKG_FP8_PER_TENSOR && scales->mode != SKG_FP8_MX32)
-        return SKG_ERR_INVALID_ARG;
-    if (scales->mode == SKG_FP8_MX32 && K % 32 != 0) return SKG_ERR_UNSUPPORTED;
+    const int mode = scales->mode;
+    if (mode != SKG_FP8_PER_TENSOR && mode != SKG_FP8_MX32) return SKG_ERR_INVALID_ARG;
+    if (mode == SKG_FP8_PER_TENSOR && (!scales->sx || !scales->sw)) return SKG_ERR_INVALID_ARG;
+    if (mode == SKG_FP8_MX32 && (!scales->x_e8m0 || !scales->w_e8m0)) return SKG_ERR_INVALID_ARG;
+    if (mode == SKG_FP8_MX32 && K % 32 != 0) return SKG_ERR_UNSUPPORTED;
     if (!aligned(x, 16) || !aligned(W, 16) || !aligned(out, 2) || (bias && !aligned(bias, 2)))
         return SKG_ERR_ALIGNMENT;
-    (void)bias;
-    return SKG_ERR_UNSUPPORTED;  // the FP8 kernels are not part of this build yet
+    if (mode == SKG_FP8_PER_TENSOR && (!aligned(scales->sx, 4) || !aligned(scales->sw, 4)))
+        return SKG_ERR_ALIGNMENT;
+    const size_t ob = (size_t)M * N * 2;
+    if (overlap(out, ob, x, (size_t)M * K) || overlap(out, ob, W, (size_t)N * K) ||
+        overlap(out, ob, bias, (size_t)N * 2))
+        return SKG_ERR_INVALID_ARG;
+    SkgPlan p;
+    rc = skinny_gemm_plan(M, N, K, SKG_DTYPE_FP8, &p);
+    if (rc != SKG_OK) return rc;
+    return run_fp8(x, W, bias, scales, out, M, N, K, p, stream);
+}
+
+extern "C" int skinny_gemm_fp8_planned(const void *x, const void *W, const void *bias,
+                                       const skinny_fp8_scales *scales, void *out, int M, int N,
+                                       int K, const SkgPlan *plan, hipStream_t stream) {
+    int rc = check_sizes(M, N, K, SKG_DTYPE_FP8);
+    if (rc != SKG_OK) return rc;
+    if (M == 0 || N == 0) return SKG_OK;
+    if (!plan || !scales || !x || !W || !out) return SKG_ERR_INVALID_ARG;
+    const int mode = scales->mode;
+    if (mode != SKG_FP8_PER_TENSOR && mode != SKG_FP8_MX32) return SKG_ERR_INVALID_ARG;
+    if (mode == SKG_FP8_PER_TENSOR && (!scales->sx || !scales->sw)) return SKG_ERR_INVALID_ARG;
+    if (mode == SKG_FP8_MX32 && (!scales->x_e8m0 || !scales->w_e8m0)) return SKG_ERR_INVALID_ARG;
+    if (mode == SKG_FP8_MX32 && K % 32 != 0) return SKG_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(out, 2) || (bias && !aligned(bias, 2)))
+        return SKG_ERR_ALIGNMENT;
+    const size_t ob = (size_t)M * N * 2;
+    if (overlap(out, ob, x, (size_t)M * K) || overlap(out, ob, W, (size_t)N * K) ||
+        overlap(out, ob, bias, (size_t)N * 2))
+        return SKG_ERR_INVALID_ARG;
+    SkgPlan p = *plan;
+    rc = complete_plan(M, N, K, SKG_DTYPE_FP8, &p);
+    if (rc != SKG_OK) return rc;
+    return run_fp8(x, W, bias, scales, out, M, N, K, p, stream);
 }
 
 extern "C" int skinny_gemm_reserve(int max_M, int max_N, int max_S, hipStream_t stream) {

@@ -61,6 +61,40 @@ constexpr bool tiled_built(int MTW, int NBW, int WM, int D) {
 // The wave arrangement of a completed TILED plan for M rows.
 void tiled_shape(const SkgPlan &p, int M, int *MTW, int *NBW, int *WM);
 
+// FP8 dot kernel: x counted packed plus its widened words (as for bf16
+// without dot2) and, in MX mode, one scale byte per (row, vector); a plan is
+// checked for the MX count, the larger.
+constexpr int kFp8DotVecs[] = {1, 2, 4};
+constexpr int fp8_dot_regs(int M, int V, bool mx) {
+    return dot_regs(M, 1, V, false) + (mx ? (M + 1) * V : 0);
+}
+constexpr int fp8_dot_max_threads(int M, int V, bool mx) {
+    return fp8_dot_regs(M, V, mx) <= 96 ? 1024 : 512;
+}
+
+// FP8 MFMA split-K (v_mfma_scale_f32_16x16x128_f8f6f4, 128-wide K steps):
+// per lane per step two 16-byte halves per operand block (8 VGPRs) and a
+// scale byte; two stages of D steps plus NB*MT accumulators of 4.
+constexpr int fp8_mfma_regs(int MT, int NB, int D) { return 2 * D * (NB + MT) * 9 + NB * MT * 4; }
+// MX variants keep one scale byte per operand block and step alive beside
+// the data and, measured on the compiler's resource report, need the full
+// 512 registers of one wave per SIMD: they are bounded to 256 threads.
+constexpr int fp8_mfma_max_threads(int MT, int NB, int D, bool mx) {
+    return (mx || fp8_mfma_regs(MT, NB, D) > 224) ? 256 : kSplitKMaxThreads;
+}
+constexpr bool fp8_mfma_built(int MT, int NB, int D) {
+    return NB * MT <= 32 && D * (NB + MT) <= 14;  // MX spills beyond (resource report)
+}
+
+// The arguments of one FP8 call, passed to the FP8 launchers.
+struct Fp8Args {
+    const void *x, *W, *bias;
+    void *out;
+    int mode;                 // SKG_FP8_PER_TENSOR or SKG_FP8_MX32
+    const float *sx, *sw;     // per-tensor scales (device)
+    const uint8_t *xe, *we;   // MX exponents (device)
+};
+
 // Host-side validation and planning (plan.cpp).  No HIP calls.
 int check_sizes(int M, int N, int K, int dtype);
 int complete_plan(int M, int N, int K, int dtype, SkgPlan *p);
@@ -79,6 +113,9 @@ int launch_splitk(const SkgPlan &p, const void *x, const void *W, const void *bi
 int launch_tiled(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
                  float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream);
 int launch_splitk_reduce(const float *ws, const void *bias, void *out, int M, int N, int S,
-                         hipStream_t stream);
+                         hipStream_t stream, const float *sx = nullptr,
+                         const float *sw = nullptr);
+int launch_fp8(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets, int M, int N,
+               int K, hipStream_t stream);
 
 }  // namespace skg

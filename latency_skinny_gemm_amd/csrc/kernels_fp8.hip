@@ -1,0 +1,424 @@
+// kernels_fp8.hip -- FP8 (OCP e4m3fn) small-M GEMM kernels for gfx950.
+//
+// Semantics ("sglang PR #28333" page, key source snippet and motivation;
+// "sglang PR #34042" page, MX block scaling):
+//   per-tensor:  out = bf16( sx*sw * sum_k xq*wq  + bias ),  the scale product
+//                applied once, in the epilogue;
+//   MX (32):     out = bf16( sum_b 2^(ex[m,b]-127) 2^(ew[n,b]-127) sum_{k in b} xq*wq + bias ),
+//                one e8m0 exponent per 32 consecutive K of every row.
+// Accumulation is fp32 throughout.
+//
+// Dot kernel (M <= 16): the bf16 dot kernel's structure (one workgroup per
+// column, 16-byte vectors = 16 fp8 values, every load issued up front,
+// DPP + LDS reduction), widening e4m3 pairs to fp32 in hardware
+// (v_cvt_pk_f32_fp8) and accumulating with fp32 FMA.  In MX mode each
+// 16-element partial is scaled by the exact power of two 2^(ex+ew-254)
+// (ldexp) before it joins the accumulator.
+//
+// MFMA kernel: the split-K kernel's structure with
+// v_mfma_scale_f32_16x16x128_f8f6f4.  A lane's operand is two 16-element
+// chunks of one row (two 16-byte loads) and its e8m0 byte scales one
+// 32-element block of the step (the lane layout is measured, see the
+// kernel); the hardware applies the scales.  Per-tensor mode passes the
+// unit exponent 127 and multiplies by sx*sw once at the end.
+#include "device_common.h"
+#include "internal.h"
+#include "splitk_common.h"
+
+namespace skg {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// OCP e8m0 pair -> the fp32 scale 2^(ex + ew - 254) applied with ldexp
+// (exact unless the result leaves fp32's range); 0xFF in either is NaN.
+__device__ __forceinline__ float mx_scale_apply(float p, unsigned ex, unsigned ew) {
+    if (ex == 0xFFu || ew == 0xFFu) return __builtin_nanf("");
+    return __builtin_amdgcn_ldexpf(p, (int)ex + (int)ew - 254);
+}
+
+// 16 e4m3 products of two 16-byte vectors added to acc, k ascending.  Each
+// byte pair is widened to fp32 with v_cvt_pk_f32_fp8 (exact: e4m3 is a
+// subset of fp32) and multiplied-added in fp32 (the product of two e4m3
+// values is exact in fp32, so each step rounds once).
+__device__ __forceinline__ float fma_word_fp8(unsigned a, unsigned b, float acc) {
+    const auto a01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)a, false);
+    const auto b01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, false);
+    const auto a23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)a, true);
+    const auto b23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, true);
+    acc = __builtin_fmaf(a01[0], b01[0], acc);
+    acc = __builtin_fmaf(a01[1], b01[1], acc);
+    acc = __builtin_fmaf(a23[0], b23[0], acc);
+    acc = __builtin_fmaf(a23[1], b23[1], acc);
+    return acc;
+}
+__device__ __forceinline__ float dot16_fp8(u32x4 a, u32x4 b, float acc) {
+    acc = fma_word_fp8(a.x, b.x, acc);
+    acc = fma_word_fp8(a.y, b.y, acc);
+    acc = fma_word_fp8(a.z, b.z, acc);
+    acc = fma_word_fp8(a.w, b.w, acc);
+    return acc;
+}
+
+__device__ __forceinline__ unsigned load_byte(Rsrc r, unsigned off) {
+    return (unsigned)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
+// ------------------------------------------------------------------ dot
+template <int M, int V, bool MX>
+__global__ void __launch_bounds__((fp8_dot_max_threads(M, V, MX)))
+    fp8_dot_kernel(const uint8_t *__restrict__ x, const uint8_t *__restrict__ W,
+                   const uint16_t *__restrict__ bias, const float *__restrict__ sx,
+                   const float *__restrict__ sw, const uint8_t *__restrict__ xe,
+                   const uint8_t *__restrict__ we, uint16_t *__restrict__ out, int N, int K) {
+    const int T = blockDim.x;
+    const int t = threadIdx.x;
+    const int n = blockIdx.x;
+    const unsigned rowb = (unsigned)K;  // one byte per element
+    const Rsrc wr = make_rsrc(W + (size_t)n * K, rowb);
+    const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
+    const int K16 = K >> 4;
+    const unsigned srow = (unsigned)(K >> 5);  // scale bytes per row (MX)
+    const Rsrc xer = make_rsrc(xe, MX ? (unsigned)M * srow : 0u);
+    const Rsrc wer = make_rsrc(we + (MX ? (size_t)n * srow : 0), MX ? srow : 0u);
+
+    u32x4 wv[V], xv[M][V];
+    unsigned wsc[V], xsc[M][V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int v = t + i * T;
+        wv[i] = load16<kCacheStream>(wr, v < K16 ? (unsigned)v * 16u : kOOB);
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int v = t + i * T;
+        const unsigned off = v < K16 ? (unsigned)v * 16u : kOOB;
+#pragma unroll
+        for (int m = 0; m < M; ++m) xv[m][i] = load16<kCacheDefault>(xr, off + (unsigned)m * rowb);
+    }
+    if constexpr (MX) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const int v = t + i * T;
+            const unsigned blk = v < K16 ? (unsigned)(v >> 1) : kOOB;  // 32-element block
+            wsc[i] = load_byte(wer, blk);
+#pragma unroll
+            for (int m = 0; m < M; ++m) xsc[m][i] = load_byte(xer, blk + (unsigned)m * srow);
+        }
+    }
+
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int v = t + i * T;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            if constexpr (MX) {
+                const float p = dot16_fp8(xv[m][i], wv[i], 0.0f);
+                if (v < K16) acc[m] += mx_scale_apply(p, xsc[m][i], wsc[i]);
+            } else {
+                acc[m] = dot16_fp8(xv[m][i], wv[i], acc[m]);
+            }
+        }
+    }
+
+    __shared__ float red[kMaxThreads / 64][M];
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int lane = t & 63;
+    const int nw = T >> 6;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float s = wave_sum(acc[m]);
+        if (lane == 0) red[wave][m] = s;
+    }
+    __syncthreads();
+    if (t < M) {
+        float s = ordered_sum<8>(nw, [&](int w) { return red[w][t]; });
+        if (!MX) s *= sx[0] * sw[0];
+        if (bias) s += bf16_to_f32(bias[n]);
+        out[(size_t)t * N + n] = f32_to_bf16_rne(s);
+    }
+}
+
+// ------------------------------------------------------------------ MFMA split-K
+template <int MT, int NB, int D, bool MX>
+__global__ void __launch_bounds__((fp8_mfma_max_threads(MT, NB, D, MX)))
+    fp8_mfma_kernel(const uint8_t *__restrict__ x, const uint8_t *__restrict__ W,
+                    const uint16_t *__restrict__ bias, const float *__restrict__ sx,
+                    const float *__restrict__ sw, const uint8_t *__restrict__ xe,
+                    const uint8_t *__restrict__ we, uint16_t *__restrict__ out,
+                    float *__restrict__ ws, unsigned *__restrict__ tickets, int M, int N, int K,
+                    int S, int k_chunk, int reduce) {
+    extern __shared__ float lds[];
+    __shared__ unsigned is_last;
+
+    const int nw = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int s = blockIdx.x % S;
+    const int j = blockIdx.x / S;
+    const int col0 = j * NB * 16;
+    const int ncols = min(NB * 16, N - col0);
+    const unsigned rowb = (unsigned)K;
+    const unsigned srow = (unsigned)(K >> 5);
+    const Rsrc wr = make_rsrc(W + (size_t)col0 * K, (unsigned)ncols * rowb);
+    const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
+    const Rsrc xer = make_rsrc(xe, MX ? (unsigned)M * srow : 0u);
+    const Rsrc wer = make_rsrc(we + (MX ? (size_t)col0 * srow : 0), MX ? (unsigned)ncols * srow : 0u);
+    const int kbeg = s * k_chunk;
+    const int kend = min(K, kbeg + k_chunk);
+    const int nsteps = (kend - kbeg + 127) >> 7;  // 128-wide K steps
+    const int spw = (nsteps + nw - 1) / nw;
+    const int first_step = wave * spw;
+    const int my_steps = max(0, min(spw, nsteps - first_step));
+    const int nchunks = (my_steps + D - 1) / D;
+    const unsigned r16 = (unsigned)(lane & 15);
+    // Operand layout of the 16x16x128 f8f6f4 MFMA (measured on MI355X): lane
+    // group g = lane/16 holds two 16-element chunks of its row, K offsets
+    // 16g and 64 + 16g of the 128-wide step, and its scale byte applies to
+    // the step's 32-element block g (K offsets 32g .. 32g+31).
+    const int g16 = (lane >> 4) * 16;
+    const int gblk = lane >> 4;
+
+    f32x4 acc[NB][MT];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // a stage: D steps of (two 16-byte halves per operand block) + MX scales
+    u32x4 wa[D][NB][2], xa[D][MT][2], wb[D][NB][2], xb[D][MT][2];
+    unsigned wsa[D][NB], xsa[D][MT], wsb[D][NB], xsb[D][MT];
+
+    auto load_stage = [&](u32x4(&wbuf)[D][NB][2], u32x4(&xbuf)[D][MT][2], unsigned(&wsc)[D][NB],
+                          unsigned(&xsc)[D][MT], int chunk) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int i = chunk * D + d;
+            const int k0 = kbeg + (first_step + i) * 128;  // the step's first K
+            const bool live = i < my_steps;
+            // each 16-element chunk and the scale's block have their own
+            // bound (K may end inside the step; per-tensor K may end halfway
+            // through a 32-element block)
+            const bool ok0 = live & (k0 + g16 < kend);
+            const bool ok1 = live & (k0 + 64 + g16 < kend);
+            const bool okb = live & (k0 + 32 * gblk < kend);
+            const unsigned koff = ok0 ? (unsigned)(k0 + g16) : kOOB;
+            const unsigned koff1 = ok1 ? (unsigned)(k0 + 64 + g16) : kOOB;
+            const unsigned boff = okb ? (unsigned)(k0 / 32 + gblk) : kOOB;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const unsigned ro = ((unsigned)nb * 16u + r16) * rowb;
+                wbuf[d][nb][0] = load16<kCacheStream>(wr, koff + ro);
+                wbuf[d][nb][1] = load16<kCacheStream>(wr, koff1 + ro);
+                if constexpr (MX) {
+                    const unsigned e = load_byte(wer, boff + ((unsigned)nb * 16u + r16) * srow);
+                    wsc[d][nb] = okb ? e : 127u;
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const unsigned ro = ((unsigned)mt * 16u + r16) * rowb;
+                xbuf[d][mt][0] = load16<kCacheDefault>(xr, koff + ro);
+                xbuf[d][mt][1] = load16<kCacheDefault>(xr, koff1 + ro);
+                if constexpr (MX) {
+                    // rows past M read as zero data; give them the unit scale
+                    const unsigned e = load_byte(xer, boff + ((unsigned)mt * 16u + r16) * srow);
+                    xsc[d][mt] = (okb && (int)(mt * 16 + r16) < M) ? e : 127u;
+                }
+            }
+        }
+    };
+    auto mma_stage = [&](u32x4(&wbuf)[D][NB][2], u32x4(&xbuf)[D][MT][2], unsigned(&wsc)[D][NB],
+                         unsigned(&xsc)[D][MT]) {
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const u32x4 a0 = xbuf[d][mt][0], a1 = xbuf[d][mt][1];
+                    const u32x4 b0 = wbuf[d][nb][0], b1 = wbuf[d][nb][1];
+                    const i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                                     (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                    const i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                                     (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+                    const int sa = MX ? (int)xsc[d][mt] : 127;
+                    const int sb = MX ? (int)wsc[d][nb] : 127;
+                    // formats 0/0: both operands fp8 e4m3; scale byte 0 of each lane
+                    acc[nb][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        a, b, acc[nb][mt], 0, 0, 0, sa, 0, sb);
+                }
+    };
+
+    if (nchunks <= 1) {
+        load_stage(wa, xa, wsa, xsa, 0);
+        mma_stage(wa, xa, wsa, xsa);
+    } else {
+        load_stage(wa, xa, wsa, xsa, 0);
+        for (int c = 0; c < nchunks; c += 2) {
+            load_stage(wb, xb, wsb, xsb, c + 1);  // past the end: zeros, unit scales
+            mma_stage(wa, xa, wsa, xsa);
+            load_stage(wa, xa, wsa, xsa, c + 2);
+            mma_stage(wb, xb, wsb, xsb);
+        }
+    }
+
+    constexpr int Q = NB * MT * 4;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                lds[(wave * Q + (nb * MT + mt) * 4 + i) * 64 + lane] = acc[nb][mt][i];
+    __syncthreads();
+    const float scale = MX ? 1.0f : sx[0] * sw[0];
+    for (int q = wave; q < Q; q += nw) {
+        float v = ordered_sum<8>(nw, [&](int w) { return lds[(w * Q + q) * 64 + lane]; });
+        const int nb = q / (MT * 4);
+        const int mt = (q >> 2) % MT;
+        const int i = q & 3;
+        const int n = col0 + nb * 16 + (lane & 15);
+        const int m = mt * 16 + (lane >> 4) * 4 + i;
+        if (m < M && n < N) {
+            if (S == 1) {
+                v *= scale;
+                if (bias) v += bf16_to_f32(bias[n]);
+                out[(size_t)m * N + n] = f32_to_bf16_rne(v);
+            } else {
+                ws[((size_t)s * M + m) * N + n] = v;
+            }
+        }
+    }
+    if (S == 1 || reduce != SKG_REDUCE_LAST) return;
+    last_arriver_reduce(ws, tickets, bias, out, M, N, S, j, col0, ncols, &is_last,
+                        MX ? nullptr : sx, MX ? nullptr : sw);
+}
+
+namespace {
+
+typedef int (*Fp8DotLaunch)(const SkgPlan &, const Fp8Args &, int, int, hipStream_t);
+typedef int (*Fp8MfmaLaunch)(const SkgPlan &, const Fp8Args &, float *, unsigned *, int, int, int,
+                             hipStream_t);
+
+template <int M, int V, bool MX>
+int launch_fp8_dot_t(const SkgPlan &p, const Fp8Args &a, int N, int K, hipStream_t stream) {
+    hipLaunchKernelGGL((fp8_dot_kernel<M, V, MX>), dim3(p.grid), dim3(p.threads), 0, stream,
+                       (const uint8_t *)a.x, (const uint8_t *)a.W, (const uint16_t *)a.bias, a.sx,
+                       a.sw, a.xe, a.we, (uint16_t *)a.out, N, K);
+    return (int)hipGetLastError();
+}
+
+template <int M, int V, bool MX>
+constexpr Fp8DotLaunch fp8_dot_entry() {
+    if constexpr (fp8_dot_regs(M, V, MX) <= kDotRegsMax)
+        return &launch_fp8_dot_t<M, V, MX>;
+    else
+        return nullptr;
+}
+
+template <int M, bool MX>
+Fp8DotLaunch fp8_dot_v(int V) {
+    switch (V) {
+    case 1: return fp8_dot_entry<M, 1, MX>();
+    case 2: return fp8_dot_entry<M, 2, MX>();
+    case 4: return fp8_dot_entry<M, 4, MX>();
+    default: return nullptr;
+    }
+}
+
+template <bool MX>
+Fp8DotLaunch fp8_dot_m(int M, int V) {
+    switch (M) {
+    case 1: return fp8_dot_v<1, MX>(V);
+    case 2: return fp8_dot_v<2, MX>(V);
+    case 3: return fp8_dot_v<3, MX>(V);
+    case 4: return fp8_dot_v<4, MX>(V);
+    case 5: return fp8_dot_v<5, MX>(V);
+    case 6: return fp8_dot_v<6, MX>(V);
+    case 7: return fp8_dot_v<7, MX>(V);
+    case 8: return fp8_dot_v<8, MX>(V);
+    case 9: return fp8_dot_v<9, MX>(V);
+    case 10: return fp8_dot_v<10, MX>(V);
+    case 11: return fp8_dot_v<11, MX>(V);
+    case 12: return fp8_dot_v<12, MX>(V);
+    case 13: return fp8_dot_v<13, MX>(V);
+    case 14: return fp8_dot_v<14, MX>(V);
+    case 15: return fp8_dot_v<15, MX>(V);
+    case 16: return fp8_dot_v<16, MX>(V);
+    default: return nullptr;
+    }
+}
+
+template <int MT, int NB, int D, bool MX>
+int launch_fp8_mfma_t(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets, int M,
+                      int N, int K, hipStream_t stream) {
+    const size_t lds_bytes = (size_t)(p.threads / 64) * NB * MT * 4 * 64 * sizeof(float);
+    hipLaunchKernelGGL((fp8_mfma_kernel<MT, NB, D, MX>), dim3(p.grid), dim3(p.threads), lds_bytes,
+                       stream, (const uint8_t *)a.x, (const uint8_t *)a.W, (const uint16_t *)a.bias,
+                       a.sx, a.sw, a.xe, a.we, (uint16_t *)a.out, ws, tickets, M, N, K, p.splits,
+                       p.k_chunk, p.reduce);
+    return (int)hipGetLastError();
+}
+
+template <int MT, int NB, int D, bool MX>
+constexpr Fp8MfmaLaunch fp8_mfma_entry() {
+    if constexpr (fp8_mfma_built(MT, NB, D))
+        return &launch_fp8_mfma_t<MT, NB, D, MX>;
+    else
+        return nullptr;
+}
+
+template <int MT, int NB, bool MX>
+Fp8MfmaLaunch fp8_mfma_d(int D) {
+    switch (D) {
+    case 1: return fp8_mfma_entry<MT, NB, 1, MX>();
+    case 2: return fp8_mfma_entry<MT, NB, 2, MX>();
+    case 4: return fp8_mfma_entry<MT, NB, 4, MX>();
+    default: return nullptr;
+    }
+}
+
+template <int MT, bool MX>
+Fp8MfmaLaunch fp8_mfma_nb(int NB, int D) {
+    return NB == 1 ? fp8_mfma_d<MT, 1, MX>(D) : NB == 2 ? fp8_mfma_d<MT, 2, MX>(D)
+                   : NB == 4 ? fp8_mfma_d<MT, 4, MX>(D) : nullptr;
+}
+
+template <bool MX>
+Fp8MfmaLaunch fp8_mfma_mt(int MT, int NB, int D) {
+    switch (MT) {
+    case 1: return fp8_mfma_nb<1, MX>(NB, D);
+    case 2: return fp8_mfma_nb<2, MX>(NB, D);
+    case 3: return fp8_mfma_nb<3, MX>(NB, D);
+    case 4: return fp8_mfma_nb<4, MX>(NB, D);
+    case 5: return fp8_mfma_nb<5, MX>(NB, D);
+    case 6: return fp8_mfma_nb<6, MX>(NB, D);
+    case 7: return fp8_mfma_nb<7, MX>(NB, D);
+    case 8: return fp8_mfma_nb<8, MX>(NB, D);
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+int launch_fp8(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets, int M, int N,
+               int K, hipStream_t stream) {
+    const bool mx = a.mode == SKG_FP8_MX32;
+    if (p.kind == SKG_KIND_DOT) {
+        Fp8DotLaunch f = mx ? fp8_dot_m<true>(M, p.depth) : fp8_dot_m<false>(M, p.depth);
+        if (!f) return (int)hipErrorInvalidConfiguration;
+        return f(p, a, N, K, stream);
+    }
+    Fp8MfmaLaunch f = mx ? fp8_mfma_mt<true>(p.m_tiles, p.cols, p.depth)
+                         : fp8_mfma_mt<false>(p.m_tiles, p.cols, p.depth);
+    if (!f) return (int)hipErrorInvalidConfiguration;
+    int rc = f(p, a, ws, tickets, M, N, K, stream);
+    if (rc != (int)hipSuccess || p.splits == 1 || p.reduce != SKG_REDUCE_KERNEL) return rc;
+    return launch_splitk_reduce(ws, a.bias, a.out, M, N, p.splits, stream, mx ? nullptr : a.sx,
+                                mx ? nullptr : a.sw);
+}
+
+}  // namespace skg

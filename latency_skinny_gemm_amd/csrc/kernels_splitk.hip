@@ -147,12 +147,14 @@ __global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
 // one, one output element per thread.
 __global__ void __launch_bounds__(256)
     splitk_reduce_kernel(const float *__restrict__ ws, const uint16_t *__restrict__ bias,
-                         uint16_t *__restrict__ out, int M, int N, int S) {
+                         uint16_t *__restrict__ out, int M, int N, int S,
+                         const float *__restrict__ sx, const float *__restrict__ sw) {
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= M * N) return;
     const int m = e / N;
     const int n = e - m * N;
     float v = ordered_sum<8>(S, [&](int ss) { return ws[((size_t)ss * M + m) * N + n]; });
+    if (sx) v *= sx[0] * sw[0];  // FP8 per-tensor scale product, applied once
     if (bias) v += bf16_to_f32(bias[n]);
     out[e] = f32_to_bf16_rne(v);
 }
@@ -214,10 +216,10 @@ SplitKLaunch pick(int MT, int NB, int D) {
 }  // namespace
 
 int launch_splitk_reduce(const float *ws, const void *bias, void *out, int M, int N, int S,
-                         hipStream_t stream) {
+                         hipStream_t stream, const float *sx, const float *sw) {
     const int elems = M * N;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((elems + 255) / 256), dim3(256), 0, stream, ws,
-                       (const uint16_t *)bias, (uint16_t *)out, M, N, S);
+                       (const uint16_t *)bias, (uint16_t *)out, M, N, S, sx, sw);
     return (int)hipGetLastError();
 }
 

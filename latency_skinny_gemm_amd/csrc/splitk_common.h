@@ -14,14 +14,17 @@ namespace skg {
 // whole workgroup's partials (its release writes the XCD's L2 back to
 // memory once per workgroup) and, in the last workgroup of the tile, its
 // acquire invalidates stale L1/L2 lines before any wave reads partials.
-// That workgroup sums the S partials in ascending s, adds the bias and
-// rounds once; it re-arms the ticket.  No workgroup waits on another.
+// That workgroup sums the S partials in ascending s, applies the FP8
+// per-tensor scale product when given (once), adds the bias and rounds
+// once; it re-arms the ticket.  No workgroup waits on another.
 __device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
                                                     unsigned *__restrict__ tickets,
                                                     const uint16_t *__restrict__ bias,
                                                     uint16_t *__restrict__ out, int M, int N,
                                                     int S, int j, int col0, int ncols,
-                                                    unsigned *is_last) {
+                                                    unsigned *is_last,
+                                                    const float *__restrict__ sx = nullptr,
+                                                    const float *__restrict__ sw = nullptr) {
     wait_all_memory();
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -33,11 +36,13 @@ __device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
     }
     __syncthreads();
     if (!*is_last) return;
+    const float scale = sx ? sx[0] * sw[0] : 1.0f;  // FP8 per-tensor: applied once, here
     const int elems = M * ncols;
     for (int e = threadIdx.x; e < elems; e += blockDim.x) {
         const int m = e / ncols;
         const int n = col0 + (e - m * ncols);
         float v = ordered_sum<8>(S, [&](int ss) { return ws[((size_t)ss * M + m) * N + n]; });
+        if (sx) v *= scale;
         if (bias) v += bf16_to_f32(bias[n]);
         out[(size_t)m * N + n] = f32_to_bf16_rne(v);
     }

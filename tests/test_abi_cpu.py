@@ -76,10 +76,69 @@ def test_fp8_validation(lib):
     sc.mode = 7
     assert lib.skinny_gemm_fp8(X, W, None, ctypes.byref(sc), OUT, 2, 8, 64, None) == skg.ERR_INVALID_ARG
     assert lib.skinny_gemm_fp8(X, W, None, None, OUT, 2, 8, 64, None) == skg.ERR_INVALID_ARG
-    sc.mode = skg.FP8_MX32
+    sc.mode = skg.FP8_PER_TENSOR   # scale pointers missing
+    assert lib.skinny_gemm_fp8(X, W, None, ctypes.byref(sc), OUT, 2, 8, 64, None) == skg.ERR_INVALID_ARG
+    sc.mode = skg.FP8_MX32         # exponent pointers missing
+    assert lib.skinny_gemm_fp8(X, W, None, ctypes.byref(sc), OUT, 2, 8, 64, None) == skg.ERR_INVALID_ARG
+    sc.x_e8m0, sc.w_e8m0 = 0x30000, 0x40000
     assert lib.skinny_gemm_fp8(X, W, None, ctypes.byref(sc), OUT, 2, 8, 48, None) == skg.ERR_UNSUPPORTED
     assert lib.skinny_gemm_fp8(X, W, None, ctypes.byref(sc), OUT, 2, 8, 40, None) == skg.ERR_UNSUPPORTED
     assert lib.skinny_gemm_fp8(X + 8, W, None, ctypes.byref(sc), OUT, 2, 8, 64, None) == skg.ERR_ALIGNMENT
+    assert lib.skinny_gemm_fp8(X, W, None, ctypes.byref(sc), X + 32, 2, 8, 64, None) == skg.ERR_INVALID_ARG
+    assert lib.skinny_gemm_fp8(X, W, None, ctypes.byref(sc), OUT, 0, 8, 64, None) == skg.OK
+    sc.mode, sc.sx, sc.sw = skg.FP8_PER_TENSOR, 0x50002, 0x60000
+    assert lib.skinny_gemm_fp8(X, W, None, ctypes.byref(sc), OUT, 2, 8, 64, None) == skg.ERR_ALIGNMENT
+
+
+FP8 = [p for p in configs.all_points() if p.dtype != "bf16"]
+
+
+@pytest.mark.parametrize("p", FP8, ids=lambda p: p.key())
+def test_fp8_plans_valid_and_cover(lib, p):
+    q = skg.plan(p.M, p.N, p.K, skg.DTYPE_FP8)
+    again = skg.plan_complete(p.M, p.N, p.K, q, skg.DTYPE_FP8)
+    assert (again.kind, again.grid, again.splits, again.k_chunk) == (q.kind, q.grid, q.splits, q.k_chunk)
+    _check_fp8_coverage(q, p.M, p.N, p.K)
+
+
+def _check_fp8_coverage(p, M, N, K):
+    if p.kind == skg.KIND_DOT:
+        T, V = p.threads, p.depth
+        K16 = K // 16
+        vecs = sorted(t + i * T for t in range(T) for i in range(V) if t + i * T < K16)
+        assert vecs == list(range(K16)) and p.grid == N and p.cols == 1
+        return
+    assert p.kind == skg.KIND_SPLITK
+    S, NB, D, kc = p.splits, p.cols, p.depth, p.k_chunk
+    nw = p.threads // 64
+    assert kc % 128 == 0 and (S - 1) * kc < K <= S * kc and p.grid == -(-N // (16 * NB)) * S
+    seen = [0] * K
+    for s in range(S):
+        kbeg, kend = s * kc, min(K, (s + 1) * kc)
+        nsteps = -(-(kend - kbeg) // 128)
+        spw = -(-nsteps // nw)
+        for w in range(nw):
+            first = w * spw
+            my = max(0, min(spw, nsteps - first))
+            nch = -(-my // D)
+            consumed = [0] if nch <= 1 else [c for c0 in range(0, nch, 2) for c in (c0, c0 + 1)]
+            for ch in consumed:
+                for d in range(D):
+                    i = ch * D + d
+                    for g in range(4):      # lane group g: chunks at 16g and 64 + 16g
+                        k0 = kbeg + (first + i) * 128
+                        for kk0 in (k0 + 16 * g, k0 + 64 + 16 * g):
+                            if i < my and kk0 < kend:
+                                for kk in range(kk0, kk0 + 16):
+                                    seen[kk] += 1
+    assert seen == [1] * K
+
+
+def test_fp8_straddling_K_covered(lib):
+    # per-tensor K = 4112 ends halfway through a 32-element block
+    for kind, T, NB, S, D in ((skg.KIND_SPLITK, 256, 1, 3, 2), (skg.KIND_SPLITK, 128, 2, 1, 4)):
+        q = skg.plan_complete(5, 48, 4112, skg.make_plan(kind, T, NB, S, D, skg.REDUCE_LAST), skg.DTYPE_FP8)
+        _check_fp8_coverage(q, 5, 48, 4112)
 
 
 def test_status_strings(lib):

@@ -1,0 +1,152 @@
+"""GPU parity of the FP8 e4m3 paths (per-tensor and MX scales) against the
+CPU oracle, through the C ABI.
+
+Random points must meet |gpu - ref| <= 2^-7 |ref| + 1e-3 sqrt(K) rms(ref);
+inputs whose every fp32 partial sum is exact (small e4m3 integers, unit or
+near-unit power-of-two scales) must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import tolerance
+from workloads import configs
+from workloads import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def skg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import latency_skinny_gemm_amd as m
+    m.lib()
+    return m
+
+
+def _plans(skg, M, N, K):
+    plans = [("default", None)]
+    if M <= 16:
+        for T in range(256, 1025, 64):
+            p = skg.make_plan(skg.KIND_DOT, T, 1)
+            try:
+                skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
+            except skg.SkinnyGemmError:
+                continue
+            plans.append((f"dot_t{T}", p))
+            break
+    mt = (M + 15) // 16
+    nb = 2 if mt <= 3 else 1
+    for (T, S, D, red) in ((256, 4, 1, skg.REDUCE_LAST), (128, 3, 2, skg.REDUCE_KERNEL),
+                           (256, 1, 1, skg.REDUCE_NONE)):
+        p = skg.make_plan(skg.KIND_SPLITK, T, nb, S, D, red)
+        try:
+            skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
+        except skg.SkinnyGemmError:
+            continue
+        plans.append((f"mfma_t{T}_s{S}_d{D}_r{red}", p))
+    return plans
+
+
+def _run(skg, plan, xq, wq, bias, **sc):
+    out = skg.gemm_fp8(xq, wq, bias=bias, **sc) if plan is None else \
+        skg.gemm_fp8_planned(xq, wq, plan, bias=bias, **sc)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def _oracle(mode, xq, wq, s1, s2, bias):
+    b = None if bias is None else gen.bits16(bias)
+    if mode == "fp8_tensor":
+        return oracle.gemm_fp8_tensor(gen.bits8(xq), gen.bits8(wq), float(s1), float(s2), b,
+                                      threads=16)
+    return oracle.gemm_fp8_mx(gen.bits8(xq), gen.bits8(wq), gen.bits8(s1), gen.bits8(s2), b,
+                              threads=16)
+
+
+def _scales(mode, s1, s2):
+    if mode == "fp8_tensor":
+        return dict(sx=s1.to(DEV), sw=s2.to(DEV))
+    return dict(xe=s1.to(DEV), we=s2.to(DEV))
+
+
+FP8_POINTS = [p for p in configs.all_points() if p.dtype != "bf16"]
+
+
+@pytest.mark.parametrize("p", FP8_POINTS, ids=lambda p: p.key())
+@pytest.mark.parametrize("with_bias", (False, True))
+def test_fp8_point_within_tolerance(skg, p, with_bias):
+    xq, wq, s1, s2 = gen.point_inputs(p)
+    bias = None
+    if with_bias:
+        bias = (torch.randn(p.N, generator=torch.Generator().manual_seed(p.M)) * 0.3).to(torch.bfloat16)
+    ref = _oracle(p.dtype, xq, wq, s1, s2, bias)
+    xd, wd = xq.to(DEV), wq.to(DEV)
+    bd = None if bias is None else bias.to(DEV)
+    for name, plan in _plans(skg, p.M, p.N, p.K):
+        out = _run(skg, plan, xd, wd, bd, **_scales(p.dtype, s1, s2))
+        ok, msg = tolerance.check(out, ref, p.K)
+        assert ok, f"{p.key()} bias={with_bias} [{name}]: {msg}"
+
+
+def _small_int_e4m3(rows, K, seed, lo=-2, hi=2):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(lo, hi + 1, (rows, K), generator=g).to(torch.float32).to(torch.float8_e4m3fn)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 4096), (5, 48, 4112), (16, 200, 2048), (37, 96, 1024),
+                                   (128, 64, 4096)])
+def test_fp8_per_tensor_integers_bitwise(skg, M, N, K):
+    xq = _small_int_e4m3(M, K, M + K)
+    wq = _small_int_e4m3(N, K, N + K + 1)
+    one = torch.ones(1, dtype=torch.float32)
+    bias = torch.randint(-3, 4, (N,), generator=torch.Generator().manual_seed(7)).to(torch.bfloat16)
+    ref = _oracle("fp8_tensor", xq, wq, 1.0, 1.0, bias)
+    for name, plan in _plans(skg, M, N, K):
+        out = _run(skg, plan, xq.to(DEV), wq.to(DEV), bias.to(DEV), sx=one.to(DEV), sw=one.to(DEV))
+        bad = np.argwhere(gen.bits16(out) != ref)
+        assert bad.size == 0, f"[{name}] {len(bad)} mismatches, first {tuple(bad[0])}"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 4096), (9, 80, 2048), (64, 48, 1024), (128, 32, 4096)])
+def test_fp8_mx_exact_scales_bitwise(skg, M, N, K):
+    # exponents 126..128 on both sides: every scaled block sum and every
+    # fp32 partial sum stays exact, so the result is unique
+    xq = _small_int_e4m3(M, K, 3 * M + K)
+    wq = _small_int_e4m3(N, K, 5 * N + K)
+    g = torch.Generator().manual_seed(M * N)
+    xe = torch.randint(126, 129, (M, K // 32), generator=g).to(torch.uint8)
+    we = torch.randint(126, 129, (N, K // 32), generator=g).to(torch.uint8)
+    ref = _oracle("fp8_mx", xq, wq, xe, we, None)
+    for name, plan in _plans(skg, M, N, K):
+        out = _run(skg, plan, xq.to(DEV), wq.to(DEV), None, xe=xe.to(DEV), we=we.to(DEV))
+        bad = np.argwhere(gen.bits16(out) != ref)
+        assert bad.size == 0, f"[{name}] {len(bad)} mismatches, first {tuple(bad[0])}"
+
+
+def test_fp8_mx_nan_exponent_propagates(skg):
+    M, N, K = 4, 40, 1024
+    xq, wq, xe, we = gen.fp8_inputs(M, N, K, "fp8_mx", seed=99)
+    xe = xe.clone()
+    xe[2, 5] = 0xFF          # row 2 of x, block 5: NaN scale
+    we = we.clone()
+    we[31, 0] = 0xFF         # column 31: NaN scale
+    ref = tolerance.widen(_oracle("fp8_mx", xq, wq, xe, we, None))
+    assert np.isnan(ref[2]).all() and np.isnan(ref[:, 31]).all()
+    for name, plan in _plans(skg, M, N, K):
+        out = tolerance.widen(_run(skg, plan, xq.to(DEV), wq.to(DEV), None, xe=xe.to(DEV), we=we.to(DEV)))
+        assert np.array_equal(np.isnan(out), np.isnan(ref)), f"[{name}]"
+
+
+def test_fp8_runs_bitwise_deterministic(skg):
+    for mode in ("fp8_tensor", "fp8_mx"):
+        xq, wq, s1, s2 = gen.fp8_inputs(16, 4096, 4096, mode, seed=5)
+        xd, wd = xq.to(DEV), wq.to(DEV)
+        for name, plan in _plans(skg, 16, 4096, 4096):
+            a = _run(skg, plan, xd, wd, None, **_scales(mode, s1, s2))
+            b = _run(skg, plan, xd, wd, None, **_scales(mode, s1, s2))
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{mode} [{name}]"
