@@ -77,6 +77,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 section")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for rocprofv3 --pmc: launch each headline call a few times on cold "
                          "weights, then a 64 MiB reference copy, and exit")
@@ -108,6 +109,72 @@ def pmc_probe(skg, torch, floors, stream, sptr, W, X, OUT, n_slots):
     stream.synchronize()
     print(json.dumps({"pmc_probe": "done", "calls_per_M": 8, "copy_bytes": COPY_BYTES}), flush=True)
     return 0
+
+
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
+
+
+def fp8_section(skg, torch, stream, sptr):
+    """FP8 e4m3, K = N = 4096, M in {1, 16, 64, 128}, per-tensor and MX
+    scales: microseconds per call over a cold pool of >= 512 MB of distinct
+    W, the achieved GB/s (W, x, out and scale bytes) and the MFMA rate
+    against the dense fp8 peak."""
+    K = N = 4096
+    dev = torch.device("cuda:0")
+    slots = -(-(512 << 20) // (N * K))
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    W = torch.empty((slots, N, K), dtype=torch.float8_e4m3fn, device=dev)
+    for i in range(slots):
+        W[i].copy_(torch.randn((N, K), generator=g, device=dev).to(torch.float8_e4m3fn))
+    res = {}
+    for M in (1, 16, 64, 128):
+        X = torch.randn((slots, M, K), generator=g, device=dev).to(torch.float8_e4m3fn)
+        O = torch.empty((slots, M, N), dtype=torch.bfloat16, device=dev)
+        one = torch.ones(1, dtype=torch.float32, device=dev)
+        XE = torch.full((M, K // 32), 127, dtype=torch.uint8, device=dev)
+        WE = torch.full((N, K // 32), 127, dtype=torch.uint8, device=dev)
+        for mode in ("tensor", "mx"):
+            sc = skg.Fp8Scales()
+            if mode == "tensor":
+                sc.mode, sc.sx, sc.sw = skg.FP8_PER_TENSOR, one.data_ptr(), one.data_ptr()
+                extra = 8
+            else:
+                sc.mode, sc.x_e8m0, sc.w_e8m0 = skg.FP8_MX32, XE.data_ptr(), WE.data_ptr()
+                extra = (M + N) * K // 32
+
+            def calls():
+                for s in range(slots):
+                    rc = skg.lib().skinny_gemm_fp8(X[s].data_ptr(), W[s].data_ptr(), None,
+                                                   ctypes.byref(sc), O[s].data_ptr(), M, N, K, sptr)
+                    if rc != 0:
+                        raise skg.SkinnyGemmError(rc, f"skinny_gemm_fp8 M={M} {mode}")
+            with torch.cuda.stream(stream):
+                calls()
+            stream.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                calls()
+            with torch.cuda.stream(stream):
+                gr.replay()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(3):
+                    gr.replay()
+                e1.record(stream)
+                e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (3 * slots)
+            del gr
+            byts = N * K + M * K + M * N * 2 + extra
+            tflops = 2.0 * M * N * K / (us * 1e-6) / 1e12
+            res[f"M{M}_{mode}"] = {"us_per_call": round(us, 3), "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+                                   "TFLOPs": round(tflops, 1),
+                                   "mfma_util": round(tflops / FP8_PEAK_TFLOPS, 4),
+                                   "kernel": {1: "dot", 2: "splitk"}[skg.plan(M, N, K, skg.DTYPE_FP8).kind]}
+        del X, O
+    del W
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -279,6 +346,8 @@ def main():
                          f"{t_cpu:.1f} s of oracle time; us/call at M=1: "
                          f"{t_cpu / reps / len(M_VALUES) * 1e6:.0f} (mean over M)"}
 
+    fp8 = None if args.no_fp8 else fp8_section(skg, torch, stream, sptr)
+
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -296,6 +365,7 @@ def main():
                    "read_stream_GBps": round(w_bytes / (t_read * 1e-6) / 1e9, 1),
                    "shape": "256 workgroups x 256 threads; read: 256 rows x 14336 B"},
         "per_m": per_m,
+        "fp8_k4096_n4096": fp8,
         "parity": parity,
     }
     print(json.dumps(line), flush=True)

@@ -37,12 +37,108 @@ def point_sets():
 
     bf16 = [p for p in configs.all_points() if p.dtype == "bf16"]
     uniq = lambda ps: sorted({(p.M, p.N, p.K) for p in ps}, key=lambda t: (t[2], t[1], t[0]))
+    fp8 = [p for p in configs.all_points() if p.dtype != "bf16"]
     return {
         "headline": uniq(configs.HEADLINE),
         "router": uniq([p for p in bf16 if p.group in ("small_bf16", "router_k7168", "router_shapes")]),
         "decode": uniq([p for p in bf16 if p.group == "decode_linear"]),
         "all": uniq(bf16),
+        "fp8": uniq(fp8),
     }
+
+
+def fp8_candidates(skg, M, N, K):
+    """Admissible FP8 plans (dot kernel for M <= 16, MFMA split-K)."""
+    out, seen = [], set()
+
+    def add(p):
+        try:
+            q = skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
+        except skg.SkinnyGemmError:
+            return
+        key = (q.kind, q.threads, q.cols, q.splits, q.depth, q.reduce, q.k_chunk)
+        if key not in seen:
+            seen.add(key)
+            out.append(q)
+
+    if M <= 16:
+        for T in DOT_THREADS:
+            add(skg.make_plan(skg.KIND_DOT, T, 1))
+    ksteps = -(-K // 128)
+    for NB in (1, 2, 4):
+        groups = -(-N // (16 * NB))
+        for S in SPLITS:
+            if S > ksteps or groups * S > 8192:
+                continue
+            for nw in (1, 2, 4, 8):
+                for d in (1, 2, 4):
+                    for red in ((skg.REDUCE_NONE,) if S == 1 else (skg.REDUCE_LAST, skg.REDUCE_KERNEL)):
+                        add(skg.make_plan(skg.KIND_SPLITK, nw * 64, NB, S, d, red))
+    return out
+
+
+def sweep_point_fp8(skg, torch, M, N, K, pool_bytes, reps, stream, log):
+    """Times every FP8 plan in both scale modes; ranks by the sum."""
+    dev = torch.device("cuda:0")
+    slots = max(4, -(-pool_bytes // (N * K)))
+    g = torch.Generator(device=dev)
+    g.manual_seed(M * 1000003 + N * 1009 + K + 7)
+    W = torch.randn((slots, N, K), generator=g, device=dev).clamp(-448, 448).to(torch.float8_e4m3fn)
+    X = torch.randn((slots, M, K), generator=g, device=dev).to(torch.float8_e4m3fn)
+    O = torch.empty((slots, M, N), dtype=torch.bfloat16, device=dev)
+    sx = torch.ones(1, dtype=torch.float32, device=dev)
+    XE = torch.full((M, K // 32), 127, dtype=torch.uint8, device=dev)
+    WE = torch.full((N, K // 32), 127, dtype=torch.uint8, device=dev)
+    modes = {"tensor": skg.Fp8Scales(), "mx": skg.Fp8Scales()}
+    modes["tensor"].mode, modes["tensor"].sx, modes["tensor"].sw = skg.FP8_PER_TENSOR, sx.data_ptr(), sx.data_ptr()
+    modes["mx"].mode, modes["mx"].x_e8m0, modes["mx"].w_e8m0 = skg.FP8_MX32, XE.data_ptr(), WE.data_ptr()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    L = skg.lib()
+    results = []
+    for p in fp8_candidates(skg, M, N, K):
+        per_mode = {}
+        for mname, sc in modes.items():
+            def calls(p=p, sc=sc):
+                for s in range(slots):
+                    rc = L.skinny_gemm_fp8_planned(X[s].data_ptr(), W[s].data_ptr(), None,
+                                                   ctypes.byref(sc), O[s].data_ptr(), M, N, K,
+                                                   ctypes.byref(p), sptr)
+                    if rc != 0:
+                        raise skg.SkinnyGemmError(rc, f"fp8 planned {p}")
+            with torch.cuda.stream(stream):
+                calls()
+            stream.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                calls()
+            times = []
+            with torch.cuda.stream(stream):
+                gr.replay()
+                for _ in range(reps):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    gr.replay()
+                    e1.record(stream)
+                    e1.synchronize()
+                    times.append(e0.elapsed_time(e1) * 1e3 / slots)
+            del gr
+            times.sort()
+            per_mode[mname] = times[len(times) // 2]
+        results.append((per_mode["tensor"] + per_mode["mx"], per_mode, p))
+    results.sort(key=lambda r: r[0])
+    _, best_modes, best = results[0]
+    rec = {"dtype": "fp8", "M": M, "N": N, "K": K, "slots": slots,
+           "best_us": round(max(best_modes.values()), 3),
+           "best_us_tensor": round(best_modes["tensor"], 3), "best_us_mx": round(best_modes["mx"], 3),
+           "best": plan_dict(best),
+           "candidates": [[round(t, 3), {k: round(v, 3) for k, v in pm.items()}, plan_dict(p)]
+                          for t, pm, p in results]}
+    log.write(json.dumps(rec) + "\n")
+    log.flush()
+    kind = {1: "dot", 2: "splitk"}[best.kind]
+    print(f"FP8 M={M:3d} N={N:5d} K={K:5d}: best per-tensor {best_modes['tensor']:7.3f} us, "
+          f"MX {best_modes['mx']:7.3f} us  {kind} {plan_dict(best)} ({len(results)} plans)", flush=True)
+    return rec
 
 
 def candidates(skg, M, N, K):
@@ -165,7 +261,8 @@ def run(args):
     t0 = time.time()
     with open(args.out, "a") as log:
         for (M, N, K) in pts:
-            sweep_point(skg, torch, M, N, K, args.pool_mb << 20, args.reps, stream, log)
+            fn = sweep_point_fp8 if args.points == "fp8" else sweep_point
+            fn(skg, torch, M, N, K, args.pool_mb << 20, args.reps, stream, log)
             torch.cuda.empty_cache()
     print(f"swept {len(pts)} points in {time.time() - t0:.0f} s", flush=True)
 
@@ -175,7 +272,7 @@ def emit_table(files, out_path=TABLE):
     for f in files:
         for line in open(f):
             r = json.loads(line)
-            key = (r["K"], r["N"], r["M"])
+            key = (r.get("dtype", "bf16"), r["K"], r["N"], r["M"])
             if key not in best or r["best_us"] < best[key]["best_us"]:
                 best[key] = r
     names = {0: "SKG_REDUCE_NONE", 1: "SKG_REDUCE_LAST", 2: "SKG_REDUCE_KERNEL"}
@@ -185,12 +282,14 @@ def emit_table(files, out_path=TABLE):
         f"// from cold-weight graph-replay timings on one MI355X ({datetime.date.today()}).",
         "// {dtype, K, N, M, {kind, threads, cols, splits, depth, waves_m, reduce, flags}},  // us/call",
     ]
-    for (K, N, M) in sorted(best):
-        b = best[(K, N, M)]["best"]
+    dtypes = {"bf16": "SKG_DTYPE_BF16", "fp8": "SKG_DTYPE_FP8"}
+    for key in sorted(best):
+        dt, K, N, M = key
+        b = best[key]["best"]
         lines.append(
-            f"{{SKG_DTYPE_BF16, {K}, {N}, {M}, {{{kinds[b['kind']]}, {b['threads']}, {b['cols']}, "
+            f"{{{dtypes[dt]}, {K}, {N}, {M}, {{{kinds[b['kind']]}, {b['threads']}, {b['cols']}, "
             f"{b['splits']}, {b['depth']}, {b.get('waves_m', 0)}, {names[b['reduce']]}, {b['flags']}}}}},"
-            f"  // {best[(K, N, M)]['best_us']:.3f}")
+            f"  // {best[key]['best_us']:.3f}")
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote {len(best)} entries to {out_path}")
@@ -198,7 +297,7 @@ def emit_table(files, out_path=TABLE):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--points", default="headline", choices=("headline", "router", "decode", "all"))
+    ap.add_argument("--points", default="headline", choices=("headline", "router", "decode", "all", "fp8"))
     ap.add_argument("--M", type=int, nargs="*", help="restrict to these M")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "sweep.jsonl"))
     ap.add_argument("--pool-mb", type=int, default=512)
