@@ -132,21 +132,24 @@ def fp8_section(skg, torch, stream, sptr):
         X = torch.randn((slots, M, K), generator=g, device=dev).to(torch.float8_e4m3fn)
         O = torch.empty((slots, M, N), dtype=torch.bfloat16, device=dev)
         one = torch.ones(1, dtype=torch.float32, device=dev)
-        XE = torch.full((M, K // 32), 127, dtype=torch.uint8, device=dev)
-        WE = torch.full((N, K // 32), 127, dtype=torch.uint8, device=dev)
+        # exponents 126..128, distinct per slot like W itself
+        XE = torch.randint(126, 129, (slots, M, K // 32), generator=g, device=dev).to(torch.uint8)
+        WE = torch.randint(126, 129, (slots, N, K // 32), generator=g, device=dev).to(torch.uint8)
         for mode in ("tensor", "mx"):
-            sc = skg.Fp8Scales()
-            if mode == "tensor":
-                sc.mode, sc.sx, sc.sw = skg.FP8_PER_TENSOR, one.data_ptr(), one.data_ptr()
-                extra = 8
-            else:
-                sc.mode, sc.x_e8m0, sc.w_e8m0 = skg.FP8_MX32, XE.data_ptr(), WE.data_ptr()
-                extra = (M + N) * K // 32
+            scs = []
+            for s in range(slots):
+                sc = skg.Fp8Scales()
+                if mode == "tensor":
+                    sc.mode, sc.sx, sc.sw = skg.FP8_PER_TENSOR, one.data_ptr(), one.data_ptr()
+                else:
+                    sc.mode, sc.x_e8m0, sc.w_e8m0 = skg.FP8_MX32, XE[s].data_ptr(), WE[s].data_ptr()
+                scs.append(sc)
+            extra = 8 if mode == "tensor" else (M + N) * K // 32
 
             def calls():
                 for s in range(slots):
                     rc = skg.lib().skinny_gemm_fp8(X[s].data_ptr(), W[s].data_ptr(), None,
-                                                   ctypes.byref(sc), O[s].data_ptr(), M, N, K, sptr)
+                                                   ctypes.byref(scs[s]), O[s].data_ptr(), M, N, K, sptr)
                     if rc != 0:
                         raise skg.SkinnyGemmError(rc, f"skinny_gemm_fp8 M={M} {mode}")
             with torch.cuda.stream(stream):
@@ -171,7 +174,7 @@ def fp8_section(skg, torch, stream, sptr):
                                    "TFLOPs": round(tflops, 1),
                                    "mfma_util": round(tflops / FP8_PEAK_TFLOPS, 4),
                                    "kernel": {1: "dot", 2: "splitk"}[skg.plan(M, N, K, skg.DTYPE_FP8).kind]}
-        del X, O
+        del X, O, XE, WE
     del W
     torch.cuda.empty_cache()
     return res
