@@ -77,7 +77,8 @@ extern "C" {
 
 #define SKG_KIND_DOT 1    /* dot-product kernel: whole K per workgroup */
 #define SKG_KIND_SPLITK 2 /* MFMA kernel, K split over workgroups */
-#define SKG_KIND_TILED 3  /* MFMA kernel with LDS-staged x and W tiles, K split
+#define SKG_KIND_TILED 3  /* MFMA kernel with x and W tiles streamed into an LDS ring
+                             (K % 32 == 0), K split
                              over workgroups (wide column tiles, larger M) */
 
 #define SKG_REDUCE_NONE 0  /* splits == 1: no cross-workgroup reduction */
@@ -85,7 +86,11 @@ extern "C" {
 #define SKG_REDUCE_KERNEL 2 /* a second kernel reduces every tile */
 
 #define SKG_FLAG_DOT2 1 /* DOT: multiply-add with v_dot2c_f32_bf16 (bf16 pairs, fp32
-                          accumulator; not rounded per IEEE step, see DESIGN) */
+                          accumulator; not rounded per IEEE step: an accumulator far
+                          below both products can be lost, error ~2^-24 of the
+                          largest term) */
+#define SKG_FLAG_TILED_WIDE 2 /* TILED: LDS stages of four 32-wide K steps (256 bytes of
+                                each row) instead of two (128 bytes) */
 
 #define SKG_MAX_M 128
 
@@ -110,21 +115,22 @@ typedef struct skinny_fp8_scales {
  * idea as a plain struct.  Fields marked (derived) are filled in by the
  * library from the others. */
 typedef struct SkgPlan {
-    int kind;     /* SKG_KIND_DOT or SKG_KIND_SPLITK */
-    int threads;  /* workgroup size, a multiple of 64, <= 1024 */
+    int kind;     /* SKG_KIND_DOT, SKG_KIND_SPLITK or SKG_KIND_TILED */
+    int threads;  /* workgroup size, a multiple of 64, <= 1024 (TILED: 256) */
     int cols;     /* DOT: output columns per workgroup (1, 2);
                      SPLITK: 16-column blocks per workgroup (1, 2, 4);
                      TILED: 16-column blocks per workgroup (1, 2, 4, 8, 16) */
     int splits;   /* SPLITK, TILED: number of K chunks S (>= 1); DOT: 1 */
     int depth;    /* SPLITK: 32-wide K steps a wave keeps in flight (1, 2, 4, 8);
-                     TILED: 32-wide K steps per pipeline chunk (1, 2, 4);
+                     TILED: stages of the LDS ring (2, 3, 4, 6, 8);
                      DOT: 16-byte vectors per thread per column (derived) */
     int waves_m;  /* TILED: waves along M (1, 2, 4; the other 4/waves_m waves
                      split the columns); 0 = chosen by the library */
     int reduce;   /* SKG_REDUCE_*; NONE iff splits == 1 */
     int flags;    /* SKG_FLAG_* */
-    int k_chunk;  /* (derived) SPLITK: K elements per split, multiple of 32 */
-    int m_tiles;  /* (derived) SPLITK: ceil(M / 16) */
+    int k_chunk;  /* (derived) SPLITK, TILED: K elements per split, multiple of 32 */
+    int m_tiles;  /* (derived) SPLITK: ceil(M / 16); TILED: the power of two
+                     (1, 2, 4, 8) at or above ceil(M / 16) */
     int grid;     /* (derived) workgroups in the main launch */
     int from_table; /* (derived) 1 when the tuned table supplied the plan */
 } SkgPlan;

@@ -14,7 +14,7 @@ import torch
 __all__ = ["SkgPlan", "SkinnyGemmError", "gemm_bf16", "gemm_bf16_planned", "gemm_fp8",
            "gemm_fp8_planned", "plan", "plan_on",
            "plan_complete", "reserve", "release_all", "status_string", "library_path",
-           "KIND_DOT", "KIND_SPLITK", "KIND_TILED", "REDUCE_NONE", "REDUCE_LAST", "REDUCE_KERNEL", "FLAG_DOT2",
+           "KIND_DOT", "KIND_SPLITK", "KIND_TILED", "REDUCE_NONE", "REDUCE_LAST", "REDUCE_KERNEL", "FLAG_DOT2", "FLAG_TILED_WIDE",
            "DTYPE_BF16", "DTYPE_FP8"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,6 +38,7 @@ REDUCE_NONE = 0
 REDUCE_LAST = 1
 REDUCE_KERNEL = 2
 FLAG_DOT2 = 1
+FLAG_TILED_WIDE = 2
 MAX_M = 128
 
 

@@ -29,11 +29,16 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFOR
 LIB_HIP = ["api.hip", "kernels_dot.hip", "kernels_splitk.hip", "kernels_tiled.hip",
            "kernels_fp8.hip"]
 LIB_HOST = ["plan.cpp"]
+# Per-file flags.  The tiled kernel keeps its accumulators in VGPRs: with the
+# compiler's default AGPR form, the loop-carried accumulators were copied
+# between AGPRs and VGPRs around every MFMA (resource report and assembly).
+EXTRA_FLAGS = {"kernels_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 FLOORS_HIP = ["floors.hip"]
 
 
 def _compile(src, obj, hip, verbose):
-    cmd = ([HIPCC] + HIP_FLAGS if hip else ["g++"] + HOST_FLAGS) + ["-c", src, "-o", obj]
+    cmd = ([HIPCC] + HIP_FLAGS if hip else ["g++"] + HOST_FLAGS) + \
+        EXTRA_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

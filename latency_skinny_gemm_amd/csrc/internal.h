@@ -47,19 +47,26 @@ constexpr bool splitk_built(int MT, int NB, int D) { return NB * MT <= 32 && D *
 // SPLITK: K steps (32 wide) in flight per wave per stage.
 constexpr int kSplitKDepths[] = {1, 2, 4, 8};
 
-// TILED: 4 waves as WM x WN; a wave owns MTW m-tiles x NBW column blocks.
-// Built when the accumulators fit 128 AGPRs, the two register stages plus
-// fragments fit the VGPRs, and the two LDS buffers fit 60 KB.
+// TILED: 4 waves as WM x WN over MT m-tiles (a power of two covering M) and
+// NB column blocks; a wave owns MT/WM x NB/WN tiles.  A ring of NS LDS
+// stages of U (2 or 4) 32-wide K steps, (MT + NB) * U KB per stage, plus
+// 1 KB of padding.  Built when the accumulators and one stage's fragments
+// fit 200 of the 256 VGPRs (the accumulators live in VGPRs), the ring fits
+// 144 KB and also holds the fp32 output tile of the epilogue, and the vmcnt
+// wait of the ring (loads of NS-2 stages) fits its 6-bit field.
 constexpr int kTiledThreads = 256;
-constexpr int tiled_pairs_per_thread(int MTW, int NBW, int WM) {
-    return ((MTW * WM + NBW * (4 / WM)) * 64 + 255) / 256;
+constexpr int kTiledMaxLds = 144 * 1024;
+constexpr int kTiledStages[] = {2, 3, 4, 6, 8};
+constexpr size_t tiled_lds_bytes(int MT, int NB, int NS, int U) {
+    return (size_t)NS * U * (MT + NB) * 1024 + 1024;
 }
-constexpr bool tiled_built(int MTW, int NBW, int WM, int D) {
-    return MTW * NBW <= 32 && 8 * D * tiled_pairs_per_thread(MTW, NBW, WM) + 4 * (MTW + NBW) <= 160 &&
-           2 * D * (MTW * WM + NBW * (4 / WM)) <= 60;
+constexpr bool tiled_built(int MT, int NB, int WM, int NS, int U) {
+    return (WM == 1 || WM == 2 || WM == 4) && MT % WM == 0 && NB % (4 / WM) == 0 &&
+           4 * (MT / WM) * (NB / (4 / WM)) + 4 * U * (MT / WM + NB / (4 / WM)) <= 200 &&
+           tiled_lds_bytes(MT, NB, NS, U) <= kTiledMaxLds &&
+           tiled_lds_bytes(MT, NB, NS, U) >= (size_t)MT * 16 * (NB * 16 + 4) * 4 &&
+           (NS - 2) * ((U * MT + 3) / 4 + (U * NB + 3) / 4) < 64;
 }
-// The wave arrangement of a completed TILED plan for M rows.
-void tiled_shape(const SkgPlan &p, int M, int *MTW, int *NBW, int *WM);
 
 // FP8 dot kernel: x counted packed plus its widened words (as for bf16
 // without dot2) and, in MX mode, one scale byte per (row, vector); a plan is

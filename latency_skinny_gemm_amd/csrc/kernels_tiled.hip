@@ -1,24 +1,31 @@
-// kernels_tiled.hip -- split-K MFMA kernel with LDS-staged operand tiles,
-// for larger M x N (the dense decode linear, M up to 128).
+// kernels_tiled.hip -- split-K MFMA kernel whose x and W tiles stream into a
+// ring of LDS stages by direct buffer-to-LDS loads, for larger M x N (the
+// dense decode linear, M up to 128).
 //
 // The "vllm PR #42562" page's split-K kernel stages A and B tiles through
-// shared memory in a multi-stage pipeline and pads M to the MMA tile.  Here
-// that staging pays off once one workgroup covers many columns and all of
-// M: every W row and every x row of a K step is loaded once per workgroup
-// and read from LDS by the waves that need it, so x is re-read once per
-// 16*NB columns instead of once per 16.
+// shared memory in a multi-stage pipeline and pads M to the MMA tile.  On
+// gfx950 the staging needs no registers: buffer_load_dwordx4 with the LDS
+// bit writes lane p's 16 bytes to LDS at (wave-uniform base) + 16*p, and an
+// out-of-range lane writes zeros (both measured on the MI355X).  So:
 //  * workgroup (j, s): columns [16*NB*j, 16*NB*(j+1)), all M rows (MT
-//    16-row tiles, rows past M read as zeros), K chunk s;
-//  * 4 waves arranged WM x WN (WM*WN = 4); wave (wm, wn) owns MTW m-tiles by
-//    NBW column blocks of the output and never shares a tile, so there is no
-//    cross-wave reduction;
-//  * per 32-wide K step the workgroup loads MT x-blocks and NB W-blocks of
-//    1 KB each.  A block is stored in LDS exactly in v_mfma_f32_16x16x32_bf16
-//    operand order (lane p holds row p%16, bytes 16*(p/16)..+16 of the
-//    step's 64 bytes), so every fragment read is one linear, conflict-free
-//    ds_read_b128;
-//  * D steps form a chunk; chunks alternate between two register sets
-//    (global loads in flight) and two LDS buffers, one barrier per chunk;
+//    16-row tiles, MT a power of two; rows past M read as zeros), K chunk s;
+//    the split index is fastest in the grid, so with S a multiple of 8 every
+//    XCD (workgroup i runs on XCD i % 8) holds one K chunk of x in its L2;
+//  * a K step is 32 wide; per step the workgroup needs MT x-blocks and NB
+//    W-blocks of 1 KB (16 rows x 64 bytes).  Lane p of the load that fills
+//    a block reads row p%16, bytes 16*(p/16)..+16 of the step, so the block
+//    lands in LDS exactly in v_mfma_f32_16x16x32_bf16 operand order and
+//    every fragment read is one linear, conflict-free ds_read_b128;
+//  * a stage holds U steps; NS stages form a ring.  Stage i+NS-1 is issued
+//    right after stage i is consumed, so NS-1 stages are in flight while
+//    one is multiplied.  Each wave waits for its own loads of the stage with
+//    s_waitcnt vmcnt (the count of its loads issued after them is fixed at
+//    compile time) and for its own LDS reads, then one s_barrier makes every
+//    wave's loads visible.
+//    The same barrier also orders the next overwrite of a slot after every
+//    wave's reads of it, so there is one barrier per stage and no fence;
+//  * 4 waves arranged WM x WN own disjoint MT/WM x NB/WN tiles of the
+//    output: no cross-wave reduction;
 //  * K splits (S > 1) reuse the ordered reductions of the split-K kernel.
 #include "device_common.h"
 #include "internal.h"
@@ -26,19 +33,59 @@
 
 namespace skg {
 
-template <int MTW, int NBW, int WM, int D>
+namespace {
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8 = 0).  Waiting for
+// lgkmcnt too means this wave's LDS reads of the slot that the next stage
+// overwrites have returned before the barrier that lets any wave refill it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
+}
+
+// s_barrier without a memory fence.  The asm statements keep the compiler
+// from moving LDS accesses across it; the hardware ordering comes from the
+// explicit vmcnt wait that precedes it.
+__device__ __forceinline__ void barrier_nofence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Chunk swizzle of row r (0..15) in a block whose rows hold 4*U chunks of
+// 16 bytes: rows 64*U bytes apart share a 256-byte bank window 4/U at a
+// time, so the XOR key is the row's index among those that share it.
+template <int U>
+__device__ __forceinline__ int swz(int r) {
+    return (r / (4 / U)) & (4 * U - 1);
+}
+
+// 16 bytes per lane from a buffer straight into LDS at dst + 16 * lane
+// (dst wave-uniform).  Kept out of the kernel body: used there directly,
+// the builtin made the host pass drop the kernels' launch stubs.
+template <int POLICY>
+__device__ __forceinline__ void lds_load16(Rsrc r, unsigned char *dst, unsigned off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, off, 0, 0, POLICY);
+}
+
+}  // namespace
+
+template <int MT, int NB, int WM, int NS, int U>
 __global__ void __launch_bounds__(256)
     tiled_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
                  const uint16_t *__restrict__ bias, uint16_t *__restrict__ out,
                  float *__restrict__ ws, unsigned *__restrict__ tickets, int M, int N, int K,
                  int S, int k_chunk, int reduce) {
     constexpr int WN = 4 / WM;
-    constexpr int MT = MTW * WM;          // 16-row tiles the workgroup covers
-    constexpr int NB = NBW * WN;          // 16-column blocks the workgroup covers
-    constexpr int BLK = MT + NB;          // 1 KB blocks per K step
-    constexpr int PAIRS = BLK * 64;       // (block, lane) pairs per step
-    constexpr int R = (PAIRS + 255) / 256;  // pairs per thread per step
-    constexpr int STEP_BYTES = BLK * 1024;
+    constexpr int MTW = MT / WM;          // m-tiles per wave
+    constexpr int NBW = NB / WN;          // column blocks per wave
+    constexpr int BLK = MT + NB;          // blocks of U KB per stage
+    constexpr int STAGE = BLK * U * 1024; // bytes per stage
+    static_assert(MT % WM == 0 && NB % WN == 0, "wave arrangement");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     __shared__ unsigned is_last;
 
@@ -55,47 +102,71 @@ __global__ void __launch_bounds__(256)
     const Rsrc wr = make_rsrc(W + (size_t)col0 * K, (unsigned)ncols * rowb);
     const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
     const int kbeg = s * k_chunk;
-    const int kend = min(K, kbeg + k_chunk);
-    const int nsteps = (kend - kbeg + 31) >> 5;
-    const int nch = (nsteps + D - 1) / D;
+    const int nsteps = (min(K, kbeg + k_chunk) - kbeg) >> 5;  // K, k_chunk: multiples of 32
+    const int nstages = (nsteps + U - 1) / U;
 
-    // per-thread load slots: pair q = t + 256*r -> (block, p); the block's
-    // row and the lane's 16-byte column inside the step's 64 bytes
-    unsigned row_off[R];   // byte offset of the row in its buffer resource
-    bool is_w[R], valid[R];
-    unsigned kbyte[R];     // 16*(p/16)
+    // Stage layout: MT x-blocks then NB W-blocks; a block is 16 rows of the
+    // stage's 64*U bytes (U steps), U KB, row-major.  Inside a row the
+    // 16-byte chunk c sits at position c ^ swz(r), so the 16 rows that one
+    // MFMA fragment read touches hit 16 different 16-byte bank groups.
+    // A load instruction fills 1 KB of a block: 16/U whole rows of 64*U
+    // contiguous bytes (lane p writes position 64*i + p of the block, i.e.
+    // row (64*i + p) / (4*U), and reads the chunk that belongs there).
+    // Wave w issues x instructions q = w + 4*i (q < MT*U) and W instructions
+    // likewise (q < NB*U); slots past those load zeros into the spare 1 KB
+    // after the ring, so every wave issues XPW + WPW loads per stage.
+    constexpr int CPR = 4 * U;            // 16-byte chunks per row and stage
+    constexpr int XB = MT * U, WB = NB * U;
+    constexpr int XPW = (XB + 3) / 4, WPW = (WB + 3) / 4;
+    constexpr int BPW = XPW + WPW;
+    unsigned xoff[XPW], woff[WPW];        // byte offset of the lane's chunk at K = 0
+    int xstep[XPW], wstep[WPW];           // step of the stage that the chunk belongs to
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int q = t + 256 * r;
-        valid[r] = q < PAIRS;
-        const int blk = q >> 6, p = q & 63;
-        is_w[r] = blk >= MT;
-        const int row = (is_w[r] ? blk - MT : blk) * 16 + (p & 15);
-        row_off[r] = (unsigned)row * rowb;
-        kbyte[r] = (unsigned)(p >> 4) * 16u;
+    for (int i = 0; i < XPW; ++i) {
+        const int q = wave + 4 * i;
+        const int lin = (q % U) * 64 + lane;
+        const int r = lin / CPR, c = (lin % CPR) ^ swz<U>(r);
+        const int row = (q / U) * 16 + r;
+        xoff[i] = (q < XB && row < M) ? (unsigned)row * rowb + (unsigned)c * 16u : kOOB;
+        xstep[i] = c >> 2;
+    }
+#pragma unroll
+    for (int i = 0; i < WPW; ++i) {
+        const int q = wave + 4 * i;
+        const int lin = (q % U) * 64 + lane;
+        const int r = lin / CPR, c = (lin % CPR) ^ swz<U>(r);
+        const int row = (q / U) * 16 + r;
+        woff[i] = (q < WB && row < ncols) ? (unsigned)row * rowb + (unsigned)c * 16u : kOOB;
+        wstep[i] = c >> 2;
     }
 
-    auto load_chunk = [&](u32x4(&regs)[D][R], int c) {
+    // Each column group walks its chunk's stages in a rotated order: the
+    // workgroups of one XCD then read different K ranges of x (and of their
+    // W rows) at any moment instead of the same lines in lockstep.
+    const int rot = j % nstages;
+    auto issue = [&](int slot, int stage) {
+        // stages past the chunk read zeros (no memory traffic)
+        int pos = stage + rot;
+        if (pos >= nstages) pos -= nstages;
+        if (stage >= nstages) pos = nstages;  // no live step
+        const unsigned k0b = (unsigned)(kbeg + pos * U * 32) * 2u;
+        unsigned char *base = lds_raw + slot * STAGE;
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int st = c * D + d;
-            const int k0 = kbeg + st * 32;
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const unsigned kb = (unsigned)k0 * 2u + kbyte[r];
-                const bool ok = valid[r] & (st < nsteps) & ((int)(kb >> 1) < kend);
-                const unsigned off = ok ? row_off[r] + kb : kOOB;
-                regs[d][r] = is_w[r] ? load16<kCacheStream>(wr, off) : load16<kCacheDefault>(xr, off);
-            }
+        for (int i = 0; i < XPW; ++i) {
+            const int q = wave + 4 * i;
+            const bool live = pos * U + xstep[i] < nsteps;
+            unsigned char *dst = q < XB ? base + (q / U) * (U * 1024) + (q % U) * 1024
+                                        : lds_raw + NS * STAGE;
+            lds_load16<kCacheDefault>(xr, dst, live ? xoff[i] + k0b : kOOB);
         }
-    };
-    auto store_chunk = [&](unsigned char *buf, u32x4(&regs)[D][R]) {
 #pragma unroll
-        for (int d = 0; d < D; ++d)
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-                if (valid[r])
-                    *reinterpret_cast<u32x4 *>(buf + d * STEP_BYTES + (t + 256 * r) * 16) = regs[d][r];
+        for (int i = 0; i < WPW; ++i) {
+            const int q = wave + 4 * i;
+            const bool live = pos * U + wstep[i] < nsteps;
+            unsigned char *dst = q < WB ? base + (MT + q / U) * (U * 1024) + (q % U) * 1024
+                                        : lds_raw + NS * STAGE;
+            lds_load16<kCacheStream>(wr, dst, live ? woff[i] + k0b : kOOB);
+        }
     };
 
     f32x4 acc[MTW][NBW];
@@ -104,17 +175,21 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
         for (int b = 0; b < NBW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute_chunk = [&](const unsigned char *buf) {
+    // fragment of step u: lane l takes row l % 16, chunk 4*u + l / 16
+    const int fr = lane & 15;
+    auto compute = [&](int slot) {
+        const unsigned char *stg = lds_raw + slot * STAGE;
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const unsigned char *stp = buf + d * STEP_BYTES;
+        for (int u = 0; u < U; ++u) {
+            const int fo = fr * (CPR * 16) + (((4 * u + (lane >> 4)) ^ swz<U>(fr)) * 16);
             u32x4 af[MTW], bf[NBW];
 #pragma unroll
             for (int a = 0; a < MTW; ++a)
-                af[a] = *reinterpret_cast<const u32x4 *>(stp + (wm * MTW + a) * 1024 + lane * 16);
+                af[a] = *reinterpret_cast<const u32x4 *>(stg + (wm * MTW + a) * (U * 1024) + fo);
 #pragma unroll
             for (int b = 0; b < NBW; ++b)
-                bf[b] = *reinterpret_cast<const u32x4 *>(stp + (MT + wn * NBW + b) * 1024 + lane * 16);
+                bf[b] = *reinterpret_cast<const u32x4 *>(stg + (MT + wn * NBW + b) * (U * 1024) +
+                                                         fo);
 #pragma unroll
             for (int a = 0; a < MTW; ++a)
 #pragma unroll
@@ -125,45 +200,56 @@ __global__ void __launch_bounds__(256)
         }
     };
 
-    unsigned char *lds0 = lds_raw;
-    unsigned char *lds1 = lds_raw + D * STEP_BYTES;
-    u32x4 ra[D][R], rb[D][R];
-    load_chunk(ra, 0);
-    for (int c = 0; c < nch; c += 2) {
-        // nch is the same for every wave of the workgroup: the branches below
-        // are uniform and every wave reaches every barrier
-        load_chunk(rb, c + 1);  // past the end: zeros, no memory traffic
-        store_chunk(lds0, ra);
-        __syncthreads();
-        compute_chunk(lds0);
-        if (c + 1 < nch) {
-            load_chunk(ra, c + 2);
-            store_chunk(lds1, rb);
-            __syncthreads();
-            compute_chunk(lds1);
-        }
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) issue(st, st);
+    for (int st = 0; st < nstages; ++st) {
+        // nstages is the same for every wave: every wave reaches every barrier
+        wait_vmcnt_lds<(NS - 2) * BPW>();
+        barrier_nofence();
+        compute(st % NS);
+        issue((st + NS - 1) % NS, st + NS - 1);
     }
+    wait_vmcnt_lds<0>();  // no load to LDS outlives the loop
 
-    // ---- epilogue: MFMA 16x16 layout, lane l register i -> row 4*(l/16)+i,
-    // column l%16 of the tile
+    // ---- epilogue.  The output tile goes through the (now idle) ring as
+    // fp32 [MT*16][NB*16 + 4], so that global stores cover whole rows:
+    // 16-byte stores of the fp32 partials, or 4 bf16 outputs per thread.
+    // MFMA 16x16 layout: lane l register i -> row 4*(l/16)+i, column l%16
+    // of the tile.  The row stride of NB*16 + 4 floats puts the 4 rows that
+    // one LDS store touches in different banks.
+    constexpr int TS = NB * 16 + 4;
+    float *tile = reinterpret_cast<float *>(lds_raw);
+    __syncthreads();  // every wave has left the ring
 #pragma unroll
     for (int a = 0; a < MTW; ++a)
 #pragma unroll
         for (int b = 0; b < NBW; ++b)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = (wm * MTW + a) * 16 + (lane >> 4) * 4 + i;
-                const int n = col0 + (wn * NBW + b) * 16 + (lane & 15);
-                if (m < M && n < N) {
-                    float v = acc[a][b][i];
-                    if (S == 1) {
-                        if (bias) v += bf16_to_f32(bias[n]);
-                        out[(size_t)m * N + n] = f32_to_bf16_rne(v);
-                    } else {
-                        ws[((size_t)s * M + m) * N + n] = v;
-                    }
-                }
-            }
+            for (int i = 0; i < 4; ++i)
+                tile[((wm * MTW + a) * 16 + (lane >> 4) * 4 + i) * TS + (wn * NBW + b) * 16 +
+                     (lane & 15)] = acc[a][b][i];
+    __syncthreads();
+    constexpr int C4 = NB * 4;  // 4-column groups per row
+    const bool vec = (N & 3) == 0;  // 16-byte aligned workspace rows
+    for (int e = t; e < M * C4; e += 256) {
+        const int r = e / C4, c = (e % C4) * 4;
+        if (c >= ncols) continue;
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(tile + r * TS + c);
+        const int n = col0 + c;
+        if (S == 1) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (c + q < ncols)
+                    out[(size_t)r * N + n + q] =
+                        f32_to_bf16_rne(bias ? v[q] + bf16_to_f32(bias[n + q]) : v[q]);
+        } else if (vec && c + 4 <= ncols) {
+            *reinterpret_cast<f32x4 *>(ws + ((size_t)s * M + r) * N + n) = v;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (c + q < ncols) ws[((size_t)s * M + r) * N + n + q] = v[q];
+        }
+    }
     if (S == 1 || reduce != SKG_REDUCE_LAST) return;
     last_arriver_reduce(ws, tickets, bias, out, M, N, S, j, col0, ncols, &is_last);
 }
@@ -173,61 +259,74 @@ namespace {
 typedef int (*TiledLaunch)(const SkgPlan &, const void *, const void *, const void *, void *,
                            float *, unsigned *, int, int, int, hipStream_t);
 
-template <int MTW, int NBW, int WM, int D>
+template <int MT, int NB, int WM, int NS, int U>
 int launch_tiled_t(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
                    float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream) {
-    constexpr int BLK = MTW * WM + NBW * (4 / WM);
-    const size_t lds_bytes = (size_t)2 * D * BLK * 1024;
-    hipLaunchKernelGGL((tiled_kernel<MTW, NBW, WM, D>), dim3(p.grid), dim3(256), lds_bytes,
+    const size_t lds_bytes = tiled_lds_bytes(MT, NB, NS, U);
+    // rings above 64 KB: allow the kernel that much dynamic LDS (once)
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&tiled_kernel<MT, NB, WM, NS, U>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    if (attr != hipSuccess) return (int)attr;
+    hipLaunchKernelGGL((tiled_kernel<MT, NB, WM, NS, U>), dim3(p.grid), dim3(256), lds_bytes,
                        stream, (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)bias,
                        (uint16_t *)out, ws, tickets, M, N, K, p.splits, p.k_chunk, p.reduce);
     return (int)hipGetLastError();
 }
 
-template <int MTW, int NBW, int WM, int D>
+template <int MT, int NB, int WM, int NS, int U>
 constexpr TiledLaunch tiled_entry() {
-    if constexpr (tiled_built(MTW, NBW, WM, D))
-        return &launch_tiled_t<MTW, NBW, WM, D>;
+    if constexpr (tiled_built(MT, NB, WM, NS, U))
+        return &launch_tiled_t<MT, NB, WM, NS, U>;
     else
         return nullptr;
 }
 
-template <int MTW, int NBW, int WM>
-TiledLaunch pick_d(int D) {
-    switch (D) {
-    case 1: return tiled_entry<MTW, NBW, WM, 1>();
-    case 2: return tiled_entry<MTW, NBW, WM, 2>();
-    case 4: return tiled_entry<MTW, NBW, WM, 4>();
+template <int MT, int NB, int WM, int U>
+TiledLaunch pick_ns(int NS) {
+    switch (NS) {
+    case 2: return tiled_entry<MT, NB, WM, 2, U>();
+    case 3: return tiled_entry<MT, NB, WM, 3, U>();
+    case 4: return tiled_entry<MT, NB, WM, 4, U>();
+    case 6: return tiled_entry<MT, NB, WM, 6, U>();
+    case 8: return tiled_entry<MT, NB, WM, 8, U>();
     default: return nullptr;
     }
 }
 
-template <int MTW, int WM>
-TiledLaunch pick_nbw(int NBW, int D) {
-    switch (NBW) {
-    case 1: return pick_d<MTW, 1, WM>(D);
-    case 2: return pick_d<MTW, 2, WM>(D);
-    case 4: return pick_d<MTW, 4, WM>(D);
-    case 8: return pick_d<MTW, 8, WM>(D);
-    default: return nullptr;
-    }
+template <int MT, int NB, int WM>
+TiledLaunch pick_u(int NS, int U) {
+    return U == 4 ? pick_ns<MT, NB, WM, 4>(NS) : U == 2 ? pick_ns<MT, NB, WM, 2>(NS) : nullptr;
 }
 
-template <int WM>
-TiledLaunch pick_mtw(int MTW, int NBW, int D) {
-    switch (MTW) {
-    case 1: return pick_nbw<1, WM>(NBW, D);
-    case 2: return pick_nbw<2, WM>(NBW, D);
-    case 4: return pick_nbw<4, WM>(NBW, D);
-    default: return nullptr;
-    }
-}
-
-TiledLaunch pick(int MTW, int NBW, int WM, int D) {
+template <int MT, int NB>
+TiledLaunch pick_wm(int WM, int NS, int U) {
     switch (WM) {
-    case 1: return pick_mtw<1>(MTW, NBW, D);
-    case 2: return pick_mtw<2>(MTW, NBW, D);
-    case 4: return pick_mtw<4>(MTW, NBW, D);
+    case 1: return pick_u<MT, NB, 1>(NS, U);
+    case 2: return pick_u<MT, NB, 2>(NS, U);
+    case 4: return pick_u<MT, NB, 4>(NS, U);
+    default: return nullptr;
+    }
+}
+
+template <int MT>
+TiledLaunch pick_nb(int NB, int WM, int NS, int U) {
+    switch (NB) {
+    case 1: return pick_wm<MT, 1>(WM, NS, U);
+    case 2: return pick_wm<MT, 2>(WM, NS, U);
+    case 4: return pick_wm<MT, 4>(WM, NS, U);
+    case 8: return pick_wm<MT, 8>(WM, NS, U);
+    case 16: return pick_wm<MT, 16>(WM, NS, U);
+    default: return nullptr;
+    }
+}
+
+TiledLaunch pick(int MT, int NB, int WM, int NS, int U) {
+    switch (MT) {
+    case 1: return pick_nb<1>(NB, WM, NS, U);
+    case 2: return pick_nb<2>(NB, WM, NS, U);
+    case 4: return pick_nb<4>(NB, WM, NS, U);
+    case 8: return pick_nb<8>(NB, WM, NS, U);
     default: return nullptr;
     }
 }
@@ -236,9 +335,8 @@ TiledLaunch pick(int MTW, int NBW, int WM, int D) {
 
 int launch_tiled(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
                  float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream) {
-    int MTW = 0, NBW = 0, WM = 0;
-    tiled_shape(p, M, &MTW, &NBW, &WM);
-    TiledLaunch f = pick(MTW, NBW, WM, p.depth);
+    const int U = (p.flags & SKG_FLAG_TILED_WIDE) ? 4 : 2;
+    TiledLaunch f = pick(p.m_tiles, p.cols, p.waves_m, p.depth, U);
     if (!f) return (int)hipErrorInvalidConfiguration;
     int rc = f(p, x, W, bias, out, ws, tickets, M, N, K, stream);
     if (rc != (int)hipSuccess || p.splits == 1 || p.reduce != SKG_REDUCE_KERNEL) return rc;

@@ -276,61 +276,118 @@ def _check_coverage(p, M, N, K):
 
 
 def _check_tiled_coverage(p, M, N, K):
-    S, NB, D, kc, WM = p.splits, p.cols, p.depth, p.k_chunk, p.waves_m
+    S, NB, NS, kc, WM = p.splits, p.cols, p.depth, p.k_chunk, p.waves_m
+    U = 4 if p.flags & skg.FLAG_TILED_WIDE else 2
     WN = 4 // WM
-    MT = -(-M // 16)
-    MTW = {1: 1, 2: 2, 3: 4, 4: 4}[-(-MT // WM)]
-    NBW = NB // WN
-    assert p.threads == 256 and NB % WN == 0 and MTW * WM >= MT
+    mt = -(-M // 16)
+    MT = next(v for v in (1, 2, 4, 8) if v >= mt)
+    assert p.m_tiles == MT and MT % WM == 0 and NB % WN == 0
+    MTW, NBW = MT // WM, NB // WN
+    assert p.threads == 256 and K % 32 == 0
     groups = -(-N // (16 * NB))
     assert p.grid == groups * S and kc % 32 == 0 and (S - 1) * kc < K <= S * kc
     # waves partition the workgroup's (m-tile, column-block) grid
     owned = sorted((wm * MTW + a, wn * NBW + b) for wm in range(WM) for wn in range(WN)
                    for a in range(MTW) for b in range(NBW))
-    assert owned == sorted((a, b) for a in range(MTW * WM) for b in range(NB))
-    # load slots: every (block, lane) pair of a step exactly once
-    blk = MTW * WM + NB
-    pairs = blk * 64
-    R = -(-pairs // 256)
-    slots = sorted(t + 256 * r for t in range(256) for r in range(R) if t + 256 * r < pairs)
-    assert slots == list(range(pairs))
-    # K: every step of every split computed once (chunks alternate buffers)
+    assert owned == sorted((a, b) for a in range(MT) for b in range(NB))
+    # a block: 16 rows x 4U chunks of 16 bytes, chunk c of row r at position
+    # r*4U + (c ^ swz(r)); instruction part i of a block fills positions
+    # 64i .. 64i+63 (lane p: position 64i + p)
+    CPR = 4 * U
+
+    def swz(r):
+        return (r // (4 // U)) & (CPR - 1)
+
+    stored = {}
+    for part in range(U):
+        for lane in range(64):
+            lin = part * 64 + lane
+            r, c = lin // CPR, (lin % CPR) ^ swz(lin // CPR)
+            assert (r, c) not in stored
+            stored[(r, c)] = lin
+    assert sorted(stored) == [(r, c) for r in range(16) for c in range(CPR)]
+    assert all(stored[(r, c)] == r * CPR + (c ^ swz(r)) for (r, c) in stored)
+    # fragment reads: step u, lane l wants row l % 16, k 32u + 8(l // 16)..+8,
+    # i.e. chunk 4u + l // 16; 16 consecutive lanes hit 16 bank groups
+    for u in range(U):
+        for g in range(4):
+            pos = [stored[(l % 16, 4 * u + l // 16)] for l in range(16 * g, 16 * g + 16)]
+            assert len({(q * 16 % 256) // 16 for q in pos}) == 16
+    # the instructions of a stage: every (block, part) once, per wave a fixed count
+    XPW, WPW = -(-(MT * U) // 4), -(-(NB * U) // 4)
+    xs = sorted(w + 4 * i for w in range(4) for i in range(XPW) if w + 4 * i < MT * U)
+    ws_ = sorted(w + 4 * i for w in range(4) for i in range(WPW) if w + 4 * i < NB * U)
+    assert xs == list(range(MT * U)) and ws_ == list(range(NB * U))
+    # the epilogue's fp32 tile [MT*16][NB*16 + 4] fits the ring; its 16-byte
+    # groups cover every (row < M, column < ncols) of every column group once
+    ring = NS * U * (MT + NB) * 1024 + 1024
+    TS = NB * 16 + 4
+    assert MT * 16 * TS * 4 <= ring and (TS * 4) % 16 == 0
+    assert len({(4 * r * TS * 4) % 256 // 64 for r in range(4)}) == 4  # rows 4 apart: other banks
+    for j in range(groups):
+        ncols = min(NB * 16, N - 16 * NB * j)
+        cov = sorted((e // (NB * 4), (e % (NB * 4)) * 4 + q) for e in range(M * NB * 4)
+                     for q in range(4) if (e % (NB * 4)) * 4 + q < ncols)
+        assert cov == [(r, c) for r in range(M) for c in range(ncols)]
+    # the ring: stages 0..NS-2 issued up front, stage st+NS-1 issued after
+    # stage st is computed into slot (st+NS-1) % NS; a slot is overwritten
+    # only after its stage was computed, and the vmcnt wait leaves exactly
+    # the loads of the NS-2 later stages outstanding
+    assert (NS - 2) * (XPW + WPW) < 64
+    for j in range(groups):  # each column group visits every stage once (rotated)
+        for s in range(S):
+            nsteps = (min(K, (s + 1) * kc) - s * kc) // 32
+            nst = -(-nsteps // U)
+            rot = j % nst
+            assert sorted((st + rot) % nst for st in range(nst)) == list(range(nst))
     seen = [0] * K
     for s in range(S):
         kbeg, kend = s * kc, min(K, (s + 1) * kc)
-        nsteps = -(-(kend - kbeg) // 32)
-        nch = -(-nsteps // D)
-        done = []
-        for c in range(0, nch, 2):
-            done.append(c)
-            if c + 1 < nch:
-                done.append(c + 1)
-        assert sorted(done) == list(range(nch))
-        for c in done:
-            for d in range(D):
-                st = c * D + d
-                for g in range(4):
-                    k = kbeg + st * 32 + 8 * g
-                    if st < nsteps and k < kend:
-                        for kk in range(k, k + 8):
-                            seen[kk] += 1
+        nsteps = (kend - kbeg) // 32
+        nst = -(-nsteps // U)
+        slot_of = {}
+        issued = []
+        for st in range(NS - 1):
+            slot_of[st % NS] = st
+            issued.append(st)
+        for st in range(nst):
+            assert issued[-1] - st == NS - 2  # stages issued after st
+            assert slot_of[st % NS] == st
+            for u in range(U):
+                step = st * U + u
+                if step < nsteps:
+                    for kk in range(32):
+                        seen[kbeg + step * 32 + kk] += 1
+            nxt = st + NS - 1
+            prev = slot_of.get(nxt % NS)
+            assert prev is None or prev <= st
+            assert nxt % NS != st % NS or NS == 1
+            slot_of[nxt % NS] = nxt
+            issued.append(nxt)
     assert seen == [1] * K
 
 
-@pytest.mark.parametrize("M,N,K,NB,wm,D,S", [
-    (128, 4096, 7168, 16, 2, 1, 16), (64, 576, 7168, 4, 0, 2, 12), (8, 4096, 7168, 8, 1, 2, 8),
-    (33, 200, 2056, 4, 0, 2, 3), (1, 2112, 7168, 16, 0, 1, 4), (5, 100, 2880, 2, 4, 1, 5)])
-def test_tiled_plans_cover(lib, M, N, K, NB, wm, D, S):
-    q = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_TILED, 256, NB, S, D, skg.REDUCE_LAST,
-                                                 waves_m=wm))
+@pytest.mark.parametrize("M,N,K,NB,wm,NS,U,S", [
+    (128, 4096, 7168, 8, 2, 4, 2, 8), (128, 4096, 7168, 8, 4, 3, 2, 16), (64, 576, 7168, 4, 0, 6, 2, 12),
+    (8, 4096, 7168, 8, 1, 6, 2, 8), (33, 200, 2080, 4, 0, 3, 4, 3), (1, 2112, 7168, 16, 0, 2, 4, 4),
+    (5, 100, 2880, 4, 1, 4, 2, 5), (100, 50, 1024, 2, 4, 3, 4, 7), (128, 4096, 7168, 8, 2, 2, 4, 8)])
+def test_tiled_plans_cover(lib, M, N, K, NB, wm, NS, U, S):
+    p = skg.make_plan(skg.KIND_TILED, 256, NB, S, NS, skg.REDUCE_LAST, waves_m=wm,
+                      flags=skg.FLAG_TILED_WIDE if U == 4 else 0)
+    q = skg.plan_complete(M, N, K, p)
     assert q.kind == skg.KIND_TILED and q.waves_m in (1, 2, 4)
     _check_coverage(q, M, N, K)
 
 
 def test_tiled_rejects_bad_plans(lib):
-    for plan in (dict(threads=128, cols=4), dict(threads=256, cols=3), dict(threads=256, cols=4, depth=8),
-                 dict(threads=256, cols=4, waves_m=3), dict(threads=256, cols=2, waves_m=1)):
-        p = skg.make_plan(skg.KIND_TILED, plan["threads"], plan["cols"], 2, plan.get("depth", 1),
-                          skg.REDUCE_LAST, waves_m=plan.get("waves_m", 0))
+    for plan in (dict(threads=128, cols=4), dict(threads=256, cols=3), dict(threads=256, cols=4, depth=5),
+                 dict(threads=256, cols=4, depth=1), dict(threads=256, cols=4, waves_m=3),
+                 dict(threads=256, cols=2, waves_m=1), dict(threads=256, cols=4, flags=1),
+                 dict(threads=256, cols=16, depth=8, flags=2)):
+        p = skg.make_plan(skg.KIND_TILED, plan["threads"], plan["cols"], 2, plan.get("depth", 4),
+                          skg.REDUCE_LAST, waves_m=plan.get("waves_m", 0), flags=plan.get("flags", 0))
         with pytest.raises(skg.SkinnyGemmError):
             skg.plan_complete(128, 4096, 7168, p)
+    # whole 32-wide steps only
+    with pytest.raises(skg.SkinnyGemmError):
+        skg.plan_complete(64, 256, 2056, skg.make_plan(skg.KIND_TILED, 256, 4, 2, 4))

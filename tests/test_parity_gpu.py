@@ -67,14 +67,20 @@ def _kernel_plans(skg, M, N, K):
                                                  depth=1, reduce=skg.REDUCE_KERNEL)))
     plans.append(("splitk_s1", skg.make_plan(skg.KIND_SPLITK, threads, cols=nb, splits=1,
                                              depth=4 if nb * mt <= 8 else 2)))
-    for (nbt, S, d, red) in ((16, 4, 1, skg.REDUCE_LAST), (8, 3, 2, skg.REDUCE_KERNEL),
-                             (4, 1, 4, skg.REDUCE_NONE), (2, 7, 1, skg.REDUCE_LAST)):
-        p = skg.make_plan(skg.KIND_TILED, 256, cols=nbt, splits=S, depth=d, reduce=red)
+    wide = skg.FLAG_TILED_WIDE
+    for (nbt, S, ns, fl, red, wm) in ((16, 4, 3, 0, skg.REDUCE_LAST, 0),
+                                      (8, 3, 2, wide, skg.REDUCE_KERNEL, 0),
+                                      (4, 1, 4, 0, skg.REDUCE_NONE, 4),
+                                      (2, 7, 2, wide, skg.REDUCE_LAST, 0),
+                                      (8, 8, 4, 0, skg.REDUCE_KERNEL, 1),
+                                      (16, 16, 4, 0, skg.REDUCE_KERNEL, 0)):
+        p = skg.make_plan(skg.KIND_TILED, 256, cols=nbt, splits=S, depth=ns, reduce=red,
+                          flags=fl, waves_m=wm)
         try:
             skg.plan_complete(M, N, K, p)
         except skg.SkinnyGemmError:
             continue
-        plans.append((f"tiled_nb{nbt}_s{S}_d{d}_r{red}", p))
+        plans.append((f"tiled_nb{nbt}_s{S}_ns{ns}_f{fl}_r{red}_wm{wm}", p))
     return plans
 
 
