@@ -78,6 +78,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 section")
+    ap.add_argument("--no-decode", action="store_true", help="skip the dense decode section")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for rocprofv3 --pmc: launch each headline call a few times on cold "
                          "weights, then a 64 MiB reference copy, and exit")
@@ -109,6 +110,64 @@ def pmc_probe(skg, torch, floors, stream, sptr, W, X, OUT, n_slots):
     stream.synchronize()
     print(json.dumps({"pmc_probe": "done", "calls_per_M": 8, "copy_bytes": COPY_BYTES}), flush=True)
     return 0
+
+
+DECODE_K = 7168
+DECODE_N = (576, 2112, 4096)
+DECODE_M = (1, 8, 32, 64, 128)
+
+
+def decode_section(skg, torch, stream, sptr):
+    """bf16 dense decode linear, K = 7168, N in {576, 2112, 4096}, M in
+    {1, 8, 32, 64, 128} (the planner's plan, no bias): microseconds per call
+    over a cold pool of >= 512 MB of distinct W, the algorithmic GB/s and
+    its fraction of 8 TB/s."""
+    dev = torch.device("cuda:0")
+    K = DECODE_K
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    res = {}
+    for N in DECODE_N:
+        slots = -(-(512 << 20) // (N * K * 2))
+        W = torch.empty((slots, N, K), dtype=torch.bfloat16, device=dev)
+        for i in range(slots):
+            W[i].copy_((torch.randn((N, K), generator=g, device=dev) * K ** -0.5).to(torch.bfloat16))
+        for M in DECODE_M:
+            X = torch.randn((slots, M, K), generator=g, device=dev).to(torch.bfloat16)
+            O = torch.empty((slots, M, N), dtype=torch.bfloat16, device=dev)
+
+            def calls():
+                for s in range(slots):
+                    rc = skg.lib().skinny_gemm_bf16(X[s].data_ptr(), W[s].data_ptr(), None, None,
+                                                    O[s].data_ptr(), M, N, K, sptr)
+                    if rc != 0:
+                        raise skg.SkinnyGemmError(rc, f"skinny_gemm_bf16 M={M} N={N}")
+            with torch.cuda.stream(stream):
+                calls()
+            stream.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                calls()
+            with torch.cuda.stream(stream):
+                gr.replay()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(3):
+                    gr.replay()
+                e1.record(stream)
+                e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (3 * slots)
+            del gr
+            byts = 2 * N * K + 2 * M * K + 2 * M * N
+            p = skg.plan(M, N, K)
+            res[f"N{N}_M{M}"] = {"us_per_call": round(us, 3),
+                                 "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+                                 "frac_of_8TBps": round(byts / (us * 1e-6) / 8e12, 4),
+                                 "kernel": {1: "dot", 2: "splitk", 3: "tiled"}[p.kind]}
+            del X, O
+        del W
+        torch.cuda.empty_cache()
+    return res
 
 
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
@@ -350,6 +409,7 @@ def main():
                          f"{t_cpu / reps / len(M_VALUES) * 1e6:.0f} (mean over M)"}
 
     fp8 = None if args.no_fp8 else fp8_section(skg, torch, stream, sptr)
+    decode = None if args.no_decode else decode_section(skg, torch, stream, sptr)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -369,6 +429,7 @@ def main():
                    "shape": "256 workgroups x 256 threads; read: 256 rows x 14336 B"},
         "per_m": per_m,
         "fp8_k4096_n4096": fp8,
+        "decode_bf16_k7168": decode,
         "parity": parity,
     }
     print(json.dumps(line), flush=True)

@@ -159,6 +159,38 @@ __global__ void __launch_bounds__(256)
     out[e] = f32_to_bf16_rne(v);
 }
 
+// The same reduction, four consecutive outputs per thread (N % 4 == 0, so
+// the four share a row and every partial load is 16 bytes).  Each of the
+// four sums adds the partials in ascending s, as above: identical bits.
+__global__ void __launch_bounds__(256)
+    splitk_reduce4_kernel(const float *__restrict__ ws, const uint16_t *__restrict__ bias,
+                          uint16_t *__restrict__ out, int M, int N, int S,
+                          const float *__restrict__ sx, const float *__restrict__ sw) {
+    const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (e >= M * N) return;
+    const size_t plane = (size_t)M * N;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 < S; i0 += 8) {
+        f32x4 t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            t[i] = (i0 + i < S) ? *reinterpret_cast<const f32x4 *>(ws + (i0 + i) * plane + e)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i0 + i < S) v += t[i];
+    }
+    const int n = e % N;
+    const float scale = sx ? sx[0] * sw[0] : 1.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float r = v[q];
+        if (sx) r *= scale;
+        if (bias) r += bf16_to_f32(bias[n + q]);
+        out[e + q] = f32_to_bf16_rne(r);
+    }
+}
+
 namespace {
 
 typedef int (*SplitKLaunch)(const SkgPlan &, const void *, const void *, const void *, void *,
@@ -218,8 +250,12 @@ SplitKLaunch pick(int MT, int NB, int D) {
 int launch_splitk_reduce(const float *ws, const void *bias, void *out, int M, int N, int S,
                          hipStream_t stream, const float *sx, const float *sw) {
     const int elems = M * N;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((elems + 255) / 256), dim3(256), 0, stream, ws,
-                       (const uint16_t *)bias, (uint16_t *)out, M, N, S, sx, sw);
+    if ((N & 3) == 0)
+        hipLaunchKernelGGL(splitk_reduce4_kernel, dim3((elems / 4 + 255) / 256), dim3(256), 0,
+                           stream, ws, (const uint16_t *)bias, (uint16_t *)out, M, N, S, sx, sw);
+    else
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((elems + 255) / 256), dim3(256), 0, stream,
+                           ws, (const uint16_t *)bias, (uint16_t *)out, M, N, S, sx, sw);
     return (int)hipGetLastError();
 }
 
