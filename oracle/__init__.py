@@ -48,6 +48,10 @@ def lib():
                                              i64, i64, i64, ctypes.c_int]
         L.oracle_gemm_fp8_mx.restype = None
         L.oracle_gemm_fp8_mx.argtypes = [P, P, P, P, P, P, P, i64, i64, i64, ctypes.c_int]
+        L.oracle_encode_e4m3.restype = ctypes.c_uint8
+        L.oracle_encode_e4m3.argtypes = [ctypes.c_float]
+        L.oracle_quant_e4m3.restype = None
+        L.oracle_quant_e4m3.argtypes = [P, i64, ctypes.c_float, P]
         L.oracle_threads_used.restype = ctypes.c_int
         L.oracle_threads_used.argtypes = [ctypes.c_int]
         _lib = L
@@ -106,6 +110,26 @@ def gemm_fp8_tensor(xq, wq, sx, sw, bias=None, out_f32=False, threads=1):
     lib().oracle_gemm_fp8_tensor(_ptr(xq), _ptr(wq), float(np.float32(sx)), float(np.float32(sw)),
                                  _ptr(b), _ptr(o16), _ptr(o32), M, N, K, threads)
     return out
+
+
+def encode_e4m3(v):
+    """Nearest e4m3fn code (ties to even) of a binary32 value in [-448, 448]."""
+    return int(lib().oracle_encode_e4m3(float(np.float32(v))))
+
+
+def quant_e4m3(x, s):
+    """Static per-tensor quantisation of bf16 codes x (any shape) with the
+    fp32 scale s: e4m3 codes of clamp(x * (1/s), -448, 448), in binary32."""
+    x = _u16(x)
+    q = np.empty(x.shape, dtype=np.uint8)
+    lib().oracle_quant_e4m3(_ptr(x), x.size, float(np.float32(s)), _ptr(q))
+    return q
+
+
+def gemm_fp8_quant(x, wq, sx, sw, bias=None, out_f32=False, threads=1):
+    """bf16 x[M,K] quantised statically with sx, then the per-tensor FP8 GEMM
+    with e4m3 wq[N,K] and sw."""
+    return gemm_fp8_tensor(quant_e4m3(x, sx), wq, sx, sw, bias, out_f32, threads)
 
 
 def gemm_fp8_mx(xq, wq, xe, we, bias=None, out_f32=False, threads=1):

@@ -31,6 +31,14 @@
  * fp32-output variant (router logits, "vllm PR #42562" page, split-K kernel
  * snippet: out dtype fp32): the same sum rounded once from fp64 to fp32.
  *
+ * Static activation quantisation ("sglang PR #28333" page, the static FP8
+ * quant kernel): with a given per-tensor scale s,
+ *     q = e4m3( clamp( x * (1 / s), -448, 448 ) ),
+ * evaluated in binary32 as that kernel does (x widened to fp32, one
+ * reciprocal, one product, round to the nearest e4m3 value, ties to even).
+ * Because these roundings decide integer codes, the oracle takes them in
+ * the same precision (binary32), not in fp64.
+ *
  * Threads: the (m, n) outputs are independent; OpenMP splits them over
  * threads.  The k order inside one output never changes, so the result is
  * bitwise identical for every thread count.
@@ -119,6 +127,49 @@ uint16_t oracle_round_bf16(double v)
 float oracle_round_f32(double v)
 {
     return (float)v;
+}
+
+/* Round a binary32 value to the nearest OCP e4m3fn code, ties to even.
+ * Finite inputs must lie in [-448, 448] (the quantiser clamps first); the
+ * top binade's quantum is 32, so nothing rounds past 448.  NaN gives the
+ * NaN code with the input's sign.  Below 2^-6 the quantum is fixed at 2^-9
+ * (subnormals). */
+uint8_t oracle_encode_e4m3(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    if (isnan(v))
+        return (uint8_t)(sign | 0x7F);
+    double a = fabs((double)v);
+    if (a == 0.0)
+        return sign;
+    int e2;
+    frexp(a, &e2);
+    int e = e2 - 1;            /* floor(log2 a) */
+    if (e < -6)
+        e = -6;                /* subnormal range */
+    int q_exp = e - 3;         /* 3 mantissa bits: quantum 2^(e-3) */
+    double r = nearbyint(ldexp(a, -q_exp));  /* exact scaling, RNE */
+    double res = ldexp(r, q_exp);
+    if (res == 0.0)
+        return sign;
+    frexp(res, &e2);
+    int E = e2 - 1;
+    if (E < -6)                /* subnormal: res = m * 2^-9, m = 1..7 */
+        return (uint8_t)(sign | (uint8_t)ldexp(res, 9));
+    int mant = (int)ldexp(res, 3 - E) - 8;   /* res = 2^E * (8 + mant) / 8 */
+    return (uint8_t)(sign | (uint8_t)((E + 7) << 3) | (uint8_t)mant);
+}
+
+/* Static per-tensor quantisation of n bf16 values with scale s. */
+void oracle_quant_e4m3(const uint16_t *x, long n, float s, uint8_t *q)
+{
+    const float inv = 1.0f / s;          /* one correctly rounded reciprocal */
+    for (long i = 0; i < n; ++i) {
+        float v = (float)oracle_decode_bf16(x[i]) * inv;  /* exact widening, one product */
+        if (!isnan(v))
+            v = v < -448.0f ? -448.0f : (v > 448.0f ? 448.0f : v);
+        q[i] = oracle_encode_e4m3(v);
+    }
 }
 
 /* ---------------------------------------------------------------- GEMMs */

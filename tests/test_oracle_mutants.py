@@ -33,6 +33,13 @@ MUTANTS = {
     "mx_scale_index": ("oracle_decode_e8m0(xe[m * KB + b])", "oracle_decode_e8m0(xe[m * KB])"),
     "fp8_double_scale": ("double acc = dot * scale;", "double acc = dot * scale * (double)sw;"),
     "subnormal_quantum": ("e = -126;", "e = -125;"),
+    "quant_divides": ("float v = (float)oracle_decode_bf16(x[i]) * inv;",
+                      "float v = (float)oracle_decode_bf16(x[i]) / s;"),
+    "quant_no_clamp": ("v = v < -448.0f ? -448.0f : (v > 448.0f ? 448.0f : v);", "(void)0;"),
+    "e4m3_round_half_up": ("double r = nearbyint(ldexp(a, -q_exp));",
+                           "double r = floor(ldexp(a, -q_exp) + 0.5);"),
+    "e4m3_subnormal_edge": ("if (e < -6)\n        e = -6;                /* subnormal range */",
+                            "if (e < -7)\n        e = -7;                /* subnormal range */"),
 }
 
 

@@ -345,3 +345,86 @@ def test_no_intermediate_fp32_rounding():
     assert out[0, 0] == 0x3FC1
     w2 = torch.tensor([[1.0078125, 2.0 ** -15]], dtype=torch.bfloat16)
     assert oracle.gemm_bf16(gen.bits16(x), gen.bits16(w2))[0, 0] == 0x3FC2
+
+
+# ------------------------------------------------ static FP8 quantisation
+# "sglang PR #28333" page, static FP8 quant kernel: q = e4m3(clamp(x * (1/s),
+# -448, 448)) in binary32.  The encoder is pinned to the e4m3 bit fields
+# (exact rationals, independent of the oracle's code) and the quantiser to
+# torch's own binary32 arithmetic and float8_e4m3fn cast.
+
+def _finite_e4m3_values():
+    vals = []
+    for code in range(256):
+        f = exact.e4m3_code_to_fraction(code)
+        if isinstance(f, Fraction):  # NaN codes are checked on their own
+            vals.append((f, code))
+    return vals
+
+
+def test_encode_e4m3_round_trips_every_code():
+    for f, code in _finite_e4m3_values():
+        got = oracle.encode_e4m3(float(f)) if f != 0 else oracle.encode_e4m3(-0.0 if code & 0x80 else 0.0)
+        assert got == code, (code, f, got)
+
+
+def test_encode_e4m3_midpoints_round_to_even():
+    pos = sorted({f for f, c in _finite_e4m3_values() if f >= 0})
+    code_of = {f: c for f, c in _finite_e4m3_values() if not (c & 0x80)}
+    for lo, hi in zip(pos, pos[1:]):
+        mid = (lo + hi) / 2
+        even = lo if code_of[lo] % 2 == 0 else hi
+        assert float(mid) == mid  # midpoints of e4m3 neighbours are binary32 values
+        assert oracle.encode_e4m3(float(mid)) == code_of[even], (lo, hi)
+        assert oracle.encode_e4m3(-float(mid)) == code_of[even] | 0x80
+        # just off the midpoint, by one binary32 ulp, the nearer neighbour wins
+        below = float(np.nextafter(np.float32(mid), np.float32(0)))
+        above = float(np.nextafter(np.float32(mid), np.float32(1e9)))
+        assert oracle.encode_e4m3(below) == code_of[lo]
+        assert oracle.encode_e4m3(above) == code_of[hi]
+    assert oracle.encode_e4m3(float("nan")) == 0x7F
+    assert oracle.encode_e4m3(-float("nan")) == 0xFF
+
+
+@pytest.mark.parametrize("s", [1.0, 0.037, 3.5, 2.0 ** -4, 1e-3, 448.0 / 7.25])
+def test_quant_matches_torch_for_every_bf16_code(s):
+    codes = np.arange(65536, dtype=np.uint16)
+    q = oracle.quant_e4m3(codes, s)
+    x = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).float()
+    inv = 1.0 / torch.tensor(s, dtype=torch.float32)
+    ref = (x * inv).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    nan = torch.isnan(x).numpy()
+    assert np.array_equal(q[~nan], ref[~nan])
+    assert np.all((q[nan] & 0x7F) == 0x7F)
+
+
+def _bf16_as_f32(code):
+    return np.array([code], np.uint16).astype(np.uint32).__lshift__(16).view(np.float32)[0]
+
+
+def test_quant_uses_the_reciprocal_not_a_division():
+    # x * (1/s) and x / s are different binary32 roundings; with this scale
+    # and x = 1.0546875 (a bf16 value) they straddle the e4m3 midpoint 1.0625
+    # between 1.0 and 1.125.  The page's kernel multiplies by the reciprocal.
+    s = np.float32(0.9926469922065735)
+    xv = np.float32(1.0546875)
+    a, b = np.float32(xv * (np.float32(1.0) / s)), np.float32(xv / s)
+    assert a != b
+    code = int(np.array([xv], np.float32).view(np.uint32)[0] >> 16)
+    q = oracle.quant_e4m3(np.array([code], np.uint16), float(s))[0]
+    ref = torch.tensor([float(a)], dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).item()
+    wrong = torch.tensor([float(b)], dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).item()
+    assert ref != wrong and q == ref
+
+
+def test_gemm_fp8_quant_composes_quant_and_gemm():
+    x, _, _ = gen.bf16_inputs(3, 8, 64, False, seed=4)
+    g = torch.Generator().manual_seed(5)
+    wcodes = gen.bits8(torch.randint(-2, 3, (8, 64), generator=g).float().to(torch.float8_e4m3fn))
+    xq = oracle.quant_e4m3(gen.bits16(x), 0.02)
+    a = oracle.gemm_fp8_quant(gen.bits16(x), wcodes, 0.02, 0.5, out_f32=True)
+    b = oracle.gemm_fp8_tensor(xq, wcodes, 0.02, 0.5, out_f32=True)
+    assert np.array_equal(a, b)
+    # and the codes are the ones the quantiser pins fix: spot-check by torch
+    ref = (x.float() * (1.0 / torch.tensor(0.02, dtype=torch.float32))).clamp(-448, 448)
+    assert np.array_equal(xq, gen.bits8(ref.to(torch.float8_e4m3fn)))
