@@ -79,6 +79,8 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 section")
     ap.add_argument("--no-decode", action="store_true", help="skip the dense decode section")
+    ap.add_argument("--no-f3", action="store_true",
+                    help="skip the fp32-output and fused-quantisation section")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for rocprofv3 --pmc: launch each headline call a few times on cold "
                          "weights, then a 64 MiB reference copy, and exit")
@@ -167,6 +169,87 @@ def decode_section(skg, torch, stream, sptr):
             del X, O
         del W
         torch.cuda.empty_cache()
+    return res
+
+
+def f3_section(skg, torch, stream, sptr):
+    """The two output/quantisation variants, microseconds per call on cold W:
+    fp32 logits beside bf16 at the router shape (K = 7168, N = 256), and the
+    FP8 GEMM on bf16 activations at K = N = 4096 with the quantisation fused
+    into the dot kernel beside quantise-then-GEMM (two launches)."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(21)
+    res = {}
+
+    def timed(calls, n):
+        with torch.cuda.stream(stream):
+            calls()
+        stream.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            calls()
+        with torch.cuda.stream(stream):
+            gr.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(3):
+                gr.replay()
+            e1.record(stream)
+            e1.synchronize()
+        del gr
+        return round(e0.elapsed_time(e1) * 1e3 / (3 * n), 3)
+
+    L = skg.lib()
+    K, N = 7168, 256
+    slots = -(-(512 << 20) // (N * K * 2))
+    W = (torch.randn((slots, N, K), generator=g, device=dev) * K ** -0.5).to(torch.bfloat16)
+    for M in (1, 8, 16):
+        X = torch.randn((slots, M, K), generator=g, device=dev).to(torch.bfloat16)
+        O16 = torch.empty((slots, M, N), dtype=torch.bfloat16, device=dev)
+        O32 = torch.empty((slots, M, N), dtype=torch.float32, device=dev)
+
+        def c16():
+            for s in range(slots):
+                assert L.skinny_gemm_bf16(X[s].data_ptr(), W[s].data_ptr(), None, None,
+                                          O16[s].data_ptr(), M, N, K, sptr) == 0
+
+        def c32():
+            for s in range(slots):
+                assert L.skinny_gemm_bf16_f32(X[s].data_ptr(), W[s].data_ptr(), None,
+                                              O32[s].data_ptr(), M, N, K, sptr) == 0
+        res[f"router_M{M}"] = {"bf16_out_us": timed(c16, slots), "fp32_out_us": timed(c32, slots)}
+    del W
+    K = N = 4096
+    slots = -(-(512 << 20) // (N * K))
+    Wq = torch.empty((slots, N, K), dtype=torch.float8_e4m3fn, device=dev)
+    for i in range(slots):
+        Wq[i].copy_(torch.randn((N, K), generator=g, device=dev).to(torch.float8_e4m3fn))
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    sx = torch.full((1,), 0.01, dtype=torch.float32, device=dev)
+    for M in (1, 8, 16):
+        X = torch.randn((slots, M, K), generator=g, device=dev).to(torch.bfloat16)
+        XQ = torch.empty((slots, M, K), dtype=torch.float8_e4m3fn, device=dev)
+        O = torch.empty((slots, M, N), dtype=torch.bfloat16, device=dev)
+        sc = skg.Fp8Scales()
+        sc.mode, sc.sx, sc.sw = skg.FP8_PER_TENSOR, sx.data_ptr(), one.data_ptr()
+
+        def fused():
+            for s in range(slots):
+                assert L.skinny_gemm_fp8_quant(X[s].data_ptr(), Wq[s].data_ptr(), None,
+                                               sx.data_ptr(), one.data_ptr(), O[s].data_ptr(),
+                                               skg.DTYPE_BF16, M, N, K, sptr) == 0
+
+        def two_step():
+            for s in range(slots):
+                assert L.skinny_quant_e4m3(X[s].data_ptr(), sx.data_ptr(), XQ[s].data_ptr(),
+                                           M * K, sptr) == 0
+                assert L.skinny_gemm_fp8(XQ[s].data_ptr(), Wq[s].data_ptr(), None,
+                                         ctypes.byref(sc), O[s].data_ptr(), M, N, K, sptr) == 0
+        res[f"fp8_quant_M{M}"] = {"fused_us": timed(fused, slots),
+                                  "quant_then_gemm_us": timed(two_step, slots)}
+    del Wq
+    torch.cuda.empty_cache()
     return res
 
 
@@ -410,6 +493,7 @@ def main():
 
     fp8 = None if args.no_fp8 else fp8_section(skg, torch, stream, sptr)
     decode = None if args.no_decode else decode_section(skg, torch, stream, sptr)
+    f3 = None if args.no_f3 else f3_section(skg, torch, stream, sptr)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -430,6 +514,7 @@ def main():
         "per_m": per_m,
         "fp8_k4096_n4096": fp8,
         "decode_bf16_k7168": decode,
+        "fp32_out_and_fused_quant": f3,
         "parity": parity,
     }
     print(json.dumps(line), flush=True)

@@ -71,6 +71,7 @@ extern "C" {
 /* ------------------------------------------------------------ enums */
 #define SKG_DTYPE_BF16 0
 #define SKG_DTYPE_FP8 1
+#define SKG_DTYPE_F32 2 /* output dtype only: fp32 logits */
 
 #define SKG_FP8_PER_TENSOR 1
 #define SKG_FP8_MX32 2
@@ -180,6 +181,46 @@ int skinny_gemm_bf16_planned(const void *x, const void *W, const void *bias, voi
  * capture.  Outside capture a call that needs more grows the workspace
  * itself; during capture it returns SKG_ERR_WORKSPACE instead. */
 int skinny_gemm_reserve(int max_M, int max_N, int max_S, hipStream_t stream);
+
+/* bf16 GEMM with fp32 output (router logits): out[m, n] = fp32 value of the
+ * fp32-accumulated sum plus bias, with no bf16 rounding.  The router split-K
+ * kernel of the "vllm PR #42562" page writes its logits in fp32 (its output
+ * dtype is fixed to float).  out: DEVICE fp32 [M, N], 4-byte aligned, not
+ * overlapping x, W or bias; everything else as skinny_gemm_bf16, with the
+ * same plans (the table's bf16 entries). */
+int skinny_gemm_bf16_f32(const void *x, const void *W, const void *bias, float *out, int M,
+                         int N, int K, hipStream_t stream);
+
+/* The same with a caller-made plan (as skinny_gemm_bf16_planned). */
+int skinny_gemm_bf16_f32_planned(const void *x, const void *W, const void *bias, float *out,
+                                 int M, int N, int K, const SkgPlan *plan, hipStream_t stream);
+
+/* Per-tensor FP8 GEMM on bf16 activations, quantised statically on the way:
+ *     q[m, k] = e4m3( clamp( x[m, k] * (1 / sx), -448, 448 ) )   (in fp32)
+ *     out     = sx * sw * sum_k q[m, k] * W[n, k]  (+ bias[n])
+ * The quantisation is the static FP8 quant kernel of the "sglang PR #28333"
+ * page (a given scale, one reciprocal, a product, a clamp, the cast to e4m3
+ * with round-to-nearest-even), followed by that page's per-tensor GEMM.
+ * The dot-product plan (small M) quantises x as it loads it, so the call is
+ * one launch; other plans quantise x into the workspace first (a second
+ * launch).  x: DEVICE bf16 [M, K], 16-byte aligned; W: DEVICE e4m3fn
+ * [N, K], 16-byte aligned; sx, sw: DEVICE fp32 scalars, 4-byte aligned;
+ * K % 16 == 0.  out_dtype: SKG_DTYPE_BF16 (bf16 out, 2-byte aligned) or
+ * SKG_DTYPE_F32 (fp32 out, 4-byte aligned).  NaN in x gives NaN outputs. */
+int skinny_gemm_fp8_quant(const void *x, const void *W, const void *bias, const float *sx,
+                          const float *sw, void *out, int out_dtype, int M, int N, int K,
+                          hipStream_t stream);
+
+/* The same with a caller-made FP8 plan (as skinny_gemm_fp8_planned). */
+int skinny_gemm_fp8_quant_planned(const void *x, const void *W, const void *bias,
+                                  const float *sx, const float *sw, void *out, int out_dtype,
+                                  int M, int N, int K, const SkgPlan *plan, hipStream_t stream);
+
+/* The static quantisation alone: q[i] = e4m3(clamp(x[i] * (1/s), -448,
+ * 448)) for i < n, as in skinny_gemm_fp8_quant.  x: DEVICE bf16 [n],
+ * q: DEVICE bytes [n], both 16-byte aligned and disjoint; s: DEVICE fp32,
+ * 4-byte aligned.  n == 0 is a no-op; n < 0 is SKG_ERR_INVALID_ARG. */
+int skinny_quant_e4m3(const void *x, const float *s, void *q, long n, hipStream_t stream);
 
 /* Frees every workspace of every device after a device synchronisation.
  * No call may be in flight. */

@@ -15,7 +15,8 @@ __all__ = ["SkgPlan", "SkinnyGemmError", "gemm_bf16", "gemm_bf16_planned", "gemm
            "gemm_fp8_planned", "plan", "plan_on",
            "plan_complete", "reserve", "release_all", "status_string", "library_path",
            "KIND_DOT", "KIND_SPLITK", "KIND_TILED", "REDUCE_NONE", "REDUCE_LAST", "REDUCE_KERNEL", "FLAG_DOT2", "FLAG_TILED_WIDE",
-           "DTYPE_BF16", "DTYPE_FP8"]
+           "DTYPE_BF16", "DTYPE_FP8", "DTYPE_F32", "gemm_bf16_f32", "gemm_fp8_quant",
+           "quant_e4m3"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libskinny_gemm.so")
@@ -29,6 +30,7 @@ ERR_WORKSPACE = -4
 ERR_HIP = -5
 DTYPE_BF16 = 0
 DTYPE_FP8 = 1
+DTYPE_F32 = 2  # output dtype only
 FP8_PER_TENSOR = 1
 FP8_MX32 = 2
 KIND_DOT = 1
@@ -90,6 +92,16 @@ def _load():
     L.skinny_gemm_fp8.restype = I
     L.skinny_gemm_fp8_planned.argtypes = [P, P, P, ctypes.POINTER(Fp8Scales), P, I, I, I, PP, P]
     L.skinny_gemm_fp8_planned.restype = I
+    L.skinny_gemm_bf16_f32.argtypes = [P, P, P, P, I, I, I, P]
+    L.skinny_gemm_bf16_f32.restype = I
+    L.skinny_gemm_bf16_f32_planned.argtypes = [P, P, P, P, I, I, I, PP, P]
+    L.skinny_gemm_bf16_f32_planned.restype = I
+    L.skinny_gemm_fp8_quant.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
+    L.skinny_gemm_fp8_quant.restype = I
+    L.skinny_gemm_fp8_quant_planned.argtypes = [P, P, P, P, P, P, I, I, I, I, PP, P]
+    L.skinny_gemm_fp8_quant_planned.restype = I
+    L.skinny_quant_e4m3.argtypes = [P, P, P, ctypes.c_long, P]
+    L.skinny_quant_e4m3.restype = I
     L.skinny_gemm_plan.argtypes = [I, I, I, I, PP]
     L.skinny_gemm_plan.restype = I
     L.skinny_gemm_plan_on.argtypes = [I, I, I, I, I, PP]
@@ -170,6 +182,79 @@ def gemm_bf16_planned(x, W, p, bias=None, out=None, stream=None):
     rc = _load().skinny_gemm_bf16_planned(_ptr(x), _ptr(W), _ptr(bias), _ptr(out), M, N, K,
                                           ctypes.byref(p), _stream_ptr(stream))
     _check(rc, f"skinny_gemm_bf16_planned(M={M}, N={N}, K={K}, {p})")
+    return out
+
+
+def gemm_bf16_f32(x, W, bias=None, out=None, plan=None, stream=None):
+    """fp32 logits: out[M,N] = x[M,K] @ W[N,K]^T (+ bias) in fp32 (no bf16
+    rounding); the library's plan, or a caller-made one."""
+    M, N, K = _check_tensors(x, W, bias, None, torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise TypeError("out must be contiguous float32 [M, N]")
+    if plan is None:
+        rc = _load().skinny_gemm_bf16_f32(_ptr(x), _ptr(W), _ptr(bias), _ptr(out), M, N, K,
+                                          _stream_ptr(stream))
+    else:
+        rc = _load().skinny_gemm_bf16_f32_planned(_ptr(x), _ptr(W), _ptr(bias), _ptr(out), M, N,
+                                                  K, ctypes.byref(plan), _stream_ptr(stream))
+    _check(rc, f"skinny_gemm_bf16_f32(M={M}, N={N}, K={K}, {plan})")
+    return out
+
+
+def _scalar_f32(name, t):
+    if t is None or t.dtype != torch.float32 or t.numel() != 1 or not t.is_cuda:
+        raise TypeError(f"{name} must be a one-element float32 device tensor")
+
+
+def gemm_fp8_quant(x, wq, sx, sw, bias=None, out_dtype=torch.bfloat16, out=None, plan=None,
+                   stream=None):
+    """bf16 x quantised statically to e4m3 with sx, times e4m3 wq with sw
+    (per-tensor): out = sx*sw*sum(q*w) (+ bias), bf16 or fp32."""
+    if x.dim() != 2 or not x.is_cuda or not x.is_contiguous() or x.dtype != torch.bfloat16:
+        raise TypeError("x must be a contiguous bf16 [M, K] device tensor")
+    if wq.dim() != 2 or not wq.is_cuda or not wq.is_contiguous() or \
+            wq.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise TypeError("wq must be a contiguous float8_e4m3fn [N, K] device tensor")
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("x[M,K] and wq[N,K] expected")
+    _scalar_f32("sx", sx)
+    _scalar_f32("sw", sw)
+    if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (N,)
+                             or not bias.is_cuda):
+        raise TypeError("bias must be bf16 [N] on the device")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    code = DTYPE_F32 if out_dtype == torch.float32 else DTYPE_BF16
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise TypeError(f"out must be contiguous {out_dtype} [M, N]")
+    args = (_ptr(x), _ptr(wq), _ptr(bias), _ptr(sx), _ptr(sw), _ptr(out), code, M, N, K)
+    if plan is None:
+        rc = _load().skinny_gemm_fp8_quant(*args, _stream_ptr(stream))
+    else:
+        rc = _load().skinny_gemm_fp8_quant_planned(*args, ctypes.byref(plan), _stream_ptr(stream))
+    _check(rc, f"skinny_gemm_fp8_quant(M={M}, N={N}, K={K}, {plan})")
+    return out
+
+
+def quant_e4m3(x, s, out=None, stream=None):
+    """Static e4m3 quantisation of a contiguous bf16 device tensor with the
+    one-element fp32 scale s; returns float8_e4m3fn of x's shape."""
+    if not x.is_cuda or not x.is_contiguous() or x.dtype != torch.bfloat16:
+        raise TypeError("x must be a contiguous bf16 device tensor")
+    _scalar_f32("s", s)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    elif out.dtype not in (torch.float8_e4m3fn, torch.uint8) or out.shape != x.shape \
+            or not out.is_contiguous():
+        raise TypeError("out must be a contiguous float8_e4m3fn tensor of x's shape")
+    rc = _load().skinny_quant_e4m3(_ptr(x), _ptr(s), _ptr(out), x.numel(), _stream_ptr(stream))
+    _check(rc, f"skinny_quant_e4m3(n={x.numel()})")
     return out
 
 

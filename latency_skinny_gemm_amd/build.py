@@ -27,7 +27,7 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFOR
               "-I", "/opt/rocm/include", "-I", INCLUDE, "-I", CSRC]
 
 LIB_HIP = ["api.hip", "kernels_dot.hip", "kernels_splitk.hip", "kernels_tiled.hip",
-           "kernels_fp8.hip"]
+           "kernels_fp8.hip", "kernels_quant.hip"]
 LIB_HOST = ["plan.cpp"]
 # Per-file flags.  The tiled kernel keeps its accumulators in VGPRs: with the
 # compiler's default AGPR form, the loop-carried accumulators were copied

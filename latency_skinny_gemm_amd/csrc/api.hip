@@ -27,13 +27,13 @@ bool overlap(const void *a, size_t abytes, const void *b, size_t bbytes) {
 }
 
 // Pointer checks shared by the bf16 entry points (sizes already checked and
-// M, N > 0).
+// M, N > 0).  out_f32: out holds fp32 (4-byte) elements instead of bf16.
 int check_pointers_bf16(const void *x, const void *W, const void *bias, void *out, int M, int N,
-                        int K) {
+                        int K, int out_f32 = 0) {
     if (!x || !W || !out) return SKG_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(W, 16)) return SKG_ERR_ALIGNMENT;
-    if (!aligned(out, 2) || (bias && !aligned(bias, 2))) return SKG_ERR_ALIGNMENT;
-    const size_t ob = (size_t)M * N * 2;
+    if (!aligned(out, out_f32 ? 4 : 2) || (bias && !aligned(bias, 2))) return SKG_ERR_ALIGNMENT;
+    const size_t ob = (size_t)M * N * (out_f32 ? 4 : 2);
     if (overlap(out, ob, x, (size_t)M * K * 2) || overlap(out, ob, W, (size_t)N * K * 2) ||
         overlap(out, ob, bias, (size_t)N * 2))
         return SKG_ERR_INVALID_ARG;
@@ -107,10 +107,10 @@ int acquire(hipStream_t stream, size_t floats, size_t tickets, float **ws, unsig
     return SKG_OK;
 }
 
-int run_bf16(const void *x, const void *W, const void *bias, void *out, int M, int N, int K,
-             const SkgPlan &p, hipStream_t stream) {
+int run_bf16(const void *x, const void *W, const void *bias, void *out, int out_f32, int M, int N,
+             int K, const SkgPlan &p, hipStream_t stream) {
     if (p.kind == SKG_KIND_DOT) {
-        int e = launch_dot(p, x, W, bias, out, M, N, K, stream);
+        int e = launch_dot(p, x, W, bias, out, out_f32, M, N, K, stream);
         return e == (int)hipSuccess ? SKG_OK : SKG_ERR_HIP;
     }
     float *ws = nullptr;
@@ -119,22 +119,115 @@ int run_bf16(const void *x, const void *W, const void *bias, void *out, int M, i
         int rc = acquire(stream, workspace_floats(p, M, N), (size_t)tile_count(p, N), &ws, &tk);
         if (rc != SKG_OK) return rc;
     }
-    int e = p.kind == SKG_KIND_TILED ? launch_tiled(p, x, W, bias, out, ws, tk, M, N, K, stream)
-                                     : launch_splitk(p, x, W, bias, out, ws, tk, M, N, K, stream);
+    int e = p.kind == SKG_KIND_TILED
+                ? launch_tiled(p, x, W, bias, out, out_f32, ws, tk, M, N, K, stream)
+                : launch_splitk(p, x, W, bias, out, out_f32, ws, tk, M, N, K, stream);
     return e == (int)hipSuccess ? SKG_OK : SKG_ERR_HIP;
 }
 
+// quant_x: x is bf16 and is quantised statically with sc->sx (per-tensor
+// mode).  The DOT kernel does it on load; every other plan quantises x into
+// the workspace first (one extra launch) and multiplies those codes.
 int run_fp8(const void *x, const void *W, const void *bias, const skinny_fp8_scales *sc, void *out,
-            int M, int N, int K, const SkgPlan &p, hipStream_t stream) {
-    Fp8Args a{x, W, bias, out, sc->mode, sc->sx, sc->sw, sc->x_e8m0, sc->w_e8m0};
+            int out_f32, bool quant_x, int M, int N, int K, const SkgPlan &p,
+            hipStream_t stream) {
+    Fp8Args a{x, W, bias, out, sc->mode, sc->sx, sc->sw, sc->x_e8m0, sc->w_e8m0, out_f32, false};
+    const bool fused =
+        quant_x && p.kind == SKG_KIND_DOT && fp8_dot_quant_ok(M, p.depth, p.threads);
+    a.qx = fused;
+    // partials first (rounded to 256 bytes), then the quantised x if needed
+    const size_t part = (p.kind != SKG_KIND_DOT && p.splits > 1)
+                            ? (workspace_floats(p, M, N) + 63) / 64 * 64
+                            : 0;
+    const size_t qfloats = (quant_x && !fused) ? ((size_t)M * K + 3) / 4 : 0;
     float *ws = nullptr;
     unsigned *tk = nullptr;
-    if (p.kind != SKG_KIND_DOT && p.splits > 1) {
-        int rc = acquire(stream, workspace_floats(p, M, N), (size_t)tile_count(p, N), &ws, &tk);
+    if (part + qfloats > 0) {
+        int rc = acquire(stream, part + qfloats, (size_t)tile_count(p, N), &ws, &tk);
         if (rc != SKG_OK) return rc;
+    }
+    if (quant_x && !fused) {
+        void *q = ws + part;
+        if (launch_quant_e4m3(x, sc->sx, q, (long)M * K, stream) != (int)hipSuccess)
+            return SKG_ERR_HIP;
+        a.x = q;
     }
     int e = launch_fp8(p, a, ws, tk, M, N, K, stream);
     return e == (int)hipSuccess ? SKG_OK : SKG_ERR_HIP;
+}
+
+// Checks of the FP8 entry points (sizes already checked, M, N > 0).
+// x_bytes: bytes per x element (1 for e4m3 codes, 2 for bf16 to quantise).
+int check_fp8(const void *x, const void *W, const void *bias, const skinny_fp8_scales *scales,
+              void *out, int out_f32, int x_bytes, int M, int N, int K) {
+    if (!scales || !x || !W || !out) return SKG_ERR_INVALID_ARG;
+    const int mode = scales->mode;
+    if (mode != SKG_FP8_PER_TENSOR && mode != SKG_FP8_MX32) return SKG_ERR_INVALID_ARG;
+    if (mode == SKG_FP8_PER_TENSOR && (!scales->sx || !scales->sw)) return SKG_ERR_INVALID_ARG;
+    if (mode == SKG_FP8_MX32 && (!scales->x_e8m0 || !scales->w_e8m0)) return SKG_ERR_INVALID_ARG;
+    if (mode == SKG_FP8_MX32 && K % 32 != 0) return SKG_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(out, out_f32 ? 4 : 2) ||
+        (bias && !aligned(bias, 2)))
+        return SKG_ERR_ALIGNMENT;
+    if (mode == SKG_FP8_PER_TENSOR && (!aligned(scales->sx, 4) || !aligned(scales->sw, 4)))
+        return SKG_ERR_ALIGNMENT;
+    const size_t ob = (size_t)M * N * (out_f32 ? 4 : 2);
+    if (overlap(out, ob, x, (size_t)M * K * x_bytes) || overlap(out, ob, W, (size_t)N * K) ||
+        overlap(out, ob, bias, (size_t)N * 2))
+        return SKG_ERR_INVALID_ARG;
+    return SKG_OK;
+}
+
+// skinny_gemm_fp8_quant and its planned form.
+int fp8_quant_common(const void *x, const void *W, const void *bias, const float *sx,
+                     const float *sw, void *out, int out_dtype, int M, int N, int K,
+                     const SkgPlan *plan, hipStream_t stream) {
+    int rc = check_sizes(M, N, K, SKG_DTYPE_FP8);
+    if (rc != SKG_OK) return rc;
+    if (out_dtype != SKG_DTYPE_BF16 && out_dtype != SKG_DTYPE_F32) return SKG_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return SKG_OK;
+    const int out_f32 = out_dtype == SKG_DTYPE_F32;
+    skinny_fp8_scales sc{SKG_FP8_PER_TENSOR, sx, sw, nullptr, nullptr};
+    rc = check_fp8(x, W, bias, &sc, out, out_f32, 2, M, N, K);
+    if (rc != SKG_OK) return rc;
+    SkgPlan p;
+    if (plan) {
+        p = *plan;
+        rc = complete_plan(M, N, K, SKG_DTYPE_FP8, &p);
+    } else {
+        rc = skinny_gemm_plan(M, N, K, SKG_DTYPE_FP8, &p);
+        // The fused dot kernel holds bf16 x until it is quantised and may
+        // need smaller workgroups than the FP8 plan: try 512 threads
+        // (enough vectors per thread follow) so the call stays one launch.
+        if (rc == SKG_OK && p.kind == SKG_KIND_DOT && !fp8_dot_quant_ok(M, p.depth, p.threads)) {
+            SkgPlan q = p;
+            q.threads = 512;
+            if (complete_plan(M, N, K, SKG_DTYPE_FP8, &q) == SKG_OK &&
+                fp8_dot_quant_ok(M, q.depth, q.threads))
+                p = q;
+        }
+    }
+    if (rc != SKG_OK) return rc;
+    return run_fp8(x, W, bias, &sc, out, out_f32, true, M, N, K, p, stream);
+}
+
+// skinny_gemm_bf16_f32 and its planned form.
+int bf16_f32_common(const void *x, const void *W, const void *bias, float *out, int M, int N,
+                    int K, const SkgPlan *plan, hipStream_t stream) {
+    int rc = check_sizes(M, N, K, SKG_DTYPE_BF16);
+    if (rc != SKG_OK) return rc;
+    if (M == 0 || N == 0) return SKG_OK;
+    rc = check_pointers_bf16(x, W, bias, out, M, N, K, 1);
+    if (rc != SKG_OK) return rc;
+    SkgPlan p;
+    if (plan) {
+        p = *plan;
+        rc = complete_plan(M, N, K, SKG_DTYPE_BF16, &p);
+    } else {
+        rc = skinny_gemm_plan(M, N, K, SKG_DTYPE_BF16, &p);
+    }
+    if (rc != SKG_OK) return rc;
+    return run_bf16(x, W, bias, out, 1, M, N, K, p, stream);
 }
 
 }  // namespace
@@ -165,7 +258,7 @@ extern "C" int skinny_gemm_bf16(const void *x, const void *W, const void *bias,
     SkgPlan p;
     rc = skinny_gemm_plan(M, N, K, SKG_DTYPE_BF16, &p);
     if (rc != SKG_OK) return rc;
-    return run_bf16(x, W, bias, out, M, N, K, p, stream);
+    return run_bf16(x, W, bias, out, 0, M, N, K, p, stream);
 }
 
 extern "C" int skinny_gemm_bf16_planned(const void *x, const void *W, const void *bias, void *out,
@@ -180,7 +273,7 @@ extern "C" int skinny_gemm_bf16_planned(const void *x, const void *W, const void
     SkgPlan p = *plan;
     rc = complete_plan(M, N, K, SKG_DTYPE_BF16, &p);
     if (rc != SKG_OK) return rc;
-    return run_bf16(x, W, bias, out, M, N, K, p, stream);
+    return run_bf16(x, W, bias, out, 0, M, N, K, p, stream);
 }
 
 extern "C" int skinny_gemm_fp8(const void *x, const void *W, const void *bias,
@@ -189,24 +282,12 @@ extern "C" int skinny_gemm_fp8(const void *x, const void *W, const void *bias,
     int rc = check_sizes(M, N, K, SKG_DTYPE_FP8);
     if (rc != SKG_OK) return rc;
     if (M == 0 || N == 0) return SKG_OK;
-    if (!scales || !x || !W || !out) return SKG_ERR_INVALID_ARG;
-    const int mode = scales->mode;
-    if (mode != SKG_FP8_PER_TENSOR && mode != SKG_FP8_MX32) return SKG_ERR_INVALID_ARG;
-    if (mode == SKG_FP8_PER_TENSOR && (!scales->sx || !scales->sw)) return SKG_ERR_INVALID_ARG;
-    if (mode == SKG_FP8_MX32 && (!scales->x_e8m0 || !scales->w_e8m0)) return SKG_ERR_INVALID_ARG;
-    if (mode == SKG_FP8_MX32 && K % 32 != 0) return SKG_ERR_UNSUPPORTED;
-    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(out, 2) || (bias && !aligned(bias, 2)))
-        return SKG_ERR_ALIGNMENT;
-    if (mode == SKG_FP8_PER_TENSOR && (!aligned(scales->sx, 4) || !aligned(scales->sw, 4)))
-        return SKG_ERR_ALIGNMENT;
-    const size_t ob = (size_t)M * N * 2;
-    if (overlap(out, ob, x, (size_t)M * K) || overlap(out, ob, W, (size_t)N * K) ||
-        overlap(out, ob, bias, (size_t)N * 2))
-        return SKG_ERR_INVALID_ARG;
+    rc = check_fp8(x, W, bias, scales, out, 0, 1, M, N, K);
+    if (rc != SKG_OK) return rc;
     SkgPlan p;
     rc = skinny_gemm_plan(M, N, K, SKG_DTYPE_FP8, &p);
     if (rc != SKG_OK) return rc;
-    return run_fp8(x, W, bias, scales, out, M, N, K, p, stream);
+    return run_fp8(x, W, bias, scales, out, 0, false, M, N, K, p, stream);
 }
 
 extern "C" int skinny_gemm_fp8_planned(const void *x, const void *W, const void *bias,
@@ -215,22 +296,51 @@ extern "C" int skinny_gemm_fp8_planned(const void *x, const void *W, const void 
     int rc = check_sizes(M, N, K, SKG_DTYPE_FP8);
     if (rc != SKG_OK) return rc;
     if (M == 0 || N == 0) return SKG_OK;
-    if (!plan || !scales || !x || !W || !out) return SKG_ERR_INVALID_ARG;
-    const int mode = scales->mode;
-    if (mode != SKG_FP8_PER_TENSOR && mode != SKG_FP8_MX32) return SKG_ERR_INVALID_ARG;
-    if (mode == SKG_FP8_PER_TENSOR && (!scales->sx || !scales->sw)) return SKG_ERR_INVALID_ARG;
-    if (mode == SKG_FP8_MX32 && (!scales->x_e8m0 || !scales->w_e8m0)) return SKG_ERR_INVALID_ARG;
-    if (mode == SKG_FP8_MX32 && K % 32 != 0) return SKG_ERR_UNSUPPORTED;
-    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(out, 2) || (bias && !aligned(bias, 2)))
-        return SKG_ERR_ALIGNMENT;
-    const size_t ob = (size_t)M * N * 2;
-    if (overlap(out, ob, x, (size_t)M * K) || overlap(out, ob, W, (size_t)N * K) ||
-        overlap(out, ob, bias, (size_t)N * 2))
-        return SKG_ERR_INVALID_ARG;
+    if (!plan) return SKG_ERR_INVALID_ARG;
+    rc = check_fp8(x, W, bias, scales, out, 0, 1, M, N, K);
+    if (rc != SKG_OK) return rc;
     SkgPlan p = *plan;
     rc = complete_plan(M, N, K, SKG_DTYPE_FP8, &p);
     if (rc != SKG_OK) return rc;
-    return run_fp8(x, W, bias, scales, out, M, N, K, p, stream);
+    return run_fp8(x, W, bias, scales, out, 0, false, M, N, K, p, stream);
+}
+
+extern "C" int skinny_gemm_bf16_f32(const void *x, const void *W, const void *bias, float *out,
+                                    int M, int N, int K, hipStream_t stream) {
+    return bf16_f32_common(x, W, bias, out, M, N, K, nullptr, stream);
+}
+
+extern "C" int skinny_gemm_bf16_f32_planned(const void *x, const void *W, const void *bias,
+                                            float *out, int M, int N, int K, const SkgPlan *plan,
+                                            hipStream_t stream) {
+    if (!plan) return SKG_ERR_INVALID_ARG;
+    return bf16_f32_common(x, W, bias, out, M, N, K, plan, stream);
+}
+
+extern "C" int skinny_gemm_fp8_quant(const void *x, const void *W, const void *bias,
+                                     const float *sx, const float *sw, void *out, int out_dtype,
+                                     int M, int N, int K, hipStream_t stream) {
+    return fp8_quant_common(x, W, bias, sx, sw, out, out_dtype, M, N, K, nullptr, stream);
+}
+
+extern "C" int skinny_gemm_fp8_quant_planned(const void *x, const void *W, const void *bias,
+                                             const float *sx, const float *sw, void *out,
+                                             int out_dtype, int M, int N, int K,
+                                             const SkgPlan *plan, hipStream_t stream) {
+    if (!plan) return SKG_ERR_INVALID_ARG;
+    return fp8_quant_common(x, W, bias, sx, sw, out, out_dtype, M, N, K, plan, stream);
+}
+
+extern "C" int skinny_quant_e4m3(const void *x, const float *s, void *q, long n,
+                                 hipStream_t stream) {
+    if (n < 0) return SKG_ERR_INVALID_ARG;
+    if (n == 0) return SKG_OK;
+    if (!x || !s || !q) return SKG_ERR_INVALID_ARG;
+    if (n > kMaxBufferBytes) return SKG_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return SKG_ERR_ALIGNMENT;
+    if (overlap(q, (size_t)n, x, (size_t)n * 2) || overlap(q, (size_t)n, s, 4))
+        return SKG_ERR_INVALID_ARG;
+    return launch_quant_e4m3(x, s, q, n, stream) == (int)hipSuccess ? SKG_OK : SKG_ERR_HIP;
 }
 
 extern "C" int skinny_gemm_reserve(int max_M, int max_N, int max_S, hipStream_t stream) {

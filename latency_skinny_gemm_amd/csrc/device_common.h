@@ -47,6 +47,44 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// The final store of one output element: bf16 (one RNE rounding of the fp32
+// value) or, for fp32 outputs, the fp32 value itself.
+__device__ __forceinline__ void store_out(void *out, size_t i, float v, int out_f32) {
+    if (out_f32)
+        static_cast<float *>(out)[i] = v;
+    else
+        static_cast<uint16_t *>(out)[i] = f32_to_bf16_rne(v);
+}
+
+// ---------------------------------------------------------------- FP8 quant
+// Static per-tensor FP8 quantisation ("sglang PR #28333" page, the static
+// FP8 quant kernel): q = e4m3(clamp(x * inv, -448, 448)) with inv = 1/s, in
+// fp32.  The clamp is written with comparisons so that NaN passes through
+// (min/max would replace it); v_cvt_pk_fp8_f32 rounds to the nearest e4m3
+// value, ties to even (checked code by code against the reference).
+__device__ __forceinline__ float quant_clamp(float v) {
+    return v > 448.0f ? 448.0f : (v < -448.0f ? -448.0f : v);
+}
+
+// Two bf16 values (low half first) -> two e4m3 codes in the low or high
+// 16 bits of `old`.
+template <bool HIGH>
+__device__ __forceinline__ int quant_pair(unsigned w, float inv, int old) {
+    return __builtin_amdgcn_cvt_pk_fp8_f32(quant_clamp(bf16_lo(w) * inv),
+                                           quant_clamp(bf16_hi(w) * inv), old, HIGH);
+}
+
+// 16 bf16 values (lo: elements 0-7, hi: 8-15) -> 16 e4m3 codes, byte k =
+// element k.
+__device__ __forceinline__ u32x4 quant16_e4m3(u32x4 lo, u32x4 hi, float inv) {
+    u32x4 r;
+    r.x = (unsigned)quant_pair<true>(lo.y, inv, quant_pair<false>(lo.x, inv, 0));
+    r.y = (unsigned)quant_pair<true>(lo.w, inv, quant_pair<false>(lo.z, inv, 0));
+    r.z = (unsigned)quant_pair<true>(hi.y, inv, quant_pair<false>(hi.x, inv, 0));
+    r.w = (unsigned)quant_pair<true>(hi.w, inv, quant_pair<false>(hi.z, inv, 0));
+    return r;
+}
+
 // acc + sum of the 8 products of two 16-byte bf16 vectors, k ascending,
 // each product exact in fp32 and each addition rounded once (fused).
 __device__ __forceinline__ float dot8_fma(u32x4 a, u32x4 b, float acc) {

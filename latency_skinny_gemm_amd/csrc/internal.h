@@ -75,8 +75,12 @@ constexpr int kFp8DotVecs[] = {1, 2, 4};
 constexpr int fp8_dot_regs(int M, int V, bool mx) {
     return dot_regs(M, 1, V, false) + (mx ? (M + 1) * V : 0);
 }
-constexpr int fp8_dot_max_threads(int M, int V, bool mx) {
-    return fp8_dot_regs(M, V, mx) <= 96 ? 1024 : 512;
+// With x arriving as bf16 and quantised on load (static per-tensor FP8),
+// each vector of a row is two 16-byte loads (8 VGPRs) until it is packed
+// into 4 VGPRs of codes; counted as 12 per (row, vector) plus W.
+constexpr int fp8q_dot_regs(int M, int V) { return M * V * 12 + 4 * V + M; }
+constexpr int fp8_dot_max_threads(int M, int V, bool mx, bool qx = false) {
+    return (qx ? fp8q_dot_regs(M, V) : fp8_dot_regs(M, V, mx)) <= 96 ? 1024 : 512;
 }
 
 // FP8 MFMA split-K (v_mfma_scale_f32_16x16x128_f8f6f4, 128-wide K steps):
@@ -100,6 +104,8 @@ struct Fp8Args {
     int mode;                 // SKG_FP8_PER_TENSOR or SKG_FP8_MX32
     const float *sx, *sw;     // per-tensor scales (device)
     const uint8_t *xe, *we;   // MX exponents (device)
+    int out_f32;              // 1: fp32 output, 0: bf16
+    bool qx;                  // x is bf16, quantised on load with sx (DOT only)
 };
 
 // Host-side validation and planning (plan.cpp).  No HIP calls.
@@ -113,16 +119,25 @@ size_t workspace_floats(const SkgPlan &p, int M, int N);
 int tile_count(const SkgPlan &p, int N);
 
 // Launchers (kernels_*.hip).  Return a hipError_t as int.
+// out_f32: 1 writes fp32 outputs, 0 bf16.
 int launch_dot(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
-               int M, int N, int K, hipStream_t stream);
+               int out_f32, int M, int N, int K, hipStream_t stream);
 int launch_splitk(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
-                  float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream);
+                  int out_f32, float *ws, unsigned *tickets, int M, int N, int K,
+                  hipStream_t stream);
 int launch_tiled(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
-                 float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream);
-int launch_splitk_reduce(const float *ws, const void *bias, void *out, int M, int N, int S,
-                         hipStream_t stream, const float *sx = nullptr,
+                 int out_f32, float *ws, unsigned *tickets, int M, int N, int K,
+                 hipStream_t stream);
+int launch_splitk_reduce(const float *ws, const void *bias, void *out, int out_f32, int M, int N,
+                         int S, hipStream_t stream, const float *sx = nullptr,
                          const float *sw = nullptr);
+// Static e4m3 quantisation of n bf16 values with the device scale s.
+int launch_quant_e4m3(const void *x, const float *s, void *q, long n, hipStream_t stream);
 int launch_fp8(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets, int M, int N,
                int K, hipStream_t stream);
+// Whether the FP8 dot kernel that quantises bf16 x on load exists for (M, V)
+// and accepts workgroups of `threads` (its registers bound it lower than the
+// plain FP8 dot kernel).
+bool fp8_dot_quant_ok(int M, int V, int threads);
 
 }  // namespace skg

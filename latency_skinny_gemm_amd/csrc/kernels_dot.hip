@@ -28,7 +28,8 @@ namespace skg {
 template <int M, int C, int V, bool DOT2>
 __global__ void __launch_bounds__((dot_max_threads(M, C, V, DOT2)))
     dot_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
-               const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int N, int K) {
+               const uint16_t *__restrict__ bias, void *__restrict__ out, int N, int K,
+               int out_f32) {
     const int T = blockDim.x;
     const int t = threadIdx.x;
     const int n0 = blockIdx.x * C;
@@ -88,7 +89,7 @@ __global__ void __launch_bounds__((dot_max_threads(M, C, V, DOT2)))
         float s = ordered_sum<8>(nw, [&](int w) { return red[w][t]; });
         if (n < N) {
             if (bias) s += bf16_to_f32(bias[n]);
-            out[(size_t)m * N + n] = f32_to_bf16_rne(s);
+            store_out(out, (size_t)m * N + n, s, out_f32);
         }
     }
 }
@@ -96,14 +97,14 @@ __global__ void __launch_bounds__((dot_max_threads(M, C, V, DOT2)))
 namespace {
 
 typedef int (*DotLaunch)(const SkgPlan &, const void *, const void *, const void *, void *, int,
-                         int, hipStream_t);
+                         int, int, hipStream_t);
 
 template <int M, int C, int V, bool DOT2>
 int launch_dot_t(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
-                 int N, int K, hipStream_t stream) {
+                 int N, int K, int out_f32, hipStream_t stream) {
     hipLaunchKernelGGL((dot_kernel<M, C, V, DOT2>), dim3(p.grid), dim3(p.threads), 0, stream,
                        (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)bias,
-                       (uint16_t *)out, N, K);
+                       out, N, K, out_f32);
     return (int)hipGetLastError();
 }
 
@@ -162,10 +163,10 @@ DotLaunch pick(int M, int C, int V, bool dot2) {
 }  // namespace
 
 int launch_dot(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
-               int M, int N, int K, hipStream_t stream) {
+               int out_f32, int M, int N, int K, hipStream_t stream) {
     DotLaunch f = pick(M, p.cols, p.depth, (p.flags & SKG_FLAG_DOT2) != 0);
     if (!f) return (int)hipErrorInvalidConfiguration;
-    return f(p, x, W, bias, out, N, K, stream);
+    return f(p, x, W, bias, out, N, K, out_f32, stream);
 }
 
 }  // namespace skg

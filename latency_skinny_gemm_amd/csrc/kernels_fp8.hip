@@ -64,18 +64,25 @@ __device__ __forceinline__ unsigned load_byte(Rsrc r, unsigned off) {
 }
 
 // ------------------------------------------------------------------ dot
-template <int M, int V, bool MX>
-__global__ void __launch_bounds__((fp8_dot_max_threads(M, V, MX)))
-    fp8_dot_kernel(const uint8_t *__restrict__ x, const uint8_t *__restrict__ W,
+// QX: x arrives as bf16 and is quantised statically with sx on load (the
+// fused form of the "sglang PR #28333" page's static quant kernel): each
+// 16-element vector is two 16-byte bf16 loads, turned into 16 e4m3 codes
+// exactly as the standalone quantisation kernel does.
+template <int M, int V, bool MX, bool QX>
+__global__ void __launch_bounds__((fp8_dot_max_threads(M, V, MX, QX)))
+    fp8_dot_kernel(const void *__restrict__ x, const uint8_t *__restrict__ W,
                    const uint16_t *__restrict__ bias, const float *__restrict__ sx,
                    const float *__restrict__ sw, const uint8_t *__restrict__ xe,
-                   const uint8_t *__restrict__ we, uint16_t *__restrict__ out, int N, int K) {
+                   const uint8_t *__restrict__ we, void *__restrict__ out, int N, int K,
+                   int out_f32) {
+    static_assert(!(MX && QX), "static quantisation is per-tensor");
     const int T = blockDim.x;
     const int t = threadIdx.x;
     const int n = blockIdx.x;
     const unsigned rowb = (unsigned)K;  // one byte per element
     const Rsrc wr = make_rsrc(W + (size_t)n * K, rowb);
-    const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
+    const unsigned xrowb = QX ? 2u * rowb : rowb;  // bf16 or e4m3 x rows
+    const Rsrc xr = make_rsrc(x, (unsigned)M * xrowb);
     const int K16 = K >> 4;
     const unsigned srow = (unsigned)(K >> 5);  // scale bytes per row (MX)
     const Rsrc xer = make_rsrc(xe, MX ? (unsigned)M * srow : 0u);
@@ -88,12 +95,28 @@ __global__ void __launch_bounds__((fp8_dot_max_threads(M, V, MX)))
         const int v = t + i * T;
         wv[i] = load16<kCacheStream>(wr, v < K16 ? (unsigned)v * 16u : kOOB);
     }
+    if constexpr (QX) {
+        const float inv = 1.0f / sx[0];  // correctly rounded (no fast-math)
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-        const int v = t + i * T;
-        const unsigned off = v < K16 ? (unsigned)v * 16u : kOOB;
+        for (int i = 0; i < V; ++i) {
+            const int v = t + i * T;
+            const unsigned off = v < K16 ? (unsigned)v * 32u : kOOB;
 #pragma unroll
-        for (int m = 0; m < M; ++m) xv[m][i] = load16<kCacheDefault>(xr, off + (unsigned)m * rowb);
+            for (int m = 0; m < M; ++m) {
+                const u32x4 lo = load16<kCacheDefault>(xr, off + (unsigned)m * xrowb);
+                const u32x4 hi = load16<kCacheDefault>(xr, off + 16u + (unsigned)m * xrowb);
+                xv[m][i] = quant16_e4m3(lo, hi, inv);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const int v = t + i * T;
+            const unsigned off = v < K16 ? (unsigned)v * 16u : kOOB;
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                xv[m][i] = load16<kCacheDefault>(xr, off + (unsigned)m * rowb);
+        }
     }
     if constexpr (MX) {
 #pragma unroll
@@ -137,7 +160,7 @@ __global__ void __launch_bounds__((fp8_dot_max_threads(M, V, MX)))
         float s = ordered_sum<8>(nw, [&](int w) { return red[w][t]; });
         if (!MX) s *= sx[0] * sw[0];
         if (bias) s += bf16_to_f32(bias[n]);
-        out[(size_t)t * N + n] = f32_to_bf16_rne(s);
+        store_out(out, (size_t)t * N + n, s, out_f32);
     }
 }
 
@@ -147,9 +170,9 @@ __global__ void __launch_bounds__((fp8_mfma_max_threads(MT, NB, D, MX)))
     fp8_mfma_kernel(const uint8_t *__restrict__ x, const uint8_t *__restrict__ W,
                     const uint16_t *__restrict__ bias, const float *__restrict__ sx,
                     const float *__restrict__ sw, const uint8_t *__restrict__ xe,
-                    const uint8_t *__restrict__ we, uint16_t *__restrict__ out,
+                    const uint8_t *__restrict__ we, void *__restrict__ out,
                     float *__restrict__ ws, unsigned *__restrict__ tickets, int M, int N, int K,
-                    int S, int k_chunk, int reduce) {
+                    int S, int k_chunk, int reduce, int out_f32) {
     extern __shared__ float lds[];
     __shared__ unsigned is_last;
 
@@ -286,14 +309,14 @@ __global__ void __launch_bounds__((fp8_mfma_max_threads(MT, NB, D, MX)))
             if (S == 1) {
                 v *= scale;
                 if (bias) v += bf16_to_f32(bias[n]);
-                out[(size_t)m * N + n] = f32_to_bf16_rne(v);
+                store_out(out, (size_t)m * N + n, v, out_f32);
             } else {
                 ws[((size_t)s * M + m) * N + n] = v;
             }
         }
     }
     if (S == 1 || reduce != SKG_REDUCE_LAST) return;
-    last_arriver_reduce(ws, tickets, bias, out, M, N, S, j, col0, ncols, &is_last,
+    last_arriver_reduce(ws, tickets, bias, out, out_f32, M, N, S, j, col0, ncols, &is_last,
                         MX ? nullptr : sx, MX ? nullptr : sw);
 }
 
@@ -303,51 +326,52 @@ typedef int (*Fp8DotLaunch)(const SkgPlan &, const Fp8Args &, int, int, hipStrea
 typedef int (*Fp8MfmaLaunch)(const SkgPlan &, const Fp8Args &, float *, unsigned *, int, int, int,
                              hipStream_t);
 
-template <int M, int V, bool MX>
+template <int M, int V, bool MX, bool QX>
 int launch_fp8_dot_t(const SkgPlan &p, const Fp8Args &a, int N, int K, hipStream_t stream) {
-    hipLaunchKernelGGL((fp8_dot_kernel<M, V, MX>), dim3(p.grid), dim3(p.threads), 0, stream,
-                       (const uint8_t *)a.x, (const uint8_t *)a.W, (const uint16_t *)a.bias, a.sx,
-                       a.sw, a.xe, a.we, (uint16_t *)a.out, N, K);
+    hipLaunchKernelGGL((fp8_dot_kernel<M, V, MX, QX>), dim3(p.grid), dim3(p.threads), 0, stream,
+                       a.x, (const uint8_t *)a.W, (const uint16_t *)a.bias, a.sx, a.sw, a.xe,
+                       a.we, a.out, N, K, a.out_f32);
     return (int)hipGetLastError();
 }
 
-template <int M, int V, bool MX>
+template <int M, int V, bool MX, bool QX>
 constexpr Fp8DotLaunch fp8_dot_entry() {
-    if constexpr (fp8_dot_regs(M, V, MX) <= kDotRegsMax)
-        return &launch_fp8_dot_t<M, V, MX>;
+    if constexpr (QX ? (!MX && fp8q_dot_regs(M, V) <= kDotRegsMax)
+                     : fp8_dot_regs(M, V, MX) <= kDotRegsMax)
+        return &launch_fp8_dot_t<M, V, MX, QX>;
     else
         return nullptr;
 }
 
-template <int M, bool MX>
+template <int M, bool MX, bool QX>
 Fp8DotLaunch fp8_dot_v(int V) {
     switch (V) {
-    case 1: return fp8_dot_entry<M, 1, MX>();
-    case 2: return fp8_dot_entry<M, 2, MX>();
-    case 4: return fp8_dot_entry<M, 4, MX>();
+    case 1: return fp8_dot_entry<M, 1, MX, QX>();
+    case 2: return fp8_dot_entry<M, 2, MX, QX>();
+    case 4: return fp8_dot_entry<M, 4, MX, QX>();
     default: return nullptr;
     }
 }
 
-template <bool MX>
+template <bool MX, bool QX>
 Fp8DotLaunch fp8_dot_m(int M, int V) {
     switch (M) {
-    case 1: return fp8_dot_v<1, MX>(V);
-    case 2: return fp8_dot_v<2, MX>(V);
-    case 3: return fp8_dot_v<3, MX>(V);
-    case 4: return fp8_dot_v<4, MX>(V);
-    case 5: return fp8_dot_v<5, MX>(V);
-    case 6: return fp8_dot_v<6, MX>(V);
-    case 7: return fp8_dot_v<7, MX>(V);
-    case 8: return fp8_dot_v<8, MX>(V);
-    case 9: return fp8_dot_v<9, MX>(V);
-    case 10: return fp8_dot_v<10, MX>(V);
-    case 11: return fp8_dot_v<11, MX>(V);
-    case 12: return fp8_dot_v<12, MX>(V);
-    case 13: return fp8_dot_v<13, MX>(V);
-    case 14: return fp8_dot_v<14, MX>(V);
-    case 15: return fp8_dot_v<15, MX>(V);
-    case 16: return fp8_dot_v<16, MX>(V);
+    case 1: return fp8_dot_v<1, MX, QX>(V);
+    case 2: return fp8_dot_v<2, MX, QX>(V);
+    case 3: return fp8_dot_v<3, MX, QX>(V);
+    case 4: return fp8_dot_v<4, MX, QX>(V);
+    case 5: return fp8_dot_v<5, MX, QX>(V);
+    case 6: return fp8_dot_v<6, MX, QX>(V);
+    case 7: return fp8_dot_v<7, MX, QX>(V);
+    case 8: return fp8_dot_v<8, MX, QX>(V);
+    case 9: return fp8_dot_v<9, MX, QX>(V);
+    case 10: return fp8_dot_v<10, MX, QX>(V);
+    case 11: return fp8_dot_v<11, MX, QX>(V);
+    case 12: return fp8_dot_v<12, MX, QX>(V);
+    case 13: return fp8_dot_v<13, MX, QX>(V);
+    case 14: return fp8_dot_v<14, MX, QX>(V);
+    case 15: return fp8_dot_v<15, MX, QX>(V);
+    case 16: return fp8_dot_v<16, MX, QX>(V);
     default: return nullptr;
     }
 }
@@ -358,8 +382,8 @@ int launch_fp8_mfma_t(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *t
     const size_t lds_bytes = (size_t)(p.threads / 64) * NB * MT * 4 * 64 * sizeof(float);
     hipLaunchKernelGGL((fp8_mfma_kernel<MT, NB, D, MX>), dim3(p.grid), dim3(p.threads), lds_bytes,
                        stream, (const uint8_t *)a.x, (const uint8_t *)a.W, (const uint16_t *)a.bias,
-                       a.sx, a.sw, a.xe, a.we, (uint16_t *)a.out, ws, tickets, M, N, K, p.splits,
-                       p.k_chunk, p.reduce);
+                       a.sx, a.sw, a.xe, a.we, a.out, ws, tickets, M, N, K, p.splits,
+                       p.k_chunk, p.reduce, a.out_f32);
     return (int)hipGetLastError();
 }
 
@@ -404,20 +428,29 @@ Fp8MfmaLaunch fp8_mfma_mt(int MT, int NB, int D) {
 
 }  // namespace
 
+bool fp8_dot_quant_ok(int M, int V, int threads) {
+    if (M < 1 || M > kDotMaxM || fp8_dot_m<false, true>(M, V) == nullptr) return false;
+    return threads <= fp8_dot_max_threads(M, V, false, true);
+}
+
 int launch_fp8(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets, int M, int N,
                int K, hipStream_t stream) {
     const bool mx = a.mode == SKG_FP8_MX32;
     if (p.kind == SKG_KIND_DOT) {
-        Fp8DotLaunch f = mx ? fp8_dot_m<true>(M, p.depth) : fp8_dot_m<false>(M, p.depth);
+        Fp8DotLaunch f = mx      ? fp8_dot_m<true, false>(M, p.depth)
+                         : a.qx ? fp8_dot_m<false, true>(M, p.depth)
+                                : fp8_dot_m<false, false>(M, p.depth);
         if (!f) return (int)hipErrorInvalidConfiguration;
         return f(p, a, N, K, stream);
     }
+    if (a.qx) return (int)hipErrorInvalidConfiguration;  // the caller quantises x first
     Fp8MfmaLaunch f = mx ? fp8_mfma_mt<true>(p.m_tiles, p.cols, p.depth)
                          : fp8_mfma_mt<false>(p.m_tiles, p.cols, p.depth);
     if (!f) return (int)hipErrorInvalidConfiguration;
     int rc = f(p, a, ws, tickets, M, N, K, stream);
     if (rc != (int)hipSuccess || p.splits == 1 || p.reduce != SKG_REDUCE_KERNEL) return rc;
-    return launch_splitk_reduce(ws, a.bias, a.out, M, N, p.splits, stream, mx ? nullptr : a.sx,
+    return launch_splitk_reduce(ws, a.bias, a.out, a.out_f32, M, N, p.splits, stream,
+                                mx ? nullptr : a.sx,
                                 mx ? nullptr : a.sw);
 }
 

@@ -33,9 +33,9 @@ namespace skg {
 template <int MT, int NB, int D>
 __global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
     splitk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
-                  const uint16_t *__restrict__ bias, uint16_t *__restrict__ out,
+                  const uint16_t *__restrict__ bias, void *__restrict__ out,
                   float *__restrict__ ws, unsigned *__restrict__ tickets, int M, int N, int K,
-                  int S, int k_chunk, int reduce) {
+                  int S, int k_chunk, int reduce, int out_f32) {
     extern __shared__ float lds[];
     __shared__ unsigned is_last;
 
@@ -132,7 +132,7 @@ __global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
         if (m < M && n < N) {
             if (S == 1) {
                 if (bias) v += bf16_to_f32(bias[n]);
-                out[(size_t)m * N + n] = f32_to_bf16_rne(v);
+                store_out(out, (size_t)m * N + n, v, out_f32);
             } else {
                 ws[((size_t)s * M + m) * N + n] = v;
             }
@@ -140,15 +140,15 @@ __global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
     }
     if (S == 1 || reduce != SKG_REDUCE_LAST) return;
 
-    last_arriver_reduce(ws, tickets, bias, out, M, N, S, j, col0, ncols, &is_last);
+    last_arriver_reduce(ws, tickets, bias, out, out_f32, M, N, S, j, col0, ncols, &is_last);
 }
 
 // Second-pass reduction: the same sum in the same order as the in-kernel
 // one, one output element per thread.
 __global__ void __launch_bounds__(256)
     splitk_reduce_kernel(const float *__restrict__ ws, const uint16_t *__restrict__ bias,
-                         uint16_t *__restrict__ out, int M, int N, int S,
-                         const float *__restrict__ sx, const float *__restrict__ sw) {
+                         void *__restrict__ out, int M, int N, int S,
+                         const float *__restrict__ sx, const float *__restrict__ sw, int out_f32) {
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= M * N) return;
     const int m = e / N;
@@ -156,7 +156,7 @@ __global__ void __launch_bounds__(256)
     float v = ordered_sum<8>(S, [&](int ss) { return ws[((size_t)ss * M + m) * N + n]; });
     if (sx) v *= sx[0] * sw[0];  // FP8 per-tensor scale product, applied once
     if (bias) v += bf16_to_f32(bias[n]);
-    out[e] = f32_to_bf16_rne(v);
+    store_out(out, e, v, out_f32);
 }
 
 // The same reduction, four consecutive outputs per thread (N % 4 == 0, so
@@ -164,8 +164,9 @@ __global__ void __launch_bounds__(256)
 // four sums adds the partials in ascending s, as above: identical bits.
 __global__ void __launch_bounds__(256)
     splitk_reduce4_kernel(const float *__restrict__ ws, const uint16_t *__restrict__ bias,
-                          uint16_t *__restrict__ out, int M, int N, int S,
-                          const float *__restrict__ sx, const float *__restrict__ sw) {
+                          void *__restrict__ out, int M, int N, int S,
+                          const float *__restrict__ sx, const float *__restrict__ sw,
+                          int out_f32) {
     const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (e >= M * N) return;
     const size_t plane = (size_t)M * N;
@@ -187,22 +188,23 @@ __global__ void __launch_bounds__(256)
         float r = v[q];
         if (sx) r *= scale;
         if (bias) r += bf16_to_f32(bias[n + q]);
-        out[e + q] = f32_to_bf16_rne(r);
+        store_out(out, e + q, r, out_f32);
     }
 }
 
 namespace {
 
 typedef int (*SplitKLaunch)(const SkgPlan &, const void *, const void *, const void *, void *,
-                            float *, unsigned *, int, int, int, hipStream_t);
+                            int, float *, unsigned *, int, int, int, hipStream_t);
 
 template <int MT, int NB, int D>
 int launch_splitk_t(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
-                    float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream) {
+                    int out_f32, float *ws, unsigned *tickets, int M, int N, int K,
+                    hipStream_t stream) {
     const size_t lds_bytes = (size_t)(p.threads / 64) * NB * MT * 4 * 64 * sizeof(float);
     hipLaunchKernelGGL((splitk_kernel<MT, NB, D>), dim3(p.grid), dim3(p.threads), lds_bytes,
                        stream, (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)bias,
-                       (uint16_t *)out, ws, tickets, M, N, K, p.splits, p.k_chunk, p.reduce);
+                       out, ws, tickets, M, N, K, p.splits, p.k_chunk, p.reduce, out_f32);
     return (int)hipGetLastError();
 }
 
@@ -247,25 +249,26 @@ SplitKLaunch pick(int MT, int NB, int D) {
 
 }  // namespace
 
-int launch_splitk_reduce(const float *ws, const void *bias, void *out, int M, int N, int S,
-                         hipStream_t stream, const float *sx, const float *sw) {
+int launch_splitk_reduce(const float *ws, const void *bias, void *out, int out_f32, int M, int N,
+                         int S, hipStream_t stream, const float *sx, const float *sw) {
     const int elems = M * N;
     if ((N & 3) == 0)
         hipLaunchKernelGGL(splitk_reduce4_kernel, dim3((elems / 4 + 255) / 256), dim3(256), 0,
-                           stream, ws, (const uint16_t *)bias, (uint16_t *)out, M, N, S, sx, sw);
+                           stream, ws, (const uint16_t *)bias, out, M, N, S, sx, sw, out_f32);
     else
         hipLaunchKernelGGL(splitk_reduce_kernel, dim3((elems + 255) / 256), dim3(256), 0, stream,
-                           ws, (const uint16_t *)bias, (uint16_t *)out, M, N, S, sx, sw);
+                           ws, (const uint16_t *)bias, out, M, N, S, sx, sw, out_f32);
     return (int)hipGetLastError();
 }
 
 int launch_splitk(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
-                  float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream) {
+                  int out_f32, float *ws, unsigned *tickets, int M, int N, int K,
+                  hipStream_t stream) {
     SplitKLaunch f = pick(p.m_tiles, p.cols, p.depth);
     if (!f) return (int)hipErrorInvalidConfiguration;
-    int rc = f(p, x, W, bias, out, ws, tickets, M, N, K, stream);
+    int rc = f(p, x, W, bias, out, out_f32, ws, tickets, M, N, K, stream);
     if (rc != (int)hipSuccess || p.splits == 1 || p.reduce != SKG_REDUCE_KERNEL) return rc;
-    return launch_splitk_reduce(ws, bias, out, M, N, p.splits, stream);
+    return launch_splitk_reduce(ws, bias, out, out_f32, M, N, p.splits, stream);
 }
 
 }  // namespace skg

@@ -77,9 +77,9 @@ __device__ __forceinline__ void lds_load16(Rsrc r, unsigned char *dst, unsigned 
 template <int MT, int NB, int WM, int NS, int U>
 __global__ void __launch_bounds__(256)
     tiled_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
-                 const uint16_t *__restrict__ bias, uint16_t *__restrict__ out,
+                 const uint16_t *__restrict__ bias, void *__restrict__ out,
                  float *__restrict__ ws, unsigned *__restrict__ tickets, int M, int N, int K,
-                 int S, int k_chunk, int reduce) {
+                 int S, int k_chunk, int reduce, int out_f32) {
     constexpr int WN = 4 / WM;
     constexpr int MTW = MT / WM;          // m-tiles per wave
     constexpr int NBW = NB / WN;          // column blocks per wave
@@ -240,8 +240,8 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 if (c + q < ncols)
-                    out[(size_t)r * N + n + q] =
-                        f32_to_bf16_rne(bias ? v[q] + bf16_to_f32(bias[n + q]) : v[q]);
+                    store_out(out, (size_t)r * N + n + q,
+                              bias ? v[q] + bf16_to_f32(bias[n + q]) : v[q], out_f32);
         } else if (vec && c + 4 <= ncols) {
             *reinterpret_cast<f32x4 *>(ws + ((size_t)s * M + r) * N + n) = v;
         } else {
@@ -251,17 +251,18 @@ __global__ void __launch_bounds__(256)
         }
     }
     if (S == 1 || reduce != SKG_REDUCE_LAST) return;
-    last_arriver_reduce(ws, tickets, bias, out, M, N, S, j, col0, ncols, &is_last);
+    last_arriver_reduce(ws, tickets, bias, out, out_f32, M, N, S, j, col0, ncols, &is_last);
 }
 
 namespace {
 
 typedef int (*TiledLaunch)(const SkgPlan &, const void *, const void *, const void *, void *,
-                           float *, unsigned *, int, int, int, hipStream_t);
+                           int, float *, unsigned *, int, int, int, hipStream_t);
 
 template <int MT, int NB, int WM, int NS, int U>
 int launch_tiled_t(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
-                   float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream) {
+                   int out_f32, float *ws, unsigned *tickets, int M, int N, int K,
+                   hipStream_t stream) {
     const size_t lds_bytes = tiled_lds_bytes(MT, NB, NS, U);
     // rings above 64 KB: allow the kernel that much dynamic LDS (once)
     static const hipError_t attr = hipFuncSetAttribute(
@@ -270,7 +271,7 @@ int launch_tiled_t(const SkgPlan &p, const void *x, const void *W, const void *b
     if (attr != hipSuccess) return (int)attr;
     hipLaunchKernelGGL((tiled_kernel<MT, NB, WM, NS, U>), dim3(p.grid), dim3(256), lds_bytes,
                        stream, (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)bias,
-                       (uint16_t *)out, ws, tickets, M, N, K, p.splits, p.k_chunk, p.reduce);
+                       out, ws, tickets, M, N, K, p.splits, p.k_chunk, p.reduce, out_f32);
     return (int)hipGetLastError();
 }
 
@@ -334,13 +335,14 @@ TiledLaunch pick(int MT, int NB, int WM, int NS, int U) {
 }  // namespace
 
 int launch_tiled(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
-                 float *ws, unsigned *tickets, int M, int N, int K, hipStream_t stream) {
+                 int out_f32, float *ws, unsigned *tickets, int M, int N, int K,
+                 hipStream_t stream) {
     const int U = (p.flags & SKG_FLAG_TILED_WIDE) ? 4 : 2;
     TiledLaunch f = pick(p.m_tiles, p.cols, p.waves_m, p.depth, U);
     if (!f) return (int)hipErrorInvalidConfiguration;
-    int rc = f(p, x, W, bias, out, ws, tickets, M, N, K, stream);
+    int rc = f(p, x, W, bias, out, out_f32, ws, tickets, M, N, K, stream);
     if (rc != (int)hipSuccess || p.splits == 1 || p.reduce != SKG_REDUCE_KERNEL) return rc;
-    return launch_splitk_reduce(ws, bias, out, M, N, p.splits, stream);
+    return launch_splitk_reduce(ws, bias, out, out_f32, M, N, p.splits, stream);
 }
 
 }  // namespace skg

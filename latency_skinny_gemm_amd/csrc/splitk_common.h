@@ -20,7 +20,7 @@ namespace skg {
 __device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
                                                     unsigned *__restrict__ tickets,
                                                     const uint16_t *__restrict__ bias,
-                                                    uint16_t *__restrict__ out, int M, int N,
+                                                    void *__restrict__ out, int out_f32, int M, int N,
                                                     int S, int j, int col0, int ncols,
                                                     unsigned *is_last,
                                                     const float *__restrict__ sx = nullptr,
@@ -44,7 +44,7 @@ __device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
         float v = ordered_sum<8>(S, [&](int ss) { return ws[((size_t)ss * M + m) * N + n]; });
         if (sx) v *= scale;
         if (bias) v += bf16_to_f32(bias[n]);
-        out[(size_t)m * N + n] = f32_to_bf16_rne(v);
+        store_out(out, (size_t)m * N + n, v, out_f32);
     }
 }
 

@@ -90,6 +90,51 @@ def test_fp8_validation(lib):
     assert lib.skinny_gemm_fp8(X, W, None, ctypes.byref(sc), OUT, 2, 8, 64, None) == skg.ERR_ALIGNMENT
 
 
+def test_bf16_f32_validation(lib):
+    f = lib.skinny_gemm_bf16_f32
+    assert f(X, W, None, OUT + 2, 2, 8, 64, None) == skg.ERR_ALIGNMENT       # fp32: 4-byte aligned
+    assert f(X, W, None, None, 2, 8, 64, None) == skg.ERR_INVALID_ARG
+    assert f(X, W, None, X + 64, 2, 8, 64, None) == skg.ERR_INVALID_ARG      # overlaps x
+    # an fp32 out is twice as long: it reaches x 16 bytes beyond a bf16 out's end
+    assert f(X, W, None, X - 2 * 8 * 4 + 16, 2, 8, 64, None) == skg.ERR_INVALID_ARG
+    assert f(X, W, None, OUT, 0, 8, 64, None) == skg.OK
+    assert f(X, W, None, OUT, 2, 8, 60, None) == skg.ERR_UNSUPPORTED
+    assert lib.skinny_gemm_bf16_f32_planned(X, W, None, OUT, 2, 8, 64, None, None) == skg.ERR_INVALID_ARG
+
+
+def test_fp8_quant_validation(lib):
+    f = lib.skinny_gemm_fp8_quant
+    SX, SW = 0x50000, 0x60000
+    assert f(X, W, None, SX, SW, OUT, 5, 2, 8, 64, None) == skg.ERR_INVALID_ARG    # out dtype
+    assert f(X, W, None, SX, SW, OUT, skg.DTYPE_FP8, 2, 8, 64, None) == skg.ERR_INVALID_ARG
+    assert f(X, W, None, None, SW, OUT, skg.DTYPE_BF16, 2, 8, 64, None) == skg.ERR_INVALID_ARG
+    assert f(X, W, None, SX, None, OUT, skg.DTYPE_BF16, 2, 8, 64, None) == skg.ERR_INVALID_ARG
+    assert f(X, W, None, SX, SW, OUT, skg.DTYPE_BF16, 2, 8, 40, None) == skg.ERR_UNSUPPORTED
+    assert f(X + 8, W, None, SX, SW, OUT, skg.DTYPE_BF16, 2, 8, 64, None) == skg.ERR_ALIGNMENT
+    assert f(X, W, None, SX + 2, SW, OUT, skg.DTYPE_BF16, 2, 8, 64, None) == skg.ERR_ALIGNMENT
+    assert f(X, W, None, SX, SW, OUT + 2, skg.DTYPE_F32, 2, 8, 64, None) == skg.ERR_ALIGNMENT
+    # x is bf16 here: 2 bytes per element, so out at x + M*K bytes still overlaps
+    assert f(X, W, None, SX, SW, X + 2 * 64, skg.DTYPE_BF16, 2, 8, 64, None) == skg.ERR_INVALID_ARG
+    assert f(X, W, None, SX, SW, OUT, skg.DTYPE_BF16, 0, 8, 64, None) == skg.OK
+    assert lib.skinny_gemm_fp8_quant_planned(X, W, None, SX, SW, OUT, skg.DTYPE_BF16, 2, 8, 64,
+                                             None, None) == skg.ERR_INVALID_ARG
+
+
+def test_quant_validation(lib):
+    f = lib.skinny_quant_e4m3
+    S = 0x50000
+    assert f(X, S, OUT, -1, None) == skg.ERR_INVALID_ARG
+    assert f(X, S, OUT, 0, None) == skg.OK
+    assert f(0, S, OUT, 0, None) == skg.OK
+    assert f(None, S, OUT, 16, None) == skg.ERR_INVALID_ARG
+    assert f(X, None, OUT, 16, None) == skg.ERR_INVALID_ARG
+    assert f(X + 2, S, OUT, 16, None) == skg.ERR_ALIGNMENT
+    assert f(X, S, OUT + 8, 16, None) == skg.ERR_ALIGNMENT
+    assert f(X, S + 1, OUT, 16, None) == skg.ERR_ALIGNMENT
+    assert f(X, S, X + 16, 16, None) == skg.ERR_INVALID_ARG   # q inside x's 32 bytes
+    assert f(X, S, OUT, 1 << 31, None) == skg.ERR_UNSUPPORTED
+
+
 FP8 = [p for p in configs.all_points() if p.dtype != "bf16"]
 
 
