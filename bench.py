@@ -315,7 +315,7 @@ def fp8_section(skg, torch, stream, sptr):
             res[f"M{M}_{mode}"] = {"us_per_call": round(us, 3), "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                                    "TFLOPs": round(tflops, 1),
                                    "mfma_util": round(tflops / FP8_PEAK_TFLOPS, 4),
-                                   "kernel": {1: "dot", 2: "splitk"}[skg.plan(M, N, K, skg.DTYPE_FP8).kind]}
+                                   "kernel": {1: "dot", 2: "splitk", 3: "tiled"}[skg.plan(M, N, K, skg.DTYPE_FP8).kind]}
         del X, O, XE, WE
     del W
     torch.cuda.empty_cache()

@@ -97,6 +97,32 @@ constexpr bool fp8_mfma_built(int MT, int NB, int D) {
     return NB * MT <= 32 && D * (NB + MT) <= 14;  // MX spills beyond (resource report)
 }
 
+// FP8 TILED: the bf16 tiled kernel's ring with 128-wide K steps; a stage
+// holds U (1 or 2) steps: (MT + NB) blocks of 16 rows x 128U bytes, plus in
+// MX mode the stage's scale bytes (rows x 4U, rounded up to 256 bytes per
+// operand).  The ring is sized for MX in both modes.  Built when the
+// accumulators and one stage's fragments fit 200 VGPRs, the ring fits
+// 144 KB and holds the epilogue tile, the vmcnt wait fits 6 bits, and each
+// operand's scales take at most one load per wave.
+constexpr int fp8_tiled_scale_bytes(int tiles, int U, bool mx) {
+    return mx ? (tiles * 16 * 4 * U + 255) / 256 * 256 : 0;
+}
+constexpr size_t fp8_tiled_stage_bytes(int MT, int NB, int U, bool mx) {
+    return (size_t)(MT + NB) * 2048 * U + fp8_tiled_scale_bytes(MT, U, mx) +
+           fp8_tiled_scale_bytes(NB, U, mx);
+}
+constexpr size_t fp8_tiled_lds_bytes(int MT, int NB, int NS, int U) {
+    return (size_t)NS * fp8_tiled_stage_bytes(MT, NB, U, true) + 1024;
+}
+constexpr bool fp8_tiled_built(int MT, int NB, int WM, int NS, int U) {
+    return (WM == 1 || WM == 2 || WM == 4) && MT % WM == 0 && NB % (4 / WM) == 0 &&
+           (U == 1 || U == 2) && MT * U <= 16 && NB * U <= 16 &&
+           4 * (MT / WM) * (NB / (4 / WM)) + 8 * U * (MT / WM + NB / (4 / WM)) <= 200 &&
+           fp8_tiled_lds_bytes(MT, NB, NS, U) <= kTiledMaxLds &&
+           fp8_tiled_lds_bytes(MT, NB, NS, U) >= (size_t)MT * 16 * (NB * 16 + 4) * 4 &&
+           (NS - 2) * ((MT * 2 * U + 3) / 4 + (NB * 2 * U + 3) / 4 + 2) < 64;
+}
+
 // The arguments of one FP8 call, passed to the FP8 launchers.
 struct Fp8Args {
     const void *x, *W, *bias;
@@ -135,6 +161,8 @@ int launch_splitk_reduce(const float *ws, const void *bias, void *out, int out_f
 int launch_quant_e4m3(const void *x, const float *s, void *q, long n, hipStream_t stream);
 int launch_fp8(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets, int M, int N,
                int K, hipStream_t stream);
+int launch_fp8_tiled(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets, int M,
+                     int N, int K, hipStream_t stream);
 // Whether the FP8 dot kernel that quantises bf16 x on load exists for (M, V)
 // and accepts workgroups of `threads` (its registers bound it lower than the
 // plain FP8 dot kernel).

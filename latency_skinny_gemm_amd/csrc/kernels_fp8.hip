@@ -444,6 +444,7 @@ int launch_fp8(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets,
         return f(p, a, N, K, stream);
     }
     if (a.qx) return (int)hipErrorInvalidConfiguration;  // the caller quantises x first
+    if (p.kind == SKG_KIND_TILED) return launch_fp8_tiled(p, a, ws, tickets, M, N, K, stream);
     Fp8MfmaLaunch f = mx ? fp8_mfma_mt<true>(p.m_tiles, p.cols, p.depth)
                          : fp8_mfma_mt<false>(p.m_tiles, p.cols, p.depth);
     if (!f) return (int)hipErrorInvalidConfiguration;

@@ -1,0 +1,367 @@
+// kernels_fp8_tiled.hip -- the LDS-ring tiled kernel for FP8 (OCP e4m3fn)
+// operands: per-tensor or MX (e8m0 per 32 K) scales, larger M x N.
+//
+// Semantics as the other FP8 kernels ("sglang PR #28333" page for the
+// per-tensor form, the scale product applied once at the end; "sglang PR
+// #34042" page for MX block scaling, applied here by the MFMA itself).
+// Structure as the bf16 tiled kernel: workgroup (j, s) owns 16*NB columns,
+// all M rows (MT tiles, rows past M read as zeros) and K chunk s; a ring of
+// NS LDS stages fed by buffer-to-LDS loads; one vmcnt wait and one barrier
+// per stage; the output tile leaves through LDS as whole rows.
+//  * a K step is 128 wide (one v_mfma_scale_f32_16x16x128_f8f6f4); a stage
+//    holds U steps, so 128*U contiguous bytes of each row;
+//  * a block is 16 rows x 128*U bytes, row-major, the 16-byte chunk c of row
+//    r at position c ^ swz(r) (the 16 rows of one fragment read land in 16
+//    bank groups); a load instruction fills 1 KB with 8/U whole row pieces;
+//  * the MFMA operand of lane l (measured on the MI355X): row l % 16, the
+//    chunks at K offsets 16g and 64 + 16g of the step (g = l / 16), and the
+//    e8m0 byte of the step's 32-element block g;
+//  * MX mode streams the scale bytes of the stage into the ring as well
+//    (4 bytes per lane, rows x 4U bytes per operand); rows past M or N read
+//    zero codes and a zero exponent, which contribute exactly 0.
+#include "device_common.h"
+#include "internal.h"
+#include "splitk_common.h"
+
+namespace skg {
+
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void barrier_nofence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Buffer-to-LDS loads of 16 or 4 bytes per lane (kept out of the kernel
+// body: used there directly, the builtin made the host pass drop the
+// kernels' launch stubs).
+template <int POLICY>
+__device__ __forceinline__ void lds_load16(Rsrc r, unsigned char *dst, unsigned off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, off, 0, 0, POLICY);
+}
+__device__ __forceinline__ void lds_load4(Rsrc r, unsigned char *dst, unsigned off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 4, off, 0, 0, 0);
+}
+
+// chunk swizzle for rows of CPR 16-byte chunks (rows sharing a 256-byte
+// bank window get different keys)
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+    return (r / (16 / CPR)) & (CPR - 1);
+}
+
+}  // namespace
+
+template <int MT, int NB, int WM, int NS, int U, bool MX>
+__global__ void __launch_bounds__(256)
+    fp8_tiled_kernel(const uint8_t *__restrict__ x, const uint8_t *__restrict__ W,
+                     const uint16_t *__restrict__ bias, const float *__restrict__ sx,
+                     const float *__restrict__ sw, const uint8_t *__restrict__ xe,
+                     const uint8_t *__restrict__ we, void *__restrict__ out,
+                     float *__restrict__ ws, unsigned *__restrict__ tickets, int M, int N, int K,
+                     int S, int k_chunk, int reduce, int out_f32) {
+    constexpr int WN = 4 / WM;
+    constexpr int MTW = MT / WM;
+    constexpr int NBW = NB / WN;
+    constexpr int CPR = 8 * U;                 // 16-byte chunks per row and stage
+    constexpr int BLKB = 16 * 128 * U;         // bytes per block
+    constexpr int XSB = fp8_tiled_scale_bytes(MT, U, MX);  // x scale bytes per stage
+    constexpr int WSB = fp8_tiled_scale_bytes(NB, U, MX);
+    constexpr int STAGE = (MT + NB) * BLKB + XSB + WSB;
+    constexpr int XI = MT * 2 * U, WI = NB * 2 * U;   // data instructions per stage
+    constexpr int XPW = (XI + 3) / 4, WPW = (WI + 3) / 4;
+    constexpr int BPW = XPW + WPW + (MX ? 2 : 0);
+    static_assert(MT % WM == 0 && NB % WN == 0, "wave arrangement");
+    static_assert(!MX || (MT * U <= 16 && NB * U <= 16), "one scale load per wave and operand");
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    __shared__ unsigned is_last;
+    unsigned char *const pad = lds_raw + NS * STAGE;  // 1 KB that padding loads fill
+
+    const int t = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int lane = t & 63;
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+    const int s = blockIdx.x % S;
+    const int j = blockIdx.x / S;
+    const int col0 = j * NB * 16;
+    const int ncols = min(NB * 16, N - col0);
+    const unsigned rowb = (unsigned)K;
+    const unsigned srow = (unsigned)(K >> 5);
+    const Rsrc wr = make_rsrc(W + (size_t)col0 * K, (unsigned)ncols * rowb);
+    const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
+    const Rsrc xer = make_rsrc(xe, MX ? (unsigned)M * srow : 0u);
+    const Rsrc wer = make_rsrc(we + (MX ? (size_t)col0 * srow : 0), MX ? (unsigned)ncols * srow : 0u);
+    const int kbeg = s * k_chunk;
+    const int nsteps = (min(K, kbeg + k_chunk) - kbeg) >> 7;  // K, k_chunk: multiples of 128
+    const int nstages = (nsteps + U - 1) / U;
+
+    // data loads: instruction q fills part q % (2U) of block q / (2U)
+    unsigned xoff[XPW], woff[WPW];
+    int xstep[XPW], wstep[WPW];
+#pragma unroll
+    for (int i = 0; i < XPW; ++i) {
+        const int q = wave + 4 * i;
+        const int lin = (q % (2 * U)) * 64 + lane;
+        const int r = lin / CPR, c = (lin % CPR) ^ swz<CPR>(r);
+        const int row = (q / (2 * U)) * 16 + r;
+        xoff[i] = (q < XI && row < M) ? (unsigned)row * rowb + (unsigned)c * 16u : kOOB;
+        xstep[i] = c >> 3;
+    }
+#pragma unroll
+    for (int i = 0; i < WPW; ++i) {
+        const int q = wave + 4 * i;
+        const int lin = (q % (2 * U)) * 64 + lane;
+        const int r = lin / CPR, c = (lin % CPR) ^ swz<CPR>(r);
+        const int row = (q / (2 * U)) * 16 + r;
+        woff[i] = (q < WI && row < ncols) ? (unsigned)row * rowb + (unsigned)c * 16u : kOOB;
+        wstep[i] = c >> 3;
+    }
+    // MX scale loads: instruction `wave` of each operand covers rows
+    // 64/U * wave .. (lane p: row p / U, dword p % U of the stage's 4U bytes)
+    const int srow_l = (64 / U) * wave + lane / U;
+    const int sdw = lane % U;
+    const bool xs_real = MX && wave * 256 < XSB;
+    const bool ws_real = MX && wave * 256 < WSB;
+    const unsigned xsoff =
+        (xs_real && srow_l < M) ? (unsigned)srow_l * srow + (unsigned)sdw * 4u : kOOB;
+    const unsigned wsoff =
+        (ws_real && srow_l < ncols) ? (unsigned)srow_l * srow + (unsigned)sdw * 4u : kOOB;
+
+    const int rot = j % nstages;
+    auto issue = [&](int slot, int stage) {
+        int pos = stage + rot;
+        if (pos >= nstages) pos -= nstages;
+        if (stage >= nstages) pos = nstages;  // no live step: zero-byte loads
+        const unsigned k0 = (unsigned)(kbeg + pos * U * 128);
+        unsigned char *base = lds_raw + slot * STAGE;
+#pragma unroll
+        for (int i = 0; i < XPW; ++i) {
+            const int q = wave + 4 * i;
+            const bool live = pos * U + xstep[i] < nsteps;
+            unsigned char *dst = q < XI ? base + (q / (2 * U)) * BLKB + (q % (2 * U)) * 1024 : pad;
+            lds_load16<kCacheDefault>(xr, dst, live ? xoff[i] + k0 : kOOB);
+        }
+#pragma unroll
+        for (int i = 0; i < WPW; ++i) {
+            const int q = wave + 4 * i;
+            const bool live = pos * U + wstep[i] < nsteps;
+            unsigned char *dst =
+                q < WI ? base + (MT + q / (2 * U)) * BLKB + (q % (2 * U)) * 1024 : pad;
+            lds_load16<kCacheStream>(wr, dst, live ? woff[i] + k0 : kOOB);
+        }
+        if constexpr (MX) {
+            const bool live = pos * U + sdw < nsteps;
+            const unsigned kb = k0 >> 5;
+            unsigned char *sb = base + (MT + NB) * BLKB;
+            lds_load4(xer, xs_real ? sb + wave * 256 : pad, live ? xsoff + kb : kOOB);
+            lds_load4(wer, ws_real ? sb + XSB + wave * 256 : pad, live ? wsoff + kb : kOOB);
+        }
+    };
+
+    f32x4 acc[MTW][NBW];
+#pragma unroll
+    for (int a = 0; a < MTW; ++a)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int fr = lane & 15, fg = lane >> 4;
+    auto compute = [&](int slot) {
+        const unsigned char *stg = lds_raw + slot * STAGE;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int o0 = fr * (CPR * 16) + (((8 * u + fg) ^ swz<CPR>(fr)) * 16);
+            const int o1 = fr * (CPR * 16) + (((8 * u + 4 + fg) ^ swz<CPR>(fr)) * 16);
+            i32x8 af[MTW], bf[NBW];
+            int as[MTW], bs[NBW];
+#pragma unroll
+            for (int a = 0; a < MTW; ++a) {
+                const unsigned char *blk = stg + (wm * MTW + a) * BLKB;
+                const u32x4 p0 = *reinterpret_cast<const u32x4 *>(blk + o0);
+                const u32x4 p1 = *reinterpret_cast<const u32x4 *>(blk + o1);
+                af[a] = i32x8{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w,
+                              (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
+                as[a] = MX ? (int)stg[(MT + NB) * BLKB + ((wm * MTW + a) * 16 + fr) * 4 * U +
+                                      4 * u + fg]
+                           : 127;
+            }
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) {
+                const unsigned char *blk = stg + (MT + wn * NBW + b) * BLKB;
+                const u32x4 p0 = *reinterpret_cast<const u32x4 *>(blk + o0);
+                const u32x4 p1 = *reinterpret_cast<const u32x4 *>(blk + o1);
+                bf[b] = i32x8{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w,
+                              (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
+                bs[b] = MX ? (int)stg[(MT + NB) * BLKB + XSB +
+                                      ((wn * NBW + b) * 16 + fr) * 4 * U + 4 * u + fg]
+                           : 127;
+            }
+#pragma unroll
+            for (int a = 0; a < MTW; ++a)
+#pragma unroll
+                for (int b = 0; b < NBW; ++b)
+                    // formats 0/0: e4m3 on both sides; scale byte 0 of each lane
+                    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        af[a], bf[b], acc[a][b], 0, 0, 0, as[a], 0, bs[b]);
+        }
+    };
+
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) issue(st, st);
+    for (int st = 0; st < nstages; ++st) {
+        // nstages is the same for every wave: every wave reaches every barrier
+        wait_vmcnt_lds<(NS - 2) * BPW>();
+        barrier_nofence();
+        compute(st % NS);
+        issue((st + NS - 1) % NS, st + NS - 1);
+    }
+    wait_vmcnt_lds<0>();  // no load to LDS outlives the loop
+
+    // ---- epilogue through LDS, as in the bf16 tiled kernel; per-tensor
+    // mode applies sx*sw once (here when S == 1, else in the reduction)
+    constexpr int TS = NB * 16 + 4;
+    float *tile = reinterpret_cast<float *>(lds_raw);
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < MTW; ++a)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                tile[((wm * MTW + a) * 16 + fg * 4 + i) * TS + (wn * NBW + b) * 16 + fr] =
+                    acc[a][b][i];
+    __syncthreads();
+    const float scale = MX ? 1.0f : sx[0] * sw[0];
+    constexpr int C4 = NB * 4;
+    const bool vec = (N & 3) == 0;
+    for (int e = t; e < M * C4; e += 256) {
+        const int r = e / C4, c = (e % C4) * 4;
+        if (c >= ncols) continue;
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(tile + r * TS + c);
+        const int n = col0 + c;
+        if (S == 1) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (c + q < ncols) {
+                    float o = MX ? v[q] : v[q] * scale;
+                    if (bias) o += bf16_to_f32(bias[n + q]);
+                    store_out(out, (size_t)r * N + n + q, o, out_f32);
+                }
+        } else if (vec && c + 4 <= ncols) {
+            *reinterpret_cast<f32x4 *>(ws + ((size_t)s * M + r) * N + n) = v;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (c + q < ncols) ws[((size_t)s * M + r) * N + n + q] = v[q];
+        }
+    }
+    if (S == 1 || reduce != SKG_REDUCE_LAST) return;
+    last_arriver_reduce(ws, tickets, bias, out, out_f32, M, N, S, j, col0, ncols, &is_last,
+                        MX ? nullptr : sx, MX ? nullptr : sw);
+}
+
+namespace {
+
+typedef int (*Fp8TiledLaunch)(const SkgPlan &, const Fp8Args &, float *, unsigned *, int, int,
+                              int, hipStream_t);
+
+template <int MT, int NB, int WM, int NS, int U, bool MX>
+int launch_fp8_tiled_t(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets, int M,
+                       int N, int K, hipStream_t stream) {
+    const size_t lds_bytes = fp8_tiled_lds_bytes(MT, NB, NS, U);
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&fp8_tiled_kernel<MT, NB, WM, NS, U, MX>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    if (attr != hipSuccess) return (int)attr;
+    hipLaunchKernelGGL((fp8_tiled_kernel<MT, NB, WM, NS, U, MX>), dim3(p.grid), dim3(256),
+                       lds_bytes, stream, (const uint8_t *)a.x, (const uint8_t *)a.W,
+                       (const uint16_t *)a.bias, a.sx, a.sw, a.xe, a.we, a.out, ws, tickets, M, N,
+                       K, p.splits, p.k_chunk, p.reduce, a.out_f32);
+    return (int)hipGetLastError();
+}
+
+template <int MT, int NB, int WM, int NS, int U, bool MX>
+constexpr Fp8TiledLaunch fp8_tiled_entry() {
+    if constexpr (fp8_tiled_built(MT, NB, WM, NS, U))
+        return &launch_fp8_tiled_t<MT, NB, WM, NS, U, MX>;
+    else
+        return nullptr;
+}
+
+template <int MT, int NB, int WM, int U, bool MX>
+Fp8TiledLaunch pick_ns(int NS) {
+    switch (NS) {
+    case 2: return fp8_tiled_entry<MT, NB, WM, 2, U, MX>();
+    case 3: return fp8_tiled_entry<MT, NB, WM, 3, U, MX>();
+    case 4: return fp8_tiled_entry<MT, NB, WM, 4, U, MX>();
+    case 6: return fp8_tiled_entry<MT, NB, WM, 6, U, MX>();
+    case 8: return fp8_tiled_entry<MT, NB, WM, 8, U, MX>();
+    default: return nullptr;
+    }
+}
+
+template <int MT, int NB, int WM, bool MX>
+Fp8TiledLaunch pick_u(int NS, int U) {
+    return U == 2 ? pick_ns<MT, NB, WM, 2, MX>(NS) : U == 1 ? pick_ns<MT, NB, WM, 1, MX>(NS)
+                                                            : nullptr;
+}
+
+template <int MT, int NB, bool MX>
+Fp8TiledLaunch pick_wm(int WM, int NS, int U) {
+    switch (WM) {
+    case 1: return pick_u<MT, NB, 1, MX>(NS, U);
+    case 2: return pick_u<MT, NB, 2, MX>(NS, U);
+    case 4: return pick_u<MT, NB, 4, MX>(NS, U);
+    default: return nullptr;
+    }
+}
+
+template <int MT, bool MX>
+Fp8TiledLaunch pick_nb(int NB, int WM, int NS, int U) {
+    switch (NB) {
+    case 1: return pick_wm<MT, 1, MX>(WM, NS, U);
+    case 2: return pick_wm<MT, 2, MX>(WM, NS, U);
+    case 4: return pick_wm<MT, 4, MX>(WM, NS, U);
+    case 8: return pick_wm<MT, 8, MX>(WM, NS, U);
+    case 16: return pick_wm<MT, 16, MX>(WM, NS, U);
+    default: return nullptr;
+    }
+}
+
+template <bool MX>
+Fp8TiledLaunch pick(int MT, int NB, int WM, int NS, int U) {
+    switch (MT) {
+    case 1: return pick_nb<1, MX>(NB, WM, NS, U);
+    case 2: return pick_nb<2, MX>(NB, WM, NS, U);
+    case 4: return pick_nb<4, MX>(NB, WM, NS, U);
+    case 8: return pick_nb<8, MX>(NB, WM, NS, U);
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+int launch_fp8_tiled(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets, int M,
+                     int N, int K, hipStream_t stream) {
+    const bool mx = a.mode == SKG_FP8_MX32;
+    const int U = (p.flags & SKG_FLAG_TILED_WIDE) ? 2 : 1;
+    Fp8TiledLaunch f = mx ? pick<true>(p.m_tiles, p.cols, p.waves_m, p.depth, U)
+                          : pick<false>(p.m_tiles, p.cols, p.waves_m, p.depth, U);
+    if (!f) return (int)hipErrorInvalidConfiguration;
+    int rc = f(p, a, ws, tickets, M, N, K, stream);
+    if (rc != (int)hipSuccess || p.splits == 1 || p.reduce != SKG_REDUCE_KERNEL) return rc;
+    return launch_splitk_reduce(ws, a.bias, a.out, a.out_f32, M, N, p.splits, stream,
+                                mx ? nullptr : a.sx, mx ? nullptr : a.sw);
+}
+
+}  // namespace skg

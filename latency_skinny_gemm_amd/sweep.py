@@ -47,6 +47,14 @@ def point_sets():
     }
 
 
+def _tiled_reductions(skg, S):
+    """Reductions tried for a tiled plan with S splits: the last arriver reads
+    S partial tiles in one workgroup, worth it only for few splits."""
+    if S == 1:
+        return (skg.REDUCE_NONE,)
+    return (skg.REDUCE_KERNEL, skg.REDUCE_LAST) if S <= 8 else (skg.REDUCE_KERNEL,)
+
+
 def fp8_candidates(skg, M, N, K):
     """Admissible FP8 plans (dot kernel for M <= 16, MFMA split-K)."""
     out, seen = [], set()
@@ -56,7 +64,8 @@ def fp8_candidates(skg, M, N, K):
             q = skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
         except skg.SkinnyGemmError:
             return
-        key = (q.kind, q.threads, q.cols, q.splits, q.depth, q.reduce, q.k_chunk)
+        key = (q.kind, q.threads, q.cols, q.splits, q.depth, q.waves_m, q.reduce, q.flags,
+               q.k_chunk)
         if key not in seen:
             seen.add(key)
             out.append(q)
@@ -64,6 +73,19 @@ def fp8_candidates(skg, M, N, K):
     if M <= 16:
         for T in DOT_THREADS:
             add(skg.make_plan(skg.KIND_DOT, T, 1))
+    # LDS-ring tiles (K % 128 == 0)
+    if K % 128 == 0 and (M > 4 or N >= 1024):
+        for NB in (2, 4, 8, 16):
+            groups = -(-N // (16 * NB))
+            for S in SPLITS:
+                if S > K // 128 or not (64 <= groups * S <= 2048):
+                    continue
+                for wm in (1, 2, 4):
+                    for ns, flags in ((2, 0), (3, 0), (4, 0), (6, 0), (2, skg.FLAG_TILED_WIDE),
+                                      (3, skg.FLAG_TILED_WIDE)):
+                        for red in _tiled_reductions(skg, S):
+                            add(skg.make_plan(skg.KIND_TILED, 256, NB, S, ns, red, flags=flags,
+                                              waves_m=wm))
     ksteps = -(-K // 128)
     for NB in (1, 2, 4):
         groups = -(-N // (16 * NB))
@@ -127,7 +149,7 @@ def sweep_point_fp8(skg, torch, M, N, K, pool_bytes, reps, stream, log):
         results.append((per_mode["tensor"] + per_mode["mx"], per_mode, p))
     results.sort(key=lambda r: r[0])
     _, best_modes, best = results[0]
-    rec = {"dtype": "fp8", "M": M, "N": N, "K": K, "slots": slots,
+    rec = {"dtype": "fp8", "M": M, "N": N, "K": K, "slots": slots, "tiled": "ring2",
            "best_us": round(max(best_modes.values()), 3),
            "best_us_tensor": round(best_modes["tensor"], 3), "best_us_mx": round(best_modes["mx"], 3),
            "best": plan_dict(best),
@@ -135,7 +157,7 @@ def sweep_point_fp8(skg, torch, M, N, K, pool_bytes, reps, stream, log):
                           for t, pm, p in results]}
     log.write(json.dumps(rec) + "\n")
     log.flush()
-    kind = {1: "dot", 2: "splitk"}[best.kind]
+    kind = {1: "dot", 2: "splitk", 3: "tiled"}[best.kind]
     print(f"FP8 M={M:3d} N={N:5d} K={K:5d}: best per-tensor {best_modes['tensor']:7.3f} us, "
           f"MX {best_modes['mx']:7.3f} us  {kind} {plan_dict(best)} ({len(results)} plans)", flush=True)
     return rec
@@ -188,7 +210,7 @@ def candidates(skg, M, N, K):
                 for wm in (1, 2, 4):
                     for ns, flags in ((2, 0), (3, 0), (4, 0), (6, 0), (2, skg.FLAG_TILED_WIDE),
                                       (3, skg.FLAG_TILED_WIDE), (4, skg.FLAG_TILED_WIDE)):
-                        for red in ((skg.REDUCE_NONE,) if S == 1 else (skg.REDUCE_KERNEL,)):
+                        for red in _tiled_reductions(skg, S):
                             add(skg.make_plan(skg.KIND_TILED, 256, NB, S, ns, red, flags=flags,
                                               waves_m=wm))
     return out

@@ -138,6 +138,25 @@ def test_quant_validation(lib):
 FP8 = [p for p in configs.all_points() if p.dtype != "bf16"]
 
 
+@pytest.mark.parametrize("M,N,K,NB,wm,NS,U,S", [
+    (128, 4096, 4096, 8, 2, 3, 1, 8), (64, 4096, 4096, 4, 0, 4, 2, 4), (16, 4096, 4096, 8, 1, 6, 1, 4),
+    (1, 1024, 4096, 16, 0, 2, 1, 2), (37, 200, 1024, 2, 4, 4, 2, 3), (128, 96, 4096, 2, 2, 3, 2, 1)])
+def test_fp8_tiled_plans_cover(lib, M, N, K, NB, wm, NS, U, S):
+    p = skg.make_plan(skg.KIND_TILED, 256, NB, S, NS, skg.REDUCE_KERNEL, waves_m=wm,
+                      flags=skg.FLAG_TILED_WIDE if U == 2 else 0)
+    q = skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
+    assert q.kind == skg.KIND_TILED
+    _check_fp8_coverage(q, M, N, K)
+
+
+def test_fp8_tiled_rejects(lib):
+    with pytest.raises(skg.SkinnyGemmError):  # whole 128-wide steps only
+        skg.plan_complete(16, 256, 4112, skg.make_plan(skg.KIND_TILED, 256, 4, 2, 3), skg.DTYPE_FP8)
+    with pytest.raises(skg.SkinnyGemmError):  # LDS: 8 stages of 16 blocks of 4 KB
+        skg.plan_complete(128, 4096, 4096, skg.make_plan(skg.KIND_TILED, 256, 8, 2, 8,
+                                                         flags=skg.FLAG_TILED_WIDE), skg.DTYPE_FP8)
+
+
 @pytest.mark.parametrize("p", FP8, ids=lambda p: p.key())
 def test_fp8_plans_valid_and_cover(lib, p):
     q = skg.plan(p.M, p.N, p.K, skg.DTYPE_FP8)
@@ -146,7 +165,77 @@ def test_fp8_plans_valid_and_cover(lib, p):
     _check_fp8_coverage(q, p.M, p.N, p.K)
 
 
+def _check_fp8_tiled_coverage(p, M, N, K):
+    S, NB, NS, kc, WM = p.splits, p.cols, p.depth, p.k_chunk, p.waves_m
+    U = 2 if p.flags & skg.FLAG_TILED_WIDE else 1
+    WN = 4 // WM
+    MT = next(v for v in (1, 2, 4, 8) if v >= -(-M // 16))
+    assert p.m_tiles == MT and MT % WM == 0 and NB % WN == 0 and p.threads == 256
+    assert K % 128 == 0 and kc % 128 == 0 and (S - 1) * kc < K <= S * kc
+    groups = -(-N // (16 * NB))
+    assert p.grid == groups * S
+    CPR = 8 * U
+
+    def swz(r):
+        return (r // (16 // CPR)) & (CPR - 1)
+
+    # a block: 16 rows x CPR chunks; part i of 2U fills positions 64i..64i+63
+    stored = {}
+    for part in range(2 * U):
+        for lane in range(64):
+            lin = part * 64 + lane
+            r, c = lin // CPR, (lin % CPR) ^ swz(lin // CPR)
+            assert (r, c) not in stored
+            stored[(r, c)] = lin
+    assert sorted(stored) == [(r, c) for r in range(16) for c in range(CPR)]
+    # the MFMA operand of lane l in step u: row l % 16, K offsets 16g and
+    # 64 + 16g of the step (g = l // 16) = chunks 8u + g and 8u + 4 + g
+    for u in range(U):
+        for g in range(4):
+            for c in (8 * u + g, 8 * u + 4 + g):
+                assert 16 * c in (128 * u + 16 * g, 128 * u + 64 + 16 * g)
+                pos = [stored[(r, c)] for r in range(16)]
+                assert len({(q * 16 % 256) // 16 for q in pos}) == 16   # 16 bank groups
+    # MX scales: wave w's load, lane p -> row (64/U) w + p // U, dword p % U,
+    # LDS byte 256 w + 4 p = row * 4U + 4 * dword; lane l of step u reads byte
+    # row * 4U + 4u + g, the exponent of block 4u + g of the stage
+    for tiles in (MT, NB):
+        rows = tiles * 16
+        nload = -(-(rows * 4 * U) // 256)
+        assert nload <= 4
+        seen_rows = {}
+        for w in range(nload):
+            for lane in range(64):
+                row, dw = (64 // U) * w + lane // U, lane % U
+                assert 256 * w + 4 * lane == row * 4 * U + 4 * dw
+                seen_rows.setdefault(row, set()).add(dw)
+        assert all(seen_rows.get(r) == set(range(U)) for r in range(rows))
+        for u in range(U):
+            for g in range(4):
+                assert (4 * u + g) * 32 == 128 * u + 32 * g
+    # every K of every split computed once (rotation a permutation)
+    for j in range(groups):
+        for s in range(S):
+            nst = -(-((min(K, (s + 1) * kc) - s * kc) // 128) // U)
+            assert sorted((st + j % nst) % nst for st in range(nst)) == list(range(nst))
+    seen = [0] * K
+    for s in range(S):
+        kbeg = s * kc
+        nsteps = (min(K, kbeg + kc) - kbeg) // 128
+        for st in range(-(-nsteps // U)):
+            for u in range(U):
+                if st * U + u < nsteps:
+                    for kk in range(128):
+                        seen[kbeg + (st * U + u) * 128 + kk] += 1
+    assert seen == [1] * K
+    XPW, WPW = -(-(MT * 2 * U) // 4), -(-(NB * 2 * U) // 4)
+    assert (NS - 2) * (XPW + WPW + 2) < 64
+
+
 def _check_fp8_coverage(p, M, N, K):
+    if p.kind == skg.KIND_TILED:
+        _check_fp8_tiled_coverage(p, M, N, K)
+        return
     if p.kind == skg.KIND_DOT:
         T, V = p.threads, p.depth
         K16 = K // 16

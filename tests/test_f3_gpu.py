@@ -155,6 +155,12 @@ def _quant_plans(skg, M, N, K):
         except skg.SkinnyGemmError:
             continue
         plans.append((f"mfma_s{S}_r{red}", p))
+    p = skg.make_plan(skg.KIND_TILED, 256, 4, 2, 3, skg.REDUCE_KERNEL)
+    try:
+        skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
+        plans.append(("tiled_s2", p))
+    except skg.SkinnyGemmError:
+        pass
     return plans
 
 

@@ -49,6 +49,17 @@ def _plans(skg, M, N, K):
         except skg.SkinnyGemmError:
             continue
         plans.append((f"mfma_t{T}_s{S}_d{D}_r{red}", p))
+    wide = skg.FLAG_TILED_WIDE
+    for (NBt, S, NS, fl, red, wm) in ((8, 4, 3, 0, skg.REDUCE_KERNEL, 0),
+                                      (4, 2, 2, wide, skg.REDUCE_LAST, 0),
+                                      (2, 1, 4, 0, skg.REDUCE_NONE, 4),
+                                      (16, 8, 2, 0, skg.REDUCE_KERNEL, 1)):
+        p = skg.make_plan(skg.KIND_TILED, 256, NBt, S, NS, red, flags=fl, waves_m=wm)
+        try:
+            skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
+        except skg.SkinnyGemmError:
+            continue
+        plans.append((f"tiled_nb{NBt}_s{S}_ns{NS}_f{fl}_r{red}_wm{wm}", p))
     return plans
 
 
