@@ -117,11 +117,13 @@ def pmc_probe(skg, torch, floors, stream, sptr, W, X, OUT, n_slots):
 DECODE_K = 7168
 DECODE_N = (576, 2112, 4096)
 DECODE_M = (1, 8, 32, 64, 128)
+LARGE_M = (256, 512)  # the larger-M regime, at N = 4096 only
 
 
 def decode_section(skg, torch, stream, sptr):
     """bf16 dense decode linear, K = 7168, N in {576, 2112, 4096}, M in
-    {1, 8, 32, 64, 128} (the planner's plan, no bias): microseconds per call
+    {1, 8, 32, 64, 128} (and 256, 512 at N = 4096; the planner's plan, no
+    bias): microseconds per call
     over a cold pool of >= 512 MB of distinct W, the algorithmic GB/s and
     its fraction of 8 TB/s."""
     dev = torch.device("cuda:0")
@@ -130,11 +132,12 @@ def decode_section(skg, torch, stream, sptr):
     g.manual_seed(11)
     res = {}
     for N in DECODE_N:
+        Ms = DECODE_M + (LARGE_M if N == 4096 else ())
         slots = -(-(512 << 20) // (N * K * 2))
         W = torch.empty((slots, N, K), dtype=torch.bfloat16, device=dev)
         for i in range(slots):
             W[i].copy_((torch.randn((N, K), generator=g, device=dev) * K ** -0.5).to(torch.bfloat16))
-        for M in DECODE_M:
+        for M in Ms:
             X = torch.randn((slots, M, K), generator=g, device=dev).to(torch.bfloat16)
             O = torch.empty((slots, M, N), dtype=torch.bfloat16, device=dev)
 
@@ -165,6 +168,7 @@ def decode_section(skg, torch, stream, sptr):
             res[f"N{N}_M{M}"] = {"us_per_call": round(us, 3),
                                  "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                                  "frac_of_8TBps": round(byts / (us * 1e-6) / 8e12, 4),
+                                 "TFLOPs": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1),
                                  "kernel": {1: "dot", 2: "splitk", 3: "tiled"}[p.kind]}
             del X, O
         del W
@@ -257,7 +261,7 @@ FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 
 
 def fp8_section(skg, torch, stream, sptr):
-    """FP8 e4m3, K = N = 4096, M in {1, 16, 64, 128}, per-tensor and MX
+    """FP8 e4m3, K = N = 4096, M in {1, 16, 64, 128, 256, 512}, per-tensor and MX
     scales: microseconds per call over a cold pool of >= 512 MB of distinct
     W, the achieved GB/s (W, x, out and scale bytes) and the MFMA rate
     against the dense fp8 peak."""
@@ -270,7 +274,7 @@ def fp8_section(skg, torch, stream, sptr):
     for i in range(slots):
         W[i].copy_(torch.randn((N, K), generator=g, device=dev).to(torch.float8_e4m3fn))
     res = {}
-    for M in (1, 16, 64, 128):
+    for M in (1, 16, 64, 128, 256, 512):
         X = torch.randn((slots, M, K), generator=g, device=dev).to(torch.float8_e4m3fn)
         O = torch.empty((slots, M, N), dtype=torch.bfloat16, device=dev)
         one = torch.ones(1, dtype=torch.float32, device=dev)

@@ -20,10 +20,13 @@
  * contiguous; the library never reads strides (the "sglang PR #30117"
  * review found leading-dimension detection error-prone).
  *
- * Domain.  1 <= M <= 128, N >= 1, K >= 8 and K % 8 == 0 (bf16) so every row
+ * Domain.  1 <= M <= 512, N >= 1, K >= 8 and K % 8 == 0 (bf16) so every row
  * starts 16-byte aligned (the "vllm PR #48774" page keeps only router shapes
  * with K a multiple of 8; the "vllm PR #42562" review settles on 16-byte
- * alignment for 128-bit loads).  M == 0 or N == 0 is a successful no-op.
+ * alignment for 128-bit loads).  Above M = 128 (the larger-M regime of the
+ * "sglang PR #34042" page's M = 512 comparison) only the tiled kernels run,
+ * in row blocks of 128, and K must also be a multiple of 32 (bf16) or 128
+ * (FP8).  M == 0 or N == 0 is a successful no-op.
  * Anything else out of domain returns SKG_ERR_UNSUPPORTED: there is no
  * silent fallback (the "sglang PR #34042" page: an explicit request errors
  * instead of falling back).
@@ -93,7 +96,7 @@ extern "C" {
 #define SKG_FLAG_TILED_WIDE 2 /* TILED: LDS stages of four 32-wide K steps (256 bytes of
                                 each row) instead of two (128 bytes) */
 
-#define SKG_MAX_M 128
+#define SKG_MAX_M 512 /* above 128 rows only tiled plans (K % 32, FP8 K % 128) */
 
 /* FP8 scales (host struct; its pointers are DEVICE pointers).
  *  mode SKG_FP8_PER_TENSOR: sx, sw -> one fp32 each (the "sglang PR #28333"

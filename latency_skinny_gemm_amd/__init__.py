@@ -41,7 +41,7 @@ REDUCE_LAST = 1
 REDUCE_KERNEL = 2
 FLAG_DOT2 = 1
 FLAG_TILED_WIDE = 2
-MAX_M = 128
+MAX_M = 512
 
 
 class SkgPlan(ctypes.Structure):

@@ -55,6 +55,9 @@ constexpr int kSplitKDepths[] = {1, 2, 4, 8};
 // 144 KB and also holds the fp32 output tile of the epilogue, and the vmcnt
 // wait of the ring (loads of NS-2 stages) fits its 6-bit field.
 constexpr int kTiledThreads = 256;
+constexpr int kTiledMaxRows = 128;  // rows per workgroup (MT <= 8); more M: row blocks
+// Row blocks of MT*16 rows that cover M (1 unless M > 128).
+constexpr int tiled_row_blocks(int M, int MT) { return (M + MT * 16 - 1) / (MT * 16); }
 constexpr int kTiledMaxLds = 144 * 1024;
 constexpr int kTiledStages[] = {2, 3, 4, 6, 8};
 constexpr size_t tiled_lds_bytes(int MT, int NB, int NS, int U) {

@@ -4,8 +4,9 @@
 // Semantics as the other FP8 kernels ("sglang PR #28333" page for the
 // per-tensor form, the scale product applied once at the end; "sglang PR
 // #34042" page for MX block scaling, applied here by the MFMA itself).
-// Structure as the bf16 tiled kernel: workgroup (j, s) owns 16*NB columns,
-// all M rows (MT tiles, rows past M read as zeros) and K chunk s; a ring of
+// Structure as the bf16 tiled kernel: workgroup (mb, j, s) owns 16*NB
+// columns, the rows of row block mb (MT tiles, rows past M read as zeros)
+// and K chunk s; a ring of
 // NS LDS stages fed by buffer-to-LDS loads; one vmcnt wait and one barrier
 // per stage; the output tile leaves through LDS as whole rows.
 //  * a K step is 128 wide (one v_mfma_scale_f32_16x16x128_f8f6f4); a stage
@@ -69,7 +70,7 @@ __global__ void __launch_bounds__(256)
                      const float *__restrict__ sw, const uint8_t *__restrict__ xe,
                      const uint8_t *__restrict__ we, void *__restrict__ out,
                      float *__restrict__ ws, unsigned *__restrict__ tickets, int M, int N, int K,
-                     int S, int k_chunk, int reduce, int out_f32) {
+                     int S, int k_chunk, int reduce, int out_f32, int MB) {
     constexpr int WN = 4 / WM;
     constexpr int MTW = MT / WM;
     constexpr int NBW = NB / WN;
@@ -92,15 +93,20 @@ __global__ void __launch_bounds__(256)
     const int lane = t & 63;
     const int wm = wave / WN;
     const int wn = wave % WN;
-    const int s = blockIdx.x % S;
-    const int j = blockIdx.x / S;
+    // workgroup (mb, j, s): row block mb of MT*16 rows (M > 128 only),
+    // column group j, K chunk s; mb fastest, then s
+    const int mb = blockIdx.x % MB;
+    const int s = (blockIdx.x / MB) % S;
+    const int j = blockIdx.x / MB / S;
+    const int row0 = mb * MT * 16;
+    const int Mb = min(MT * 16, M - row0);  // rows of this block
     const int col0 = j * NB * 16;
     const int ncols = min(NB * 16, N - col0);
     const unsigned rowb = (unsigned)K;
     const unsigned srow = (unsigned)(K >> 5);
     const Rsrc wr = make_rsrc(W + (size_t)col0 * K, (unsigned)ncols * rowb);
-    const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
-    const Rsrc xer = make_rsrc(xe, MX ? (unsigned)M * srow : 0u);
+    const Rsrc xr = make_rsrc(x + (size_t)row0 * K, (unsigned)Mb * rowb);
+    const Rsrc xer = make_rsrc(xe + (MX ? (size_t)row0 * srow : 0), MX ? (unsigned)Mb * srow : 0u);
     const Rsrc wer = make_rsrc(we + (MX ? (size_t)col0 * srow : 0), MX ? (unsigned)ncols * srow : 0u);
     const int kbeg = s * k_chunk;
     const int nsteps = (min(K, kbeg + k_chunk) - kbeg) >> 7;  // K, k_chunk: multiples of 128
@@ -115,7 +121,7 @@ __global__ void __launch_bounds__(256)
         const int lin = (q % (2 * U)) * 64 + lane;
         const int r = lin / CPR, c = (lin % CPR) ^ swz<CPR>(r);
         const int row = (q / (2 * U)) * 16 + r;
-        xoff[i] = (q < XI && row < M) ? (unsigned)row * rowb + (unsigned)c * 16u : kOOB;
+        xoff[i] = (q < XI && row < Mb) ? (unsigned)row * rowb + (unsigned)c * 16u : kOOB;
         xstep[i] = c >> 3;
     }
 #pragma unroll
@@ -134,7 +140,7 @@ __global__ void __launch_bounds__(256)
     const bool xs_real = MX && wave * 256 < XSB;
     const bool ws_real = MX && wave * 256 < WSB;
     const unsigned xsoff =
-        (xs_real && srow_l < M) ? (unsigned)srow_l * srow + (unsigned)sdw * 4u : kOOB;
+        (xs_real && srow_l < Mb) ? (unsigned)srow_l * srow + (unsigned)sdw * 4u : kOOB;
     const unsigned wsoff =
         (ws_real && srow_l < ncols) ? (unsigned)srow_l * srow + (unsigned)sdw * 4u : kOOB;
 
@@ -244,27 +250,29 @@ __global__ void __launch_bounds__(256)
     const float scale = MX ? 1.0f : sx[0] * sw[0];
     constexpr int C4 = NB * 4;
     const bool vec = (N & 3) == 0;
-    for (int e = t; e < M * C4; e += 256) {
+    for (int e = t; e < Mb * C4; e += 256) {
         const int r = e / C4, c = (e % C4) * 4;
         if (c >= ncols) continue;
         const f32x4 v = *reinterpret_cast<const f32x4 *>(tile + r * TS + c);
         const int n = col0 + c;
+        const size_t m = (size_t)(row0 + r);
         if (S == 1) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 if (c + q < ncols) {
                     float o = MX ? v[q] : v[q] * scale;
                     if (bias) o += bf16_to_f32(bias[n + q]);
-                    store_out(out, (size_t)r * N + n + q, o, out_f32);
+                    store_out(out, m * N + n + q, o, out_f32);
                 }
         } else if (vec && c + 4 <= ncols) {
-            *reinterpret_cast<f32x4 *>(ws + ((size_t)s * M + r) * N + n) = v;
+            *reinterpret_cast<f32x4 *>(ws + ((size_t)s * M + m) * N + n) = v;
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if (c + q < ncols) ws[((size_t)s * M + r) * N + n + q] = v[q];
+                if (c + q < ncols) ws[((size_t)s * M + m) * N + n + q] = v[q];
         }
     }
+    // (the planner gives REDUCE_LAST only with one row block)
     if (S == 1 || reduce != SKG_REDUCE_LAST) return;
     last_arriver_reduce(ws, tickets, bias, out, out_f32, M, N, S, j, col0, ncols, &is_last,
                         MX ? nullptr : sx, MX ? nullptr : sw);
@@ -286,7 +294,7 @@ int launch_fp8_tiled_t(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *
     hipLaunchKernelGGL((fp8_tiled_kernel<MT, NB, WM, NS, U, MX>), dim3(p.grid), dim3(256),
                        lds_bytes, stream, (const uint8_t *)a.x, (const uint8_t *)a.W,
                        (const uint16_t *)a.bias, a.sx, a.sw, a.xe, a.we, a.out, ws, tickets, M, N,
-                       K, p.splits, p.k_chunk, p.reduce, a.out_f32);
+                       K, p.splits, p.k_chunk, p.reduce, a.out_f32, tiled_row_blocks(M, MT));
     return (int)hipGetLastError();
 }
 

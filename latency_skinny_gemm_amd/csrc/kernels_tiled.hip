@@ -7,8 +7,9 @@
 // gfx950 the staging needs no registers: buffer_load_dwordx4 with the LDS
 // bit writes lane p's 16 bytes to LDS at (wave-uniform base) + 16*p, and an
 // out-of-range lane writes zeros (both measured on the MI355X).  So:
-//  * workgroup (j, s): columns [16*NB*j, 16*NB*(j+1)), all M rows (MT
-//    16-row tiles, MT a power of two; rows past M read as zeros), K chunk s;
+//  * workgroup (mb, j, s): columns [16*NB*j, 16*NB*(j+1)), rows of row
+//    block mb (MT 16-row tiles, MT a power of two; one block covers M up to
+//    128, more rows take blocks of 128; rows past M read as zeros), K chunk s;
 //    the split index is fastest in the grid, so with S a multiple of 8 every
 //    XCD (workgroup i runs on XCD i % 8) holds one K chunk of x in its L2;
 //  * a K step is 32 wide; per step the workgroup needs MT x-blocks and NB
@@ -79,7 +80,7 @@ __global__ void __launch_bounds__(256)
     tiled_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
                  const uint16_t *__restrict__ bias, void *__restrict__ out,
                  float *__restrict__ ws, unsigned *__restrict__ tickets, int M, int N, int K,
-                 int S, int k_chunk, int reduce, int out_f32) {
+                 int S, int k_chunk, int reduce, int out_f32, int MB) {
     constexpr int WN = 4 / WM;
     constexpr int MTW = MT / WM;          // m-tiles per wave
     constexpr int NBW = NB / WN;          // column blocks per wave
@@ -94,13 +95,18 @@ __global__ void __launch_bounds__(256)
     const int lane = t & 63;
     const int wm = wave / WN;
     const int wn = wave % WN;
-    const int s = blockIdx.x % S;
-    const int j = blockIdx.x / S;
+    // workgroup (mb, j, s): row block mb of MT*16 rows (M > 128 only),
+    // column group j, K chunk s; mb fastest, then s
+    const int mb = blockIdx.x % MB;
+    const int s = (blockIdx.x / MB) % S;
+    const int j = blockIdx.x / MB / S;
+    const int row0 = mb * MT * 16;
+    const int Mb = min(MT * 16, M - row0);  // rows of this block
     const int col0 = j * NB * 16;
     const int ncols = min(NB * 16, N - col0);
     const unsigned rowb = (unsigned)K * 2u;
     const Rsrc wr = make_rsrc(W + (size_t)col0 * K, (unsigned)ncols * rowb);
-    const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
+    const Rsrc xr = make_rsrc(x + (size_t)row0 * K, (unsigned)Mb * rowb);
     const int kbeg = s * k_chunk;
     const int nsteps = (min(K, kbeg + k_chunk) - kbeg) >> 5;  // K, k_chunk: multiples of 32
     const int nstages = (nsteps + U - 1) / U;
@@ -127,7 +133,7 @@ __global__ void __launch_bounds__(256)
         const int lin = (q % U) * 64 + lane;
         const int r = lin / CPR, c = (lin % CPR) ^ swz<U>(r);
         const int row = (q / U) * 16 + r;
-        xoff[i] = (q < XB && row < M) ? (unsigned)row * rowb + (unsigned)c * 16u : kOOB;
+        xoff[i] = (q < XB && row < Mb) ? (unsigned)row * rowb + (unsigned)c * 16u : kOOB;
         xstep[i] = c >> 2;
     }
 #pragma unroll
@@ -231,25 +237,27 @@ __global__ void __launch_bounds__(256)
     __syncthreads();
     constexpr int C4 = NB * 4;  // 4-column groups per row
     const bool vec = (N & 3) == 0;  // 16-byte aligned workspace rows
-    for (int e = t; e < M * C4; e += 256) {
+    for (int e = t; e < Mb * C4; e += 256) {
         const int r = e / C4, c = (e % C4) * 4;
         if (c >= ncols) continue;
         const f32x4 v = *reinterpret_cast<const f32x4 *>(tile + r * TS + c);
         const int n = col0 + c;
+        const size_t m = (size_t)(row0 + r);
         if (S == 1) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 if (c + q < ncols)
-                    store_out(out, (size_t)r * N + n + q,
+                    store_out(out, m * N + n + q,
                               bias ? v[q] + bf16_to_f32(bias[n + q]) : v[q], out_f32);
         } else if (vec && c + 4 <= ncols) {
-            *reinterpret_cast<f32x4 *>(ws + ((size_t)s * M + r) * N + n) = v;
+            *reinterpret_cast<f32x4 *>(ws + ((size_t)s * M + m) * N + n) = v;
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if (c + q < ncols) ws[((size_t)s * M + r) * N + n + q] = v[q];
+                if (c + q < ncols) ws[((size_t)s * M + m) * N + n + q] = v[q];
         }
     }
+    // (the planner gives REDUCE_LAST only with one row block)
     if (S == 1 || reduce != SKG_REDUCE_LAST) return;
     last_arriver_reduce(ws, tickets, bias, out, out_f32, M, N, S, j, col0, ncols, &is_last);
 }
@@ -271,7 +279,8 @@ int launch_tiled_t(const SkgPlan &p, const void *x, const void *W, const void *b
     if (attr != hipSuccess) return (int)attr;
     hipLaunchKernelGGL((tiled_kernel<MT, NB, WM, NS, U>), dim3(p.grid), dim3(256), lds_bytes,
                        stream, (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)bias,
-                       out, ws, tickets, M, N, K, p.splits, p.k_chunk, p.reduce, out_f32);
+                       out, ws, tickets, M, N, K, p.splits, p.k_chunk, p.reduce, out_f32,
+                       tiled_row_blocks(M, MT));
     return (int)hipGetLastError();
 }
 

@@ -43,7 +43,9 @@ def point_sets():
         "router": uniq([p for p in bf16 if p.group in ("small_bf16", "router_k7168", "router_shapes")]),
         "decode": uniq([p for p in bf16 if p.group == "decode_linear"]),
         "all": uniq(bf16),
-        "fp8": uniq(fp8),
+        "fp8": uniq([p for p in fp8 if p.group.startswith("fp8_")]),
+        "large_bf16": uniq([p for p in configs.larger_m_full() if p.dtype == "bf16"]),
+        "large_fp8": uniq([p for p in configs.larger_m_full() if p.dtype != "bf16"]),
     }
 
 
@@ -286,7 +288,7 @@ def run(args):
     t0 = time.time()
     with open(args.out, "a") as log:
         for (M, N, K) in pts:
-            fn = sweep_point_fp8 if args.points == "fp8" else sweep_point
+            fn = sweep_point_fp8 if args.points in ("fp8", "large_fp8") else sweep_point
             fn(skg, torch, M, N, K, args.pool_mb << 20, args.reps, stream, log)
             torch.cuda.empty_cache()
     print(f"swept {len(pts)} points in {time.time() - t0:.0f} s", flush=True)
@@ -351,7 +353,8 @@ def emit_table(files, out_path=TABLE):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--points", default="headline", choices=("headline", "router", "decode", "all", "fp8"))
+    ap.add_argument("--points", default="headline",
+                    choices=("headline", "router", "decode", "all", "fp8", "large_bf16", "large_fp8"))
     ap.add_argument("--M", type=int, nargs="*", help="restrict to these M")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "sweep.jsonl"))
     ap.add_argument("--pool-mb", type=int, default=512)

@@ -49,7 +49,8 @@ X, W, OUT, B = 0x10000, 0x200000, 0x4000000, 0x8000000
     ((X, W, 0, 0, OUT, 2, 8, -64), skg.ERR_INVALID_ARG),
     ((X, W, 0, 0, OUT, 0, 8, 64), skg.OK),          # empty: no launch
     ((0, 0, 0, 0, 0, 5, 0, 64), skg.OK),            # empty: no launch
-    ((X, W, 0, 0, OUT, 129, 8, 64), skg.ERR_UNSUPPORTED),
+    ((X, W, 0, 0, OUT, 513, 8, 64), skg.ERR_UNSUPPORTED),
+    ((X, W, 0, 0, OUT, 129, 8, 72), skg.ERR_UNSUPPORTED),   # > 128 rows: K % 32
     ((X, W, 0, 0, OUT, 2, 8, 60), skg.ERR_UNSUPPORTED),
     ((X, W, 0, 0, OUT, 2, 8, 0), skg.ERR_UNSUPPORTED),
     ((X, W, 0, 0, OUT, 2, 8, 4), skg.ERR_UNSUPPORTED),
@@ -140,13 +141,29 @@ FP8 = [p for p in configs.all_points() if p.dtype != "bf16"]
 
 @pytest.mark.parametrize("M,N,K,NB,wm,NS,U,S", [
     (128, 4096, 4096, 8, 2, 3, 1, 8), (64, 4096, 4096, 4, 0, 4, 2, 4), (16, 4096, 4096, 8, 1, 6, 1, 4),
-    (1, 1024, 4096, 16, 0, 2, 1, 2), (37, 200, 1024, 2, 4, 4, 2, 3), (128, 96, 4096, 2, 2, 3, 2, 1)])
+    (1, 1024, 4096, 16, 0, 2, 1, 2), (37, 200, 1024, 2, 4, 4, 2, 3), (128, 96, 4096, 2, 2, 3, 2, 1),
+    (512, 4096, 4096, 2, 4, 3, 2, 2), (300, 200, 1024, 4, 2, 3, 1, 4)])
 def test_fp8_tiled_plans_cover(lib, M, N, K, NB, wm, NS, U, S):
     p = skg.make_plan(skg.KIND_TILED, 256, NB, S, NS, skg.REDUCE_KERNEL, waves_m=wm,
                       flags=skg.FLAG_TILED_WIDE if U == 2 else 0)
     q = skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
     assert q.kind == skg.KIND_TILED
     _check_fp8_coverage(q, M, N, K)
+
+
+def test_large_M_takes_tiled_plans_only(lib):
+    for dt, K in ((skg.DTYPE_BF16, 7168), (skg.DTYPE_FP8, 4096)):
+        for M in (129, 256, 512):
+            assert skg.plan(M, 4096, K, dt).kind == skg.KIND_TILED
+            with pytest.raises(skg.SkinnyGemmError):
+                skg.plan_complete(M, 4096, K, skg.make_plan(skg.KIND_SPLITK, 256, 1, 4, 1), dt)
+            with pytest.raises(skg.SkinnyGemmError):  # last arriver: one row block only
+                skg.plan_complete(M, 4096, K, skg.make_plan(skg.KIND_TILED, 256, 4, 2, 2,
+                                                            skg.REDUCE_LAST), dt)
+            q = skg.plan_complete(M, 4096, K, skg.make_plan(skg.KIND_TILED, 256, 4, 2, 2), dt)
+            assert q.reduce == skg.REDUCE_KERNEL and q.m_tiles == 8
+    with pytest.raises(skg.SkinnyGemmError):
+        skg.plan(513, 64, 1024)
 
 
 def test_fp8_tiled_rejects(lib):
@@ -169,11 +186,13 @@ def _check_fp8_tiled_coverage(p, M, N, K):
     S, NB, NS, kc, WM = p.splits, p.cols, p.depth, p.k_chunk, p.waves_m
     U = 2 if p.flags & skg.FLAG_TILED_WIDE else 1
     WN = 4 // WM
-    MT = next(v for v in (1, 2, 4, 8) if v >= -(-M // 16))
+    MT = next((v for v in (1, 2, 4, 8) if v >= -(-M // 16)), 8)
     assert p.m_tiles == MT and MT % WM == 0 and NB % WN == 0 and p.threads == 256
     assert K % 128 == 0 and kc % 128 == 0 and (S - 1) * kc < K <= S * kc
     groups = -(-N // (16 * NB))
-    assert p.grid == groups * S
+    MB = -(-M // (MT * 16))
+    assert MB == 1 or (MT == 8 and p.reduce != skg.REDUCE_LAST)
+    assert p.grid == MB * groups * S
     CPR = 8 * U
 
     def swz(r):
@@ -284,7 +303,7 @@ def test_status_strings(lib):
 
 def test_reserve_rejects_bad_sizes(lib):
     assert lib.skinny_gemm_reserve(0, 10, 1, None) == skg.ERR_INVALID_ARG
-    assert lib.skinny_gemm_reserve(129, 10, 1, None) == skg.ERR_INVALID_ARG
+    assert lib.skinny_gemm_reserve(513, 10, 1, None) == skg.ERR_INVALID_ARG
     assert lib.skinny_gemm_reserve(4, 10, 10000, None) == skg.ERR_INVALID_ARG
 
 
@@ -298,6 +317,8 @@ def test_default_rule_without_table(lib, p):
     # a made-up 200-CU device never uses the MI355X table: the pages' rule
     q = skg.plan_on(p.M, p.N, p.K, 200)
     want = skg.KIND_DOT if (p.M <= 4 or p.K < 2048) else skg.KIND_SPLITK
+    if p.M > 128:
+        want = skg.KIND_TILED  # above 128 rows only the tiled kernel runs
     assert q.kind == want and q.from_table == 0
     _check_coverage(q, p.M, p.N, p.K)
 
@@ -324,6 +345,8 @@ def test_table_entries_are_exact_and_valid(lib):
     # every table entry is returned for its exact (M, N, K) at 256 CUs, and
     # its completed plan covers the problem
     for p in BF16:
+        if p.group == "larger_m":  # parity points, not swept
+            continue
         q = skg.plan(p.M, p.N, p.K)
         assert q.from_table == 1, p.key()
         _check_coverage(q, p.M, p.N, p.K)
@@ -414,12 +437,19 @@ def _check_tiled_coverage(p, M, N, K):
     U = 4 if p.flags & skg.FLAG_TILED_WIDE else 2
     WN = 4 // WM
     mt = -(-M // 16)
-    MT = next(v for v in (1, 2, 4, 8) if v >= mt)
+    MT = next((v for v in (1, 2, 4, 8) if v >= mt), 8)
     assert p.m_tiles == MT and MT % WM == 0 and NB % WN == 0
     MTW, NBW = MT // WM, NB // WN
     assert p.threads == 256 and K % 32 == 0
     groups = -(-N // (16 * NB))
-    assert p.grid == groups * S and kc % 32 == 0 and (S - 1) * kc < K <= S * kc
+    MB = -(-M // (MT * 16))   # row blocks (only above 128 rows)
+    assert MB == 1 or (MT == 8 and p.reduce != skg.REDUCE_LAST)
+    assert p.grid == MB * groups * S and kc % 32 == 0 and (S - 1) * kc < K <= S * kc
+    # the grid's (mb, j, s) decode: mb fastest, then s, then j
+    dec = sorted((b % MB, (b // MB) % S, b // MB // S) for b in range(p.grid))
+    assert dec == sorted((mb, s, j) for mb in range(MB) for s in range(S) for j in range(groups))
+    rows = sorted(mb * MT * 16 + r for mb in range(MB) for r in range(min(MT * 16, M - mb * MT * 16)))
+    assert rows == list(range(M))
     # waves partition the workgroup's (m-tile, column-block) grid
     owned = sorted((wm * MTW + a, wn * NBW + b) for wm in range(WM) for wn in range(WN)
                    for a in range(MTW) for b in range(NBW))
@@ -458,11 +488,12 @@ def _check_tiled_coverage(p, M, N, K):
     TS = NB * 16 + 4
     assert MT * 16 * TS * 4 <= ring and (TS * 4) % 16 == 0
     assert len({(4 * r * TS * 4) % 256 // 64 for r in range(4)}) == 4  # rows 4 apart: other banks
+    Mb = min(M, MT * 16)
     for j in range(groups):
         ncols = min(NB * 16, N - 16 * NB * j)
-        cov = sorted((e // (NB * 4), (e % (NB * 4)) * 4 + q) for e in range(M * NB * 4)
+        cov = sorted((e // (NB * 4), (e % (NB * 4)) * 4 + q) for e in range(Mb * NB * 4)
                      for q in range(4) if (e % (NB * 4)) * 4 + q < ncols)
-        assert cov == [(r, c) for r in range(M) for c in range(ncols)]
+        assert cov == [(r, c) for r in range(Mb) for c in range(ncols)]
     # the ring: stages 0..NS-2 issued up front, stage st+NS-1 issued after
     # stage st is computed into slot (st+NS-1) % NS; a slot is overwritten
     # only after its stage was computed, and the vmcnt wait leaves exactly
@@ -502,11 +533,13 @@ def _check_tiled_coverage(p, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,NB,wm,NS,U,S", [
+    (512, 4096, 7168, 4, 2, 2, 4, 1), (200, 576, 2048, 8, 2, 4, 2, 2), (129, 64, 1024, 2, 4, 3, 2, 3),
     (128, 4096, 7168, 8, 2, 4, 2, 8), (128, 4096, 7168, 8, 4, 3, 2, 16), (64, 576, 7168, 4, 0, 6, 2, 12),
     (8, 4096, 7168, 8, 1, 6, 2, 8), (33, 200, 2080, 4, 0, 3, 4, 3), (1, 2112, 7168, 16, 0, 2, 4, 4),
     (5, 100, 2880, 4, 1, 4, 2, 5), (100, 50, 1024, 2, 4, 3, 4, 7), (128, 4096, 7168, 8, 2, 2, 4, 8)])
 def test_tiled_plans_cover(lib, M, N, K, NB, wm, NS, U, S):
-    p = skg.make_plan(skg.KIND_TILED, 256, NB, S, NS, skg.REDUCE_LAST, waves_m=wm,
+    red = skg.REDUCE_LAST if M <= 128 else skg.REDUCE_KERNEL  # last arriver: one row block
+    p = skg.make_plan(skg.KIND_TILED, 256, NB, S, NS, red, waves_m=wm,
                       flags=skg.FLAG_TILED_WIDE if U == 4 else 0)
     q = skg.plan_complete(M, N, K, p)
     assert q.kind == skg.KIND_TILED and q.waves_m in (1, 2, 4)

@@ -233,8 +233,12 @@ def test_error_statuses_on_device(skg):
                       torch.zeros(8, 60, dtype=torch.bfloat16, device=DEV))
     assert e.value.status == skg.ERR_UNSUPPORTED  # K % 8 != 0
     with pytest.raises(skg.SkinnyGemmError) as e:
-        skg.gemm_bf16(torch.zeros(129, 64, dtype=torch.bfloat16, device=DEV), w)
-    assert e.value.status == skg.ERR_UNSUPPORTED  # M > 128
+        skg.gemm_bf16(torch.zeros(513, 64, dtype=torch.bfloat16, device=DEV), w)
+    assert e.value.status == skg.ERR_UNSUPPORTED  # M > 512
+    with pytest.raises(skg.SkinnyGemmError) as e:
+        skg.gemm_bf16(torch.zeros(129, 72, dtype=torch.bfloat16, device=DEV),
+                      torch.zeros(8, 72, dtype=torch.bfloat16, device=DEV))
+    assert e.value.status == skg.ERR_UNSUPPORTED  # M > 128 needs K % 32 == 0
     lib = skg.lib()
     flat = torch.zeros(2 * 64 + 8, dtype=torch.bfloat16, device=DEV)
     out = torch.zeros(2, 8, dtype=torch.bfloat16, device=DEV)
@@ -244,3 +248,25 @@ def test_error_statuses_on_device(skg):
     rc = lib.skinny_gemm_bf16(x.data_ptr(), w.data_ptr(), None, None, x.data_ptr(), 2, 8, 64, None)
     assert rc == skg.ERR_INVALID_ARG  # out overlaps x
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------ larger M at full size
+# M = 512 on the dense decode shape (N = 4096, K = 7168): the oracle computes
+# sampled outputs one by one (an output depends only on its row of x and its
+# row of W), in every row block and column group corner.
+@pytest.mark.parametrize("bias", (False, True))
+def test_large_M_full_size_sampled(skg, bias):
+    M, N, K = 512, 4096, 7168
+    x, w, b = gen.bf16_inputs(M, N, K, bias, seed=512 + bias)
+    xd, wd = x.to(DEV), w.to(DEV)
+    bd = None if b is None else b.to(DEV)
+    out = skg.gemm_bf16(xd, wd, bd)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 255, 300, 384, 511])
+    cols = np.concatenate([np.arange(0, 16), np.arange(4080, 4096),
+                           np.random.default_rng(1).integers(0, N, 32)])
+    ref = oracle.gemm_bf16(gen.bits16(x[rows]), gen.bits16(w[cols]),
+                           None if b is None else gen.bits16(b[cols]), threads=16)
+    got = out.cpu()[rows][:, cols]
+    ok, msg = tolerance.check(got, ref, K)
+    assert ok, msg

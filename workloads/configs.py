@@ -60,9 +60,29 @@ def fp8_square(mode):
             for M in (1, 16, 64, 128)]
 
 
+def larger_m():
+    """The larger-M regime (M = 129-512, row blocks of 128), at sizes the
+    oracle finishes in seconds: bf16 with and without bias, FP8 in both
+    scale modes."""
+    return ([Point("larger_m", "bf16", 129, 96, 1024, True),
+             Point("larger_m", "bf16", 256, 576, 2048, False),
+             Point("larger_m", "bf16", 512, 512, 2048, True)]
+            + [Point("larger_m", mode, M, 512, 2048, False)
+               for mode in ("fp8_tensor", "fp8_mx") for M in (200, 512)])
+
+
+def larger_m_full():
+    """The larger-M regime at full size (swept and benchmarked; parity is
+    checked on sampled outputs): bf16 dense decode K = 7168, N = 4096 and
+    FP8 K = N = 4096, M in {256, 512}."""
+    return ([Point("larger_m_full", "bf16", M, 4096, 7168, False) for M in (256, 512)]
+            + [Point("larger_m_full", mode, M, 4096, 4096, False)
+               for mode in ("fp8_tensor", "fp8_mx") for M in (256, 512)])
+
+
 def all_points():
     return (small_bf16() + router_k7168() + router_shapes() + decode_linear()
-            + fp8_square("fp8_tensor") + fp8_square("fp8_mx"))
+            + fp8_square("fp8_tensor") + fp8_square("fp8_mx") + larger_m())
 
 
 # The headline workload: bf16, K = 7168, N = 256, M = 1..16.
