@@ -109,7 +109,11 @@ def test_point_within_tolerance(skg, p):
 
 
 EXACT_SHAPES = [(1, 256, 2048), (3, 100, 2880), (4, 128, 2880), (5, 384, 7168), (9, 256, 4096),
-                (16, 256, 6144), (16, 37, 8), (33, 72, 264), (64, 576, 7168), (128, 200, 2056)]
+                (16, 256, 6144), (16, 37, 8), (33, 72, 264), (64, 576, 7168), (128, 200, 2056),
+                # ragged and degenerate: one column, one row, the shortest K, a K
+                # of one 32-wide step, M just past a tile and past one row block
+                (1, 1, 8), (2, 1, 4096), (17, 17, 1056), (7, 300, 32), (129, 33, 96),
+                (130, 1, 64), (300, 20, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", EXACT_SHAPES)
