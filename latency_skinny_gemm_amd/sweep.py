@@ -77,7 +77,7 @@ def fp8_candidates(skg, M, N, K):
             add(skg.make_plan(skg.KIND_DOT, T, 1))
     # LDS-ring tiles (K % 128 == 0)
     if K % 128 == 0 and (M > 4 or N >= 1024):
-        for NB in (2, 4, 8, 16):
+        for NB in (1, 2, 4, 8, 16):
             groups = -(-N // (16 * NB))
             for S in SPLITS:
                 if S > K // 128 or not (64 <= groups * S <= 2048):
@@ -204,7 +204,7 @@ def candidates(skg, M, N, K):
     # LDS-ring tiles (K % 32 == 0): worth it once a workgroup covers many
     # columns; stages and steps per stage cover 2-16 steps in flight
     if (M > 4 or N >= 1024) and K % 32 == 0:
-        for NB in (2, 4, 8, 16):
+        for NB in (1, 2, 4, 8, 16):
             groups = -(-N // (16 * NB))
             for S in SPLITS:
                 if S > ksteps or not (64 <= groups * S <= 2048):
