@@ -121,7 +121,7 @@ typedef struct skinny_fp8_scales {
 typedef struct SkgPlan {
     int kind;     /* SKG_KIND_DOT, SKG_KIND_SPLITK or SKG_KIND_TILED */
     int threads;  /* workgroup size, a multiple of 64, <= 1024 (TILED: 256) */
-    int cols;     /* DOT: output columns per workgroup (1, 2);
+    int cols;     /* DOT: output columns per workgroup (bf16: 1, 2; FP8: 1, 2, 4);
                      SPLITK: 16-column blocks per workgroup (1, 2, 4);
                      TILED: 16-column blocks per workgroup (1, 2, 4, 8, 16) */
     int splits;   /* SPLITK, TILED: number of K chunks S (>= 1); DOT: 1 */
@@ -205,8 +205,9 @@ int skinny_gemm_bf16_f32_planned(const void *x, const void *W, const void *bias,
  * page (a given scale, one reciprocal, a product, a clamp, the cast to e4m3
  * with round-to-nearest-even), followed by that page's per-tensor GEMM.
  * The dot-product plan (small M) quantises x as it loads it, so the call is
- * one launch; other plans quantise x into the workspace first (a second
- * launch).  x: DEVICE bf16 [M, K], 16-byte aligned; W: DEVICE e4m3fn
+ * one launch (the automatic plan then shares each x load over four or two
+ * columns where it can); other plans quantise x into the workspace first (a
+ * second launch).  x: DEVICE bf16 [M, K], 16-byte aligned; W: DEVICE e4m3fn
  * [N, K], 16-byte aligned; sx, sw: DEVICE fp32 scalars, 4-byte aligned;
  * K % 16 == 0.  out_dtype: SKG_DTYPE_BF16 (bf16 out, 2-byte aligned) or
  * SKG_DTYPE_F32 (fp32 out, 4-byte aligned).  NaN in x gives NaN outputs. */

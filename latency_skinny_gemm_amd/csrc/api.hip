@@ -133,7 +133,7 @@ int run_fp8(const void *x, const void *W, const void *bias, const skinny_fp8_sca
             hipStream_t stream) {
     Fp8Args a{x, W, bias, out, sc->mode, sc->sx, sc->sw, sc->x_e8m0, sc->w_e8m0, out_f32, false};
     const bool fused =
-        quant_x && p.kind == SKG_KIND_DOT && fp8_dot_quant_ok(M, p.depth, p.threads);
+        quant_x && p.kind == SKG_KIND_DOT && fp8_dot_quant_ok(M, p.cols, p.depth, p.threads);
     a.qx = fused;
     // partials first (rounded to 256 bytes), then the quantised x if needed
     const size_t part = (p.kind != SKG_KIND_DOT && p.splits > 1)
@@ -196,15 +196,25 @@ int fp8_quant_common(const void *x, const void *W, const void *bias, const float
         rc = complete_plan(M, N, K, SKG_DTYPE_FP8, &p);
     } else {
         rc = skinny_gemm_plan(M, N, K, SKG_DTYPE_FP8, &p);
-        // The fused dot kernel holds bf16 x until it is quantised and may
-        // need smaller workgroups than the FP8 plan: try 512 threads
-        // (enough vectors per thread follow) so the call stays one launch.
-        if (rc == SKG_OK && p.kind == SKG_KIND_DOT && !fp8_dot_quant_ok(M, p.depth, p.threads)) {
-            SkgPlan q = p;
-            q.threads = 512;
-            if (complete_plan(M, N, K, SKG_DTYPE_FP8, &q) == SKG_OK &&
-                fp8_dot_quant_ok(M, q.depth, q.threads))
-                p = q;
+        // Where the FP8 table picks the dot kernel, the fused form reads x
+        // as bf16 (twice the bytes of its codes) in every workgroup, so it
+        // takes four (else two) columns per workgroup of 256 threads to cut
+        // those L2 reads; failing both, the table's plan, else 512 threads
+        // (the fused kernel holds bf16 x until it is quantised and may need
+        // smaller workgroups).  At K = N = 4096 four columns took M = 1
+        // from 6.9 to 5.5 us and M = 4 from 17.0 to 10.4 us.
+        if (rc == SKG_OK && p.kind == SKG_KIND_DOT) {
+            const int tries[4][2] = {{256, 4}, {256, 2}, {p.threads, p.cols}, {512, p.cols}};
+            for (const auto &t : tries) {
+                SkgPlan q = p;
+                q.threads = t[0];
+                q.cols = t[1];
+                if (complete_plan(M, N, K, SKG_DTYPE_FP8, &q) == SKG_OK &&
+                    fp8_dot_quant_ok(M, q.cols, q.depth, q.threads)) {
+                    p = q;
+                    break;
+                }
+            }
         }
     }
     if (rc != SKG_OK) return rc;

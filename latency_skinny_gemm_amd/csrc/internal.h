@@ -73,17 +73,27 @@ constexpr bool tiled_built(int MT, int NB, int WM, int NS, int U) {
 
 // FP8 dot kernel: x counted packed plus its widened words (as for bf16
 // without dot2) and, in MX mode, one scale byte per (row, vector); a plan is
-// checked for the MX count, the larger.
+// checked for the MX count, the larger.  With several columns the compiler
+// keeps every x vector widened to fp32 (16 VGPRs) for reuse across the
+// columns, so C > 1 is also bounded by that count (fitted to the compiler's
+// resource report, conservatively: no kernel built under it spills).
 constexpr int kFp8DotVecs[] = {1, 2, 4};
-constexpr int fp8_dot_regs(int M, int V, bool mx) {
-    return dot_regs(M, 1, V, false) + (mx ? (M + 1) * V : 0);
+constexpr int fp8_dot_wide_regs(int M, int C, int V) {
+    return C > 1 ? 16 * M * V + 8 * C * V + C * M + 16 : 0;
+}
+constexpr int fp8_dot_regs(int M, int C, int V, bool mx) {
+    const int base = dot_regs(M, C, V, false) + (mx ? (M + C) * V : 0);
+    return base > fp8_dot_wide_regs(M, C, V) ? base : fp8_dot_wide_regs(M, C, V);
 }
 // With x arriving as bf16 and quantised on load (static per-tensor FP8),
 // each vector of a row is two 16-byte loads (8 VGPRs) until it is packed
 // into 4 VGPRs of codes; counted as 12 per (row, vector) plus W.
-constexpr int fp8q_dot_regs(int M, int V) { return M * V * 12 + 4 * V + M; }
-constexpr int fp8_dot_max_threads(int M, int V, bool mx, bool qx = false) {
-    return (qx ? fp8q_dot_regs(M, V) : fp8_dot_regs(M, V, mx)) <= 96 ? 1024 : 512;
+constexpr int fp8q_dot_regs(int M, int C, int V) {
+    const int base = M * V * 12 + 4 * C * V + C * M;
+    return base > fp8_dot_wide_regs(M, C, V) ? base : fp8_dot_wide_regs(M, C, V);
+}
+constexpr int fp8_dot_max_threads(int M, int C, int V, bool mx, bool qx = false) {
+    return (qx ? fp8q_dot_regs(M, C, V) : fp8_dot_regs(M, C, V, mx)) <= 96 ? 1024 : 512;
 }
 
 // FP8 MFMA split-K (v_mfma_scale_f32_16x16x128_f8f6f4, 128-wide K steps):
@@ -169,6 +179,6 @@ int launch_fp8_tiled(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *ti
 // Whether the FP8 dot kernel that quantises bf16 x on load exists for (M, V)
 // and accepts workgroups of `threads` (its registers bound it lower than the
 // plain FP8 dot kernel).
-bool fp8_dot_quant_ok(int M, int V, int threads);
+bool fp8_dot_quant_ok(int M, int C, int V, int threads);
 
 }  // namespace skg

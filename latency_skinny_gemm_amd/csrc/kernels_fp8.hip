@@ -68,8 +68,9 @@ __device__ __forceinline__ unsigned load_byte(Rsrc r, unsigned off) {
 // fused form of the "sglang PR #28333" page's static quant kernel): each
 // 16-element vector is two 16-byte bf16 loads, turned into 16 e4m3 codes
 // exactly as the standalone quantisation kernel does.
-template <int M, int V, bool MX, bool QX>
-__global__ void __launch_bounds__((fp8_dot_max_threads(M, V, MX, QX)))
+// C output columns per workgroup share each x load.
+template <int M, int C, int V, bool MX, bool QX>
+__global__ void __launch_bounds__((fp8_dot_max_threads(M, C, V, MX, QX)))
     fp8_dot_kernel(const void *__restrict__ x, const uint8_t *__restrict__ W,
                    const uint16_t *__restrict__ bias, const float *__restrict__ sx,
                    const float *__restrict__ sw, const uint8_t *__restrict__ xe,
@@ -78,22 +79,25 @@ __global__ void __launch_bounds__((fp8_dot_max_threads(M, V, MX, QX)))
     static_assert(!(MX && QX), "static quantisation is per-tensor");
     const int T = blockDim.x;
     const int t = threadIdx.x;
-    const int n = blockIdx.x;
+    const int n0 = blockIdx.x * C;
+    const int ncols = min(C, N - n0);
     const unsigned rowb = (unsigned)K;  // one byte per element
-    const Rsrc wr = make_rsrc(W + (size_t)n * K, rowb);
+    const Rsrc wr = make_rsrc(W + (size_t)n0 * K, (unsigned)ncols * rowb);
     const unsigned xrowb = QX ? 2u * rowb : rowb;  // bf16 or e4m3 x rows
     const Rsrc xr = make_rsrc(x, (unsigned)M * xrowb);
     const int K16 = K >> 4;
     const unsigned srow = (unsigned)(K >> 5);  // scale bytes per row (MX)
     const Rsrc xer = make_rsrc(xe, MX ? (unsigned)M * srow : 0u);
-    const Rsrc wer = make_rsrc(we + (MX ? (size_t)n * srow : 0), MX ? srow : 0u);
+    const Rsrc wer = make_rsrc(we + (MX ? (size_t)n0 * srow : 0), MX ? (unsigned)ncols * srow : 0u);
 
-    u32x4 wv[V], xv[M][V];
-    unsigned wsc[V], xsc[M][V];
+    u32x4 wv[C][V], xv[M][V];
+    unsigned wsc[C][V], xsc[M][V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const int v = t + i * T;
-        wv[i] = load16<kCacheStream>(wr, v < K16 ? (unsigned)v * 16u : kOOB);
+        const unsigned off = v < K16 ? (unsigned)v * 16u : kOOB;
+#pragma unroll
+        for (int c = 0; c < C; ++c) wv[c][i] = load16<kCacheStream>(wr, off + (unsigned)c * rowb);
     }
     if constexpr (QX) {
         const float inv = 1.0f / sx[0];  // correctly rounded (no fast-math)
@@ -123,44 +127,55 @@ __global__ void __launch_bounds__((fp8_dot_max_threads(M, V, MX, QX)))
         for (int i = 0; i < V; ++i) {
             const int v = t + i * T;
             const unsigned blk = v < K16 ? (unsigned)(v >> 1) : kOOB;  // 32-element block
-            wsc[i] = load_byte(wer, blk);
+#pragma unroll
+            for (int c = 0; c < C; ++c) wsc[c][i] = load_byte(wer, blk + (unsigned)c * srow);
 #pragma unroll
             for (int m = 0; m < M; ++m) xsc[m][i] = load_byte(xer, blk + (unsigned)m * srow);
         }
     }
 
-    float acc[M];
+    float acc[C][M];
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[c][m] = 0.0f;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const int v = t + i * T;
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            if constexpr (MX) {
-                const float p = dot16_fp8(xv[m][i], wv[i], 0.0f);
-                if (v < K16) acc[m] += mx_scale_apply(p, xsc[m][i], wsc[i]);
-            } else {
-                acc[m] = dot16_fp8(xv[m][i], wv[i], acc[m]);
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                if constexpr (MX) {
+                    const float p = dot16_fp8(xv[m][i], wv[c][i], 0.0f);
+                    if (v < K16) acc[c][m] += mx_scale_apply(p, xsc[m][i], wsc[c][i]);
+                } else {
+                    acc[c][m] = dot16_fp8(xv[m][i], wv[c][i], acc[c][m]);
+                }
             }
-        }
     }
 
-    __shared__ float red[kMaxThreads / 64][M];
+    __shared__ float red[kMaxThreads / 64][C * M];
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int lane = t & 63;
     const int nw = T >> 6;
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-        const float s = wave_sum(acc[m]);
-        if (lane == 0) red[wave][m] = s;
-    }
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float s = wave_sum(acc[c][m]);
+            if (lane == 0) red[wave][c * M + m] = s;
+        }
     __syncthreads();
-    if (t < M) {
+    if (t < C * M) {
+        const int c = t / M, m = t - (t / M) * M;
+        const int n = n0 + c;
         float s = ordered_sum<8>(nw, [&](int w) { return red[w][t]; });
-        if (!MX) s *= sx[0] * sw[0];
-        if (bias) s += bf16_to_f32(bias[n]);
-        store_out(out, (size_t)t * N + n, s, out_f32);
+        if (n < N) {
+            if (!MX) s *= sx[0] * sw[0];
+            if (bias) s += bf16_to_f32(bias[n]);
+            store_out(out, (size_t)m * N + n, s, out_f32);
+        }
     }
 }
 
@@ -326,52 +341,62 @@ typedef int (*Fp8DotLaunch)(const SkgPlan &, const Fp8Args &, int, int, hipStrea
 typedef int (*Fp8MfmaLaunch)(const SkgPlan &, const Fp8Args &, float *, unsigned *, int, int, int,
                              hipStream_t);
 
-template <int M, int V, bool MX, bool QX>
+template <int M, int C, int V, bool MX, bool QX>
 int launch_fp8_dot_t(const SkgPlan &p, const Fp8Args &a, int N, int K, hipStream_t stream) {
-    hipLaunchKernelGGL((fp8_dot_kernel<M, V, MX, QX>), dim3(p.grid), dim3(p.threads), 0, stream,
+    hipLaunchKernelGGL((fp8_dot_kernel<M, C, V, MX, QX>), dim3(p.grid), dim3(p.threads), 0, stream,
                        a.x, (const uint8_t *)a.W, (const uint16_t *)a.bias, a.sx, a.sw, a.xe,
                        a.we, a.out, N, K, a.out_f32);
     return (int)hipGetLastError();
 }
 
-template <int M, int V, bool MX, bool QX>
+template <int M, int C, int V, bool MX, bool QX>
 constexpr Fp8DotLaunch fp8_dot_entry() {
-    if constexpr (QX ? (!MX && fp8q_dot_regs(M, V) <= kDotRegsMax)
-                     : fp8_dot_regs(M, V, MX) <= kDotRegsMax)
-        return &launch_fp8_dot_t<M, V, MX, QX>;
+    if constexpr (QX ? (!MX && fp8q_dot_regs(M, C, V) <= kDotRegsMax)
+                     : fp8_dot_regs(M, C, V, MX) <= kDotRegsMax)
+        return &launch_fp8_dot_t<M, C, V, MX, QX>;
     else
         return nullptr;
 }
 
-template <int M, bool MX, bool QX>
+template <int M, int C, bool MX, bool QX>
 Fp8DotLaunch fp8_dot_v(int V) {
     switch (V) {
-    case 1: return fp8_dot_entry<M, 1, MX, QX>();
-    case 2: return fp8_dot_entry<M, 2, MX, QX>();
-    case 4: return fp8_dot_entry<M, 4, MX, QX>();
+    case 1: return fp8_dot_entry<M, C, 1, MX, QX>();
+    case 2: return fp8_dot_entry<M, C, 2, MX, QX>();
+    case 4: return fp8_dot_entry<M, C, 4, MX, QX>();
+    default: return nullptr;
+    }
+}
+
+template <int M, bool MX, bool QX>
+Fp8DotLaunch fp8_dot_c(int C, int V) {
+    switch (C) {
+    case 1: return fp8_dot_v<M, 1, MX, QX>(V);
+    case 2: return fp8_dot_v<M, 2, MX, QX>(V);
+    case 4: return fp8_dot_v<M, 4, MX, QX>(V);
     default: return nullptr;
     }
 }
 
 template <bool MX, bool QX>
-Fp8DotLaunch fp8_dot_m(int M, int V) {
+Fp8DotLaunch fp8_dot_m(int M, int C, int V) {
     switch (M) {
-    case 1: return fp8_dot_v<1, MX, QX>(V);
-    case 2: return fp8_dot_v<2, MX, QX>(V);
-    case 3: return fp8_dot_v<3, MX, QX>(V);
-    case 4: return fp8_dot_v<4, MX, QX>(V);
-    case 5: return fp8_dot_v<5, MX, QX>(V);
-    case 6: return fp8_dot_v<6, MX, QX>(V);
-    case 7: return fp8_dot_v<7, MX, QX>(V);
-    case 8: return fp8_dot_v<8, MX, QX>(V);
-    case 9: return fp8_dot_v<9, MX, QX>(V);
-    case 10: return fp8_dot_v<10, MX, QX>(V);
-    case 11: return fp8_dot_v<11, MX, QX>(V);
-    case 12: return fp8_dot_v<12, MX, QX>(V);
-    case 13: return fp8_dot_v<13, MX, QX>(V);
-    case 14: return fp8_dot_v<14, MX, QX>(V);
-    case 15: return fp8_dot_v<15, MX, QX>(V);
-    case 16: return fp8_dot_v<16, MX, QX>(V);
+    case 1: return fp8_dot_c<1, MX, QX>(C, V);
+    case 2: return fp8_dot_c<2, MX, QX>(C, V);
+    case 3: return fp8_dot_c<3, MX, QX>(C, V);
+    case 4: return fp8_dot_c<4, MX, QX>(C, V);
+    case 5: return fp8_dot_c<5, MX, QX>(C, V);
+    case 6: return fp8_dot_c<6, MX, QX>(C, V);
+    case 7: return fp8_dot_c<7, MX, QX>(C, V);
+    case 8: return fp8_dot_c<8, MX, QX>(C, V);
+    case 9: return fp8_dot_c<9, MX, QX>(C, V);
+    case 10: return fp8_dot_c<10, MX, QX>(C, V);
+    case 11: return fp8_dot_c<11, MX, QX>(C, V);
+    case 12: return fp8_dot_c<12, MX, QX>(C, V);
+    case 13: return fp8_dot_c<13, MX, QX>(C, V);
+    case 14: return fp8_dot_c<14, MX, QX>(C, V);
+    case 15: return fp8_dot_c<15, MX, QX>(C, V);
+    case 16: return fp8_dot_c<16, MX, QX>(C, V);
     default: return nullptr;
     }
 }
@@ -428,18 +453,18 @@ Fp8MfmaLaunch fp8_mfma_mt(int MT, int NB, int D) {
 
 }  // namespace
 
-bool fp8_dot_quant_ok(int M, int V, int threads) {
-    if (M < 1 || M > kDotMaxM || fp8_dot_m<false, true>(M, V) == nullptr) return false;
-    return threads <= fp8_dot_max_threads(M, V, false, true);
+bool fp8_dot_quant_ok(int M, int C, int V, int threads) {
+    if (M < 1 || M > kDotMaxM || fp8_dot_m<false, true>(M, C, V) == nullptr) return false;
+    return threads <= fp8_dot_max_threads(M, C, V, false, true);
 }
 
 int launch_fp8(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets, int M, int N,
                int K, hipStream_t stream) {
     const bool mx = a.mode == SKG_FP8_MX32;
     if (p.kind == SKG_KIND_DOT) {
-        Fp8DotLaunch f = mx      ? fp8_dot_m<true, false>(M, p.depth)
-                         : a.qx ? fp8_dot_m<false, true>(M, p.depth)
-                                : fp8_dot_m<false, false>(M, p.depth);
+        Fp8DotLaunch f = mx      ? fp8_dot_m<true, false>(M, p.cols, p.depth)
+                         : a.qx ? fp8_dot_m<false, true>(M, p.cols, p.depth)
+                                : fp8_dot_m<false, false>(M, p.cols, p.depth);
         if (!f) return (int)hipErrorInvalidConfiguration;
         return f(p, a, N, K, stream);
     }

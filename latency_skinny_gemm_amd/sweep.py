@@ -74,7 +74,8 @@ def fp8_candidates(skg, M, N, K):
 
     if M <= 16:
         for T in DOT_THREADS:
-            add(skg.make_plan(skg.KIND_DOT, T, 1))
+            for C in (1, 2, 4):
+                add(skg.make_plan(skg.KIND_DOT, T, C))
     # LDS-ring tiles (K % 128 == 0)
     if K % 128 == 0 and (M > 4 or N >= 1024):
         for NB in (1, 2, 4, 8, 16):
@@ -356,7 +357,7 @@ def main():
     ap.add_argument("--points", default="headline",
                     choices=("headline", "router", "decode", "all", "fp8", "large_bf16", "large_fp8"))
     ap.add_argument("--M", type=int, nargs="*", help="restrict to these M")
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "sweep.jsonl"))
+    ap.add_argument("--out", default="sweep.jsonl", help="JSON-lines log the sweep appends to")
     ap.add_argument("--pool-mb", type=int, default=512)
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--emit-table", nargs="+", metavar="JSONL")

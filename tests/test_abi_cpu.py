@@ -259,7 +259,13 @@ def _check_fp8_coverage(p, M, N, K):
         T, V = p.threads, p.depth
         K16 = K // 16
         vecs = sorted(t + i * T for t in range(T) for i in range(V) if t + i * T < K16)
-        assert vecs == list(range(K16)) and p.grid == N and p.cols == 1
+        assert vecs == list(range(K16)) and p.cols in (1, 2, 4)
+        C = p.cols
+        assert p.grid == -(-N // C)
+        cols = [n for b in range(p.grid) for c in range(C) if (n := b * C + c) < N]
+        assert cols == list(range(N))
+        # the cross-wave sums for C * M outputs fit in one pass of the threads
+        assert C * M <= T
         return
     assert p.kind == skg.KIND_SPLITK
     S, NB, D, kc = p.splits, p.cols, p.depth, p.k_chunk
@@ -285,6 +291,26 @@ def _check_fp8_coverage(p, M, N, K):
                                 for kk in range(kk0, kk0 + 16):
                                     seen[kk] += 1
     assert seen == [1] * K
+
+
+@pytest.mark.parametrize("M,N,K,T,C", [
+    (1, 4096, 4096, 256, 2), (1, 4097, 4096, 256, 4), (16, 4096, 4096, 512, 4), (3, 5, 4112, 256, 4),
+    (8, 2, 7168, 1024, 2)])
+def test_fp8_dot_columns_cover(lib, M, N, K, T, C):
+    try:
+        q = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_DOT, T, C), skg.DTYPE_FP8)
+    except skg.SkinnyGemmError:
+        # only a register budget may refuse: one column fits where C does not
+        skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_DOT, min(T, 512), 1), skg.DTYPE_FP8)
+        return
+    _check_fp8_coverage(q, M, N, K)
+
+
+def test_fp8_dot_column_counts(lib):
+    with pytest.raises(skg.SkinnyGemmError):
+        skg.plan_complete(1, 4096, 4096, skg.make_plan(skg.KIND_DOT, 256, 3), skg.DTYPE_FP8)
+    q = skg.plan_complete(1, 4097, 4096, skg.make_plan(skg.KIND_DOT, 256, 4), skg.DTYPE_FP8)
+    assert q.grid == 1025 and q.cols == 4
 
 
 def test_fp8_straddling_K_covered(lib):

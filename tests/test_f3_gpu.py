@@ -139,13 +139,13 @@ def test_f32_output_small_integers_exact(skg, M, N, K):
 def _quant_plans(skg, M, N, K):
     plans = [("default", None)]
     if M <= 16:
-        for T in (256, 512, 1024):
-            p = skg.make_plan(skg.KIND_DOT, T, 1)
+        for T, C in ((256, 1), (512, 1), (1024, 1), (256, 2), (256, 4)):
+            p = skg.make_plan(skg.KIND_DOT, T, C)
             try:
                 skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
             except skg.SkinnyGemmError:
                 continue
-            plans.append((f"dot_t{T}", p))
+            plans.append((f"dot_t{T}_c{C}", p))
     mt = (M + 15) // 16
     for (T, NB, S, D, red) in ((256, 1, 4, 1, skg.REDUCE_KERNEL), (256, 2 if mt <= 3 else 1, 1, 1,
                                                                    skg.REDUCE_NONE)):

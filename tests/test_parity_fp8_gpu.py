@@ -31,14 +31,15 @@ def skg():
 def _plans(skg, M, N, K):
     plans = [("default", None)]
     if M <= 16:
-        for T in range(256, 1025, 64):
-            p = skg.make_plan(skg.KIND_DOT, T, 1)
-            try:
-                skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
-            except skg.SkinnyGemmError:
-                continue
-            plans.append((f"dot_t{T}", p))
-            break
+        for C in (1, 2, 4):
+            for T in range(256, 1025, 64):
+                p = skg.make_plan(skg.KIND_DOT, T, C)
+                try:
+                    skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
+                except skg.SkinnyGemmError:
+                    continue
+                plans.append((f"dot_t{T}_c{C}", p))
+                break
     mt = (M + 15) // 16
     nb = 2 if mt <= 3 else 1
     for (T, S, D, red) in ((256, 4, 1, skg.REDUCE_LAST), (128, 3, 2, skg.REDUCE_KERNEL),
@@ -110,7 +111,7 @@ def _small_int_e4m3(rows, K, seed, lo=-2, hi=2):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 4096), (5, 48, 4112), (16, 200, 2048), (37, 96, 1024),
-                                   (128, 64, 4096)])
+                                   (128, 64, 4096), (2, 7, 4096), (4, 1, 1024)])
 def test_fp8_per_tensor_integers_bitwise(skg, M, N, K):
     xq = _small_int_e4m3(M, K, M + K)
     wq = _small_int_e4m3(N, K, N + K + 1)
@@ -123,7 +124,8 @@ def test_fp8_per_tensor_integers_bitwise(skg, M, N, K):
         assert bad.size == 0, f"[{name}] {len(bad)} mismatches, first {tuple(bad[0])}"
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 64, 4096), (9, 80, 2048), (64, 48, 1024), (128, 32, 4096)])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 4096), (9, 80, 2048), (64, 48, 1024), (128, 32, 4096),
+                                   (3, 5, 2048)])
 def test_fp8_mx_exact_scales_bitwise(skg, M, N, K):
     # exponents 126..128 on both sides: every scaled block sum and every
     # fp32 partial sum stays exact, so the result is unique
