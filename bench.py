@@ -81,6 +81,10 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the dense decode section")
     ap.add_argument("--no-f3", action="store_true",
                     help="skip the fp32-output and fused-quantisation section")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="for rocprofv3 --pmc: the MFMA configurations (FP8 K = N = 4096 at "
+                         "M >= 64, bf16 K = 7168, N = 4096 at M >= 128), a few cold calls each, "
+                         "and exit")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for rocprofv3 --pmc: launch each headline call a few times on cold "
                          "weights, then a 64 MiB reference copy, and exit")
@@ -111,6 +115,69 @@ def pmc_probe(skg, torch, floors, stream, sptr, W, X, OUT, n_slots):
             raise RuntimeError(f"skinny_floor_copy failed: {rc}")
     stream.synchronize()
     print(json.dumps({"pmc_probe": "done", "calls_per_M": 8, "copy_bytes": COPY_BYTES}), flush=True)
+    return 0
+
+
+MFMA_PROBE_CALLS = 4
+
+
+def mfma_probe(skg, torch, stream, sptr):
+    """Eager launches for MFMA counter passes: MFMA_PROBE_CALLS cold calls
+    (each on its own W) of every configuration below, in the printed order;
+    all inputs are made before the first GEMM, so the library's dispatches
+    are exactly the printed calls (two each for plans with a reduction
+    kernel)."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    n = MFMA_PROBE_CALLS
+    K8 = N8 = 4096
+    W8 = torch.empty((2 * n, N8, K8), dtype=torch.float8_e4m3fn, device=dev)
+    for i in range(2 * n):
+        W8[i].copy_(torch.randn((N8, K8), generator=g, device=dev).to(torch.float8_e4m3fn))
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    WE = torch.randint(126, 129, (N8, K8 // 32), generator=g, device=dev).to(torch.uint8)
+    KB, NB = DECODE_K, 4096
+    WB = (torch.randn((n, NB, KB), generator=g, device=dev) * KB ** -0.5).to(torch.bfloat16)
+    fp8_m, bf16_m = (64, 128, 256, 512), (128, 256, 512)
+    X8 = {M: torch.randn((M, K8), generator=g, device=dev).to(torch.float8_e4m3fn) for M in fp8_m}
+    XE = {M: torch.randint(126, 129, (M, K8 // 32), generator=g, device=dev).to(torch.uint8)
+          for M in fp8_m}
+    XB = {M: torch.randn((M, KB), generator=g, device=dev).to(torch.bfloat16) for M in bf16_m}
+    out = torch.empty((512, 4096), dtype=torch.float32, device=dev)  # room for either dtype
+    torch.cuda.synchronize()
+    order = []
+    with torch.cuda.stream(stream):
+        slot = 0
+        for M in fp8_m:
+            for mode in ("tensor", "mx"):
+                sc = skg.Fp8Scales()
+                if mode == "tensor":
+                    sc.mode, sc.sx, sc.sw = skg.FP8_PER_TENSOR, one.data_ptr(), one.data_ptr()
+                else:
+                    sc.mode, sc.x_e8m0, sc.w_e8m0 = skg.FP8_MX32, XE[M].data_ptr(), WE.data_ptr()
+                p = skg.plan(M, N8, K8, skg.DTYPE_FP8)
+                for _ in range(n):
+                    rc = skg.lib().skinny_gemm_fp8(X8[M].data_ptr(), W8[slot].data_ptr(), None,
+                                                   ctypes.byref(sc), out.data_ptr(), M, N8, K8, sptr)
+                    if rc != 0:
+                        raise skg.SkinnyGemmError(rc, f"mfma probe fp8 M={M}")
+                    slot = (slot + 1) % (2 * n)
+                order.append({"config": f"fp8_{mode}_M{M}_N{N8}_K{K8}", "calls": n,
+                              "dispatches_per_call": 2 if p.reduce == skg.REDUCE_KERNEL else 1,
+                              "flops_per_call": 2 * M * N8 * K8})
+        for M in bf16_m:
+            p = skg.plan(M, NB, KB)
+            for i in range(n):
+                rc = skg.lib().skinny_gemm_bf16(XB[M].data_ptr(), WB[i].data_ptr(), None, None,
+                                                out.data_ptr(), M, NB, KB, sptr)
+                if rc != 0:
+                    raise skg.SkinnyGemmError(rc, f"mfma probe bf16 M={M}")
+            order.append({"config": f"bf16_M{M}_N{NB}_K{KB}", "calls": n,
+                          "dispatches_per_call": 2 if p.reduce == skg.REDUCE_KERNEL else 1,
+                          "flops_per_call": 2 * M * NB * KB})
+    stream.synchronize()
+    print(json.dumps({"mfma_probe": order}), flush=True)
     return 0
 
 
@@ -339,6 +406,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.mfma_probe:
+        st = torch.cuda.Stream()
+        return mfma_probe(skg, torch, st, ctypes.c_void_p(st.cuda_stream))
     floors = ctypes.CDLL(os.path.join(ROOT, "latency_skinny_gemm_amd", "libskinny_floors.so"))
     floors.skinny_floor_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     floors.skinny_floor_read.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
