@@ -7,6 +7,7 @@ reductions).  Random inputs must meet the elementwise bound
 partial sum is exact (small integers, one-hot, all-ones) must match the
 oracle bit for bit.
 """
+import ctypes
 import functools
 
 import numpy as np
@@ -225,6 +226,45 @@ def test_graph_replays_match_eager(skg):
         torch.cuda.synchronize()
         for e, o in zip(eager, outs):
             assert torch.equal(e.view(torch.int16), o.view(torch.int16))
+
+
+def test_capture_needs_reserved_workspace(skg):
+    # a split plan captured on a stream with no workspace is refused (no
+    # allocation or synchronisation inside a capture); once reserved, the
+    # same capture replays equal to the eager result
+    M, N, K = 16, 256, 7168
+    x, w, b = _dev(*gen.bf16_inputs(M, N, K, True, seed=123))
+    plan = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_SPLITK, 256, 1, 16, 4,
+                                                    skg.REDUCE_KERNEL))
+    skg.release_all()
+    stream = torch.cuda.Stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    out = torch.zeros(M, N, dtype=torch.bfloat16, device=DEV)
+    lib = skg.lib()
+
+    def call():
+        return lib.skinny_gemm_bf16_planned(x.data_ptr(), w.data_ptr(), b.data_ptr(),
+                                            out.data_ptr(), M, N, K, ctypes.byref(plan), sptr)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        rc = call()
+    assert rc == skg.ERR_WORKSPACE
+    del g
+    with torch.cuda.stream(stream):
+        skg.reserve(M, N, 16)
+        assert call() == skg.OK
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        rc = call()
+    assert rc == skg.OK
+    for _ in range(3):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
 
 
 def test_error_statuses_on_device(skg):
