@@ -26,6 +26,7 @@ Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu]
 import argparse
 import ctypes
 import json
+import statistics
 import os
 import sys
 import time
@@ -119,6 +120,17 @@ def pmc_probe(skg, torch, floors, stream, sptr, W, X, OUT, n_slots):
 
 
 MFMA_PROBE_CALLS = 4
+PER_M_REPLAYS = 11  # timed graph replays per M: median, p10, p90
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def mfma_probe(skg, torch, stream, sptr):
@@ -486,12 +498,29 @@ def main():
     value = step_bytes / (t_steps / args.steps) / 1e9
 
     # ---------------------------------------------------------------- per M
+    def replay_times(gr, reps):
+        """Seconds of each of `reps` timed replays (one warm-up replay first)."""
+        out = []
+        with torch.cuda.stream(stream):
+            gr.replay()
+            for _ in range(reps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                gr.replay()
+                e1.record(stream)
+                e1.synchronize()
+                out.append(e0.elapsed_time(e1) / 1e3)
+        return sorted(out)
+
     per_m = {}
     for M in M_VALUES:
         gr = capture(lambda M=M: [launch(s, M) for s in range(n_slots)])
-        t = time_graphs([gr], 3, 1)
-        us = t / (3 * n_slots) * 1e6
-        per_m[M] = {"us_per_call": round(us, 3), "GBps": round(call_bytes(M) / (us * 1e-6) / 1e9, 1),
+        ts = [t / n_slots * 1e6 for t in replay_times(gr, PER_M_REPLAYS)]
+        us = statistics.median(ts)
+        per_m[M] = {"us_per_call": round(us, 3), "p10_us": round(ts[len(ts) // 10], 3),
+                    "p90_us": round(ts[(9 * len(ts)) // 10], 3),
+                    "GBps": round(call_bytes(M) / (us * 1e-6) / 1e9, 1),
                     "kernel": kind_name[plans[M].kind], "plan": {k: v for k, v in plans[M].as_dict().items()
                                                                 if k in ("threads", "cols", "splits", "depth", "reduce", "grid")}}
         del gr
@@ -508,8 +537,22 @@ def main():
             floors.skinny_floor_read(ctypes.c_void_p(W[s].data_ptr()), N_DIM, K_DIM * 2, 256,
                                      ctypes.c_void_p(sink.data_ptr()), sptr)
 
-    t_empty = time_graphs([capture(floor_empty)], 3, 1) / (3 * n_slots) * 1e6
-    t_read = time_graphs([capture(floor_read)], 3, 1) / (3 * n_slots) * 1e6
+    t_empty = statistics.median(replay_times(capture(floor_empty), PER_M_REPLAYS)) / n_slots * 1e6
+    t_read = statistics.median(replay_times(capture(floor_read), PER_M_REPLAYS)) / n_slots * 1e6
+    for M in M_VALUES:  # context: the same bytes read by a plain stream at this size
+        per_m[M]["of_read_floor"] = round(t_read / per_m[M]["us_per_call"], 3)
+
+    # ---------------------------------------------------------------- determinism
+    # every plan twice on the same inputs: the outputs must agree bit for bit
+    det = torch.empty((2, Ms, N_DIM), dtype=torch.bfloat16, device=dev)
+    deterministic = True
+    for M in M_VALUES:
+        for r in range(2):
+            with torch.cuda.stream(stream):
+                launch(1, M)
+                det[r, :M].copy_(OUT[1, :M])
+            stream.synchronize()
+        deterministic &= bool(torch.equal(det[0, :M].view(torch.int16), det[1, :M].view(torch.int16)))
 
     # ---------------------------------------------------------------- roofline
     by_kind = {}
@@ -559,11 +602,22 @@ def main():
                         worst = f"M={M}: {msg}"
             reps += 1
         parity = worst
+        # one host thread: the median of 3 passes over M = 1..16
+        one = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            for M in M_VALUES:
+                oracle.gemm_bf16(xb[:M], wb, threads=1)
+            one.append(time.perf_counter() - t0)
+        step = sum(call_bytes(M) for M in M_VALUES)
         cpu = {"value": round(done_bytes / t_cpu / 1e9, 4), "unit": "GB/s",
                "cores": oracle.threads_used(threads), "kind": "oracle",
                "sample": f"{reps} pass(es) over M=1..16 at K=7168, N=256 (pool slot 0); "
-                         f"{t_cpu:.1f} s of oracle time; us/call at M=1: "
-                         f"{t_cpu / reps / len(M_VALUES) * 1e6:.0f} (mean over M)"}
+                         f"{t_cpu:.1f} s of oracle time; us/call: "
+                         f"{t_cpu / reps / len(M_VALUES) * 1e6:.0f} (mean over M)",
+               "single_thread_value": round(step / statistics.median(one) / 1e9, 4),
+               "single_thread_sample": "median of 3 passes over M=1..16, one thread",
+               "cpu_model": cpu_model()}
 
     fp8 = None if args.no_fp8 else fp8_section(skg, torch, stream, sptr)
     decode = None if args.no_decode else decode_section(skg, torch, stream, sptr)
@@ -590,6 +644,7 @@ def main():
         "decode_bf16_k7168": decode,
         "fp32_out_and_fused_quant": f3,
         "parity": parity,
+        "deterministic": deterministic,
     }
     print(json.dumps(line), flush=True)
     return 0
