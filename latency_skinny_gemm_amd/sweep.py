@@ -308,29 +308,37 @@ def _still_valid(skg, dt, M, N, K, b):
 
 def emit_table(files, out_path=TABLE):
     """Per (dtype, K, N, M), the fastest swept plan that the current planner
-    still accepts, over every record of the given sweep logs."""
+    still accepts, over every record of the given sweep logs.  A plan timed
+    in several logs is ranked by the median of its timings, so one lucky
+    run does not pick it."""
+    import statistics
+
     import latency_skinny_gemm_amd as skg
 
-    cands = {}
+    timings = {}
     for f in files:
         for line in open(f):
             r = json.loads(line)
             key = (r.get("dtype", "bf16"), r["K"], r["N"], r["M"])
             for c in r["candidates"]:
                 us, plan = (c[0], c[-1])
-                if key[0] == "fp8":
-                    us = sum(c[1].values())  # both scale modes, ranked by their sum
                 # TILED timings of earlier tiled kernels mean other plans
                 if plan["kind"] == 3 and r.get("tiled") != "ring2":
                     continue
-                cands.setdefault(key, []).append((us, plan, c))
+                # FP8: both scale modes, ranked by their sum; shown as the slower
+                rank, shown = (sum(c[1].values()), max(c[1].values())) if key[0] == "fp8" else (us, us)
+                ident = tuple(plan.get(f, 0) for f in ("kind", "threads", "cols", "splits", "depth",
+                                                          "waves_m", "reduce", "flags"))
+                slot = timings.setdefault(key, {}).setdefault(ident, (plan, [], []))
+                slot[1].append(rank)
+                slot[2].append(shown)
     best = {}
-    for key, lst in cands.items():
+    for key, plans in timings.items():
         dt, K, N, M = key
-        for us, plan, c in sorted(lst, key=lambda c: c[0]):
+        ranked = sorted(plans.values(), key=lambda v: statistics.median(v[1]))
+        for plan, ranks, shown in ranked:
             if _still_valid(skg, dt, M, N, K, plan):
-                shown = max(c[1].values()) if dt == "fp8" else us
-                best[key] = {"best_us": shown, "best": plan}
+                best[key] = {"best_us": statistics.median(shown), "best": plan}
                 break
     names = {0: "SKG_REDUCE_NONE", 1: "SKG_REDUCE_LAST", 2: "SKG_REDUCE_KERNEL"}
     kinds = {1: "SKG_KIND_DOT", 2: "SKG_KIND_SPLITK", 3: "SKG_KIND_TILED"}
