@@ -209,6 +209,28 @@ def test_fused_quant_equals_quant_then_gemm(skg, M):
         assert torch.equal(fused.cpu().view(torch.int16), two.cpu().view(torch.int16)), f"[{name}]"
 
 
+@pytest.mark.parametrize("M,N", [(1, 1021), (3, 6), (5, 1)])
+def test_fused_quant_ragged_columns(skg, M, N):
+    # several columns per workgroup with N not a multiple of them: the last
+    # workgroup's missing columns read zeros and store nothing
+    K = 2048
+    x = (torch.randn(M, K, generator=torch.Generator().manual_seed(N)) * 3).to(torch.bfloat16)
+    _, wq, _, sw = gen.fp8_inputs(M, N, K, "fp8_tensor", seed=N + 1)
+    bias = (torch.randn(N, generator=torch.Generator().manual_seed(2)) * 0.3).to(torch.bfloat16)
+    xd, wd, bd = x.to(DEV), wq.to(DEV), bias.to(DEV)
+    sxd, swd = _f32(0.02), sw.to(DEV)
+    for C in (2, 4):
+        plan = skg.make_plan(skg.KIND_DOT, 256, C)
+        out = torch.full((M + 2, N), -5.0, dtype=torch.bfloat16, device=DEV)
+        fused = skg.gemm_fp8_quant(xd, wd, sxd, swd, bias=bd, plan=plan, out=out[1:M + 1])
+        xq = skg.quant_e4m3(xd, sxd)
+        two = skg.gemm_fp8_planned(xq, wd, skg.make_plan(skg.KIND_DOT, 256, 1), sx=sxd, sw=swd, bias=bd)
+        torch.cuda.synchronize()
+        host = out.cpu()
+        assert torch.all(host[0] == -5.0) and torch.all(host[M + 1] == -5.0), f"C={C}: guard rows"
+        assert torch.equal(fused.cpu().view(torch.int16), two.cpu().view(torch.int16)), f"C={C}"
+
+
 @pytest.mark.parametrize("M,bias", [(1, False), (16, True), (64, False), (128, True)])
 def test_fused_quant_points_within_tolerance(skg, M, bias):
     N = K = 4096
