@@ -168,7 +168,7 @@ def mfma_probe(skg, torch, stream, sptr):
                     sc.mode, sc.sx, sc.sw = skg.FP8_PER_TENSOR, one.data_ptr(), one.data_ptr()
                 else:
                     sc.mode, sc.x_e8m0, sc.w_e8m0 = skg.FP8_MX32, XE[M].data_ptr(), WE.data_ptr()
-                p = skg.plan(M, N8, K8, skg.DTYPE_FP8)
+                p = skg.plan(M, N8, K8, skg.DTYPE_FP8 if mode == "tensor" else skg.DTYPE_FP8_MX)
                 for _ in range(n):
                     rc = skg.lib().skinny_gemm_fp8(X8[M].data_ptr(), W8[slot].data_ptr(), None,
                                                    ctypes.byref(sc), out.data_ptr(), M, N8, K8, sptr)
@@ -398,7 +398,8 @@ def fp8_section(skg, torch, stream, sptr):
             res[f"M{M}_{mode}"] = {"us_per_call": round(us, 3), "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                                    "TFLOPs": round(tflops, 1),
                                    "mfma_util": round(tflops / FP8_PEAK_TFLOPS, 4),
-                                   "kernel": {1: "dot", 2: "splitk", 3: "tiled"}[skg.plan(M, N, K, skg.DTYPE_FP8).kind]}
+                                   "kernel": {1: "dot", 2: "splitk", 3: "tiled"}[skg.plan(
+                                       M, N, K, skg.DTYPE_FP8 if mode == "tensor" else skg.DTYPE_FP8_MX).kind]}
         del X, O, XE, WE
     del W
     torch.cuda.empty_cache()

@@ -75,6 +75,12 @@ extern "C" {
 #define SKG_DTYPE_BF16 0
 #define SKG_DTYPE_FP8 1
 #define SKG_DTYPE_F32 2 /* output dtype only: fp32 logits */
+/* Planning dtype for FP8 with MX block scales (skinny_gemm_plan and
+ * skinny_gemm_plan_complete only): the same kernels and limits as
+ * SKG_DTYPE_FP8 with K % 32 == 0, but its own dispatch-table entries, since
+ * the two scale modes are fastest with different plans.  The GEMM entry
+ * points take the mode from skinny_fp8_scales. */
+#define SKG_DTYPE_FP8_MX 3
 
 #define SKG_FP8_PER_TENSOR 1
 #define SKG_FP8_MX32 2
@@ -155,8 +161,8 @@ int skinny_gemm_fp8(const void *x, const void *W, const void *bias,
                     const skinny_fp8_scales *scales, void *out, int M, int N, int K,
                     hipStream_t stream);
 
-/* FP8 GEMM with a caller-made plan (kinds SKG_KIND_DOT or SKG_KIND_SPLITK;
- * completed as by skinny_gemm_plan_complete with SKG_DTYPE_FP8). */
+/* FP8 GEMM with a caller-made plan (any kind; completed as by
+ * skinny_gemm_plan_complete with SKG_DTYPE_FP8). */
 int skinny_gemm_fp8_planned(const void *x, const void *W, const void *bias,
                             const skinny_fp8_scales *scales, void *out, int M, int N, int K,
                             const SkgPlan *plan, hipStream_t stream);
@@ -164,8 +170,10 @@ int skinny_gemm_fp8_planned(const void *x, const void *W, const void *bias,
 /* The dispatcher's decision for (M, N, K, dtype), written to *plan; no HIP
  * call.  The "vllm PR #48774" page's rule: a tuned (K, N) -> {M: config}
  * table first, else the default (dot product when M <= 4 or K < 2048, else
- * split-K).  Our table comes from a sweep on MI355X.  Returns SKG_OK, or the
- * error the GEMM call would return for these sizes. */
+ * split-K).  Our table comes from a sweep on MI355X.  dtype: SKG_DTYPE_BF16,
+ * SKG_DTYPE_FP8 (per-tensor scales) or SKG_DTYPE_FP8_MX (MX block scales;
+ * skinny_gemm_fp8 plans with it when given SKG_FP8_MX32).  Returns SKG_OK, or
+ * the error the GEMM call would return for these sizes. */
 int skinny_gemm_plan(int M, int N, int K, int dtype, SkgPlan *plan);
 
 /* Checks a caller-made plan for (M, N, K, dtype) and fills its derived

@@ -15,7 +15,7 @@ __all__ = ["SkgPlan", "SkinnyGemmError", "gemm_bf16", "gemm_bf16_planned", "gemm
            "gemm_fp8_planned", "plan", "plan_on",
            "plan_complete", "reserve", "release_all", "status_string", "library_path",
            "KIND_DOT", "KIND_SPLITK", "KIND_TILED", "REDUCE_NONE", "REDUCE_LAST", "REDUCE_KERNEL", "FLAG_DOT2", "FLAG_TILED_WIDE",
-           "DTYPE_BF16", "DTYPE_FP8", "DTYPE_F32", "gemm_bf16_f32", "gemm_fp8_quant",
+           "DTYPE_BF16", "DTYPE_FP8", "DTYPE_F32", "DTYPE_FP8_MX", "gemm_bf16_f32", "gemm_fp8_quant",
            "quant_e4m3"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +31,7 @@ ERR_HIP = -5
 DTYPE_BF16 = 0
 DTYPE_FP8 = 1
 DTYPE_F32 = 2  # output dtype only
+DTYPE_FP8_MX = 3  # planning only: FP8 with MX block scales (its own table entries)
 FP8_PER_TENSOR = 1
 FP8_MX32 = 2
 KIND_DOT = 1

@@ -295,7 +295,8 @@ extern "C" int skinny_gemm_fp8(const void *x, const void *W, const void *bias,
     rc = check_fp8(x, W, bias, scales, out, 0, 1, M, N, K);
     if (rc != SKG_OK) return rc;
     SkgPlan p;
-    rc = skinny_gemm_plan(M, N, K, SKG_DTYPE_FP8, &p);
+    rc = skinny_gemm_plan(M, N, K, scales->mode == SKG_FP8_MX32 ? SKG_DTYPE_FP8_MX : SKG_DTYPE_FP8,
+                          &p);
     if (rc != SKG_OK) return rc;
     return run_fp8(x, W, bias, scales, out, 0, false, M, N, K, p, stream);
 }

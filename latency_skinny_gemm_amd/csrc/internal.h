@@ -9,6 +9,10 @@
 
 namespace skg {
 
+// FP8 plans, per-tensor or MX scales: the same kernels and limits; the two
+// dtypes only key separate dispatch-table entries.
+constexpr bool is_fp8(int dtype) { return dtype == SKG_DTYPE_FP8 || dtype == SKG_DTYPE_FP8_MX; }
+
 // Limits of the kernels as built.
 constexpr int kMaxThreads = 1024;
 constexpr int kDotMaxM = 16;          // dot kernel is instantiated for M = 1..16

@@ -300,7 +300,8 @@ def _still_valid(skg, dt, M, N, K, b):
     p = skg.make_plan(b["kind"], b["threads"], b["cols"], b["splits"], b["depth"], b["reduce"],
                       flags=b["flags"], waves_m=b.get("waves_m", 0))
     try:
-        q = skg.plan_complete(M, N, K, p, skg.DTYPE_FP8 if dt == "fp8" else skg.DTYPE_BF16)
+        q = skg.plan_complete(M, N, K, p, {"fp8": skg.DTYPE_FP8, "fp8_mx": skg.DTYPE_FP8_MX}.get(
+            dt, skg.DTYPE_BF16))
     except skg.SkinnyGemmError:
         return False
     return (q.splits, q.depth, q.cols) == (b["splits"], b["depth"], b["cols"])
@@ -325,20 +326,20 @@ def emit_table(files, out_path=TABLE):
                 # TILED timings of earlier tiled kernels mean other plans
                 if plan["kind"] == 3 and r.get("tiled") != "ring2":
                     continue
-                # FP8: both scale modes, ranked by their sum; shown as the slower
-                rank, shown = (sum(c[1].values()), max(c[1].values())) if key[0] == "fp8" else (us, us)
                 ident = tuple(plan.get(f, 0) for f in ("kind", "threads", "cols", "splits", "depth",
                                                           "waves_m", "reduce", "flags"))
-                slot = timings.setdefault(key, {}).setdefault(ident, (plan, [], []))
-                slot[1].append(rank)
-                slot[2].append(shown)
+                # FP8: one entry per scale mode, each from that mode's timing
+                per_key = [(key, us)] if key[0] != "fp8" else \
+                    [(key, c[1]["tensor"]), (("fp8_mx",) + key[1:], c[1]["mx"])]
+                for k, t in per_key:
+                    timings.setdefault(k, {}).setdefault(ident, (plan, []))[1].append(t)
     best = {}
     for key, plans in timings.items():
         dt, K, N, M = key
         ranked = sorted(plans.values(), key=lambda v: statistics.median(v[1]))
-        for plan, ranks, shown in ranked:
+        for plan, ts in ranked:
             if _still_valid(skg, dt, M, N, K, plan):
-                best[key] = {"best_us": statistics.median(shown), "best": plan}
+                best[key] = {"best_us": statistics.median(ts), "best": plan}
                 break
     names = {0: "SKG_REDUCE_NONE", 1: "SKG_REDUCE_LAST", 2: "SKG_REDUCE_KERNEL"}
     kinds = {1: "SKG_KIND_DOT", 2: "SKG_KIND_SPLITK", 3: "SKG_KIND_TILED"}
@@ -347,7 +348,7 @@ def emit_table(files, out_path=TABLE):
         f"// from cold-weight graph-replay timings on one MI355X ({datetime.date.today()}).",
         "// {dtype, K, N, M, {kind, threads, cols, splits, depth, waves_m, reduce, flags}},  // us/call",
     ]
-    dtypes = {"bf16": "SKG_DTYPE_BF16", "fp8": "SKG_DTYPE_FP8"}
+    dtypes = {"bf16": "SKG_DTYPE_BF16", "fp8": "SKG_DTYPE_FP8", "fp8_mx": "SKG_DTYPE_FP8_MX"}
     for key in sorted(best):
         dt, K, N, M = key
         b = best[key]["best"]

@@ -174,12 +174,42 @@ def test_fp8_tiled_rejects(lib):
                                                          flags=skg.FLAG_TILED_WIDE), skg.DTYPE_FP8)
 
 
+def _fp8_dtype(p):
+    return skg.DTYPE_FP8_MX if p.dtype == "fp8_mx" else skg.DTYPE_FP8
+
+
 @pytest.mark.parametrize("p", FP8, ids=lambda p: p.key())
 def test_fp8_plans_valid_and_cover(lib, p):
-    q = skg.plan(p.M, p.N, p.K, skg.DTYPE_FP8)
-    again = skg.plan_complete(p.M, p.N, p.K, q, skg.DTYPE_FP8)
+    dt = _fp8_dtype(p)
+    q = skg.plan(p.M, p.N, p.K, dt)
+    again = skg.plan_complete(p.M, p.N, p.K, q, dt)
     assert (again.kind, again.grid, again.splits, again.k_chunk) == (q.kind, q.grid, q.splits, q.k_chunk)
     _check_fp8_coverage(q, p.M, p.N, p.K)
+    if p.group.startswith("fp8_"):  # the swept FP8 points: one table entry per scale mode
+        assert q.from_table == 1, p.key()
+
+
+def test_fp8_mx_planning_dtype(lib):
+    # the same kernels and limits as per-tensor FP8, K % 32 == 0, and its own
+    # table entries (at M = 16 the two modes are fastest with different kernels)
+    with pytest.raises(skg.SkinnyGemmError) as e:
+        skg.plan(4, 256, 4112, skg.DTYPE_FP8_MX)
+    assert e.value.status == skg.ERR_UNSUPPORTED
+    assert skg.plan(4, 256, 4112, skg.DTYPE_FP8).kind in (skg.KIND_DOT, skg.KIND_SPLITK)
+    for kind, T, NB, S, D in ((skg.KIND_DOT, 256, 1, 1, 0), (skg.KIND_SPLITK, 256, 1, 4, 2),
+                              (skg.KIND_TILED, 256, 4, 2, 3)):
+        a = skg.plan_complete(16, 4096, 4096, skg.make_plan(kind, T, NB, S, D, skg.REDUCE_KERNEL if S > 1
+                                                            else skg.REDUCE_NONE), skg.DTYPE_FP8)
+        b = skg.plan_complete(16, 4096, 4096, skg.make_plan(kind, T, NB, S, D, skg.REDUCE_KERNEL if S > 1
+                                                            else skg.REDUCE_NONE), skg.DTYPE_FP8_MX)
+        assert a.as_dict() == b.as_dict()
+    t = skg.plan(16, 4096, 4096, skg.DTYPE_FP8)
+    m = skg.plan(16, 4096, 4096, skg.DTYPE_FP8_MX)
+    assert t.from_table == m.from_table == 1
+    assert (t.kind, t.cols, t.splits) != (m.kind, m.cols, m.splits)
+    # off the table both fall back to the same rule
+    assert skg.plan(16, 4096, 2048, skg.DTYPE_FP8).as_dict() == \
+        skg.plan(16, 4096, 2048, skg.DTYPE_FP8_MX).as_dict()
 
 
 def _check_fp8_tiled_coverage(p, M, N, K):
