@@ -22,6 +22,7 @@
 //    zero codes and a zero exponent, which contribute exactly 0.
 #include "device_common.h"
 #include "internal.h"
+#include "lds_limit.h"
 #include "splitk_common.h"
 
 namespace skg {
@@ -287,9 +288,10 @@ template <int MT, int NB, int WM, int NS, int U, bool MX>
 int launch_fp8_tiled_t(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets, int M,
                        int N, int K, hipStream_t stream) {
     const size_t lds_bytes = fp8_tiled_lds_bytes(MT, NB, NS, U);
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&fp8_tiled_kernel<MT, NB, WM, NS, U, MX>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    static std::atomic<unsigned long long> lds_set{0};  // devices whose limit is set
+    const hipError_t attr = allow_dynamic_lds(
+        reinterpret_cast<const void *>(&fp8_tiled_kernel<MT, NB, WM, NS, U, MX>), lds_bytes,
+        lds_set);
     if (attr != hipSuccess) return (int)attr;
     hipLaunchKernelGGL((fp8_tiled_kernel<MT, NB, WM, NS, U, MX>), dim3(p.grid), dim3(256),
                        lds_bytes, stream, (const uint8_t *)a.x, (const uint8_t *)a.W,

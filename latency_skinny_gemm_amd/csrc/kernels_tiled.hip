@@ -30,6 +30,7 @@
 //  * K splits (S > 1) reuse the ordered reductions of the split-K kernel.
 #include "device_common.h"
 #include "internal.h"
+#include "lds_limit.h"
 #include "splitk_common.h"
 
 namespace skg {
@@ -272,10 +273,10 @@ int launch_tiled_t(const SkgPlan &p, const void *x, const void *W, const void *b
                    int out_f32, float *ws, unsigned *tickets, int M, int N, int K,
                    hipStream_t stream) {
     const size_t lds_bytes = tiled_lds_bytes(MT, NB, NS, U);
-    // rings above 64 KB: allow the kernel that much dynamic LDS (once)
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&tiled_kernel<MT, NB, WM, NS, U>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    // rings above 64 KB: allow the kernel that much dynamic LDS (once per device)
+    static std::atomic<unsigned long long> lds_set{0};
+    const hipError_t attr = allow_dynamic_lds(
+        reinterpret_cast<const void *>(&tiled_kernel<MT, NB, WM, NS, U>), lds_bytes, lds_set);
     if (attr != hipSuccess) return (int)attr;
     hipLaunchKernelGGL((tiled_kernel<MT, NB, WM, NS, U>), dim3(p.grid), dim3(256), lds_bytes,
                        stream, (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)bias,
