@@ -127,7 +127,7 @@ typedef struct skinny_fp8_scales {
 typedef struct SkgPlan {
     int kind;     /* SKG_KIND_DOT, SKG_KIND_SPLITK or SKG_KIND_TILED */
     int threads;  /* workgroup size, a multiple of 64, <= 1024 (TILED: 256) */
-    int cols;     /* DOT: output columns per workgroup (bf16: 1, 2; FP8: 1, 2, 4);
+    int cols;     /* DOT: output columns per workgroup (bf16: 1-4; FP8: 1, 2, 4);
                      SPLITK: 16-column blocks per workgroup (1, 2, 4);
                      TILED: 16-column blocks per workgroup (1, 2, 4, 8, 16) */
     int splits;   /* SPLITK, TILED: number of K chunks S (>= 1); DOT: 1 */

@@ -135,6 +135,8 @@ template <int M>
 DotLaunch pick_c(int C, int V, bool dot2) {
     if (C == 1) return dot2 ? pick_v<M, 1, true>(V) : pick_v<M, 1, false>(V);
     if (C == 2) return dot2 ? pick_v<M, 2, true>(V) : pick_v<M, 2, false>(V);
+    if (C == 3) return dot2 ? pick_v<M, 3, true>(V) : pick_v<M, 3, false>(V);
+    if (C == 4) return dot2 ? pick_v<M, 4, true>(V) : pick_v<M, 4, false>(V);
     return nullptr;
 }
 

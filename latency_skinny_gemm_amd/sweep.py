@@ -27,6 +27,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 TABLE = os.path.join(HERE, "csrc", "dispatch_table.inc")
 
+KIND_NAMES = {"dot": 1, "splitk": 2, "tiled": 3}
 DOT_THREADS = (64, 128, 192, 256, 320, 384, 448, 512, 640, 768, 896, 1024)
 SPLITS = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64)
 
@@ -190,7 +191,7 @@ def candidates(skg, M, N, K):
 
     if M <= 16:
         for flags in (0, skg.FLAG_DOT2):
-            for cols in (1, 2):
+            for cols in (1, 2, 3, 4):
                 for T in DOT_THREADS:
                     add(skg.make_plan(skg.KIND_DOT, T, cols, flags=flags))
     ksteps = -(-K // 32)
@@ -231,7 +232,7 @@ def plan_dict(p):
                                        "reduce", "flags", "k_chunk", "grid")}
 
 
-def sweep_point(skg, torch, M, N, K, pool_bytes, reps, stream, log):
+def sweep_point(skg, torch, M, N, K, pool_bytes, reps, stream, log, kinds=None):
     dev = torch.device("cuda:0")
     slots = max(4, -(-pool_bytes // (N * K * 2)))
     g = torch.Generator(device=dev)
@@ -243,6 +244,9 @@ def sweep_point(skg, torch, M, N, K, pool_bytes, reps, stream, log):
     L = skg.lib()
     results = []
     for p in candidates(skg, M, N, K):
+        if kinds and p.kind not in kinds:
+            continue
+
         def calls(p=p):
             for s in range(slots):
                 rc = L.skinny_gemm_bf16_planned(X[s].data_ptr(), W[s].data_ptr(), None,
@@ -268,6 +272,8 @@ def sweep_point(skg, torch, M, N, K, pool_bytes, reps, stream, log):
         del gr
         times.sort()
         results.append((times[len(times) // 2], p))
+    if not results:
+        return None
     results.sort(key=lambda r: r[0])
     best_us, best = results[0]
     rec = {"M": M, "N": N, "K": K, "slots": slots, "tiled": "ring2", "best_us": round(best_us, 3),
@@ -296,8 +302,11 @@ def run(args):
     t0 = time.time()
     with open(args.out, "a") as log:
         for (M, N, K) in pts:
-            fn = sweep_point_fp8 if args.points in ("fp8", "large_fp8") else sweep_point
-            fn(skg, torch, M, N, K, args.pool_mb << 20, args.reps, stream, log)
+            if args.points in ("fp8", "large_fp8"):
+                sweep_point_fp8(skg, torch, M, N, K, args.pool_mb << 20, args.reps, stream, log)
+            else:
+                sweep_point(skg, torch, M, N, K, args.pool_mb << 20, args.reps, stream, log,
+                            kinds={KIND_NAMES[k] for k in args.kinds} if args.kinds else None)
             torch.cuda.empty_cache()
     print(f"swept {len(pts)} points in {time.time() - t0:.0f} s", flush=True)
 
@@ -379,6 +388,9 @@ def main():
     ap.add_argument("--pool-mb", type=int, default=512)
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--emit-table", nargs="+", metavar="JSONL")
+    ap.add_argument("--kinds", nargs="*", choices=sorted(KIND_NAMES),
+                    help="bf16 points: time only these kernel kinds (the table ranks each plan "
+                         "over every log, so a partial sweep adds to earlier ones)")
     args = ap.parse_args()
     if args.emit_table:
         emit_table(args.emit_table)

@@ -414,7 +414,7 @@ def test_table_entries_are_exact_and_valid(lib):
     (dict(kind=9, threads=256), 4, 256, 2048),
     (dict(kind=skg.KIND_DOT, threads=100), 4, 256, 2048),
     (dict(kind=skg.KIND_DOT, threads=2048), 4, 256, 2048),
-    (dict(kind=skg.KIND_DOT, threads=256, cols=3), 4, 256, 2048),
+    (dict(kind=skg.KIND_DOT, threads=256, cols=5), 4, 256, 2048),
     (dict(kind=skg.KIND_DOT, threads=64), 4, 256, 7168),        # > 8 vectors a thread
     (dict(kind=skg.KIND_DOT, threads=256), 17, 256, 2048),      # DOT is built for M <= 16
     (dict(kind=skg.KIND_DOT, threads=1024), 16, 256, 7168),     # registers at 1024 threads
