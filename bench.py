@@ -45,27 +45,37 @@ def call_bytes(M, N=N_DIM, K=K_DIM):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dot_bf16_router_k7168_n256_traffic.md")
-KERNEL_SOURCES = ("kernels_dot.hip", "kernels_splitk.hip", "device_common.h", "dispatch_table.inc")
+KERNEL_SOURCES = ("kernels_dot.hip", "kernels_splitk.hip", "splitk_common.h", "device_common.h")
+ROUTER_TABLE_KEY = "SKG_DTYPE_BF16, 7168, 256,"  # the table rows of the router workload
+
+
+def router_sources_sha256():
+    """SHA-256 of what the router workload runs: the kernel sources and the
+    dispatch-table rows of (bf16, K = 7168, N = 256)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "latency_skinny_gemm_amd", "csrc")
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(csrc, "dispatch_table.inc")) as fh:
+        h.update("".join(l for l in fh if ROUTER_TABLE_KEY in l).encode())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 --pmc
     summary (FETCH_SIZE and WRITE_SIZE scaled by a plain copy), or None when
     there is none or the kernel sources changed since it was taken."""
-    import hashlib
-
     if kernel != "dot" or not os.path.exists(TRAFFIC_FILE):
         return None
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "latency_skinny_gemm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
     fields = {}
     for line in open(TRAFFIC_FILE):
         if " = " in line:
             k, v = line.strip().split(" = ", 1)
             fields[k] = v
-    if fields.get("kernel_sources_sha256") != h.hexdigest():
+    if fields.get("kernel_sources_sha256") != router_sources_sha256():
         return None
     return float(fields["traffic_bytes_per_launch_dot"])
 

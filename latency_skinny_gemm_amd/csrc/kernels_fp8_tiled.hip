@@ -229,8 +229,13 @@ __global__ void __launch_bounds__(256)
         // nstages is the same for every wave: every wave reaches every barrier
         wait_vmcnt_lds<(NS - 2) * BPW>();
         barrier_nofence();
-        compute(st % NS);
+        // The refill goes to the slot consumed in the previous iteration:
+        // every wave's reads of it returned (lgkmcnt(0)) before the barrier,
+        // so it is issued before this stage's MFMAs and NS - 1 stages stay
+        // in flight while they run.  The wait above still counts NS - 2
+        // stages issued after the one it waits for.
         issue((st + NS - 1) % NS, st + NS - 1);
+        compute(st % NS);
     }
     wait_vmcnt_lds<0>();  // no load to LDS outlives the loop
 

@@ -17,8 +17,9 @@
 //    a block reads row p%16, bytes 16*(p/16)..+16 of the step, so the block
 //    lands in LDS exactly in v_mfma_f32_16x16x32_bf16 operand order and
 //    every fragment read is one linear, conflict-free ds_read_b128;
-//  * a stage holds U steps; NS stages form a ring.  Stage i+NS-1 is issued
-//    right after stage i is consumed, so NS-1 stages are in flight while
+//  * a stage holds U steps; NS stages form a ring.  Stage i+NS-1 goes into
+//    the slot of stage i-1 as soon as every wave has read that slot (the
+//    barrier before stage i's MFMAs), so NS-1 stages are in flight while
 //    one is multiplied.  Each wave waits for its own loads of the stage with
 //    s_waitcnt vmcnt (the count of its loads issued after them is fixed at
 //    compile time) and for its own LDS reads, then one s_barrier makes every
@@ -213,8 +214,13 @@ __global__ void __launch_bounds__(256)
         // nstages is the same for every wave: every wave reaches every barrier
         wait_vmcnt_lds<(NS - 2) * BPW>();
         barrier_nofence();
-        compute(st % NS);
+        // The refill goes to the slot consumed in the previous iteration:
+        // every wave's reads of it returned (lgkmcnt(0)) before the barrier,
+        // so it is issued before this stage's MFMAs and NS - 1 stages stay
+        // in flight while they run.  The wait above still counts NS - 2
+        // stages issued after the one it waits for.
         issue((st + NS - 1) % NS, st + NS - 1);
+        compute(st % NS);
     }
     wait_vmcnt_lds<0>();  // no load to LDS outlives the loop
 
