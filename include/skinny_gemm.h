@@ -132,7 +132,7 @@ typedef struct SkgPlan {
                      TILED: 16-column blocks per workgroup (1, 2, 4, 8, 16) */
     int splits;   /* SPLITK, TILED: number of K chunks S (>= 1); DOT: 1 */
     int depth;    /* SPLITK: 32-wide K steps a wave keeps in flight (1, 2, 4, 8);
-                     TILED: stages of the LDS ring (2, 3, 4, 6, 8);
+                     TILED: stages of the LDS ring (2, 3, 4, 5, 6, 8);
                      DOT: 16-byte vectors per thread per column (derived) */
     int waves_m;  /* TILED: waves along M (1, 2, 4; the other 4/waves_m waves
                      split the columns); 0 = chosen by the library */

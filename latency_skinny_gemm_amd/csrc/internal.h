@@ -62,8 +62,10 @@ constexpr int kTiledThreads = 256;
 constexpr int kTiledMaxRows = 128;  // rows per workgroup (MT <= 8); more M: row blocks
 // Row blocks of MT*16 rows that cover M (1 unless M > 128).
 constexpr int tiled_row_blocks(int M, int MT) { return (M + MT * 16 - 1) / (MT * 16); }
-constexpr int kTiledMaxLds = 144 * 1024;
-constexpr int kTiledStages[] = {2, 3, 4, 6, 8};
+// gfx950 gives a workgroup up to 160 KB of LDS; the tiled kernels keep 256
+// bytes of it for their static variables.
+constexpr int kTiledMaxLds = 160 * 1024 - 256;
+constexpr int kTiledStages[] = {2, 3, 4, 5, 6, 8};
 constexpr size_t tiled_lds_bytes(int MT, int NB, int NS, int U) {
     return (size_t)NS * U * (MT + NB) * 1024 + 1024;
 }

@@ -319,6 +319,7 @@ Fp8TiledLaunch pick_ns(int NS) {
     case 2: return fp8_tiled_entry<MT, NB, WM, 2, U, MX>();
     case 3: return fp8_tiled_entry<MT, NB, WM, 3, U, MX>();
     case 4: return fp8_tiled_entry<MT, NB, WM, 4, U, MX>();
+    case 5: return fp8_tiled_entry<MT, NB, WM, 5, U, MX>();
     case 6: return fp8_tiled_entry<MT, NB, WM, 6, U, MX>();
     case 8: return fp8_tiled_entry<MT, NB, WM, 8, U, MX>();
     default: return nullptr;

@@ -305,6 +305,7 @@ TiledLaunch pick_ns(int NS) {
     case 2: return tiled_entry<MT, NB, WM, 2, U>();
     case 3: return tiled_entry<MT, NB, WM, 3, U>();
     case 4: return tiled_entry<MT, NB, WM, 4, U>();
+    case 5: return tiled_entry<MT, NB, WM, 5, U>();
     case 6: return tiled_entry<MT, NB, WM, 6, U>();
     case 8: return tiled_entry<MT, NB, WM, 8, U>();
     default: return nullptr;

@@ -85,8 +85,9 @@ def fp8_candidates(skg, M, N, K):
                 if S > K // 128 or not (64 <= groups * S <= 2048):
                     continue
                 for wm in (1, 2, 4):
-                    for ns, flags in ((2, 0), (3, 0), (4, 0), (6, 0), (2, skg.FLAG_TILED_WIDE),
-                                      (3, skg.FLAG_TILED_WIDE)):
+                    for ns, flags in ((2, 0), (3, 0), (4, 0), (5, 0), (6, 0), (8, 0),
+                                      (2, skg.FLAG_TILED_WIDE), (3, skg.FLAG_TILED_WIDE),
+                                      (4, skg.FLAG_TILED_WIDE), (5, skg.FLAG_TILED_WIDE)):
                         for red in _tiled_reductions(skg, S):
                             add(skg.make_plan(skg.KIND_TILED, 256, NB, S, ns, red, flags=flags,
                                               waves_m=wm))
@@ -219,8 +220,10 @@ def candidates(skg, M, N, K):
                 if S > ksteps or not (64 <= groups * S <= 2048):
                     continue
                 for wm in (1, 2, 4):
-                    for ns, flags in ((2, 0), (3, 0), (4, 0), (6, 0), (2, skg.FLAG_TILED_WIDE),
-                                      (3, skg.FLAG_TILED_WIDE), (4, skg.FLAG_TILED_WIDE)):
+                    for ns, flags in ((2, 0), (3, 0), (4, 0), (5, 0), (6, 0), (8, 0),
+                                      (2, skg.FLAG_TILED_WIDE), (3, skg.FLAG_TILED_WIDE),
+                                      (4, skg.FLAG_TILED_WIDE), (5, skg.FLAG_TILED_WIDE),
+                                      (6, skg.FLAG_TILED_WIDE)):
                         for red in _tiled_reductions(skg, S):
                             add(skg.make_plan(skg.KIND_TILED, 256, NB, S, ns, red, flags=flags,
                                               waves_m=wm))

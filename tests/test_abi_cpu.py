@@ -603,7 +603,7 @@ def test_tiled_plans_cover(lib, M, N, K, NB, wm, NS, U, S):
 
 
 def test_tiled_rejects_bad_plans(lib):
-    for plan in (dict(threads=128, cols=4), dict(threads=256, cols=3), dict(threads=256, cols=4, depth=5),
+    for plan in (dict(threads=128, cols=4), dict(threads=256, cols=3), dict(threads=256, cols=4, depth=7),
                  dict(threads=256, cols=4, depth=1), dict(threads=256, cols=4, waves_m=3),
                  dict(threads=256, cols=2, waves_m=1), dict(threads=256, cols=4, flags=1),
                  dict(threads=256, cols=16, depth=8, flags=2)):

@@ -54,7 +54,9 @@ def _plans(skg, M, N, K):
     for (NBt, S, NS, fl, red, wm) in ((8, 4, 3, 0, skg.REDUCE_KERNEL, 0),
                                       (4, 2, 2, wide, skg.REDUCE_LAST, 0),
                                       (2, 1, 4, 0, skg.REDUCE_NONE, 4),
-                                      (16, 8, 2, 0, skg.REDUCE_KERNEL, 1)):
+                                      (16, 8, 2, 0, skg.REDUCE_KERNEL, 1),
+                                      (2, 3, 5, 0, skg.REDUCE_KERNEL, 0),
+                                      (4, 2, 5, wide, skg.REDUCE_KERNEL, 2)):
         p = skg.make_plan(skg.KIND_TILED, 256, NBt, S, NS, red, flags=fl, waves_m=wm)
         try:
             skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)

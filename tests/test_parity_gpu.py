@@ -74,7 +74,9 @@ def _kernel_plans(skg, M, N, K):
                                       (4, 1, 4, 0, skg.REDUCE_NONE, 4),
                                       (2, 7, 2, wide, skg.REDUCE_LAST, 0),
                                       (8, 8, 4, 0, skg.REDUCE_KERNEL, 1),
-                                      (16, 16, 4, 0, skg.REDUCE_KERNEL, 0)):
+                                      (16, 16, 4, 0, skg.REDUCE_KERNEL, 0),
+                                      (4, 3, 5, wide, skg.REDUCE_KERNEL, 0),
+                                      (2, 2, 6, wide, skg.REDUCE_KERNEL, 2)):
         p = skg.make_plan(skg.KIND_TILED, 256, cols=nbt, splits=S, depth=ns, reduce=red,
                           flags=fl, waves_m=wm)
         try:
