@@ -95,10 +95,9 @@ __global__ void __launch_bounds__(256)
     const int wm = wave / WN;
     const int wn = wave % WN;
     // workgroup (mb, j, s): row block mb of MT*16 rows (M > 128 only),
-    // column group j, K chunk s; mb fastest, then s
-    const int mb = blockIdx.x % MB;
-    const int s = (blockIdx.x / MB) % S;
-    const int j = blockIdx.x / MB / S;
+    // column group j, K chunk s
+    const TiledPos pos_ = tiled_position(blockIdx.x, MB, S, gridDim.x / MB);
+    const int mb = pos_.mb, s = pos_.s, j = pos_.j;
     const int row0 = mb * MT * 16;
     const int Mb = min(MT * 16, M - row0);  // rows of this block
     const int col0 = j * NB * 16;

@@ -7,6 +7,28 @@
 
 namespace skg {
 
+// Grid position of a tiled workgroup b: row block mb (M > 128 only), K chunk
+// s and column group j, in a grid of MB * G workgroups (G = S * column
+// groups).  Where G is a multiple of 8 the MB row blocks of one (s, j) take
+// workgroup ids 8 apart, so they run on one XCD (workgroup i runs on XCD
+// i % 8) and that XCD's L2 fetches their shared W tile once; otherwise mb
+// is fastest.  s is fastest among the (s, j) pairs in both cases.
+struct TiledPos {
+    int mb, s, j;
+};
+__device__ __forceinline__ TiledPos tiled_position(int b, int MB, int S, int G) {
+    int mb, sj;
+    if (MB > 1 && G % 8 == 0) {
+        const int q = b / (8 * MB), r = b % (8 * MB);
+        mb = r / 8;
+        sj = q * 8 + r % 8;
+    } else {
+        mb = b % MB;
+        sj = b / MB;
+    }
+    return TiledPos{mb, sj % S, sj / S};
+}
+
 // Called by every thread of a workgroup that has just written its fp32
 // partial ws[s][m][n] for the columns [col0, col0 + ncols) of tile j.
 // Every wave waits until its partial stores are in the L2; then one

@@ -212,6 +212,16 @@ def test_fp8_mx_planning_dtype(lib):
         skg.plan(16, 4096, 2048, skg.DTYPE_FP8_MX).as_dict()
 
 
+def _tiled_position(b, MB, S, G):
+    """The tiled kernels' workgroup -> (row block, K chunk, column group)."""
+    if MB > 1 and G % 8 == 0:
+        q, r = divmod(b, 8 * MB)
+        mb, sj = r // 8, q * 8 + r % 8
+    else:
+        mb, sj = b % MB, b // MB
+    return mb, sj % S, sj // S
+
+
 def _check_fp8_tiled_coverage(p, M, N, K):
     S, NB, NS, kc, WM = p.splits, p.cols, p.depth, p.k_chunk, p.waves_m
     U = 2 if p.flags & skg.FLAG_TILED_WIDE else 1
@@ -223,6 +233,8 @@ def _check_fp8_tiled_coverage(p, M, N, K):
     MB = -(-M // (MT * 16))
     assert MB == 1 or (MT == 8 and p.reduce != skg.REDUCE_LAST)
     assert p.grid == MB * groups * S
+    dec = [_tiled_position(b, MB, S, p.grid // MB) for b in range(p.grid)]
+    assert sorted(dec) == sorted((mb, s, j) for mb in range(MB) for s in range(S) for j in range(groups))
     CPR = 8 * U
 
     def swz(r):
@@ -501,9 +513,15 @@ def _check_tiled_coverage(p, M, N, K):
     MB = -(-M // (MT * 16))   # row blocks (only above 128 rows)
     assert MB == 1 or (MT == 8 and p.reduce != skg.REDUCE_LAST)
     assert p.grid == MB * groups * S and kc % 32 == 0 and (S - 1) * kc < K <= S * kc
-    # the grid's (mb, j, s) decode: mb fastest, then s, then j
-    dec = sorted((b % MB, (b // MB) % S, b // MB // S) for b in range(p.grid))
-    assert dec == sorted((mb, s, j) for mb in range(MB) for s in range(S) for j in range(groups))
+    # the grid's (mb, s, j) decode, and the row blocks of one (s, j) on one
+    # XCD (ids 8 apart) whenever the (s, j) pairs come in whole groups of 8
+    dec = [_tiled_position(b, MB, S, p.grid // MB) for b in range(p.grid)]
+    assert sorted(dec) == sorted((mb, s, j) for mb in range(MB) for s in range(S) for j in range(groups))
+    if (p.grid // MB) % 8 == 0:
+        xcd = {}
+        for b, (mb, s, j) in enumerate(dec):
+            xcd.setdefault((s, j), set()).add(b % 8)
+        assert all(len(v) == 1 for v in xcd.values())
     rows = sorted(mb * MT * 16 + r for mb in range(MB) for r in range(min(MT * 16, M - mb * MT * 16)))
     assert rows == list(range(M))
     # waves partition the workgroup's (m-tile, column-block) grid
