@@ -16,7 +16,6 @@ constexpr bool is_fp8(int dtype) { return dtype == SKG_DTYPE_FP8 || dtype == SKG
 // Limits of the kernels as built.
 constexpr int kMaxThreads = 1024;
 constexpr int kDotMaxM = 16;          // dot kernel is instantiated for M = 1..16
-constexpr int kSplitKMaxThreads = 512;
 constexpr int kSplitKMaxLdsFloats = 16384;  // 64 KB of LDS for the wave reduction
 constexpr int kMaxSplits = 256;
 constexpr int kNumCusMI355X = 256;
@@ -41,10 +40,11 @@ constexpr int dot_max_threads(int M, int C, int V, bool dot2) {
 
 // SPLITK per-lane registers: two stages of D steps of (NB + MT) vectors and
 // NB*MT accumulators of 4 (those may live in AGPRs).  Above 224 the kernel
-// is bounded to 256 threads (one wave per SIMD), else 512.
+// is bounded to 256 threads (one wave per SIMD); up to 96 it may run 1024
+// (16 waves: four per SIMD at 128 VGPRs), else 512.
 constexpr int splitk_regs(int MT, int NB, int D) { return 2 * D * (NB + MT) * 4 + NB * MT * 4; }
 constexpr int splitk_max_threads(int MT, int NB, int D) {
-    return splitk_regs(MT, NB, D) > 224 ? 256 : kSplitKMaxThreads;
+    return splitk_regs(MT, NB, D) > 224 ? 256 : splitk_regs(MT, NB, D) <= 96 ? 1024 : 512;
 }
 constexpr bool splitk_built(int MT, int NB, int D) { return NB * MT <= 32 && D * (NB + MT) <= 40; }
 
@@ -110,7 +110,7 @@ constexpr int fp8_mfma_regs(int MT, int NB, int D) { return 2 * D * (NB + MT) * 
 // the data and, measured on the compiler's resource report, need the full
 // 512 registers of one wave per SIMD: they are bounded to 256 threads.
 constexpr int fp8_mfma_max_threads(int MT, int NB, int D, bool mx) {
-    return (mx || fp8_mfma_regs(MT, NB, D) > 224) ? 256 : kSplitKMaxThreads;
+    return (mx || fp8_mfma_regs(MT, NB, D) > 224) ? 256 : 512;
 }
 constexpr bool fp8_mfma_built(int MT, int NB, int D) {
     return NB * MT <= 32 && D * (NB + MT) <= 14;  // MX spills beyond (resource report)

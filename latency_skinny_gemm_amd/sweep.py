@@ -205,7 +205,7 @@ def candidates(skg, M, N, K):
             if S > ksteps or groups * S > 8192:
                 continue
             sps = -(-ksteps // S)
-            for nw in (1, 2, 4, 8):
+            for nw in (1, 2, 4, 8, 16):
                 spw = -(-sps // nw)
                 D = next((d for d in (1, 2, 4, 8) if d >= spw), 8)
                 for d in sorted({D, max(1, D // 2)}):

@@ -68,6 +68,13 @@ def _kernel_plans(skg, M, N, K):
                                                  depth=1, reduce=skg.REDUCE_KERNEL)))
     plans.append(("splitk_s1", skg.make_plan(skg.KIND_SPLITK, threads, cols=nb, splits=1,
                                              depth=4 if nb * mt <= 8 else 2)))
+    for (S, D, red) in ((1, 4, skg.REDUCE_NONE), (3, 2, skg.REDUCE_KERNEL)):  # 16 waves
+        p = skg.make_plan(skg.KIND_SPLITK, 1024, cols=1, splits=S, depth=D, reduce=red)
+        try:
+            skg.plan_complete(M, N, K, p)
+        except skg.SkinnyGemmError:
+            continue
+        plans.append((f"splitk_t1024_s{S}", p))
     wide = skg.FLAG_TILED_WIDE
     for (nbt, S, ns, fl, red, wm) in ((16, 4, 3, 0, skg.REDUCE_LAST, 0),
                                       (8, 3, 2, wide, skg.REDUCE_KERNEL, 0),
