@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -57,6 +58,16 @@ std::mutex g_mu;
 std::vector<Workspace> g_ws;
 std::vector<void *> g_retired;  // replaced buffers, freed by release_all
 
+// Calls find their workspace without the lock through a per-thread copy of
+// the last one they used, valid while no workspace has been replaced or
+// freed since: every such change bumps the generation (under the lock).
+std::atomic<unsigned> g_generation{1};
+struct WorkspaceCache {
+    unsigned generation;
+    Workspace w;
+};
+thread_local WorkspaceCache t_cache{0, Workspace{-1, nullptr, nullptr, 0, nullptr, 0}};
+
 int grow(Workspace &w, size_t floats, size_t tickets) {
     if (floats > w.ws_floats) {
         float *p = nullptr;
@@ -64,6 +75,7 @@ int grow(Workspace &w, size_t floats, size_t tickets) {
         if (w.ws) g_retired.push_back(w.ws);
         w.ws = p;
         w.ws_floats = floats;
+        g_generation.fetch_add(1, std::memory_order_acq_rel);
     }
     if (tickets > w.n_tickets) {
         unsigned *t = nullptr;
@@ -72,6 +84,7 @@ int grow(Workspace &w, size_t floats, size_t tickets) {
         if (w.tickets) g_retired.push_back(w.tickets);
         w.tickets = t;
         w.n_tickets = tickets;
+        g_generation.fetch_add(1, std::memory_order_acq_rel);
     }
     return SKG_OK;
 }
@@ -87,6 +100,13 @@ Workspace *find(int device, hipStream_t stream) {
 int acquire(hipStream_t stream, size_t floats, size_t tickets, float **ws, unsigned **tk) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SKG_ERR_HIP;
+    const Workspace &c = t_cache.w;  // fast path: no lock
+    if (t_cache.generation == g_generation.load(std::memory_order_acquire) && c.device == dev &&
+        c.stream == stream && c.ws_floats >= floats && c.n_tickets >= tickets) {
+        *ws = c.ws;
+        *tk = c.tickets;
+        return SKG_OK;
+    }
     std::lock_guard<std::mutex> lock(g_mu);
     Workspace *w = find(dev, stream);
     if (!w || w->ws_floats < floats || w->n_tickets < tickets) {
@@ -104,6 +124,7 @@ int acquire(hipStream_t stream, size_t floats, size_t tickets, float **ws, unsig
     }
     *ws = w->ws;
     *tk = w->tickets;
+    t_cache = WorkspaceCache{g_generation.load(std::memory_order_acquire), *w};
     return SKG_OK;
 }
 
@@ -375,15 +396,19 @@ extern "C" int skinny_gemm_release_all(void) {
                 rc = SKG_ERR_HIP;
         (void)hipSetDevice(cur);
     }
+    int cur = 0;
+    (void)hipGetDevice(&cur);
     for (auto &w : g_ws) {
         (void)hipSetDevice(w.device);
         if (w.ws && hipFree(w.ws) != hipSuccess) rc = SKG_ERR_HIP;
         if (w.tickets && hipFree(w.tickets) != hipSuccess) rc = SKG_ERR_HIP;
     }
+    (void)hipSetDevice(cur);
     for (void *p : g_retired)
         if (hipFree(p) != hipSuccess) rc = SKG_ERR_HIP;
     g_ws.clear();
     g_retired.clear();
+    g_generation.fetch_add(1, std::memory_order_acq_rel);  // every per-thread copy is stale
     return rc;
 }
 

@@ -274,6 +274,59 @@ def test_capture_needs_reserved_workspace(skg):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+    del g
+    # after a release the next eager call on the stream allocates afresh
+    skg.release_all()
+    out.fill_(0)
+    with torch.cuda.stream(stream):
+        assert call() == skg.OK
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+
+
+def test_threads_on_their_own_streams(skg):
+    # host threads calling at once on their own streams: each stream gets
+    # its own workspace (grown while the others run), and every result equals
+    # the single-threaded one bit for bit
+    import threading
+
+    lib = skg.lib()
+    cases = []
+    for i, (M, N, K, S) in enumerate(((16, 256, 7168, 16), (32, 576, 7168, 8), (8, 384, 4096, 4),
+                                      (64, 1024, 2048, 2))):
+        x, w, b = _dev(*gen.bf16_inputs(M, N, K, True, seed=700 + i))
+        plan = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_SPLITK, 256, 1, S, 2,
+                                                        skg.REDUCE_KERNEL))
+        ref = skg.gemm_bf16_planned(x, w, plan, b)
+        cases.append((M, N, K, x, w, b, plan, ref))
+    torch.cuda.synchronize()
+    skg.release_all()
+    errors = []
+
+    def worker(case):
+        M, N, K, x, w, b, plan, ref = case
+        stream = torch.cuda.Stream()
+        sptr = ctypes.c_void_p(stream.cuda_stream)
+        outs = [torch.zeros(M, N, dtype=torch.bfloat16, device=DEV) for _ in range(20)]
+        torch.cuda.synchronize()
+        for o in outs:
+            rc = lib.skinny_gemm_bf16_planned(x.data_ptr(), w.data_ptr(), b.data_ptr(), o.data_ptr(),
+                                              M, N, K, ctypes.byref(plan), sptr)
+            if rc != skg.OK:
+                errors.append(f"M={M}: status {rc}")
+                return
+        stream.synchronize()
+        for o in outs:
+            if not torch.equal(o.view(torch.int16), ref.view(torch.int16)):
+                errors.append(f"M={M} N={N}: differs from the single-threaded result")
+                return
+
+    threads = [threading.Thread(target=worker, args=(c,)) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
 
 
 def test_error_statuses_on_device(skg):
