@@ -203,13 +203,50 @@ def mfma_probe(skg, torch, stream, sptr):
     return 0
 
 
+SECTION_REPLAYS = 11  # timed graph replays per configuration of a section
+
+
+def graph_times(torch, stream, calls, n_calls, reps=SECTION_REPLAYS):
+    """Runs calls() once eagerly (growing any workspace outside capture),
+    captures it in a graph and replays it: returns the median, p10 and p90
+    microseconds per call over `reps` timed replays after one warm-up."""
+    with torch.cuda.stream(stream):
+        calls()
+    stream.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=stream):
+        calls()
+    ts = []
+    with torch.cuda.stream(stream):
+        gr.replay()
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            gr.replay()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / n_calls)
+    del gr
+    ts.sort()
+    return ts[len(ts) // 2], ts[len(ts) // 10], ts[(9 * len(ts)) // 10]
+
+
+def sample_outputs(M, N):
+    """Rows and columns of an output sampled for the oracle check: the first
+    and last row and 32 columns spread over N (the last one included)."""
+    rows = sorted({0, M - 1})
+    cols = sorted({(i * (N - 1)) // 31 for i in range(32)})
+    return rows, cols
+
+
 DECODE_K = 7168
 DECODE_N = (576, 2112, 4096)
 DECODE_M = (1, 8, 32, 64, 128)
 LARGE_M = (256, 512)  # the larger-M regime, at N = 4096 only
 
 
-def decode_section(skg, torch, stream, sptr):
+def decode_section(skg, torch, stream, sptr, samples):
     """bf16 dense decode linear, K = 7168, N in {576, 2112, 4096}, M in
     {1, 8, 32, 64, 128} (and 256, 512 at N = 4096; the planner's plan, no
     bias): microseconds per call
@@ -236,25 +273,16 @@ def decode_section(skg, torch, stream, sptr):
                                                     O[s].data_ptr(), M, N, K, sptr)
                     if rc != 0:
                         raise skg.SkinnyGemmError(rc, f"skinny_gemm_bf16 M={M} N={N}")
-            with torch.cuda.stream(stream):
-                calls()
-            stream.synchronize()
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr, stream=stream):
-                calls()
-            with torch.cuda.stream(stream):
-                gr.replay()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for _ in range(3):
-                    gr.replay()
-                e1.record(stream)
-                e1.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / (3 * slots)
-            del gr
+            us, p10, p90 = graph_times(torch, stream, calls, slots)
+            torch.cuda.synchronize()
+            rows, cols = sample_outputs(M, N)
+            samples.append({"key": f"decode_N{N}_M{M}", "kind": "bf16", "K": K,
+                            "x": X[0][rows].cpu(), "w": W[0][cols].cpu(),
+                            "out": O[0][rows][:, cols].cpu()})
             byts = 2 * N * K + 2 * M * K + 2 * M * N
             p = skg.plan(M, N, K)
-            res[f"N{N}_M{M}"] = {"us_per_call": round(us, 3),
+            res[f"N{N}_M{M}"] = {"us_per_call": round(us, 3), "p10_us": round(p10, 3),
+                                 "p90_us": round(p90, 3),
                                  "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                                  "frac_of_8TBps": round(byts / (us * 1e-6) / 8e12, 4),
                                  "TFLOPs": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1),
@@ -276,22 +304,7 @@ def f3_section(skg, torch, stream, sptr):
     res = {}
 
     def timed(calls, n):
-        with torch.cuda.stream(stream):
-            calls()
-        stream.synchronize()
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr, stream=stream):
-            calls()
-        with torch.cuda.stream(stream):
-            gr.replay()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(3):
-                gr.replay()
-            e1.record(stream)
-            e1.synchronize()
-        del gr
-        return round(e0.elapsed_time(e1) * 1e3 / (3 * n), 3)
+        return round(graph_times(torch, stream, calls, n)[0], 3)
 
     L = skg.lib()
     K, N = 7168, 256
@@ -349,7 +362,7 @@ def f3_section(skg, torch, stream, sptr):
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 
 
-def fp8_section(skg, torch, stream, sptr):
+def fp8_section(skg, torch, stream, sptr, samples):
     """FP8 e4m3, K = N = 4096, M in {1, 16, 64, 128, 256, 512}, per-tensor and MX
     scales: microseconds per call over a cold pool of >= 512 MB of distinct
     W, the achieved GB/s (W, x, out and scale bytes) and the MFMA rate
@@ -387,25 +400,19 @@ def fp8_section(skg, torch, stream, sptr):
                                                    ctypes.byref(scs[s]), O[s].data_ptr(), M, N, K, sptr)
                     if rc != 0:
                         raise skg.SkinnyGemmError(rc, f"skinny_gemm_fp8 M={M} {mode}")
-            with torch.cuda.stream(stream):
-                calls()
-            stream.synchronize()
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr, stream=stream):
-                calls()
-            with torch.cuda.stream(stream):
-                gr.replay()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for _ in range(3):
-                    gr.replay()
-                e1.record(stream)
-                e1.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / (3 * slots)
-            del gr
+            us, p10, p90 = graph_times(torch, stream, calls, slots)
+            torch.cuda.synchronize()
+            rows, cols = sample_outputs(M, N)
+            samp = {"key": f"fp8_{mode}_M{M}", "kind": f"fp8_{mode}", "K": K,
+                    "x": X[0][rows].cpu(), "w": W[0][cols].cpu(), "out": O[0][rows][:, cols].cpu()}
+            if mode == "mx":
+                samp["xe"], samp["we"] = XE[0][rows].cpu(), WE[0][cols].cpu()
+            samples.append(samp)
             byts = N * K + M * K + M * N * 2 + extra
             tflops = 2.0 * M * N * K / (us * 1e-6) / 1e12
-            res[f"M{M}_{mode}"] = {"us_per_call": round(us, 3), "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+            res[f"M{M}_{mode}"] = {"us_per_call": round(us, 3), "p10_us": round(p10, 3),
+                                   "p90_us": round(p90, 3),
+                                   "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                                    "TFLOPs": round(tflops, 1),
                                    "mfma_util": round(tflops / FP8_PEAK_TFLOPS, 4),
                                    "kernel": {1: "dot", 2: "splitk", 3: "tiled"}[skg.plan(
@@ -414,6 +421,34 @@ def fp8_section(skg, torch, stream, sptr):
     del W
     torch.cuda.empty_cache()
     return res
+
+
+def check_samples(samples):
+    """The sampled outputs of the timed sections against the oracle: "ok"
+    when all are within the tolerance, else the first failure."""
+    import torch
+
+    import oracle
+    from oracle import tolerance
+
+    def bits16(t):
+        return t.contiguous().view(torch.int16).numpy().view("uint16")
+
+    def bits8(t):
+        return t.contiguous().view(torch.uint8).numpy()
+
+    for s in samples:
+        if s["kind"] == "bf16":
+            ref = oracle.gemm_bf16(bits16(s["x"]), bits16(s["w"]), threads=16)
+        elif s["kind"] == "fp8_tensor":
+            ref = oracle.gemm_fp8_tensor(bits8(s["x"]), bits8(s["w"]), 1.0, 1.0, threads=16)
+        else:
+            ref = oracle.gemm_fp8_mx(bits8(s["x"]), bits8(s["w"]), bits8(s["xe"]), bits8(s["we"]),
+                                     threads=16)
+        ok, msg = tolerance.check(s["out"], ref, s["K"])
+        if not ok:
+            return f"{s['key']}: {msg}"
+    return f"ok ({len(samples)} configurations, 2 rows x 32 columns each)"
 
 
 def main():
@@ -638,9 +673,14 @@ def main():
                "single_thread_sample": "median of 3 passes over M=1..16, one thread",
                "cpu_model": cpu_model()}
 
-    fp8 = None if args.no_fp8 else fp8_section(skg, torch, stream, sptr)
-    decode = None if args.no_decode else decode_section(skg, torch, stream, sptr)
+    samples = []  # sampled outputs of the FP8 and decode sections, checked below
+    fp8 = None if args.no_fp8 else fp8_section(skg, torch, stream, sptr, samples)
+    decode = None if args.no_decode else decode_section(skg, torch, stream, sptr, samples)
     f3 = None if args.no_f3 else f3_section(skg, torch, stream, sptr)
+    # CPU-baseline leg, continued: the sections' sampled outputs against the oracle
+    parity_sections = None
+    if not args.no_cpu and samples:
+        parity_sections = check_samples(samples)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -663,6 +703,7 @@ def main():
         "decode_bf16_k7168": decode,
         "fp32_out_and_fused_quant": f3,
         "parity": parity,
+        "parity_sections": parity_sections,
         "deterministic": deterministic,
     }
     print(json.dumps(line), flush=True)
