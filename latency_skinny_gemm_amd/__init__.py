@@ -133,10 +133,27 @@ def _check(status, what):
         raise SkinnyGemmError(status, what)
 
 
-def _stream_ptr(stream):
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+def _one_device(*ts):
+    """The device of the given tensors (None entries skipped); all must share it."""
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"all tensors must be on one device, got {dev} and {t.device}")
+    return dev
+
+
+def _launch(dev, stream, fn, *args):
+    """fn(*args, stream) with `dev` current (the library keeps its workspaces
+    per current device) on `stream`, else dev's current stream."""
+    with torch.cuda.device(dev):
+        s = torch.cuda.current_stream() if stream is None else stream
+        if s.device != dev:
+            raise ValueError(f"stream is on {s.device}, the tensors on {dev}")
+        return fn(*args, ctypes.c_void_p(s.cuda_stream))
 
 
 def _ptr(t):
@@ -169,8 +186,8 @@ def gemm_bf16(x, W, bias=None, out=None, stream=None):
     M, N, K = _check_tensors(x, W, bias, out, torch.bfloat16)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    rc = _load().skinny_gemm_bf16(_ptr(x), _ptr(W), _ptr(bias), None, _ptr(out), M, N, K,
-                                  _stream_ptr(stream))
+    rc = _launch(_one_device(x, W, bias, out), stream, _load().skinny_gemm_bf16, _ptr(x), _ptr(W),
+                 _ptr(bias), None, _ptr(out), M, N, K)
     _check(rc, f"skinny_gemm_bf16(M={M}, N={N}, K={K})")
     return out
 
@@ -180,8 +197,8 @@ def gemm_bf16_planned(x, W, p, bias=None, out=None, stream=None):
     M, N, K = _check_tensors(x, W, bias, out, torch.bfloat16)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    rc = _load().skinny_gemm_bf16_planned(_ptr(x), _ptr(W), _ptr(bias), _ptr(out), M, N, K,
-                                          ctypes.byref(p), _stream_ptr(stream))
+    rc = _launch(_one_device(x, W, bias, out), stream, _load().skinny_gemm_bf16_planned, _ptr(x),
+                 _ptr(W), _ptr(bias), _ptr(out), M, N, K, ctypes.byref(p))
     _check(rc, f"skinny_gemm_bf16_planned(M={M}, N={N}, K={K}, {p})")
     return out
 
@@ -194,12 +211,13 @@ def gemm_bf16_f32(x, W, bias=None, out=None, plan=None, stream=None):
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     elif out.dtype != torch.float32 or tuple(out.shape) != (M, N) or not out.is_contiguous():
         raise TypeError("out must be contiguous float32 [M, N]")
+    dev = _one_device(x, W, bias, out)
     if plan is None:
-        rc = _load().skinny_gemm_bf16_f32(_ptr(x), _ptr(W), _ptr(bias), _ptr(out), M, N, K,
-                                          _stream_ptr(stream))
+        rc = _launch(dev, stream, _load().skinny_gemm_bf16_f32, _ptr(x), _ptr(W), _ptr(bias),
+                     _ptr(out), M, N, K)
     else:
-        rc = _load().skinny_gemm_bf16_f32_planned(_ptr(x), _ptr(W), _ptr(bias), _ptr(out), M, N,
-                                                  K, ctypes.byref(plan), _stream_ptr(stream))
+        rc = _launch(dev, stream, _load().skinny_gemm_bf16_f32_planned, _ptr(x), _ptr(W),
+                     _ptr(bias), _ptr(out), M, N, K, ctypes.byref(plan))
     _check(rc, f"skinny_gemm_bf16_f32(M={M}, N={N}, K={K}, {plan})")
     return out
 
@@ -235,10 +253,11 @@ def gemm_fp8_quant(x, wq, sx, sw, bias=None, out_dtype=torch.bfloat16, out=None,
     elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or not out.is_contiguous():
         raise TypeError(f"out must be contiguous {out_dtype} [M, N]")
     args = (_ptr(x), _ptr(wq), _ptr(bias), _ptr(sx), _ptr(sw), _ptr(out), code, M, N, K)
+    dev = _one_device(x, wq, bias, sx, sw, out)
     if plan is None:
-        rc = _load().skinny_gemm_fp8_quant(*args, _stream_ptr(stream))
+        rc = _launch(dev, stream, _load().skinny_gemm_fp8_quant, *args)
     else:
-        rc = _load().skinny_gemm_fp8_quant_planned(*args, ctypes.byref(plan), _stream_ptr(stream))
+        rc = _launch(dev, stream, _load().skinny_gemm_fp8_quant_planned, *args, ctypes.byref(plan))
     _check(rc, f"skinny_gemm_fp8_quant(M={M}, N={N}, K={K}, {plan})")
     return out
 
@@ -254,7 +273,8 @@ def quant_e4m3(x, s, out=None, stream=None):
     elif out.dtype not in (torch.float8_e4m3fn, torch.uint8) or out.shape != x.shape \
             or not out.is_contiguous():
         raise TypeError("out must be a contiguous float8_e4m3fn tensor of x's shape")
-    rc = _load().skinny_quant_e4m3(_ptr(x), _ptr(s), _ptr(out), x.numel(), _stream_ptr(stream))
+    rc = _launch(_one_device(x, s, out), stream, _load().skinny_quant_e4m3, _ptr(x), _ptr(s),
+                 _ptr(out), x.numel())
     _check(rc, f"skinny_quant_e4m3(n={x.numel()})")
     return out
 
@@ -297,8 +317,8 @@ def _fp8_args(xq, wq, sx, sw, xe, we, bias, out):
 def gemm_fp8(xq, wq, sx=None, sw=None, xe=None, we=None, bias=None, out=None, stream=None):
     """FP8 e4m3 GEMM, bf16 out: per-tensor (sx, sw) or MX (xe, we) scales."""
     M, N, K, sc, out = _fp8_args(xq, wq, sx, sw, xe, we, bias, out)
-    rc = _load().skinny_gemm_fp8(_ptr(xq), _ptr(wq), _ptr(bias), ctypes.byref(sc), _ptr(out),
-                                 M, N, K, _stream_ptr(stream))
+    rc = _launch(_one_device(xq, wq, sx, sw, xe, we, bias, out), stream, _load().skinny_gemm_fp8,
+                 _ptr(xq), _ptr(wq), _ptr(bias), ctypes.byref(sc), _ptr(out), M, N, K)
     _check(rc, f"skinny_gemm_fp8(M={M}, N={N}, K={K}, mode={sc.mode})")
     return out
 
@@ -306,8 +326,9 @@ def gemm_fp8(xq, wq, sx=None, sw=None, xe=None, we=None, bias=None, out=None, st
 def gemm_fp8_planned(xq, wq, p, sx=None, sw=None, xe=None, we=None, bias=None, out=None,
                      stream=None):
     M, N, K, sc, out = _fp8_args(xq, wq, sx, sw, xe, we, bias, out)
-    rc = _load().skinny_gemm_fp8_planned(_ptr(xq), _ptr(wq), _ptr(bias), ctypes.byref(sc),
-                                         _ptr(out), M, N, K, ctypes.byref(p), _stream_ptr(stream))
+    rc = _launch(_one_device(xq, wq, sx, sw, xe, we, bias, out), stream,
+                 _load().skinny_gemm_fp8_planned, _ptr(xq), _ptr(wq), _ptr(bias), ctypes.byref(sc),
+                 _ptr(out), M, N, K, ctypes.byref(p))
     _check(rc, f"skinny_gemm_fp8_planned(M={M}, N={N}, K={K}, {p})")
     return out
 
@@ -341,8 +362,12 @@ def plan_complete(M, N, K, p, dtype=DTYPE_BF16):
 
 
 def reserve(max_M, max_N, max_S, stream=None):
-    _check(_load().skinny_gemm_reserve(max_M, max_N, max_S, _stream_ptr(stream)),
-           "skinny_gemm_reserve")
+    """Reserves split-K workspace for `stream` (else the current stream) on
+    the stream's device."""
+    s = torch.cuda.current_stream() if stream is None else stream
+    with torch.cuda.device(s.device):
+        _check(_load().skinny_gemm_reserve(max_M, max_N, max_S, ctypes.c_void_p(s.cuda_stream)),
+               "skinny_gemm_reserve")
 
 
 def release_all():
