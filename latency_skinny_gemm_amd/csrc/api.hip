@@ -154,7 +154,9 @@ int run_fp8(const void *x, const void *W, const void *bias, const skinny_fp8_sca
             hipStream_t stream) {
     Fp8Args a{x, W, bias, out, sc->mode, sc->sx, sc->sw, sc->x_e8m0, sc->w_e8m0, out_f32, false};
     const bool fused =
-        quant_x && p.kind == SKG_KIND_DOT && fp8_dot_quant_ok(M, p.cols, p.depth, p.threads);
+        quant_x && ((p.kind == SKG_KIND_DOT && fp8_dot_quant_ok(M, p.cols, p.depth, p.threads)) ||
+                    (p.kind == SKG_KIND_SPLITK &&
+                     fp8_mfma_quant_ok(p.m_tiles, p.cols, p.depth, p.threads)));
     a.qx = fused;
     // partials first (rounded to 256 bytes), then the quantised x if needed
     const size_t part = (p.kind != SKG_KIND_DOT && p.splits > 1)

@@ -115,6 +115,15 @@ constexpr int fp8_mfma_max_threads(int MT, int NB, int D, bool mx) {
 constexpr bool fp8_mfma_built(int MT, int NB, int D) {
     return NB * MT <= 32 && D * (NB + MT) <= 14;  // MX spills beyond (resource report)
 }
+// With x arriving as bf16 (fused static quantisation, per-tensor only), a
+// stage keeps 16 VGPRs of raw x per (step, m-tile) instead of 8; built for
+// up to 32 rows (the small-M plans the fused path meets).  The conversion
+// needs temporaries beside them: above 160 by this count the resource
+// report showed spills, so the bound is 160.
+constexpr int fp8q_mfma_regs(int MT, int NB, int D) { return 2 * D * (NB * 9 + MT * 16) + NB * MT * 4; }
+constexpr bool fp8q_mfma_built(int MT, int NB, int D) {
+    return MT <= 2 && fp8_mfma_built(MT, NB, D) && fp8q_mfma_regs(MT, NB, D) <= 160;
+}
 
 // FP8 TILED: the bf16 tiled kernel's ring with 128-wide K steps; a stage
 // holds U (1 or 2) steps: (MT + NB) blocks of 16 rows x 128U bytes, plus in
@@ -186,5 +195,6 @@ int launch_fp8_tiled(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *ti
 // and accepts workgroups of `threads` (its registers bound it lower than the
 // plain FP8 dot kernel).
 bool fp8_dot_quant_ok(int M, int C, int V, int threads);
+bool fp8_mfma_quant_ok(int MT, int NB, int D, int threads);
 
 }  // namespace skg

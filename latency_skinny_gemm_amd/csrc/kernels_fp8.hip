@@ -180,9 +180,13 @@ __global__ void __launch_bounds__((fp8_dot_max_threads(M, C, V, MX, QX)))
 }
 
 // ------------------------------------------------------------------ MFMA split-K
-template <int MT, int NB, int D, bool MX>
-__global__ void __launch_bounds__((fp8_mfma_max_threads(MT, NB, D, MX)))
-    fp8_mfma_kernel(const uint8_t *__restrict__ x, const uint8_t *__restrict__ W,
+// QX: x arrives as bf16 and is quantised statically with sx, as in the dot
+// kernel: the stage keeps the raw bf16 (four 16-byte loads per step and
+// m-tile) and each 16-element chunk becomes 16 e4m3 codes just before its
+// MFMAs, with the same conversion as the standalone quantisation kernel.
+template <int MT, int NB, int D, bool MX, bool QX>
+__global__ void __launch_bounds__((QX ? 256 : fp8_mfma_max_threads(MT, NB, D, MX)))
+    fp8_mfma_kernel(const void *__restrict__ x, const uint8_t *__restrict__ W,
                     const uint16_t *__restrict__ bias, const float *__restrict__ sx,
                     const float *__restrict__ sw, const uint8_t *__restrict__ xe,
                     const uint8_t *__restrict__ we, void *__restrict__ out,
@@ -198,10 +202,12 @@ __global__ void __launch_bounds__((fp8_mfma_max_threads(MT, NB, D, MX)))
     const int j = blockIdx.x / S;
     const int col0 = j * NB * 16;
     const int ncols = min(NB * 16, N - col0);
+    static_assert(!(MX && QX), "static quantisation is per-tensor");
     const unsigned rowb = (unsigned)K;
+    const unsigned xrowb = QX ? 2u * rowb : rowb;  // bf16 or e4m3 x rows
     const unsigned srow = (unsigned)(K >> 5);
     const Rsrc wr = make_rsrc(W + (size_t)col0 * K, (unsigned)ncols * rowb);
-    const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
+    const Rsrc xr = make_rsrc(x, (unsigned)M * xrowb);
     const Rsrc xer = make_rsrc(xe, MX ? (unsigned)M * srow : 0u);
     const Rsrc wer = make_rsrc(we + (MX ? (size_t)col0 * srow : 0), MX ? (unsigned)ncols * srow : 0u);
     const int kbeg = s * k_chunk;
@@ -225,11 +231,14 @@ __global__ void __launch_bounds__((fp8_mfma_max_threads(MT, NB, D, MX)))
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // a stage: D steps of (two 16-byte halves per operand block) + MX scales
-    u32x4 wa[D][NB][2], xa[D][MT][2], wb[D][NB][2], xb[D][MT][2];
+    // a stage: D steps of (two 16-byte halves per operand block, x as bf16
+    // taking four) + MX scales
+    constexpr int XH = QX ? 4 : 2;
+    const float inv = QX ? 1.0f / sx[0] : 0.0f;  // correctly rounded (no fast-math)
+    u32x4 wa[D][NB][2], xa[D][MT][XH], wb[D][NB][2], xb[D][MT][XH];
     unsigned wsa[D][NB], xsa[D][MT], wsb[D][NB], xsb[D][MT];
 
-    auto load_stage = [&](u32x4(&wbuf)[D][NB][2], u32x4(&xbuf)[D][MT][2], unsigned(&wsc)[D][NB],
+    auto load_stage = [&](u32x4(&wbuf)[D][NB][2], u32x4(&xbuf)[D][MT][XH], unsigned(&wsc)[D][NB],
                           unsigned(&xsc)[D][MT], int chunk) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -257,9 +266,18 @@ __global__ void __launch_bounds__((fp8_mfma_max_threads(MT, NB, D, MX)))
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const unsigned ro = ((unsigned)mt * 16u + r16) * rowb;
-                xbuf[d][mt][0] = load16<kCacheDefault>(xr, koff + ro);
-                xbuf[d][mt][1] = load16<kCacheDefault>(xr, koff1 + ro);
+                const unsigned ro = ((unsigned)mt * 16u + r16) * xrowb;
+                if constexpr (QX) {
+                    const unsigned q0 = ok0 ? (unsigned)(k0 + g16) * 2u : kOOB;
+                    const unsigned q1 = ok1 ? (unsigned)(k0 + 64 + g16) * 2u : kOOB;
+                    xbuf[d][mt][0] = load16<kCacheDefault>(xr, q0 + ro);
+                    xbuf[d][mt][1] = load16<kCacheDefault>(xr, q0 + 16u + ro);
+                    xbuf[d][mt][2] = load16<kCacheDefault>(xr, q1 + ro);
+                    xbuf[d][mt][3] = load16<kCacheDefault>(xr, q1 + 16u + ro);
+                } else {
+                    xbuf[d][mt][0] = load16<kCacheDefault>(xr, koff + ro);
+                    xbuf[d][mt][1] = load16<kCacheDefault>(xr, koff1 + ro);
+                }
                 if constexpr (MX) {
                     // rows past M read as zero data; give them the unit scale
                     const unsigned e = load_byte(xer, boff + ((unsigned)mt * 16u + r16) * srow);
@@ -268,15 +286,22 @@ __global__ void __launch_bounds__((fp8_mfma_max_threads(MT, NB, D, MX)))
             }
         }
     };
-    auto mma_stage = [&](u32x4(&wbuf)[D][NB][2], u32x4(&xbuf)[D][MT][2], unsigned(&wsc)[D][NB],
+    auto mma_stage = [&](u32x4(&wbuf)[D][NB][2], u32x4(&xbuf)[D][MT][XH], unsigned(&wsc)[D][NB],
                          unsigned(&xsc)[D][MT]) {
 #pragma unroll
         for (int d = 0; d < D; ++d)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int mt = 0; mt < MT; ++mt) {
+                u32x4 a0, a1;
+                if constexpr (QX) {
+                    a0 = quant16_e4m3(xbuf[d][mt][0], xbuf[d][mt][1], inv);
+                    a1 = quant16_e4m3(xbuf[d][mt][2], xbuf[d][mt][3], inv);
+                } else {
+                    a0 = xbuf[d][mt][0];
+                    a1 = xbuf[d][mt][1];
+                }
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const u32x4 a0 = xbuf[d][mt][0], a1 = xbuf[d][mt][1];
+                for (int nb = 0; nb < NB; ++nb) {
                     const u32x4 b0 = wbuf[d][nb][0], b1 = wbuf[d][nb][1];
                     const i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
@@ -288,6 +313,7 @@ __global__ void __launch_bounds__((fp8_mfma_max_threads(MT, NB, D, MX)))
                     acc[nb][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         a, b, acc[nb][mt], 0, 0, 0, sa, 0, sb);
                 }
+            }
     };
 
     if (nchunks <= 1) {
@@ -401,57 +427,61 @@ Fp8DotLaunch fp8_dot_m(int M, int C, int V) {
     }
 }
 
-template <int MT, int NB, int D, bool MX>
+template <int MT, int NB, int D, bool MX, bool QX>
 int launch_fp8_mfma_t(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets, int M,
                       int N, int K, hipStream_t stream) {
     const size_t lds_bytes = (size_t)(p.threads / 64) * NB * MT * 4 * 64 * sizeof(float);
-    hipLaunchKernelGGL((fp8_mfma_kernel<MT, NB, D, MX>), dim3(p.grid), dim3(p.threads), lds_bytes,
-                       stream, (const uint8_t *)a.x, (const uint8_t *)a.W, (const uint16_t *)a.bias,
+    hipLaunchKernelGGL((fp8_mfma_kernel<MT, NB, D, MX, QX>), dim3(p.grid), dim3(p.threads),
+                       lds_bytes, stream, a.x, (const uint8_t *)a.W, (const uint16_t *)a.bias,
                        a.sx, a.sw, a.xe, a.we, a.out, ws, tickets, M, N, K, p.splits,
                        p.k_chunk, p.reduce, a.out_f32);
     return (int)hipGetLastError();
 }
 
-template <int MT, int NB, int D, bool MX>
+template <int MT, int NB, int D, bool MX, bool QX>
 constexpr Fp8MfmaLaunch fp8_mfma_entry() {
-    if constexpr (fp8_mfma_built(MT, NB, D))
-        return &launch_fp8_mfma_t<MT, NB, D, MX>;
+    if constexpr (QX ? fp8q_mfma_built(MT, NB, D) : fp8_mfma_built(MT, NB, D))
+        return &launch_fp8_mfma_t<MT, NB, D, MX, QX>;
     else
         return nullptr;
 }
 
-template <int MT, int NB, bool MX>
+template <int MT, int NB, bool MX, bool QX>
 Fp8MfmaLaunch fp8_mfma_d(int D) {
     switch (D) {
-    case 1: return fp8_mfma_entry<MT, NB, 1, MX>();
-    case 2: return fp8_mfma_entry<MT, NB, 2, MX>();
-    case 4: return fp8_mfma_entry<MT, NB, 4, MX>();
+    case 1: return fp8_mfma_entry<MT, NB, 1, MX, QX>();
+    case 2: return fp8_mfma_entry<MT, NB, 2, MX, QX>();
+    case 4: return fp8_mfma_entry<MT, NB, 4, MX, QX>();
     default: return nullptr;
     }
 }
 
-template <int MT, bool MX>
+template <int MT, bool MX, bool QX>
 Fp8MfmaLaunch fp8_mfma_nb(int NB, int D) {
-    return NB == 1 ? fp8_mfma_d<MT, 1, MX>(D) : NB == 2 ? fp8_mfma_d<MT, 2, MX>(D)
-                   : NB == 4 ? fp8_mfma_d<MT, 4, MX>(D) : nullptr;
+    return NB == 1 ? fp8_mfma_d<MT, 1, MX, QX>(D) : NB == 2 ? fp8_mfma_d<MT, 2, MX, QX>(D)
+                   : NB == 4 ? fp8_mfma_d<MT, 4, MX, QX>(D) : nullptr;
 }
 
-template <bool MX>
+template <bool MX, bool QX>
 Fp8MfmaLaunch fp8_mfma_mt(int MT, int NB, int D) {
     switch (MT) {
-    case 1: return fp8_mfma_nb<1, MX>(NB, D);
-    case 2: return fp8_mfma_nb<2, MX>(NB, D);
-    case 3: return fp8_mfma_nb<3, MX>(NB, D);
-    case 4: return fp8_mfma_nb<4, MX>(NB, D);
-    case 5: return fp8_mfma_nb<5, MX>(NB, D);
-    case 6: return fp8_mfma_nb<6, MX>(NB, D);
-    case 7: return fp8_mfma_nb<7, MX>(NB, D);
-    case 8: return fp8_mfma_nb<8, MX>(NB, D);
+    case 1: return fp8_mfma_nb<1, MX, QX>(NB, D);
+    case 2: return fp8_mfma_nb<2, MX, QX>(NB, D);
+    case 3: return fp8_mfma_nb<3, MX, QX>(NB, D);
+    case 4: return fp8_mfma_nb<4, MX, QX>(NB, D);
+    case 5: return fp8_mfma_nb<5, MX, QX>(NB, D);
+    case 6: return fp8_mfma_nb<6, MX, QX>(NB, D);
+    case 7: return fp8_mfma_nb<7, MX, QX>(NB, D);
+    case 8: return fp8_mfma_nb<8, MX, QX>(NB, D);
     default: return nullptr;
     }
 }
 
 }  // namespace
+
+bool fp8_mfma_quant_ok(int MT, int NB, int D, int threads) {
+    return threads <= 256 && fp8_mfma_mt<false, true>(MT, NB, D) != nullptr;
+}
 
 bool fp8_dot_quant_ok(int M, int C, int V, int threads) {
     if (M < 1 || M > kDotMaxM || fp8_dot_m<false, true>(M, C, V) == nullptr) return false;
@@ -468,10 +498,13 @@ int launch_fp8(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets,
         if (!f) return (int)hipErrorInvalidConfiguration;
         return f(p, a, N, K, stream);
     }
-    if (a.qx) return (int)hipErrorInvalidConfiguration;  // the caller quantises x first
+    // fused quantisation: the dot and MFMA split-K kernels only (the caller
+    // quantises x first for every other plan)
+    if (a.qx && (mx || p.kind != SKG_KIND_SPLITK)) return (int)hipErrorInvalidConfiguration;
     if (p.kind == SKG_KIND_TILED) return launch_fp8_tiled(p, a, ws, tickets, M, N, K, stream);
-    Fp8MfmaLaunch f = mx ? fp8_mfma_mt<true>(p.m_tiles, p.cols, p.depth)
-                         : fp8_mfma_mt<false>(p.m_tiles, p.cols, p.depth);
+    Fp8MfmaLaunch f = mx     ? fp8_mfma_mt<true, false>(p.m_tiles, p.cols, p.depth)
+                      : a.qx ? fp8_mfma_mt<false, true>(p.m_tiles, p.cols, p.depth)
+                             : fp8_mfma_mt<false, false>(p.m_tiles, p.cols, p.depth);
     if (!f) return (int)hipErrorInvalidConfiguration;
     int rc = f(p, a, ws, tickets, M, N, K, stream);
     if (rc != (int)hipSuccess || p.splits == 1 || p.reduce != SKG_REDUCE_KERNEL) return rc;

@@ -148,13 +148,14 @@ def _quant_plans(skg, M, N, K):
             plans.append((f"dot_t{T}_c{C}", p))
     mt = (M + 15) // 16
     for (T, NB, S, D, red) in ((256, 1, 4, 1, skg.REDUCE_KERNEL), (256, 2 if mt <= 3 else 1, 1, 1,
-                                                                   skg.REDUCE_NONE)):
+                                                                   skg.REDUCE_NONE),
+                               (256, 1, 3, 2, skg.REDUCE_LAST), (128, 4, 2, 1, skg.REDUCE_KERNEL)):
         p = skg.make_plan(skg.KIND_SPLITK, T, NB, S, D, red)
         try:
             skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
         except skg.SkinnyGemmError:
             continue
-        plans.append((f"mfma_s{S}_r{red}", p))
+        plans.append((f"mfma_t{T}_nb{NB}_s{S}_d{D}_r{red}", p))
     p = skg.make_plan(skg.KIND_TILED, 256, 4, 2, 3, skg.REDUCE_KERNEL)
     try:
         skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
