@@ -22,7 +22,7 @@ constexpr int kNumCusMI355X = 256;
 constexpr long kMaxBufferBytes = 0x7FFFFFFFL;  // one buffer resource covers < 2 GiB
 
 // DOT: vectors (16 B) per thread per column that the kernel is built for.
-constexpr int kDotVecs[] = {1, 2, 3, 4, 6, 8};
+constexpr int kDotVecs[] = {1, 2, 3, 4, 6, 8, 12, 14, 16};
 // Registers a DOT thread holds: C rows of W and M rows of x, V 16-byte
 // vectors each, x counted twice (the compiler widens x to fp32 ahead of
 // use), and C*M accumulators.  Only the 256 architectural VGPRs feed VALU

@@ -74,6 +74,23 @@ __global__ void __launch_bounds__((dot_max_threads(M, C, V, DOT2)))
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
     const int lane = t & 63;
     const int nw = T >> 6;
+    if (nw == 1) {
+        // One wave: its sums are the totals, in every lane, so lane c*M + m
+        // stores output (c, m) with no LDS round trip and no barrier.  The
+        // sum starts from 0 as the cross-wave sum below does: same bits.
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float s = 0.0f + wave_sum(acc[c][m]);
+                const int n = n0 + c;
+                if (lane == c * M + m && n < N) {
+                    if (bias) s += bf16_to_f32(bias[n]);
+                    store_out(out, (size_t)m * N + n, s, out_f32);
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int c = 0; c < C; ++c)
 #pragma unroll
@@ -127,6 +144,9 @@ DotLaunch pick_v(int V) {
     case 4: return dot_entry<M, C, 4, DOT2>();
     case 6: return dot_entry<M, C, 6, DOT2>();
     case 8: return dot_entry<M, C, 8, DOT2>();
+    case 12: return dot_entry<M, C, 12, DOT2>();
+    case 14: return dot_entry<M, C, 14, DOT2>();
+    case 16: return dot_entry<M, C, 16, DOT2>();
     default: return nullptr;
     }
 }

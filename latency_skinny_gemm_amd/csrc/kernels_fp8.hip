@@ -159,6 +159,24 @@ __global__ void __launch_bounds__((fp8_dot_max_threads(M, C, V, MX, QX)))
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int lane = t & 63;
     const int nw = T >> 6;
+    if (nw == 1) {
+        // One wave: its sums are the totals, in every lane, so lane c*M + m
+        // stores output (c, m) with no LDS round trip and no barrier (the
+        // same bits as the cross-wave sum below, which starts from 0 too).
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float s = 0.0f + wave_sum(acc[c][m]);
+                const int n = n0 + c;
+                if (lane == c * M + m && n < N) {
+                    if (!MX) s *= sx[0] * sw[0];
+                    if (bias) s += bf16_to_f32(bias[n]);
+                    store_out(out, (size_t)m * N + n, s, out_f32);
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int c = 0; c < C; ++c)
 #pragma unroll

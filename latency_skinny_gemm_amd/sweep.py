@@ -161,7 +161,7 @@ def sweep_point_fp8(skg, torch, M, N, K, pool_bytes, reps, stream, log):
     results.sort(key=lambda r: r[0])
     _, best_modes, best = results[0]
     rec = {"dtype": "fp8", "M": M, "N": N, "K": K, "slots": slots, "tiled": "ring2",
-           "mx_scales": "per_slot",
+           "mx_scales": "per_slot", "dot_wave1": "direct",
            "best_us": round(max(best_modes.values()), 3),
            "best_us_tensor": round(best_modes["tensor"], 3), "best_us_mx": round(best_modes["mx"], 3),
            "best": plan_dict(best),
@@ -279,7 +279,8 @@ def sweep_point(skg, torch, M, N, K, pool_bytes, reps, stream, log, kinds=None):
         return None
     results.sort(key=lambda r: r[0])
     best_us, best = results[0]
-    rec = {"M": M, "N": N, "K": K, "slots": slots, "tiled": "ring2", "best_us": round(best_us, 3),
+    rec = {"M": M, "N": N, "K": K, "slots": slots, "tiled": "ring2", "dot_wave1": "direct",
+           "best_us": round(best_us, 3),
            "best": plan_dict(best),
            "candidates": [[round(us, 3), plan_dict(p)] for us, p in results]}
     log.write(json.dumps(rec) + "\n")
@@ -344,6 +345,9 @@ def emit_table(files, out_path=TABLE):
                 us, plan = (c[0], c[-1])
                 # TILED timings of earlier tiled kernels mean other plans
                 if plan["kind"] == 3 and r.get("tiled") != "ring2":
+                    continue
+                # so do one-wave dot timings from before its direct-store path
+                if plan["kind"] == 1 and plan["threads"] == 64 and r.get("dot_wave1") != "direct":
                     continue
                 ident = tuple(plan.get(f, 0) for f in ("kind", "threads", "cols", "splits", "depth",
                                                           "waves_m", "reduce", "flags"))

@@ -139,7 +139,7 @@ def test_f32_output_small_integers_exact(skg, M, N, K):
 def _quant_plans(skg, M, N, K):
     plans = [("default", None)]
     if M <= 16:
-        for T, C in ((256, 1), (512, 1), (1024, 1), (256, 2), (256, 4)):
+        for T, C in ((64, 1), (256, 1), (512, 1), (1024, 1), (256, 2), (256, 4)):
             p = skg.make_plan(skg.KIND_DOT, T, C)
             try:
                 skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)

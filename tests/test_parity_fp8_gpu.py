@@ -40,6 +40,12 @@ def _plans(skg, M, N, K):
                     continue
                 plans.append((f"dot_t{T}_c{C}", p))
                 break
+            p = skg.make_plan(skg.KIND_DOT, 64, C)  # one wave: no LDS
+            try:
+                skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
+                plans.append((f"dot_t64_c{C}", p))
+            except skg.SkinnyGemmError:
+                pass
     mt = (M + 15) // 16
     nb = 2 if mt <= 3 else 1
     for (T, S, D, red) in ((256, 4, 1, skg.REDUCE_LAST), (128, 3, 2, skg.REDUCE_KERNEL),

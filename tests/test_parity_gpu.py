@@ -59,6 +59,12 @@ def _kernel_plans(skg, M, N, K):
                         continue
                     plans.append((f"dot_c{cols}_t{threads}_f{flags}", p))
                     break
+                p = skg.make_plan(skg.KIND_DOT, 64, cols=cols, flags=flags)  # one wave: no LDS
+                try:
+                    skg.plan_complete(M, N, K, p)
+                    plans.append((f"dot_c{cols}_t64_f{flags}", p))
+                except skg.SkinnyGemmError:
+                    pass
     mt = (M + 15) // 16
     nb = 4 if mt >= 4 else (2 if mt >= 2 else 1)
     threads = 128 if nb * mt > 16 else 256
