@@ -23,6 +23,9 @@ constexpr long kMaxBufferBytes = 0x7FFFFFFFL;  // one buffer resource covers < 2
 
 // DOT: vectors (16 B) per thread per column that the kernel is built for.
 constexpr int kDotVecs[] = {1, 2, 3, 4, 6, 8, 12, 14, 16};
+// One-wave dot workgroups (64 threads) store without the LDS reduction for
+// M up to this (larger M run 64 threads through the general kernel).
+constexpr int kDotOneWaveMaxM = 8;
 // Registers a DOT thread holds: C rows of W and M rows of x, V 16-byte
 // vectors each, x counted twice (the compiler widens x to fp32 ahead of
 // use), and C*M accumulators.  Only the 256 architectural VGPRs feed VALU

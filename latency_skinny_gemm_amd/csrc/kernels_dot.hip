@@ -25,8 +25,10 @@
 
 namespace skg {
 
-template <int M, int C, int V, bool DOT2>
-__global__ void __launch_bounds__((dot_max_threads(M, C, V, DOT2)))
+// W1: the workgroup is one wave (its own instantiation, so the multi-wave
+// kernels compile exactly as without it).
+template <int M, int C, int V, bool DOT2, bool W1>
+__global__ void __launch_bounds__((W1 ? 64 : dot_max_threads(M, C, V, DOT2)))
     dot_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
                const uint16_t *__restrict__ bias, void *__restrict__ out, int N, int K,
                int out_f32) {
@@ -74,7 +76,7 @@ __global__ void __launch_bounds__((dot_max_threads(M, C, V, DOT2)))
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
     const int lane = t & 63;
     const int nw = T >> 6;
-    if (nw == 1) {
+    if constexpr (W1) {
         // One wave: its sums are the totals, in every lane, so lane c*M + m
         // stores output (c, m) with no LDS round trip and no barrier.  The
         // sum starts from 0 as the cross-wave sum below does: same bits.
@@ -119,7 +121,15 @@ typedef int (*DotLaunch)(const SkgPlan &, const void *, const void *, const void
 template <int M, int C, int V, bool DOT2>
 int launch_dot_t(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
                  int N, int K, int out_f32, hipStream_t stream) {
-    hipLaunchKernelGGL((dot_kernel<M, C, V, DOT2>), dim3(p.grid), dim3(p.threads), 0, stream,
+    if constexpr (M <= kDotOneWaveMaxM) {
+        if (p.threads == 64) {
+            hipLaunchKernelGGL((dot_kernel<M, C, V, DOT2, true>), dim3(p.grid), dim3(64), 0,
+                               stream, (const uint16_t *)x, (const uint16_t *)W,
+                               (const uint16_t *)bias, out, N, K, out_f32);
+            return (int)hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((dot_kernel<M, C, V, DOT2, false>), dim3(p.grid), dim3(p.threads), 0, stream,
                        (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)bias,
                        out, N, K, out_f32);
     return (int)hipGetLastError();

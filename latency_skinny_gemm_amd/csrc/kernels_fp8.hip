@@ -68,9 +68,11 @@ __device__ __forceinline__ unsigned load_byte(Rsrc r, unsigned off) {
 // fused form of the "sglang PR #28333" page's static quant kernel): each
 // 16-element vector is two 16-byte bf16 loads, turned into 16 e4m3 codes
 // exactly as the standalone quantisation kernel does.
-// C output columns per workgroup share each x load.
-template <int M, int C, int V, bool MX, bool QX>
-__global__ void __launch_bounds__((fp8_dot_max_threads(M, C, V, MX, QX)))
+// C output columns per workgroup share each x load.  W1: the workgroup is
+// one wave (its own instantiation, so the multi-wave kernels compile exactly
+// as without it).
+template <int M, int C, int V, bool MX, bool QX, bool W1>
+__global__ void __launch_bounds__((W1 ? 64 : fp8_dot_max_threads(M, C, V, MX, QX)))
     fp8_dot_kernel(const void *__restrict__ x, const uint8_t *__restrict__ W,
                    const uint16_t *__restrict__ bias, const float *__restrict__ sx,
                    const float *__restrict__ sw, const uint8_t *__restrict__ xe,
@@ -159,7 +161,7 @@ __global__ void __launch_bounds__((fp8_dot_max_threads(M, C, V, MX, QX)))
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int lane = t & 63;
     const int nw = T >> 6;
-    if (nw == 1) {
+    if constexpr (W1) {
         // One wave: its sums are the totals, in every lane, so lane c*M + m
         // stores output (c, m) with no LDS round trip and no barrier (the
         // same bits as the cross-wave sum below, which starts from 0 too).
@@ -387,9 +389,17 @@ typedef int (*Fp8MfmaLaunch)(const SkgPlan &, const Fp8Args &, float *, unsigned
 
 template <int M, int C, int V, bool MX, bool QX>
 int launch_fp8_dot_t(const SkgPlan &p, const Fp8Args &a, int N, int K, hipStream_t stream) {
-    hipLaunchKernelGGL((fp8_dot_kernel<M, C, V, MX, QX>), dim3(p.grid), dim3(p.threads), 0, stream,
-                       a.x, (const uint8_t *)a.W, (const uint16_t *)a.bias, a.sx, a.sw, a.xe,
-                       a.we, a.out, N, K, a.out_f32);
+    if constexpr (M <= kDotOneWaveMaxM) {
+        if (p.threads == 64) {
+            hipLaunchKernelGGL((fp8_dot_kernel<M, C, V, MX, QX, true>), dim3(p.grid), dim3(64), 0,
+                               stream, a.x, (const uint8_t *)a.W, (const uint16_t *)a.bias, a.sx,
+                               a.sw, a.xe, a.we, a.out, N, K, a.out_f32);
+            return (int)hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((fp8_dot_kernel<M, C, V, MX, QX, false>), dim3(p.grid), dim3(p.threads), 0,
+                       stream, a.x, (const uint8_t *)a.W, (const uint16_t *)a.bias, a.sx, a.sw,
+                       a.xe, a.we, a.out, N, K, a.out_f32);
     return (int)hipGetLastError();
 }
 
