@@ -455,8 +455,9 @@ def check_samples(samples):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the GEMM is replicated or sharded per GPU with no collective; see the design notes)",
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              "(each GPU runs the GEMM on its own shard of W with no collective, so one GPU's "
+              "throughput is the figure)",
               file=sys.stderr)
         return 2
     import torch
@@ -512,7 +513,7 @@ def main():
         return gr
 
     with torch.cuda.stream(stream):
-        skg.reserve(Ms, N_DIM, 256)
+        skg.reserve(Ms, N_DIM, K_DIM, 256)
         # eager warm-up of every plan (and a first correctness sample below)
         for M in M_VALUES:
             launch(0, M)

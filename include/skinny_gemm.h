@@ -186,12 +186,18 @@ int skinny_gemm_plan_complete(int M, int N, int K, int dtype, SkgPlan *plan);
 int skinny_gemm_bf16_planned(const void *x, const void *W, const void *bias, void *out,
                              int M, int N, int K, const SkgPlan *plan, hipStream_t stream);
 
-/* Reserves split-K workspace for `stream` on the current device, large
- * enough for any plan with M <= max_M, N <= max_N and splits <= max_S.
- * Allocates (hipMalloc) and zeroes the tile counters; call it before graph
- * capture.  Outside capture a call that needs more grows the workspace
- * itself; during capture it returns SKG_ERR_WORKSPACE instead. */
-int skinny_gemm_reserve(int max_M, int max_N, int max_S, hipStream_t stream);
+/* Reserves workspace for `stream` on the current device, large enough for
+ * any call with M <= max_M, N <= max_N, K <= max_K and a plan of at most
+ * max_S splits: the split partials (fp32 [S][M][N]) plus, for
+ * skinny_gemm_fp8_quant plans that quantise x before the GEMM, room for its
+ * M*K e4m3 codes.  max_K = 0 reserves no such room (enough for every other
+ * entry point).  Allocates (hipMalloc) and zeroes the tile counters; call it
+ * before graph capture.  Outside capture a call that needs more grows the
+ * workspace itself; during capture it returns SKG_ERR_WORKSPACE instead.
+ * SKG_ERR_INVALID_ARG if max_M, max_N or max_S is below 1, max_M exceeds
+ * SKG_MAX_M, max_S exceeds 256, max_K is negative, or max_K * 1024 bytes
+ * reaches 2 GiB. */
+int skinny_gemm_reserve(int max_M, int max_N, int max_K, int max_S, hipStream_t stream);
 
 /* bf16 GEMM with fp32 output (router logits): out[m, n] = fp32 value of the
  * fp32-accumulated sum plus bias, with no bf16 rounding.  The router split-K

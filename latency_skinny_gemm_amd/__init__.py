@@ -109,7 +109,7 @@ def _load():
     L.skinny_gemm_plan_on.restype = I
     L.skinny_gemm_plan_complete.argtypes = [I, I, I, I, PP]
     L.skinny_gemm_plan_complete.restype = I
-    L.skinny_gemm_reserve.argtypes = [I, I, I, P]
+    L.skinny_gemm_reserve.argtypes = [I, I, I, I, P]
     L.skinny_gemm_reserve.restype = I
     L.skinny_gemm_release_all.argtypes = []
     L.skinny_gemm_release_all.restype = I
@@ -361,12 +361,15 @@ def plan_complete(M, N, K, p, dtype=DTYPE_BF16):
     return q
 
 
-def reserve(max_M, max_N, max_S, stream=None):
-    """Reserves split-K workspace for `stream` (else the current stream) on
-    the stream's device."""
+def reserve(max_M, max_N, max_K, max_S, stream=None):
+    """Reserves workspace for `stream` (else the current stream) on the
+    stream's device: for calls with M <= max_M, N <= max_N, K <= max_K and
+    at most max_S splits (max_K = 0: no room for gemm_fp8_quant's quantised
+    x)."""
     s = torch.cuda.current_stream() if stream is None else stream
     with torch.cuda.device(s.device):
-        _check(_load().skinny_gemm_reserve(max_M, max_N, max_S, ctypes.c_void_p(s.cuda_stream)),
+        _check(_load().skinny_gemm_reserve(max_M, max_N, max_K, max_S,
+                                           ctypes.c_void_p(s.cuda_stream)),
                "skinny_gemm_reserve")
 
 

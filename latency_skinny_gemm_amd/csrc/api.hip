@@ -158,11 +158,11 @@ int run_fp8(const void *x, const void *W, const void *bias, const skinny_fp8_sca
                     (p.kind == SKG_KIND_SPLITK &&
                      fp8_mfma_quant_ok(p.m_tiles, p.cols, p.depth, p.threads)));
     a.qx = fused;
-    // partials first (rounded to 256 bytes), then the quantised x if needed
-    const size_t part = (p.kind != SKG_KIND_DOT && p.splits > 1)
-                            ? (workspace_floats(p, M, N) + 63) / 64 * 64
-                            : 0;
-    const size_t qfloats = (quant_x && !fused) ? ((size_t)M * K + 3) / 4 : 0;
+    // partials first, then the quantised x if needed (the partials then
+    // rounded up to 256 bytes, so that x starts aligned)
+    const size_t qfloats = (quant_x && !fused) ? quant_floats(M, K) : 0;
+    size_t part = (p.kind != SKG_KIND_DOT && p.splits > 1) ? workspace_floats(p, M, N) : 0;
+    if (qfloats) part = round_floats(part);
     float *ws = nullptr;
     unsigned *tk = nullptr;
     if (part + qfloats > 0) {
@@ -264,6 +264,10 @@ int bf16_f32_common(const void *x, const void *W, const void *bias, float *out, 
 }
 
 }  // namespace
+
+size_t round_floats(size_t floats) { return (floats + 63) / 64 * 64; }
+
+size_t quant_floats(int M, int K) { return ((size_t)M * K + 3) / 4; }
 
 size_t workspace_floats(const SkgPlan &p, int M, int N) {
     return p.splits > 1 ? (size_t)p.splits * M * N : 0;
@@ -377,13 +381,19 @@ extern "C" int skinny_quant_e4m3(const void *x, const float *s, void *q, long n,
     return launch_quant_e4m3(x, s, q, n, stream) == (int)hipSuccess ? SKG_OK : SKG_ERR_HIP;
 }
 
-extern "C" int skinny_gemm_reserve(int max_M, int max_N, int max_S, hipStream_t stream) {
-    if (max_M < 1 || max_N < 1 || max_S < 1 || max_M > SKG_MAX_M || max_S > kMaxSplits)
+extern "C" int skinny_gemm_reserve(int max_M, int max_N, int max_K, int max_S,
+                                   hipStream_t stream) {
+    if (max_M < 1 || max_N < 1 || max_K < 0 || max_S < 1 || max_M > SKG_MAX_M ||
+        max_S > kMaxSplits || (long)SKG_MAX_M * max_K * 2 > kMaxBufferBytes)
         return SKG_ERR_INVALID_ARG;
     float *ws = nullptr;
     unsigned *tk = nullptr;
-    // the most tiles any plan can have: 16-column blocks of max_N
-    return acquire(stream, (size_t)max_S * max_M * max_N, (size_t)(max_N + 15) / 16, &ws, &tk);
+    // the largest request any call can make: split partials, rounded, then
+    // x quantised into the workspace (skinny_gemm_fp8_quant's two-launch
+    // plans); the most tiles any plan can have: 16-column blocks of max_N
+    const size_t floats =
+        round_floats((size_t)max_S * max_M * max_N) + quant_floats(max_M, max_K);
+    return acquire(stream, floats, (size_t)(max_N + 15) / 16, &ws, &tk);
 }
 
 extern "C" int skinny_gemm_release_all(void) {

@@ -171,8 +171,12 @@ int complete_plan(int M, int N, int K, int dtype, SkgPlan *p);
 int default_plan(int M, int N, int K, int dtype, int num_cus, SkgPlan *p);
 bool table_plan(int M, int N, int K, int dtype, SkgPlan *p);
 
-// Workspace needed by a completed plan (api.cpp).
+// Workspace needed by a completed plan (api.hip): fp32 split partials, and
+// room for M*K e4m3 codes where x is quantised before the GEMM (placed after
+// the partials, which are then rounded up to 64 floats).
 size_t workspace_floats(const SkgPlan &p, int M, int N);
+size_t round_floats(size_t floats);
+size_t quant_floats(int M, int K);
 int tile_count(const SkgPlan &p, int N);
 
 // Launchers (kernels_*.hip).  Return a hipError_t as int.

@@ -302,7 +302,7 @@ def run(args):
         pts = [p for p in pts if p[0] in args.M]
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        skg.reserve(128, 4096, 64)
+        skg.reserve(128, 4096, 0, 64)
     t0 = time.time()
     with open(args.out, "a") as log:
         for (M, N, K) in pts:

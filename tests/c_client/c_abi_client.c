@@ -103,7 +103,7 @@ int main(void) {
     plans[1].depth = 3;
     plans[1].reduce = SKG_REDUCE_KERNEL;
     const char *names[2] = {"split-K plan", "tiled plan"};
-    rc = skinny_gemm_reserve(M, N, 8, stream);
+    rc = skinny_gemm_reserve(M, N, K, 8, stream);
     if (rc != SKG_OK) {
         fprintf(stderr, "skinny_gemm_reserve: %s\n", skinny_gemm_status_string(rc));
         return 1;

@@ -370,9 +370,14 @@ def test_status_strings(lib):
 
 
 def test_reserve_rejects_bad_sizes(lib):
-    assert lib.skinny_gemm_reserve(0, 10, 1, None) == skg.ERR_INVALID_ARG
-    assert lib.skinny_gemm_reserve(513, 10, 1, None) == skg.ERR_INVALID_ARG
-    assert lib.skinny_gemm_reserve(4, 10, 10000, None) == skg.ERR_INVALID_ARG
+    assert lib.skinny_gemm_reserve(0, 10, 64, 1, None) == skg.ERR_INVALID_ARG
+    assert lib.skinny_gemm_reserve(513, 10, 64, 1, None) == skg.ERR_INVALID_ARG
+    assert lib.skinny_gemm_reserve(4, 10, 64, 10000, None) == skg.ERR_INVALID_ARG
+    assert lib.skinny_gemm_reserve(4, 10, 64, 257, None) == skg.ERR_INVALID_ARG
+    assert lib.skinny_gemm_reserve(4, 0, 64, 1, None) == skg.ERR_INVALID_ARG
+    assert lib.skinny_gemm_reserve(4, 10, -1, 1, None) == skg.ERR_INVALID_ARG
+    # 512 rows of 2-byte x at this K would pass 2 GiB
+    assert lib.skinny_gemm_reserve(4, 10, (1 << 21), 1, None) == skg.ERR_INVALID_ARG
 
 
 # ------------------------------------------------------------------ planner

@@ -260,3 +260,61 @@ def test_fused_quant_nan_row(skg):
         torch.cuda.synchronize()
         got = tolerance.widen(out.cpu())
         assert np.array_equal(np.isnan(got), np.isnan(ref)), f"[{name}]"
+
+
+def test_capture_after_reserve_with_quantised_x_in_workspace(skg):
+    # A tiled plan quantises x into the workspace before the GEMM, after the
+    # split partials (rounded up to 64 floats); with S*M*N = 3000 the
+    # rounding matters.  reserve(M, N, K, S) must cover both requests, and
+    # the plain FP8 call with the same plan (partials only, unrounded), so
+    # that both can be captured with no eager call first.
+    import ctypes
+
+    M, N, K, S = 5, 300, 4096, 2
+    x = (torch.randn(M, K, generator=torch.Generator().manual_seed(5)) * 2).to(torch.bfloat16)
+    _, wq, _, sw = gen.fp8_inputs(M, N, K, "fp8_tensor", seed=6)
+    xd, wd = x.to(DEV), wq.to(DEV)
+    sxd, swd = _f32(0.013), sw.to(DEV)
+    xq = skg.quant_e4m3(xd, sxd)
+    plan = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_TILED, 256, 4, S, 3,
+                                                    skg.REDUCE_KERNEL), skg.DTYPE_FP8)
+    sc = skg.Fp8Scales()
+    sc.mode, sc.sx, sc.sw = skg.FP8_PER_TENSOR, sxd.data_ptr(), swd.data_ptr()
+    lib = skg.lib()
+    torch.cuda.synchronize()
+    skg.release_all()
+    stream = torch.cuda.Stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    out_q = torch.zeros(M, N, dtype=torch.bfloat16, device=DEV)
+    out_p = torch.zeros(M, N, dtype=torch.bfloat16, device=DEV)
+
+    def calls():
+        rq = lib.skinny_gemm_fp8_quant_planned(xd.data_ptr(), wd.data_ptr(), None, sxd.data_ptr(),
+                                               swd.data_ptr(), out_q.data_ptr(), skg.DTYPE_BF16,
+                                               M, N, K, ctypes.byref(plan), sptr)
+        rp = lib.skinny_gemm_fp8_planned(xq.data_ptr(), wd.data_ptr(), None, ctypes.byref(sc),
+                                         out_p.data_ptr(), M, N, K, ctypes.byref(plan), sptr)
+        return rq, rp
+    with torch.cuda.stream(stream):
+        skg.reserve(M, N, K, S)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        rcs = calls()
+    assert rcs == (skg.OK, skg.OK), rcs
+    with torch.cuda.stream(stream):
+        assert calls() == (skg.OK, skg.OK)
+    torch.cuda.synchronize()
+    eager_q, eager_p = out_q.clone(), out_p.clone()
+    # the fused quantisation and the quantise-then-GEMM path agree bit for bit
+    assert torch.equal(eager_q.view(torch.int16), eager_p.view(torch.int16))
+    for _ in range(3):
+        out_q.fill_(0)
+        out_p.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_q.view(torch.int16), eager_q.view(torch.int16))
+        assert torch.equal(out_p.view(torch.int16), eager_p.view(torch.int16))
+    del g
+    skg.release_all()

@@ -225,7 +225,7 @@ def test_graph_replays_match_eager(skg):
         x, w, b = gen.bf16_inputs(M, N, K, False, seed=M * N)
         data.append(_dev(x, w, b))
     with torch.cuda.stream(stream):
-        skg.reserve(128, 4096, 64)
+        skg.reserve(128, 4096, 0, 64)
         eager = [skg.gemm_bf16(x, w, b) for (x, w, b) in data]
     torch.cuda.synchronize()
     outs = [torch.empty_like(e) for e in eager]
@@ -266,7 +266,7 @@ def test_capture_needs_reserved_workspace(skg):
     assert rc == skg.ERR_WORKSPACE
     del g
     with torch.cuda.stream(stream):
-        skg.reserve(M, N, 16)
+        skg.reserve(M, N, K, 16)
         assert call() == skg.OK
     torch.cuda.synchronize()
     eager = out.clone()
