@@ -26,7 +26,9 @@
  * alignment for 128-bit loads).  Above M = 128 (the larger-M regime of the
  * "sglang PR #34042" page's M = 512 comparison) only the tiled kernels run,
  * in row blocks of 128, and K must also be a multiple of 32 (bf16) or 128
- * (FP8).  M == 0 or N == 0 is a successful no-op.
+ * (FP8).  M * N < 2^31, and a plan must exist whose launch counts fewer
+ * than 2^32 work-items (grid * threads; about N * 256 for the dot kernel
+ * at large K).  M == 0 or N == 0 is a successful no-op.
  * Anything else out of domain returns SKG_ERR_UNSUPPORTED: there is no
  * silent fallback (the "sglang PR #34042" page: an explicit request errors
  * instead of falling back).
@@ -178,7 +180,8 @@ int skinny_gemm_plan(int M, int N, int K, int dtype, SkgPlan *plan);
 
 /* Checks a caller-made plan for (M, N, K, dtype) and fills its derived
  * fields.  SKG_ERR_INVALID_ARG if the plan cannot cover the problem or
- * exceeds a kernel limit.  No HIP call. */
+ * exceeds a kernel limit (among them: grid * threads below 2^32, the
+ * launch's 32-bit work-item count).  No HIP call. */
 int skinny_gemm_plan_complete(int M, int N, int K, int dtype, SkgPlan *plan);
 
 /* bf16 GEMM with a caller-made plan (completed as above): for sweeps and

@@ -449,6 +449,34 @@ def test_complete_rejects_invalid_plans(lib, plan, M, N, K):
     assert e.value.status == skg.ERR_INVALID_ARG
 
 
+def test_launch_size_limits(lib):
+    # the output plane is indexed by int: M * N < 2^31, else unsupported
+    p = skg.SkgPlan()
+    assert lib.skinny_gemm_plan(2, 1 << 30, 64, skg.DTYPE_BF16, ctypes.byref(p)) == \
+        skg.ERR_UNSUPPORTED
+    # within that domain the automatic planner refuses what no plan can launch
+    assert lib.skinny_gemm_plan(1, (1 << 31) - 1, 64, skg.DTYPE_BF16, ctypes.byref(p)) == \
+        skg.ERR_UNSUPPORTED
+    q = skg.plan(1, 1 << 24, 64)
+    assert q.grid * q.threads < (1 << 32)
+    # grid * threads is a 32-bit work-item count: 2^26 one-wave workgroups
+    # of 64 threads reach 2^32 and are refused; one fewer column fits
+    n = 1 << 26
+    with pytest.raises(skg.SkinnyGemmError) as e:
+        skg.plan_complete(1, n, 64, skg.make_plan(skg.KIND_DOT, 64, 1))
+    assert e.value.status == skg.ERR_INVALID_ARG
+    assert skg.plan_complete(1, n - 1, 64, skg.make_plan(skg.KIND_DOT, 64, 1)).grid == n - 1
+    assert skg.plan_complete(1, n, 64, skg.make_plan(skg.KIND_DOT, 64, 2)).grid == n // 2
+    with pytest.raises(skg.SkinnyGemmError):
+        skg.plan_complete(1, n, 128, skg.make_plan(skg.KIND_DOT, 64, 1), skg.DTYPE_FP8)
+    # split plans multiply the column groups by the splits
+    with pytest.raises(skg.SkinnyGemmError):
+        skg.plan_complete(8, 1 << 24, 2048, skg.make_plan(skg.KIND_SPLITK, 256, 1, 64, 2,
+                                                          skg.REDUCE_KERNEL))
+    assert skg.plan_complete(8, 1 << 16, 2048, skg.make_plan(skg.KIND_SPLITK, 256, 1, 64, 2,
+                                                             skg.REDUCE_KERNEL)).grid == 4096 * 64
+
+
 def test_complete_drops_empty_splits(lib):
     # K = 2880 has 90 steps of 32; 64 splits of ceil(90/64) = 2 steps leave
     # only 45 non-empty splits
