@@ -156,6 +156,16 @@ def _launch(dev, stream, fn, *args):
         return fn(*args, ctypes.c_void_p(s.cuda_stream))
 
 
+def _empty(shape, dtype, device, stream):
+    """A new output tensor, allocated for the stream the call runs on (so the
+    caching allocator does not hand its memory to other work on another
+    stream while the call may still write it)."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -185,7 +195,7 @@ def gemm_bf16(x, W, bias=None, out=None, stream=None):
     """out[M,N] = x[M,K] @ W[N,K]^T (+ bias), bf16, on the library's plan."""
     M, N, K = _check_tensors(x, W, bias, out, torch.bfloat16)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        out = _empty((M, N), torch.bfloat16, x.device, stream)
     rc = _launch(_one_device(x, W, bias, out), stream, _load().skinny_gemm_bf16, _ptr(x), _ptr(W),
                  _ptr(bias), None, _ptr(out), M, N, K)
     _check(rc, f"skinny_gemm_bf16(M={M}, N={N}, K={K})")
@@ -196,7 +206,7 @@ def gemm_bf16_planned(x, W, p, bias=None, out=None, stream=None):
     """As gemm_bf16, with a caller-made SkgPlan (completed by the library)."""
     M, N, K = _check_tensors(x, W, bias, out, torch.bfloat16)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        out = _empty((M, N), torch.bfloat16, x.device, stream)
     rc = _launch(_one_device(x, W, bias, out), stream, _load().skinny_gemm_bf16_planned, _ptr(x),
                  _ptr(W), _ptr(bias), _ptr(out), M, N, K, ctypes.byref(p))
     _check(rc, f"skinny_gemm_bf16_planned(M={M}, N={N}, K={K}, {p})")
@@ -208,7 +218,7 @@ def gemm_bf16_f32(x, W, bias=None, out=None, plan=None, stream=None):
     rounding); the library's plan, or a caller-made one."""
     M, N, K = _check_tensors(x, W, bias, None, torch.bfloat16)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+        out = _empty((M, N), torch.float32, x.device, stream)
     elif out.dtype != torch.float32 or tuple(out.shape) != (M, N) or not out.is_contiguous():
         raise TypeError("out must be contiguous float32 [M, N]")
     dev = _one_device(x, W, bias, out)
@@ -249,7 +259,7 @@ def gemm_fp8_quant(x, wq, sx, sw, bias=None, out_dtype=torch.bfloat16, out=None,
         raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
     code = DTYPE_F32 if out_dtype == torch.float32 else DTYPE_BF16
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+        out = _empty((M, N), out_dtype, x.device, stream)
     elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or not out.is_contiguous():
         raise TypeError(f"out must be contiguous {out_dtype} [M, N]")
     args = (_ptr(x), _ptr(wq), _ptr(bias), _ptr(sx), _ptr(sw), _ptr(out), code, M, N, K)
@@ -269,7 +279,7 @@ def quant_e4m3(x, s, out=None, stream=None):
         raise TypeError("x must be a contiguous bf16 device tensor")
     _scalar_f32("s", s)
     if out is None:
-        out = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+        out = _empty(x.shape, torch.float8_e4m3fn, x.device, stream)
     elif out.dtype not in (torch.float8_e4m3fn, torch.uint8) or out.shape != x.shape \
             or not out.is_contiguous():
         raise TypeError("out must be a contiguous float8_e4m3fn tensor of x's shape")
@@ -279,7 +289,7 @@ def quant_e4m3(x, s, out=None, stream=None):
     return out
 
 
-def _fp8_args(xq, wq, sx, sw, xe, we, bias, out):
+def _fp8_args(xq, wq, sx, sw, xe, we, bias, out, stream):
     """Checks FP8 operands; returns (M, N, K, Fp8Scales, out)."""
     for name, t in (("xq", xq), ("wq", wq)):
         if t.dim() != 2 or not t.is_cuda or not t.is_contiguous():
@@ -308,7 +318,7 @@ def _fp8_args(xq, wq, sx, sw, xe, we, bias, out):
                              or not bias.is_cuda):
         raise TypeError("bias must be bf16 [N] on the device")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+        out = _empty((M, N), torch.bfloat16, xq.device, stream)
     elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
         raise TypeError("out must be contiguous bf16 [M, N]")
     return M, N, K, sc, out
@@ -316,7 +326,7 @@ def _fp8_args(xq, wq, sx, sw, xe, we, bias, out):
 
 def gemm_fp8(xq, wq, sx=None, sw=None, xe=None, we=None, bias=None, out=None, stream=None):
     """FP8 e4m3 GEMM, bf16 out: per-tensor (sx, sw) or MX (xe, we) scales."""
-    M, N, K, sc, out = _fp8_args(xq, wq, sx, sw, xe, we, bias, out)
+    M, N, K, sc, out = _fp8_args(xq, wq, sx, sw, xe, we, bias, out, stream)
     rc = _launch(_one_device(xq, wq, sx, sw, xe, we, bias, out), stream, _load().skinny_gemm_fp8,
                  _ptr(xq), _ptr(wq), _ptr(bias), ctypes.byref(sc), _ptr(out), M, N, K)
     _check(rc, f"skinny_gemm_fp8(M={M}, N={N}, K={K}, mode={sc.mode})")
@@ -325,7 +335,7 @@ def gemm_fp8(xq, wq, sx=None, sw=None, xe=None, we=None, bias=None, out=None, st
 
 def gemm_fp8_planned(xq, wq, p, sx=None, sw=None, xe=None, we=None, bias=None, out=None,
                      stream=None):
-    M, N, K, sc, out = _fp8_args(xq, wq, sx, sw, xe, we, bias, out)
+    M, N, K, sc, out = _fp8_args(xq, wq, sx, sw, xe, we, bias, out, stream)
     rc = _launch(_one_device(xq, wq, sx, sw, xe, we, bias, out), stream,
                  _load().skinny_gemm_fp8_planned, _ptr(xq), _ptr(wq), _ptr(bias), ctypes.byref(sc),
                  _ptr(out), M, N, K, ctypes.byref(p))

@@ -382,3 +382,20 @@ def test_large_M_full_size_sampled(skg, bias):
     got = out.cpu()[rows][:, cols]
     ok, msg = tolerance.check(got, ref, K)
     assert ok, msg
+
+
+def test_binding_side_stream_matches_current_stream(skg):
+    # the binding runs a call on the stream it is given (its new output is
+    # allocated for that stream): the same bits as on the current stream
+    M, N, K = 12, 384, 7168
+    x, w, b = _dev(*gen.bf16_inputs(M, N, K, True, seed=321))
+    ref = skg.gemm_bf16(x, w, b)
+    ref32 = skg.gemm_bf16_f32(x, w, b)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = skg.gemm_bf16(x, w, b, stream=side)
+    got32 = skg.gemm_bf16_f32(x, w, b, stream=side)
+    side.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(got32.view(torch.int32), ref32.view(torch.int32))
