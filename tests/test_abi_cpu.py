@@ -388,12 +388,13 @@ BF16 = [p for p in configs.all_points() if p.dtype == "bf16"]
 @pytest.mark.parametrize("p", BF16, ids=lambda p: p.key())
 def test_default_rule_without_table(lib, p):
     # a made-up 200-CU device never uses the MI355X table: the pages' rule
-    # (dot product for M <= 4 or K < 2048), else the tiled kernel (split-K
-    # only where K is not a multiple of 32)
+    # (dot product for M <= 4 or K < 2048, here also up to 16 rows at
+    # N <= 512 with x of at most 192 KB), else the tiled kernel (split-K only
+    # where K is not a multiple of 32)
     q = skg.plan_on(p.M, p.N, p.K, 200)
     if p.M > 128:
         want = skg.KIND_TILED  # above 128 rows only the tiled kernel runs
-    elif p.M <= 4 or p.K < 2048:
+    elif p.M <= 4 or p.K < 2048 or (p.M <= 16 and p.N <= 512 and p.M * p.K <= 98304):
         want = skg.KIND_DOT
     else:
         want = skg.KIND_TILED if p.K % 32 == 0 else skg.KIND_SPLITK
@@ -417,8 +418,8 @@ def test_library_plan_is_valid_and_covers(lib, p):
 def test_split_count_follows_cu_count(lib):
     # the default rule (no table below 256 CUs) sizes the grid to the device
     for K, kind in ((7168, skg.KIND_TILED), (7176, skg.KIND_SPLITK)):
-        small = skg.plan_on(8, 256, K, 64)
-        big = skg.plan_on(8, 256, K, 200)
+        small = skg.plan_on(16, 1024, K, 64)
+        big = skg.plan_on(16, 1024, K, 200)
         assert small.kind == big.kind == kind and small.from_table == big.from_table == 0
         assert small.splits < big.splits
         assert small.grid >= 48 and big.grid >= 150
