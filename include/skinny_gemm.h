@@ -171,11 +171,14 @@ int skinny_gemm_fp8_planned(const void *x, const void *W, const void *bias,
 
 /* The dispatcher's decision for (M, N, K, dtype), written to *plan; no HIP
  * call.  The "vllm PR #48774" page's rule: a tuned (K, N) -> {M: config}
- * table first, else the default: the dot product when M <= 4 or K < 2048
- * (the page's threshold; for bf16 also up to 16 rows when N <= 512 and
- * M * K <= 98304), else the tiled MFMA kernel (bf16 above 4 rows,
- * FP8 above 16, and from 5 to 16 rows when N < 2048), else split-K (where
- * K is not a multiple of 32, or FP8 at 5 to 16 rows with N >= 2048).  Our table comes from a sweep on MI355X.  dtype: SKG_DTYPE_BF16,
+ * table first (ours, from a sweep on MI355X), else a default rule.
+ *   bf16: the dot product when M <= 4 or K < 2048 (the page's threshold),
+ *         or up to 16 rows when N <= 512 and M * K <= 98304; else the
+ *         tiled MFMA kernel; split-K where K is not a multiple of 32.
+ *   FP8:  the dot product when M <= 4; from 5 to 16 rows split-K without
+ *         a K split when N >= 2048, else the tiled kernel; above 16 rows
+ *         the tiled kernel (K % 128 == 0), else split-K.
+ * dtype: SKG_DTYPE_BF16,
  * SKG_DTYPE_FP8 (per-tensor scales) or SKG_DTYPE_FP8_MX (MX block scales;
  * skinny_gemm_fp8 plans with it when given SKG_FP8_MX32).  Returns SKG_OK, or
  * the error the GEMM call would return for these sizes. */
