@@ -415,6 +415,31 @@ def test_library_plan_is_valid_and_covers(lib, p):
     _check_coverage(q, p.M, p.N, p.K)
 
 
+def test_default_rule_details(lib):
+    # bf16 dot plans: the dot instruction, two vectors per thread above 4
+    # rows, and 4 (else 2) columns while two workgroups per CU remain
+    q = skg.plan_on(12, 256, 6144, 255)
+    assert (q.kind, q.flags, q.depth, q.cols) == (skg.KIND_DOT, skg.FLAG_DOT2, 2, 1)
+    assert q.threads == 384
+    q = skg.plan_on(2, 4096, 7168, 255)
+    assert (q.kind, q.cols) == (skg.KIND_DOT, 4) and q.grid == 1024
+    q = skg.plan_on(2, 768, 7168, 255)
+    assert (q.kind, q.cols) == (skg.KIND_DOT, 1)  # 2 columns would leave 384 < 510 workgroups
+    # past the x bound of the small-N rule: the tiled kernel
+    assert skg.plan_on(16, 512, 7168, 255).kind == skg.KIND_TILED
+    assert skg.plan_on(12, 512, 7168, 255).kind == skg.KIND_DOT
+    # FP8 from 5 to 16 rows: no K split with N >= 2048 (128 groups of 16
+    # columns fill half of 255 CUs), else tiled; above 16 rows tiled
+    q = skg.plan_on(8, 2048, 4096, 255, skg.DTYPE_FP8)
+    assert (q.kind, q.splits, q.depth) == (skg.KIND_SPLITK, 1, 2)
+    assert skg.plan_on(12, 1024, 4096, 255, skg.DTYPE_FP8).kind == skg.KIND_TILED
+    assert skg.plan_on(24, 8192, 4096, 255, skg.DTYPE_FP8).kind == skg.KIND_TILED
+    q = skg.plan_on(2, 4096, 4096, 255, skg.DTYPE_FP8)
+    assert (q.kind, q.cols) == (skg.KIND_DOT, 1)
+    # FP8 K not a multiple of 128 above 16 rows: split-K
+    assert skg.plan_on(24, 4096, 4112, 255, skg.DTYPE_FP8).kind == skg.KIND_SPLITK
+
+
 def test_split_count_follows_cu_count(lib):
     # the default rule (no table below 256 CUs) sizes the grid to the device
     for K, kind in ((7168, skg.KIND_TILED), (7176, skg.KIND_SPLITK)):
