@@ -227,10 +227,12 @@ int skinny_gemm_bf16_f32_planned(const void *x, const void *W, const void *bias,
  * The quantisation is the static FP8 quant kernel of the "sglang PR #28333"
  * page (a given scale, one reciprocal, a product, a clamp, the cast to e4m3
  * with round-to-nearest-even), followed by that page's per-tensor GEMM.
- * The dot-product plan and the MFMA split-K plan (up to 32 rows) quantise x
- * as they load it, so the call is one launch (the automatic dot plan then
- * shares each x load over four or two columns where it can); other plans
- * quantise x into the workspace first (a second launch).  x: DEVICE bf16 [M, K], 16-byte aligned; W: DEVICE e4m3fn
+ * The dot-product plan quantises x as it loads it, so the call is one
+ * launch (the automatic dot plan then shares each x load over four or two
+ * columns where it can).  A caller's MFMA split-K plan (up to 32 rows) does
+ * too; the automatic plan, and every other plan, quantises x into the
+ * workspace first (a second launch: faster than quantising in every
+ * workgroup once the split-K kernel takes over from the dot kernel).  x: DEVICE bf16 [M, K], 16-byte aligned; W: DEVICE e4m3fn
  * [N, K], 16-byte aligned; sx, sw: DEVICE fp32 scalars, 4-byte aligned;
  * K % 16 == 0.  out_dtype: SKG_DTYPE_BF16 (bf16 out, 2-byte aligned) or
  * SKG_DTYPE_F32 (fp32 out, 4-byte aligned).  NaN in x gives NaN outputs. */
