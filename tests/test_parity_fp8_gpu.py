@@ -171,3 +171,32 @@ def test_fp8_runs_bitwise_deterministic(skg):
             a = _run(skg, plan, xd, wd, None, **_scales(mode, s1, s2))
             b = _run(skg, plan, xd, wd, None, **_scales(mode, s1, s2))
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{mode} [{name}]"
+
+
+# FP8 shapes off the dispatch table, one per branch of the default rule: the
+# dot kernel, split-K without a K split (N >= 2048), the tiled kernel (from 5
+# rows below N = 2048, and above 16 rows), split-K for K % 128 != 0
+FP8_DEFAULT_RULE_SHAPES = [(2, 1024, 1024), (8, 2048, 1024), (12, 1024, 2048), (24, 512, 1024),
+                           (24, 512, 1040)]
+
+
+@pytest.mark.parametrize("shape", FP8_DEFAULT_RULE_SHAPES, ids=str)
+def test_fp8_default_rule_plans_within_tolerance(skg, shape):
+    M, N, K = shape
+    q = skg.plan(M, N, K, skg.DTYPE_FP8)
+    assert q.from_table == 0
+    if M <= 4:
+        want = skg.KIND_DOT
+    elif M <= 16 and N >= 2048:
+        want = skg.KIND_SPLITK
+    else:
+        want = skg.KIND_TILED if K % 128 == 0 else skg.KIND_SPLITK
+    assert q.kind == want, q
+    if want == skg.KIND_SPLITK and M <= 16:
+        assert q.splits == 1
+    xq, wq, s1, s2 = gen.fp8_inputs(M, N, K, "fp8_tensor", seed=M + N + K)
+    bias = (torch.randn(N, generator=torch.Generator().manual_seed(K)) * 0.5).to(torch.bfloat16)
+    ref = _oracle("fp8_tensor", xq, wq, s1, s2, bias)
+    out = _run(skg, None, xq.to(DEV), wq.to(DEV), bias.to(DEV), **_scales("fp8_tensor", s1, s2))
+    ok, msg = tolerance.check(out, ref, K)
+    assert ok, f"{shape} plan {q}: {msg}"

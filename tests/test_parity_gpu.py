@@ -399,3 +399,26 @@ def test_binding_side_stream_matches_current_stream(skg):
     side.synchronize()
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
     assert torch.equal(got32.view(torch.int32), ref32.view(torch.int32))
+
+
+# shapes off the dispatch table, one per branch of the default rule: the
+# dot kernel with 4 and with 1 column(s), the small-N dot kernel above 4
+# rows, the tiled kernel, and split-K for K not a multiple of 32
+DEFAULT_RULE_SHAPES = [(2, 2048, 1024), (3, 300, 2048), (12, 256, 3072), (6, 1536, 2048),
+                       (24, 640, 2048), (8, 700, 2056)]
+
+
+@pytest.mark.parametrize("shape", DEFAULT_RULE_SHAPES, ids=str)
+def test_default_rule_plans_within_tolerance(skg, shape):
+    M, N, K = shape
+    q = skg.plan(M, N, K)
+    assert q.from_table == 0
+    if M <= 4 or (N <= 512 and M * K <= 98304):
+        assert q.kind == skg.KIND_DOT
+    else:
+        assert q.kind == (skg.KIND_TILED if K % 32 == 0 else skg.KIND_SPLITK)
+    x, w, b = gen.bf16_inputs(M, N, K, True, seed=M + N + K)
+    ref = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w), gen.bits16(b), threads=16)
+    out = _run(skg, *_dev(x, w, b), None)
+    ok, msg = tolerance.check(out, ref, K)
+    assert ok, f"{shape} plan {q}: {msg}"
