@@ -22,7 +22,7 @@ constexpr int kNumCusMI355X = 256;
 constexpr long kMaxBufferBytes = 0x7FFFFFFFL;  // one buffer resource covers < 2 GiB
 
 // DOT: vectors (16 B) per thread per column that the kernel is built for.
-constexpr int kDotVecs[] = {1, 2, 3, 4, 6, 8, 12, 14, 16};
+constexpr int kDotVecs[] = {1, 2, 3, 4, 6, 7, 8, 12, 14, 16};
 // One-wave dot workgroups (64 threads) store without the LDS reduction for
 // M up to this (larger M run 64 threads through the general kernel).
 constexpr int kDotOneWaveMaxM = 8;

@@ -153,6 +153,7 @@ DotLaunch pick_v(int V) {
     case 3: return dot_entry<M, C, 3, DOT2>();
     case 4: return dot_entry<M, C, 4, DOT2>();
     case 6: return dot_entry<M, C, 6, DOT2>();
+    case 7: return dot_entry<M, C, 7, DOT2>();
     case 8: return dot_entry<M, C, 8, DOT2>();
     case 12: return dot_entry<M, C, 12, DOT2>();
     case 14: return dot_entry<M, C, 14, DOT2>();
