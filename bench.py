@@ -290,7 +290,7 @@ def decode_section(skg, torch, stream, sptr, samples):
             res[f"N{N}_M{M}"] = {"us_per_call": round(us, 3), "p10_us": round(p10, 3),
                                  "p90_us": round(p90, 3),
                                  "GBps": round(byts / (us * 1e-6) / 1e9, 1),
-                                 "frac_of_8TBps": round(byts / (us * 1e-6) / 8e12, 4),
+                                 "frac_of_8TBps": round(byts / (us * 1e-6) / (PEAK_GBS * 1e9), 4),
                                  "TFLOPs": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1),
                                  "kernel": {1: "dot", 2: "splitk", 3: "tiled"}[p.kind]}
             del X, O
@@ -419,6 +419,7 @@ def fp8_section(skg, torch, stream, sptr, samples):
             res[f"M{M}_{mode}"] = {"us_per_call": round(us, 3), "p10_us": round(p10, 3),
                                    "p90_us": round(p90, 3),
                                    "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+                                   "frac_of_8TBps": round(byts / (us * 1e-6) / (PEAK_GBS * 1e9), 4),
                                    "TFLOPs": round(tflops, 1),
                                    "mfma_util": round(tflops / FP8_PEAK_TFLOPS, 4),
                                    "kernel": {1: "dot", 2: "splitk", 3: "tiled"}[skg.plan(
@@ -582,6 +583,7 @@ def main():
         per_m[M] = {"us_per_call": round(us, 3), "p10_us": round(ts[len(ts) // 10], 3),
                     "p90_us": round(ts[(9 * len(ts)) // 10], 3),
                     "GBps": round(call_bytes(M) / (us * 1e-6) / 1e9, 1),
+                    "frac_of_8TBps": round(call_bytes(M) / (us * 1e-6) / (PEAK_GBS * 1e9), 4),
                     "kernel": kind_name[plans[M].kind], "plan": {k: v for k, v in plans[M].as_dict().items()
                                                                 if k in ("threads", "cols", "splits", "depth", "reduce", "grid")}}
         del gr
