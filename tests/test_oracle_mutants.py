@@ -32,6 +32,27 @@ MUTANTS = {
     "e4m3_bias": ("v = ldexp(8.0 + (double)m, e - 10);", "v = ldexp(8.0 + (double)m, e - 11);"),
     "mx_scale_index": ("oracle_decode_e8m0(xe[m * KB + b])", "oracle_decode_e8m0(xe[m * KB])"),
     "fp8_double_scale": ("double acc = dot * scale;", "double acc = dot * scale * (double)sw;"),
+    # FP8 bias placement: before the per-tensor scale product, dropped, and
+    # (MX) dropped or folded into the first block before its scales
+    "fp8_bias_before_scale": ("double acc = dot * scale;\n            if (bias)\n                acc += oracle_decode_bf16(bias[n]);",
+                              "double acc = dot;\n            if (bias)\n                acc += oracle_decode_bf16(bias[n]);\n            acc *= scale;"),
+    "fp8_bias_dropped": ("double acc = dot * scale;\n            if (bias)\n                acc += oracle_decode_bf16(bias[n]);",
+                         "double acc = dot * scale;\n            (void)bias;"),
+    "mx_bias_dropped": ("* block;\n            }\n            if (bias)\n                acc += oracle_decode_bf16(bias[n]);",
+                        "* block;\n            }\n            (void)bias;"),
+    "mx_bias_in_first_block": (
+        "double block = 0.0;\n"
+        "                for (long k = b * 32; k < b * 32 + 32; ++k)\n"
+        "                    block += oracle_decode_e4m3(xq[m * K + k]) * oracle_decode_e4m3(wq[n * K + k]);\n"
+        "                acc += oracle_decode_e8m0(xe[m * KB + b]) * oracle_decode_e8m0(we[n * KB + b]) * block;\n"
+        "            }\n"
+        "            if (bias)\n"
+        "                acc += oracle_decode_bf16(bias[n]);",
+        "double block = (b == 0 && bias) ? oracle_decode_bf16(bias[n]) : 0.0;\n"
+        "                for (long k = b * 32; k < b * 32 + 32; ++k)\n"
+        "                    block += oracle_decode_e4m3(xq[m * K + k]) * oracle_decode_e4m3(wq[n * K + k]);\n"
+        "                acc += oracle_decode_e8m0(xe[m * KB + b]) * oracle_decode_e8m0(we[n * KB + b]) * block;\n"
+        "            }"),
     "subnormal_quantum": ("e = -126;", "e = -125;"),
     "quant_divides": ("float v = (float)oracle_decode_bf16(x[i]) * inv;",
                       "float v = (float)oracle_decode_bf16(x[i]) / s;"),

@@ -333,6 +333,109 @@ def test_fp8_mx_exact_and_invariants():
                           oracle.gemm_fp8_tensor(xb, wb, 1.0, 1.0))
 
 
+# FP8 with bias.  Per-tensor: out = RNE_bf16(sx * sw * sum(xq * wq) + bias),
+# the scale product applied once, to the sum only, and the bias added after
+# it ("sglang PR #28333" page: the key source snippet adds the bias to the
+# GEMM's output; its motivation section makes the scales belong to the
+# product, applied once).  MX: the bias is added after every block's scaled
+# partial ("sglang PR #34042" page).  The scales here are non-unit powers of
+# two and the bias is large enough to move the rounded output, so a bias
+# placed before the scale product (shrunk by sx * sw) or dropped gives other
+# bits; the tests check that they would.
+
+def _int_bias(N, seed, lo=-3, hi=3):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(lo, hi + 1, (N,), generator=g).to(torch.bfloat16)
+
+
+def _small_int_codes(rows, K, seed):
+    g = torch.Generator().manual_seed(seed)
+    return gen.bits8(torch.randint(-2, 3, (rows, K), generator=g).float().to(torch.float8_e4m3fn))
+
+
+def test_fp8_per_tensor_bias_after_the_scale_exact():
+    sx, sw = 2.0 ** -3, 2.0 ** -2
+    # (a) small e4m3 integers: every value is a small exact rational
+    M, N, K = 4, 9, 64
+    xb, wb = _small_int_codes(M, K, 61), _small_int_codes(N, K, 62)
+    bias = _int_bias(N, 63)
+    bb = gen.bits16(bias)
+    out = oracle.gemm_fp8_tensor(xb, wb, sx, sw, bb)
+    dot = _e4m3_int(xb) @ _e4m3_int(wb).T  # units of 2^-18
+    s = Fraction(1, 32)
+    moved = 0
+    for m in range(M):
+        for n in range(N):
+            d = Fraction(int(dot[m, n]), 2 ** 18)
+            b = exact.bf16_code_to_fraction(bb[n])
+            want = exact.round_fraction(d * s + b, **exact.BF16)
+            assert exact.bf16_code_to_fraction(out[m, n]) == want, (m, n)
+            before = exact.round_fraction((d + b) * s, **exact.BF16)
+            dropped = exact.round_fraction(d * s, **exact.BF16)
+            moved += (before != want) and (dropped != want)
+    # the pin separates the right placement from both wrong ones
+    assert moved >= (M * N) // 2, moved
+    # (b) codes quantised from N(0,1) with the same scales and a bias of the
+    # outputs' own size
+    M, N, K = 3, 7, 256
+    xq, wq, _, _ = gen.fp8_inputs(M, N, K, "fp8_tensor", seed=64)
+    xb, wb = gen.bits8(xq), gen.bits8(wq)
+    dot = _e4m3_int(xb) @ _e4m3_int(wb).T
+    g = torch.Generator().manual_seed(65)
+    bias = (torch.randn(N, generator=g) * float(np.abs(dot).mean()) * 2.0 ** -23).to(torch.bfloat16)
+    bb = gen.bits16(bias)
+    out = oracle.gemm_fp8_tensor(xb, wb, sx, sw, bb)
+    for m in range(M):
+        for n in range(N):
+            want = exact.round_fraction(Fraction(int(dot[m, n]), 2 ** 18) * s
+                                        + exact.bf16_code_to_fraction(bb[n]), **exact.BF16)
+            assert exact.bf16_code_to_fraction(out[m, n]) == want, (m, n)
+
+
+def test_fp8_mx_bias_after_every_block_exact():
+    M, N, K = 3, 6, 128
+    # (a) small e4m3 integers, exponents 125..129: exact values
+    xb, wb = _small_int_codes(M, K, 71), _small_int_codes(N, K, 72)
+    rng = np.random.default_rng(73)
+    xe = rng.integers(125, 130, size=(M, K // 32)).astype(np.uint8)
+    we = rng.integers(125, 130, size=(N, K // 32)).astype(np.uint8)
+    bias = _int_bias(N, 74)
+    bb = gen.bits16(bias)
+    xi, wi = _e4m3_int(xb), _e4m3_int(wb)
+
+    def scaled(m, n, xe_, we_):
+        s = Fraction(0)
+        for blk in range(K // 32):
+            part = int(np.dot(xi[m, blk * 32:(blk + 1) * 32], wi[n, blk * 32:(blk + 1) * 32]))
+            s += Fraction(part, 2 ** 18) * Fraction(2) ** (int(xe_[m, blk]) - 127) \
+                * Fraction(2) ** (int(we_[n, blk]) - 127)
+        return s
+
+    out = oracle.gemm_fp8_mx(xb, wb, xe, we, bb)
+    moved = 0
+    for m in range(M):
+        for n in range(N):
+            b = exact.bf16_code_to_fraction(bb[n])
+            want = exact.round_fraction(scaled(m, n, xe, we) + b, **exact.BF16)
+            assert exact.bf16_code_to_fraction(out[m, n]) == want, (m, n)
+            moved += exact.round_fraction(scaled(m, n, xe, we), **exact.BF16) != want
+    assert moved >= (M * N) // 2, moved
+    # (b) codes quantised from N(0,1) with their own block exponents and a
+    # bias of the outputs' size
+    xq, wq, xe2, we2 = gen.fp8_inputs(M, N, K, "fp8_mx", seed=75)
+    xb, wb, xe2, we2 = gen.bits8(xq), gen.bits8(wq), gen.bits8(xe2), gen.bits8(we2)
+    xi, wi = _e4m3_int(xb), _e4m3_int(wb)
+    mag = float(np.mean([abs(float(scaled(m, n, xe2, we2))) for m in range(M) for n in range(N)]))
+    bias = (torch.randn(N, generator=torch.Generator().manual_seed(76)) * mag).to(torch.bfloat16)
+    bb = gen.bits16(bias)
+    out = oracle.gemm_fp8_mx(xb, wb, xe2, we2, bb)
+    for m in range(M):
+        for n in range(N):
+            want = exact.round_fraction(scaled(m, n, xe2, we2) + exact.bf16_code_to_fraction(bb[n]),
+                                        **exact.BF16)
+            assert exact.bf16_code_to_fraction(out[m, n]) == want, (m, n)
+
+
 def test_no_intermediate_fp32_rounding():
     # 1.5 * (1 + 2^-7) = 1.51171875 is exactly the midpoint of the bf16
     # neighbours 1.5078125 and 1.515625.  Subtracting 2^-30 (from
