@@ -50,8 +50,12 @@
  *
  * Threads.  The planner and its table are immutable; calls from several
  * host threads are safe.  Split-K calls use a workspace owned per (device,
- * stream): calls that overlap in time on the same stream's workspace race,
- * calls on different streams do not.
+ * stream), and for hipStreamPerThread (one handle, a different stream in
+ * every host thread) per (device, calling thread): calls that overlap in
+ * time on the same workspace race, calls on different streams do not.  A
+ * graph captured on a stream keeps that stream's workspace: replay it on
+ * its capture stream, or at least never while other calls that use that
+ * workspace run.
  */
 #ifndef SKINNY_GEMM_H
 #define SKINNY_GEMM_H
@@ -251,8 +255,10 @@ int skinny_gemm_fp8_quant_planned(const void *x, const void *W, const void *bias
  * 4-byte aligned.  n == 0 is a no-op; n < 0 is SKG_ERR_INVALID_ARG. */
 int skinny_quant_e4m3(const void *x, const float *s, void *q, long n, hipStream_t stream);
 
-/* Frees every workspace of every device after a device synchronisation.
- * No call may be in flight. */
+/* Frees every workspace the library holds, on each device it holds one on,
+ * after synchronising those devices (and only those); the current device is
+ * the same afterwards.  With nothing held it makes no HIP call.  No call may
+ * be in flight. */
 int skinny_gemm_release_all(void);
 
 /* Human-readable name of a status code (static storage). */

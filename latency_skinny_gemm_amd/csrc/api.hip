@@ -43,11 +43,14 @@ int check_pointers_bf16(const void *x, const void *W, const void *bias, void *ou
 
 // ---------------------------------------------------------------- workspace
 // Split-K partials (fp32 [S][M][N]) and one ticket counter per output tile,
-// owned per (device, stream).  Counters are zero at rest: the workgroup that
-// reduces a tile sets its counter back to zero.
+// owned per (device, stream, owner).  Counters are zero at rest: the
+// workgroup that reduces a tile sets its counter back to zero.  owner is 0
+// except for hipStreamPerThread, one handle that names a different stream
+// in every host thread: its workspaces belong to the calling thread.
 struct Workspace {
     int device;
     hipStream_t stream;
+    long owner;
     float *ws;
     size_t ws_floats;
     unsigned *tickets;
@@ -56,7 +59,11 @@ struct Workspace {
 
 std::mutex g_mu;
 std::vector<Workspace> g_ws;
-std::vector<void *> g_retired;  // replaced buffers, freed by release_all
+struct Retired {
+    int device;
+    void *p;
+};
+std::vector<Retired> g_retired;  // replaced buffers, freed by release_all
 
 // Calls find their workspace without the lock through a per-thread copy of
 // the last one they used, valid while no workspace has been replaced or
@@ -66,13 +73,28 @@ struct WorkspaceCache {
     unsigned generation;
     Workspace w;
 };
-thread_local WorkspaceCache t_cache{0, Workspace{-1, nullptr, nullptr, 0, nullptr, 0}};
+thread_local WorkspaceCache t_cache{0, Workspace{-1, nullptr, 0, nullptr, 0, nullptr, 0}};
 
-int grow(Workspace &w, size_t floats, size_t tickets) {
+// The owner of a stream's workspace: the calling host thread for
+// hipStreamPerThread, else 0 (any thread).
+long stream_owner(hipStream_t stream) {
+    if (stream != hipStreamPerThread) return 0;
+    static std::atomic<long> next{1};
+    thread_local const long tag = next.fetch_add(1, std::memory_order_relaxed);
+    return tag;
+}
+
+// Grows w for `stream` (outside graph capture; the caller has synchronised
+// the stream, so no kernel still uses a buffer that is retired here).  New
+// tile counters are zeroed on `stream` itself: a plain hipMemset is queued
+// on the null stream, which a non-blocking stream does not wait for, so the
+// first kernel could read uninitialised counters and no workgroup of a tile
+// would see itself arrive last.
+int grow(Workspace &w, size_t floats, size_t tickets, hipStream_t stream) {
     if (floats > w.ws_floats) {
         float *p = nullptr;
         if (hipMalloc((void **)&p, floats * sizeof(float)) != hipSuccess) return SKG_ERR_HIP;
-        if (w.ws) g_retired.push_back(w.ws);
+        if (w.ws) g_retired.push_back(Retired{w.device, w.ws});
         w.ws = p;
         w.ws_floats = floats;
         g_generation.fetch_add(1, std::memory_order_acq_rel);
@@ -80,8 +102,9 @@ int grow(Workspace &w, size_t floats, size_t tickets) {
     if (tickets > w.n_tickets) {
         unsigned *t = nullptr;
         if (hipMalloc((void **)&t, tickets * sizeof(unsigned)) != hipSuccess) return SKG_ERR_HIP;
-        if (hipMemset(t, 0, tickets * sizeof(unsigned)) != hipSuccess) return SKG_ERR_HIP;
-        if (w.tickets) g_retired.push_back(w.tickets);
+        if (hipMemsetAsync(t, 0, tickets * sizeof(unsigned), stream) != hipSuccess)
+            return SKG_ERR_HIP;
+        if (w.tickets) g_retired.push_back(Retired{w.device, w.tickets});
         w.tickets = t;
         w.n_tickets = tickets;
         g_generation.fetch_add(1, std::memory_order_acq_rel);
@@ -89,37 +112,40 @@ int grow(Workspace &w, size_t floats, size_t tickets) {
     return SKG_OK;
 }
 
-Workspace *find(int device, hipStream_t stream) {
+Workspace *find(int device, hipStream_t stream, long owner) {
     for (auto &w : g_ws)
-        if (w.device == device && w.stream == stream) return &w;
+        if (w.device == device && w.stream == stream && w.owner == owner) return &w;
     return nullptr;
 }
 
-// Workspace for this (device, stream) with room for the request.  Grows it
-// outside graph capture; during capture a short workspace is an error.
+// Workspace for this (device, stream, owner) with room for the request.
+// Grows it outside graph capture; during capture a short workspace is an
+// error.
 int acquire(hipStream_t stream, size_t floats, size_t tickets, float **ws, unsigned **tk) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SKG_ERR_HIP;
+    const long owner = stream_owner(stream);
     const Workspace &c = t_cache.w;  // fast path: no lock
     if (t_cache.generation == g_generation.load(std::memory_order_acquire) && c.device == dev &&
-        c.stream == stream && c.ws_floats >= floats && c.n_tickets >= tickets) {
+        c.stream == stream && c.owner == owner && c.ws_floats >= floats &&
+        c.n_tickets >= tickets) {
         *ws = c.ws;
         *tk = c.tickets;
         return SKG_OK;
     }
     std::lock_guard<std::mutex> lock(g_mu);
-    Workspace *w = find(dev, stream);
+    Workspace *w = find(dev, stream, owner);
     if (!w || w->ws_floats < floats || w->n_tickets < tickets) {
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return SKG_ERR_HIP;
         if (cs != hipStreamCaptureStatusNone) return SKG_ERR_WORKSPACE;
         if (!w) {
-            g_ws.push_back(Workspace{dev, stream, nullptr, 0, nullptr, 0});
+            g_ws.push_back(Workspace{dev, stream, owner, nullptr, 0, nullptr, 0});
             w = &g_ws.back();
         }
         // no kernel of this stream may still use a buffer we retire
         if (hipStreamSynchronize(stream) != hipSuccess) return SKG_ERR_HIP;
-        int rc = grow(*w, floats, tickets);
+        int rc = grow(*w, floats, tickets, stream);
         if (rc != SKG_OK) return rc;
     }
     *ws = w->ws;
@@ -403,26 +429,30 @@ extern "C" int skinny_gemm_reserve(int max_M, int max_N, int max_K, int max_S,
 
 extern "C" int skinny_gemm_release_all(void) {
     std::lock_guard<std::mutex> lock(g_mu);
-    int rc = SKG_OK;
-    int ndev = 0;
-    if (hipGetDeviceCount(&ndev) == hipSuccess) {
-        int cur = 0;
-        (void)hipGetDevice(&cur);
-        for (int d = 0; d < ndev; ++d)
-            if (hipSetDevice(d) == hipSuccess && hipDeviceSynchronize() != hipSuccess)
-                rc = SKG_ERR_HIP;
-        (void)hipSetDevice(cur);
-    }
+    if (g_ws.empty() && g_retired.empty()) return SKG_OK;  // nothing held: no HIP call
     int cur = 0;
-    (void)hipGetDevice(&cur);
-    for (auto &w : g_ws) {
-        (void)hipSetDevice(w.device);
+    if (hipGetDevice(&cur) != hipSuccess) return SKG_ERR_HIP;
+    // only the devices this library holds memory on: wait for their work,
+    // then free it there
+    std::vector<int> devs;
+    auto note = [&](int d) {
+        for (int e : devs)
+            if (e == d) return;
+        devs.push_back(d);
+    };
+    for (const auto &w : g_ws) note(w.device);
+    for (const auto &r : g_retired) note(r.device);
+    int rc = SKG_OK;
+    for (int d : devs)
+        if (hipSetDevice(d) != hipSuccess || hipDeviceSynchronize() != hipSuccess) rc = SKG_ERR_HIP;
+    for (const auto &w : g_ws) {
+        if (hipSetDevice(w.device) != hipSuccess) rc = SKG_ERR_HIP;
         if (w.ws && hipFree(w.ws) != hipSuccess) rc = SKG_ERR_HIP;
         if (w.tickets && hipFree(w.tickets) != hipSuccess) rc = SKG_ERR_HIP;
     }
-    (void)hipSetDevice(cur);
-    for (void *p : g_retired)
-        if (hipFree(p) != hipSuccess) rc = SKG_ERR_HIP;
+    for (const auto &r : g_retired)
+        if (hipSetDevice(r.device) != hipSuccess || hipFree(r.p) != hipSuccess) rc = SKG_ERR_HIP;
+    if (hipSetDevice(cur) != hipSuccess) rc = SKG_ERR_HIP;
     g_ws.clear();
     g_retired.clear();
     g_generation.fetch_add(1, std::memory_order_acq_rel);  // every per-thread copy is stale

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 X, W, OUT, B = 0x10000, 0x200000, 0x4000000, 0x8000000
 
 
-@pytest.mark.parametrize("args,status", [
+BF16_BAD_ARGS = [
     ((X, W, 0, 0, OUT, -1, 8, 64), skg.ERR_INVALID_ARG),
     ((X, W, 0, 0, OUT, 2, -8, 64), skg.ERR_INVALID_ARG),
     ((X, W, 0, 0, OUT, 2, 8, -64), skg.ERR_INVALID_ARG),
@@ -65,11 +65,20 @@ X, W, OUT, B = 0x10000, 0x200000, 0x4000000, 0x8000000
     ((X, W, 0, 0, X + 64, 2, 8, 64), skg.ERR_INVALID_ARG),   # out overlaps x
     ((X, W, 0, 0, W + 1000, 2, 8, 64), skg.ERR_INVALID_ARG), # out overlaps W
     ((X, W, B, 0, B - 2, 2, 8, 64), skg.ERR_INVALID_ARG),    # out overlaps bias
-])
+]
+
+
+@pytest.mark.parametrize("args,status", BF16_BAD_ARGS)
 def test_bf16_validation_before_any_device_call(lib, args, status):
     x, w, b, sc, o, M, N, K = args
     assert lib.skinny_gemm_bf16(x or None, w or None, b or None, sc or None, o or None,
                                 M, N, K, None) == status
+
+
+def test_release_all_with_nothing_held_makes_no_device_call(lib):
+    # no workspace was ever made in this process (no GPU here): nothing to
+    # free, and no HIP call that would fail without a device
+    assert lib.skinny_gemm_release_all() == skg.OK
 
 
 def test_fp8_validation(lib):

@@ -335,6 +335,97 @@ def test_threads_on_their_own_streams(skg):
     assert not errors, errors
 
 
+def test_first_call_on_a_fresh_non_blocking_stream(skg):
+    # A new workspace's tile counters are zeroed on the call's own stream.
+    # torch's side streams do not wait for the null stream, so counters
+    # zeroed there could still hold old bytes when the first kernel reads
+    # them and whole tiles would go unwritten.  Old bytes are planted first:
+    # memory filled with 0xFF and handed back to HIP, which the library's
+    # next allocations are likely to reuse.
+    M, N, K = 20, 700, 2056
+    x, w, b = _dev(*gen.bf16_inputs(M, N, K, True, seed=901))
+    plan = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_SPLITK, 256, 2, 11, 2, skg.REDUCE_LAST))
+    ref = oracle.gemm_bf16(gen.bits16(x.cpu()), gen.bits16(w.cpu()), gen.bits16(b.cpu()), threads=16)
+    for trial in range(3):
+        torch.cuda.synchronize()
+        skg.release_all()
+        junk = torch.full((64 << 20,), -1, dtype=torch.int32, device=DEV)
+        torch.cuda.synchronize()
+        del junk
+        torch.cuda.empty_cache()
+        stream = torch.cuda.Stream()
+        out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        torch.cuda.synchronize()
+        got = skg.gemm_bf16_planned(x, w, plan, b, out=out, stream=stream)
+        stream.synchronize()
+        ok, msg = tolerance.check(got.cpu(), ref, K)
+        assert ok, f"trial {trial}: {msg}"
+
+
+def test_per_thread_stream_workspaces_belong_to_threads(skg):
+    # hipStreamPerThread is one handle for a different stream in every host
+    # thread; the library keys its workspaces by the calling thread there, so
+    # threads running split-K calls with different split counts at once do
+    # not share partials or tile counters
+    import threading
+
+    lib = skg.lib()
+    per_thread = ctypes.c_void_p(2)  # hipStreamPerThread
+    cases = []
+    for i, (M, N, K, S, red) in enumerate(((16, 256, 7168, 16, skg.REDUCE_LAST),
+                                           (16, 256, 7168, 7, skg.REDUCE_LAST),
+                                           (8, 384, 4096, 4, skg.REDUCE_KERNEL),
+                                           (8, 384, 4096, 9, skg.REDUCE_LAST))):
+        x, w, b = _dev(*gen.bf16_inputs(M, N, K, True, seed=800 + i))
+        plan = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_SPLITK, 256, 1, S, 2, red))
+        ref = skg.gemm_bf16_planned(x, w, plan, b)
+        cases.append((M, N, K, x, w, b, plan, ref))
+    torch.cuda.synchronize()
+    errors = []
+    start = threading.Barrier(len(cases))
+
+    def worker(case):
+        M, N, K, x, w, b, plan, ref = case
+        torch.cuda.set_device(0)
+        outs = [torch.zeros(M, N, dtype=torch.bfloat16, device=DEV) for _ in range(30)]
+        torch.cuda.synchronize()
+        # one eager call grows this thread's workspace, then all run at once
+        if lib.skinny_gemm_bf16_planned(x.data_ptr(), w.data_ptr(), b.data_ptr(), outs[0].data_ptr(),
+                                        M, N, K, ctypes.byref(plan), per_thread) != skg.OK:
+            errors.append(f"M={M} S={plan.splits}: first call failed")
+        start.wait()
+        for o in outs:
+            rc = lib.skinny_gemm_bf16_planned(x.data_ptr(), w.data_ptr(), b.data_ptr(), o.data_ptr(),
+                                              M, N, K, ctypes.byref(plan), per_thread)
+            if rc != skg.OK:
+                errors.append(f"M={M}: status {rc}")
+                return
+        torch.cuda.synchronize()
+        for o in outs:
+            if not torch.equal(o.view(torch.int16), ref.view(torch.int16)):
+                errors.append(f"M={M} S={plan.splits}: differs from the single-threaded result")
+                return
+
+    threads = [threading.Thread(target=worker, args=(c,)) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+
+
+def test_release_all_keeps_the_current_device(skg):
+    M, N, K = 16, 256, 7168
+    x, w, b = _dev(*gen.bf16_inputs(M, N, K, False, seed=5))
+    skg.gemm_bf16_planned(x, w, skg.make_plan(skg.KIND_SPLITK, 256, 1, 8, 2, skg.REDUCE_KERNEL))
+    torch.cuda.synchronize()
+    before = torch.cuda.current_device()
+    skg.release_all()
+    assert torch.cuda.current_device() == before
+    skg.release_all()  # nothing held: a no-op
+    assert torch.cuda.current_device() == before
+
+
 def test_error_statuses_on_device(skg):
     x = torch.zeros(2, 64, dtype=torch.bfloat16, device=DEV)
     w = torch.zeros(8, 64, dtype=torch.bfloat16, device=DEV)
