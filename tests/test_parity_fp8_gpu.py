@@ -149,6 +149,80 @@ def test_fp8_mx_exact_scales_bitwise(skg, M, N, K):
         assert bad.size == 0, f"[{name}] {len(bad)} mismatches, first {tuple(bad[0])}"
 
 
+# The bias with non-unit scales.  Per-tensor: out = bf16(sx * sw * sum + bias),
+# the scale product applied once to the sum and the bias added after it
+# ("sglang PR #28333" page: the key source snippet adds the bias to the
+# GEMM's output; the motivation section: the scales are applied once).
+# With e4m3 integers, sx = 2^-3, sw = 2^-2 and an integer bias every value
+# is exact in fp32, so the output is unique; a bias added before the scale
+# product (shrunk 32x) or dropped gives other bits in most elements, which
+# each test checks on the oracle before it compares a plan.
+POW2_SX, POW2_SW = 2.0 ** -3, 2.0 ** -2
+
+
+def _int_bias(N, seed):
+    return torch.randint(-3, 4, (N,), generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16)
+
+
+def _sees_bias(ref, wrong):
+    return (ref != wrong).mean() > 0.5
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 4096), (5, 48, 4112), (16, 200, 2048), (37, 96, 1024),
+                                   (128, 64, 4096), (2, 7, 4096), (4, 1, 1024)])
+def test_fp8_per_tensor_pow2_scales_bias_bitwise(skg, M, N, K):
+    xq = _small_int_e4m3(M, K, 11 * M + K)
+    wq = _small_int_e4m3(N, K, 13 * N + K)
+    bias = _int_bias(N, M + N)
+    ref = _oracle("fp8_tensor", xq, wq, POW2_SX, POW2_SW, bias)
+    assert _sees_bias(ref, _oracle("fp8_tensor", xq, wq, POW2_SX, POW2_SW, None))
+    shrunk = (bias.float() * (POW2_SX * POW2_SW)).to(torch.bfloat16)  # bias before the scales
+    assert _sees_bias(ref, _oracle("fp8_tensor", xq, wq, POW2_SX, POW2_SW, shrunk))
+    sx = torch.tensor([POW2_SX], dtype=torch.float32, device=DEV)
+    sw = torch.tensor([POW2_SW], dtype=torch.float32, device=DEV)
+    for name, plan in _plans(skg, M, N, K):
+        out = _run(skg, plan, xq.to(DEV), wq.to(DEV), bias.to(DEV), sx=sx, sw=sw)
+        bad = np.argwhere(gen.bits16(out) != ref)
+        assert bad.size == 0, f"[{name}] {len(bad)} mismatches, first {tuple(bad[0])}"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 4096), (8, 80, 2048), (16, 48, 4096), (100, 40, 1024)])
+def test_fp8_quant_pow2_scales_bias_bitwise(skg, M, N, K):
+    # bf16 x = q * sx with small integers q: the static quantisation returns
+    # exactly q, so the fused call must equal the integer reference bit for bit
+    q = _small_int_e4m3(M, K, 17 * M + K)
+    x = (q.float() * POW2_SX).to(torch.bfloat16)
+    wq = _small_int_e4m3(N, K, 19 * N + K)
+    bias = _int_bias(N, 2 * M + N)
+    ref = _oracle("fp8_tensor", q, wq, POW2_SX, POW2_SW, bias)
+    assert _sees_bias(ref, _oracle("fp8_tensor", q, wq, POW2_SX, POW2_SW, None))
+    sx = torch.tensor([POW2_SX], dtype=torch.float32, device=DEV)
+    sw = torch.tensor([POW2_SW], dtype=torch.float32, device=DEV)
+    out = skg.gemm_fp8_quant(x.to(DEV), wq.to(DEV), sx, sw, bias=bias.to(DEV))
+    torch.cuda.synchronize()
+    bad = np.argwhere(gen.bits16(out.cpu()) != ref)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {tuple(bad[0])}"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 4096), (9, 80, 2048), (64, 48, 1024), (128, 32, 4096),
+                                   (3, 5, 2048)])
+def test_fp8_mx_exact_scales_bias_bitwise(skg, M, N, K):
+    # MX: the bias is added once, after every block's scaled partial ("sglang
+    # PR #34042" page: block scales inside the sum, the bias outside it)
+    xq = _small_int_e4m3(M, K, 7 * M + K)
+    wq = _small_int_e4m3(N, K, 3 * N + K)
+    g = torch.Generator().manual_seed(M * N + 1)
+    xe = torch.randint(126, 129, (M, K // 32), generator=g).to(torch.uint8)
+    we = torch.randint(126, 129, (N, K // 32), generator=g).to(torch.uint8)
+    bias = _int_bias(N, M * N + 2)
+    ref = _oracle("fp8_mx", xq, wq, xe, we, bias)
+    assert _sees_bias(ref, _oracle("fp8_mx", xq, wq, xe, we, None))
+    for name, plan in _plans(skg, M, N, K):
+        out = _run(skg, plan, xq.to(DEV), wq.to(DEV), bias.to(DEV), xe=xe.to(DEV), we=we.to(DEV))
+        bad = np.argwhere(gen.bits16(out) != ref)
+        assert bad.size == 0, f"[{name}] {len(bad)} mismatches, first {tuple(bad[0])}"
+
+
 def test_fp8_mx_nan_exponent_propagates(skg):
     M, N, K = 4, 40, 1024
     xq, wq, xe, we = gen.fp8_inputs(M, N, K, "fp8_mx", seed=99)
