@@ -156,6 +156,26 @@ typedef struct SkgPlan {
 int skinny_gemm_bf16(const void *x, const void *W, const void *bias, const void *scales,
                      void *out, int M, int N, int K, hipStream_t stream);
 
+/* skinny_gemm_bf16 for callers that cannot allocate device memory: code
+ * under HIP graph capture with no workspace reserved, serving loops and
+ * harnesses that forbid hipMalloc.  Same arguments, plans and results as
+ * skinny_gemm_bf16 (bit for bit), and it never calls hipMalloc, hipFree or
+ * an allocating routine.  Split-K and tiled plans keep their fp32 partials
+ * in a fixed device array inside the library, 8 MiB (2^21 floats) per GPU,
+ * held from the first call on that GPU until the process ends; a plan whose
+ * partials (splits * M * N floats) exceed it returns SKG_ERR_WORKSPACE and
+ * launches nothing.  Such plans reduce with the second kernel (a plan that
+ * would use the last-arriver reduction is switched to it: same sums, same
+ * order, same bits), so nothing in the array has to start at zero.  Every
+ * call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (on any streams) race and give wrong results; calls ordered on
+ * one stream do not.  A GPU's first call looks up the array's device
+ * address (hipGetSymbolAddress, no allocation): make one call on each GPU
+ * before capturing a graph there. */
+int skinny_gemm_bf16_noalloc(const void *x, const void *W, const void *bias,
+                             const void *scales, void *out, int M, int N, int K,
+                             hipStream_t stream);
+
 /* FP8 e4m3fn GEMM with bf16 bias and output; `scales` is a HOST pointer to
  * the struct above (its pointers are device pointers; sx, sw 4-byte
  * aligned).  x[M,K] and W[N,K] are e4m3fn bytes, row-major, 16-byte

@@ -87,6 +87,8 @@ def _load():
     PP = ctypes.POINTER(SkgPlan)
     L.skinny_gemm_bf16.argtypes = [P, P, P, P, P, I, I, I, P]
     L.skinny_gemm_bf16.restype = I
+    L.skinny_gemm_bf16_noalloc.argtypes = [P, P, P, P, P, I, I, I, P]
+    L.skinny_gemm_bf16_noalloc.restype = I
     L.skinny_gemm_bf16_planned.argtypes = [P, P, P, P, I, I, I, PP, P]
     L.skinny_gemm_bf16_planned.restype = I
     L.skinny_gemm_fp8.argtypes = [P, P, P, ctypes.POINTER(Fp8Scales), P, I, I, I, P]
@@ -199,6 +201,19 @@ def gemm_bf16(x, W, bias=None, out=None, stream=None):
     rc = _launch(_one_device(x, W, bias, out), stream, _load().skinny_gemm_bf16, _ptr(x), _ptr(W),
                  _ptr(bias), None, _ptr(out), M, N, K)
     _check(rc, f"skinny_gemm_bf16(M={M}, N={N}, K={K})")
+    return out
+
+
+def gemm_bf16_noalloc(x, W, bias, out, stream=None):
+    """As gemm_bf16 through skinny_gemm_bf16_noalloc: `out` must be given
+    (nothing is allocated); split partials use the library's fixed per-GPU
+    array, so calls that overlap in time on one GPU race."""
+    M, N, K = _check_tensors(x, W, bias, out, torch.bfloat16)
+    if out is None:
+        raise TypeError("gemm_bf16_noalloc needs an output tensor")
+    rc = _launch(_one_device(x, W, bias, out), stream, _load().skinny_gemm_bf16_noalloc, _ptr(x),
+                 _ptr(W), _ptr(bias), None, _ptr(out), M, N, K)
+    _check(rc, f"skinny_gemm_bf16_noalloc(M={M}, N={N}, K={K})")
     return out
 
 

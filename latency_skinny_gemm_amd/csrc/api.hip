@@ -459,6 +459,78 @@ extern "C" int skinny_gemm_release_all(void) {
     return rc;
 }
 
+// ---------------------------------------------------------------- no allocation
+// skinny_gemm_bf16_noalloc keeps its split partials in this file-scope
+// device array instead of an allocated workspace: each device that loads
+// the library holds one copy, at its own address, until the process ends.
+// Host code never passes `scratch` itself (on the host it is only a stand-in
+// symbol); it passes the address hipGetSymbolAddress returns on the device,
+// looked up once per device with that device current.
+constexpr size_t kScratchFloats = size_t(1) << 21;  // 8 MiB of fp32 partials
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<float *> g_scratch[kMaxScratchDevices];
+
+// The current device's copy of `scratch`, found once per device.
+int scratch_on_current_device(float **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SKG_ERR_HIP;
+    if (dev < 0 || dev >= kMaxScratchDevices) return SKG_ERR_UNSUPPORTED;
+    float *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_acquire);
+        if (!p) {
+            void *q = nullptr;
+            if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q)
+                return SKG_ERR_HIP;
+            p = static_cast<float *>(q);
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return SKG_OK;
+}
+
+}  // namespace
+
+extern "C" int skinny_gemm_bf16_noalloc(const void *x, const void *W, const void *bias,
+                                        const void *scales, void *out, int M, int N, int K,
+                                        hipStream_t stream) {
+    int rc = check_sizes(M, N, K, SKG_DTYPE_BF16);
+    if (rc != SKG_OK) return rc;
+    if (M == 0 || N == 0) return SKG_OK;
+    if (scales) return SKG_ERR_INVALID_ARG;
+    rc = check_pointers_bf16(x, W, bias, out, M, N, K);
+    if (rc != SKG_OK) return rc;
+    SkgPlan p;
+    rc = skinny_gemm_plan(M, N, K, SKG_DTYPE_BF16, &p);
+    if (rc != SKG_OK) return rc;
+    if (p.kind == SKG_KIND_DOT || p.splits == 1)
+        return run_bf16(x, W, bias, out, 0, M, N, K, p, stream);
+    // The last-arriver reduction needs tile counters that are zero at rest;
+    // the second-kernel reduction sums the same partials in the same order
+    // (identical bits) and needs nothing but this call's partials, which it
+    // reads after the main kernel has written all of them.
+    if (p.reduce == SKG_REDUCE_LAST) {
+        p.reduce = SKG_REDUCE_KERNEL;
+        rc = complete_plan(M, N, K, SKG_DTYPE_BF16, &p);
+        if (rc != SKG_OK) return rc;
+    }
+    if (workspace_floats(p, M, N) > kScratchFloats) return SKG_ERR_WORKSPACE;
+    float *ws = nullptr;
+    rc = scratch_on_current_device(&ws);
+    if (rc != SKG_OK) return rc;
+    const int e = p.kind == SKG_KIND_TILED
+                      ? launch_tiled(p, x, W, bias, out, 0, ws, nullptr, M, N, K, stream)
+                      : launch_splitk(p, x, W, bias, out, 0, ws, nullptr, M, N, K, stream);
+    return e == (int)hipSuccess ? SKG_OK : SKG_ERR_HIP;
+}
+
 extern "C" const char *skinny_gemm_status_string(int status) {
     switch (status) {
     case SKG_OK: return "SKG_OK";

@@ -75,6 +75,21 @@ def test_bf16_validation_before_any_device_call(lib, args, status):
                                 M, N, K, None) == status
 
 
+def test_noalloc_validates_as_skinny_gemm_bf16(lib):
+    # the same host-side checks, in the same order, before any HIP call
+    for args, status in BF16_BAD_ARGS:
+        x, w, b, sc, o, M, N, K = args
+        assert lib.skinny_gemm_bf16_noalloc(x or None, w or None, b or None, sc or None, o or None,
+                                            M, N, K, None) == status, args
+    # partials beyond the fixed 2^21-float array: rejected before any HIP
+    # call (M = 512, N = 4096, K = 7168 plans 2 splits: 2^22 floats)
+    x, w, o = 1 << 40, 2 << 40, 3 << 40
+    p = skg.plan(512, 4096, 7168)
+    assert p.splits * 512 * 4096 > 1 << 21
+    assert lib.skinny_gemm_bf16_noalloc(x, w, None, None, o, 512, 4096, 7168, None) == \
+        skg.ERR_WORKSPACE
+
+
 def test_release_all_with_nothing_held_makes_no_device_call(lib):
     # no workspace was ever made in this process (no GPU here): nothing to
     # free, and no HIP call that would fail without a device
