@@ -168,4 +168,81 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// ---------------------------------------------------------------- reduce-scatter
+// The wave-wide sums of P = 2^L values that every lane holds (v[0..P-1]),
+// each sum landing in its own group of lanes: afterwards v[0] of lane l is
+// the sum over all 64 lanes of value index l >> (6 - L).  Six exchange
+// levels, in a fixed order: lanes l and l^32, then l and l^16 (the two
+// v_permlane*_swap instructions of gfx950), then l and 15-l within a
+// 16-lane row (row_mirror), l and 7-l within 8 (row_half_mirror), l^2 and
+// l^1 (quad_perm).  At each of the first L levels the lanes whose level bit
+// is 1 keep the upper half of the values and the others the lower half, so
+// each level halves the values a lane holds; the remaining levels add the
+// single value and its partner.  A level pairs the same two lanes for every
+// value index, and a pair's sum does not depend on which lane forms it (fp
+// addition commutes), so every index is summed by the same tree: the bits
+// do not depend on where a value sits in v.  Values of different indices
+// are never added together, so padding v with zeros changes nothing.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// The partner's x at exchange level LEV (2..5) within a 16-lane row.
+template <int LEV>
+__device__ __forceinline__ float rs_partner(float x) {
+    if constexpr (LEV == 2) return dpp_f<kDppMirror>(x);
+    else if constexpr (LEV == 3) return dpp_f<kDppHalfMirror>(x);
+    else if constexpr (LEV == 4) return dpp_f<kDppQuadSwap2>(x);
+    else return dpp_f<kDppQuadSwap1>(x);
+}
+
+// One exchange level: lanes l and its level-LEV partner (l^32, l^16, 15-l
+// in a row, 7-l in 8, l^2, l^1).  While a lane still holds more than one
+// value it keeps the upper half when its level bit (bit 5 - LEV) is set,
+// else the lower half, each added to the partner's copy of the same index.
+template <int L, int LEV>
+__device__ __forceinline__ void rs_level(float (&v)[1 << L], unsigned lane) {
+    constexpr int n = LEV < L ? (1 << (L - LEV)) : 1;  // values held before this level
+    if constexpr (LEV < 2) {
+        // one swap exchanges the two values of a pair between the halves
+        // (rows); r[0] + r[1] is the sum of the index this lane keeps
+        constexpr int h = n > 1 ? n / 2 : 1;
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+            const unsigned a = __float_as_uint(v[i]);
+            const unsigned b = n > 1 ? __float_as_uint(v[i + (n > 1 ? h : 0)]) : a;
+            const auto r = LEV == 0 ? __builtin_amdgcn_permlane32_swap(a, b, false, false)
+                                    : __builtin_amdgcn_permlane16_swap(a, b, false, false);
+            v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+    } else {
+        const bool upper = (lane >> (5 - LEV)) & 1u;
+        if constexpr (n > 1) {
+            constexpr int h = n / 2;
+#pragma unroll
+            for (int i = 0; i < h; ++i) {
+                const float keep = upper ? v[i + h] : v[i];
+                const float send = upper ? v[i] : v[i + h];
+                v[i] = keep + rs_partner<LEV>(send);
+            }
+        } else {
+            v[0] = v[0] + rs_partner<LEV>(v[0]);
+        }
+    }
+}
+
+template <int L>
+__device__ __forceinline__ float wave_reduce_scatter(float (&v)[1 << L]) {
+    static_assert(L >= 0 && L <= 6, "at most 64 values per lane");
+    const unsigned lane = threadIdx.x & 63u;
+    rs_level<L, 0>(v, lane);
+    rs_level<L, 1>(v, lane);
+    rs_level<L, 2>(v, lane);
+    rs_level<L, 3>(v, lane);
+    rs_level<L, 4>(v, lane);
+    rs_level<L, 5>(v, lane);
+    return v[0];
+}
+
 }  // namespace skg

@@ -15,9 +15,11 @@
 //  * the multiply-add is either fp32 FMA on widened bf16 (one IEEE rounding
 //    per product) or, with SKG_FLAG_DOT2, gfx950's bf16 dot instruction
 //    (two products per instruction on packed operands, no widening);
-//  * the per-thread sums are reduced over the wave by DPP row moves and two
-//    shuffles, then over the waves through LDS in wave order, then bias is
-//    added in fp32 and the sum is rounded once to bf16.
+//  * the per-thread sums of all C*M outputs are reduced over the wave
+//    together by a reduce-scatter (two lane-swap levels and four DPP
+//    levels, each halving the values a lane holds), then over the waves
+//    through LDS in wave order, then bias is added in fp32 and the sum is
+//    rounded once to bf16.
 // Every reduction order is fixed: the result is bitwise reproducible for a
 // given plan and input.
 #include "device_common.h"
@@ -72,36 +74,41 @@ __global__ void __launch_bounds__((W1 ? 64 : dot_max_threads(M, C, V, DOT2)))
                 acc[c][m] = DOT2 ? dot8_dot2(xv[m][i], wv[c][i], acc[c][m])
                                  : dot8_fma(xv[m][i], wv[c][i], acc[c][m]);
 
-    __shared__ float red[kMaxThreads / 64][C * M];
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
+    // Reduce-scatter the C*M per-lane sums over the wave (padded with zeros
+    // to a power of two): lane l ends with the wave's total of index
+    // l >> (6 - L), index c*M + m; the first lane of each index group owns it.
+    constexpr int CM = C * M;
+    constexpr int L = CM <= 1 ? 0 : CM <= 2 ? 1 : CM <= 4 ? 2 : CM <= 8 ? 3 : CM <= 16 ? 4 : CM <= 32 ? 5 : 6;
+    static_assert(CM <= 64, "one value index per lane at most");
+    float part[1 << L];
+#pragma unroll
+    for (int i = 0; i < (1 << L); ++i) part[i] = i < CM ? acc[i / M][i % M] : 0.0f;
+    const float total = wave_reduce_scatter<L>(part);
     const int lane = t & 63;
+    const int idx = lane >> (6 - L);
+    const bool owner = (lane & ((1 << (6 - L)) - 1)) == 0 && idx < CM;
+
+    __shared__ float red[kMaxThreads / 64][CM];
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
     const int nw = T >> 6;
     if constexpr (W1) {
-        // One wave: its sums are the totals, in every lane, so lane c*M + m
-        // stores output (c, m) with no LDS round trip and no barrier.  The
-        // sum starts from 0 as the cross-wave sum below does: same bits.
-#pragma unroll
-        for (int c = 0; c < C; ++c)
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float s = 0.0f + wave_sum(acc[c][m]);
-                const int n = n0 + c;
-                if (lane == c * M + m && n < N) {
-                    if (bias) s += bf16_to_f32(bias[n]);
-                    store_out(out, (size_t)m * N + n, s, out_f32);
-                }
+        // One wave: its totals are final, so each owner lane stores its
+        // output with no LDS round trip and no barrier.  The sum starts from
+        // 0 as the cross-wave sum below does: same bits.
+        if (owner) {
+            const int c = idx / M, m = idx - (idx / M) * M;
+            const int n = n0 + c;
+            if (n < N) {
+                float s = 0.0f + total;
+                if (bias) s += bf16_to_f32(bias[n]);
+                store_out(out, (size_t)m * N + n, s, out_f32);
             }
+        }
         return;
     }
-#pragma unroll
-    for (int c = 0; c < C; ++c)
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float s = wave_sum(acc[c][m]);
-            if (lane == 0) red[wave][c * M + m] = s;
-        }
+    if (owner) red[wave][idx] = total;
     __syncthreads();
-    if (t < C * M) {
+    if (t < CM) {
         const int c = t / M;
         const int m = t - c * M;
         const int n = n0 + c;

@@ -157,35 +157,40 @@ __global__ void __launch_bounds__((W1 ? 64 : fp8_dot_max_threads(M, C, V, MX, QX
             }
     }
 
-    __shared__ float red[kMaxThreads / 64][C * M];
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    // the C*M sums over the wave by one reduce-scatter (lane l ends with the
+    // total of index l >> (6 - L), index c*M + m), then over the waves in
+    // wave order
+    constexpr int CM = C * M;
+    constexpr int L = CM <= 1 ? 0 : CM <= 2 ? 1 : CM <= 4 ? 2 : CM <= 8 ? 3 : CM <= 16 ? 4 : CM <= 32 ? 5 : 6;
+    static_assert(CM <= 64, "one value index per lane at most");
+    float part[1 << L];
+#pragma unroll
+    for (int i = 0; i < (1 << L); ++i) part[i] = i < CM ? acc[i / M][i % M] : 0.0f;
+    const float total = wave_reduce_scatter<L>(part);
     const int lane = t & 63;
+    const int idx = lane >> (6 - L);
+    const bool owner = (lane & ((1 << (6 - L)) - 1)) == 0 && idx < CM;
+
+    __shared__ float red[kMaxThreads / 64][CM];
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int nw = T >> 6;
     if constexpr (W1) {
-        // One wave: its sums are the totals, in every lane, so lane c*M + m
-        // stores output (c, m) with no LDS round trip and no barrier (the
-        // same bits as the cross-wave sum below, which starts from 0 too).
-#pragma unroll
-        for (int c = 0; c < C; ++c)
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float s = 0.0f + wave_sum(acc[c][m]);
-                const int n = n0 + c;
-                if (lane == c * M + m && n < N) {
-                    if (!MX) s *= sx[0] * sw[0];
-                    if (bias) s += bf16_to_f32(bias[n]);
-                    store_out(out, (size_t)m * N + n, s, out_f32);
-                }
+        // One wave: its totals are final, so each owner lane stores its
+        // output with no LDS round trip and no barrier (the same bits as the
+        // cross-wave sum below, which starts from 0 too).
+        if (owner) {
+            const int c = idx / M, m = idx - (idx / M) * M;
+            const int n = n0 + c;
+            if (n < N) {
+                float s = 0.0f + total;
+                if (!MX) s *= sx[0] * sw[0];
+                if (bias) s += bf16_to_f32(bias[n]);
+                store_out(out, (size_t)m * N + n, s, out_f32);
             }
+        }
         return;
     }
-#pragma unroll
-    for (int c = 0; c < C; ++c)
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float s = wave_sum(acc[c][m]);
-            if (lane == 0) red[wave][c * M + m] = s;
-        }
+    if (owner) red[wave][idx] = total;
     __syncthreads();
     if (t < C * M) {
         const int c = t / M, m = t - (t / M) * M;
@@ -372,7 +377,7 @@ __global__ void __launch_bounds__((QX ? 256 : fp8_mfma_max_threads(MT, NB, D, MX
                 if (bias) v += bf16_to_f32(bias[n]);
                 store_out(out, (size_t)m * N + n, v, out_f32);
             } else {
-                ws[((size_t)s * M + m) * N + n] = v;
+                put_partial(ws, ((size_t)s * M + m) * N + n, v, reduce == SKG_REDUCE_LAST);
             }
         }
     }

@@ -20,9 +20,9 @@
 //  * the waves' 16x16 fp32 tiles are summed through LDS in wave order;
 //  * with S > 1 each workgroup writes its fp32 partial to the workspace
 //    ws[s][m][n]; the partials are then summed in ascending s by either the
-//    last workgroup of the tile to finish (a device-scope ticket counter,
-//    release/acquire fences; no workgroup ever waits on another) or by a
-//    second kernel.  Both add the same numbers in the same order, so the
+//    last workgroup of the tile to finish (partials stored at device scope,
+//    a device-scope ticket counter and device-scope loads, no cache
+//    write-back; no workgroup ever waits on another) or by a second kernel.  Both add the same numbers in the same order, so the
 //    output does not depend on which workgroup finishes last.
 #include "device_common.h"
 #include "internal.h"
@@ -134,7 +134,7 @@ __global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
                 if (bias) v += bf16_to_f32(bias[n]);
                 store_out(out, (size_t)m * N + n, v, out_f32);
             } else {
-                ws[((size_t)s * M + m) * N + n] = v;
+                put_partial(ws, ((size_t)s * M + m) * N + n, v, reduce == SKG_REDUCE_LAST);
             }
         }
     }

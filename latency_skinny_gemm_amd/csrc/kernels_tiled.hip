@@ -243,6 +243,7 @@ __global__ void __launch_bounds__(256)
     __syncthreads();
     constexpr int C4 = NB * 4;  // 4-column groups per row
     const bool vec = (N & 3) == 0;  // 16-byte aligned workspace rows
+    const bool coherent = reduce == SKG_REDUCE_LAST;  // partials read by the last arriver
     for (int e = t; e < Mb * C4; e += 256) {
         const int r = e / C4, c = (e % C4) * 4;
         if (c >= ncols) continue;
@@ -256,11 +257,11 @@ __global__ void __launch_bounds__(256)
                     store_out(out, m * N + n + q,
                               bias ? v[q] + bf16_to_f32(bias[n + q]) : v[q], out_f32);
         } else if (vec && c + 4 <= ncols) {
-            *reinterpret_cast<f32x4 *>(ws + ((size_t)s * M + m) * N + n) = v;
+            put_partial4(ws, ((size_t)s * M + m) * N + n, v, coherent);
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if (c + q < ncols) ws[((size_t)s * M + m) * N + n + q] = v[q];
+                if (c + q < ncols) put_partial(ws, ((size_t)s * M + m) * N + n + q, v[q], coherent);
         }
     }
     // (the planner gives REDUCE_LAST only with one row block)

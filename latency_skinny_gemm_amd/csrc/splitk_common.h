@@ -29,16 +29,45 @@ __device__ __forceinline__ TiledPos tiled_position(int b, int MB, int S, int G) 
     return TiledPos{mb, sj % S, sj / S};
 }
 
+// A split's fp32 partial ws[s][m][n].  With the last-arriver reduction
+// (coherent) each store is an agent-scope relaxed atomic store, which
+// writes through to the device's coherence point (global_store ... sc1):
+// once it has completed, a workgroup on any XCD reads it with agent-scope
+// loads, and no cache of the device has to be written back or invalidated.
+// For the second-kernel reduction, which reads after a kernel boundary,
+// plain stores.
+__device__ __forceinline__ void put_partial(float *ws, size_t i, float v, bool coherent) {
+    if (coherent)
+        __hip_atomic_store(ws + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        ws[i] = v;
+}
+
+// Four consecutive partials (ws + i 16-byte aligned).
+__device__ __forceinline__ void put_partial4(float *ws, size_t i, f32x4 v, bool coherent) {
+    if (coherent) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            __hip_atomic_store(ws + i + q, v[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        *reinterpret_cast<f32x4 *>(ws + i) = v;
+    }
+}
+
 // Called by every thread of a workgroup that has just written its fp32
-// partial ws[s][m][n] for the columns [col0, col0 + ncols) of tile j.
-// Every wave waits until its partial stores are in the L2; then one
-// agent-scope acquire-release ticket increment by thread 0 publishes the
-// whole workgroup's partials (its release writes the XCD's L2 back to
-// memory once per workgroup) and, in the last workgroup of the tile, its
-// acquire invalidates stale L1/L2 lines before any wave reads partials.
-// That workgroup sums the S partials in ascending s, applies the FP8
-// per-tensor scale product when given (once), adds the bias and rounds
-// once; it re-arms the ticket.  No workgroup waits on another.
+// partial for the columns [col0, col0 + ncols) of tile j with
+// put_partial(..., coherent = true).  Every wave waits until its partial
+// stores have completed at device scope, then a barrier, then thread 0
+// counts the workgroup in with one agent-scope relaxed atomic add on the
+// tile's ticket.  The workgroup that counts last has seen every other
+// workgroup's add, each made after that workgroup's stores completed, so
+// its agent-scope loads of the partials return the stored values.  No
+// fence writes back or invalidates an L2: the ordering comes from the
+// explicit wait, the barrier and the atomic, all at device scope.  That
+// workgroup sums the S partials in ascending s, applies the FP8 per-tensor
+// scale product when given (once), adds the bias and rounds once; it
+// re-arms the ticket (the next kernel on the stream sees the zero after
+// the kernel boundary).  No workgroup waits on another.
 __device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
                                                     unsigned *__restrict__ tickets,
                                                     const uint16_t *__restrict__ bias,
@@ -51,7 +80,7 @@ __device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned prev =
-            __hip_atomic_fetch_add(&tickets[j], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&tickets[j], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *is_last = (prev == (unsigned)S - 1u) ? 1u : 0u;
         if (*is_last)  // every partial of tile j has arrived: rearm for the next call
             __hip_atomic_store(&tickets[j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -63,7 +92,10 @@ __device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
     for (int e = threadIdx.x; e < elems; e += blockDim.x) {
         const int m = e / ncols;
         const int n = col0 + (e - m * ncols);
-        float v = ordered_sum<8>(S, [&](int ss) { return ws[((size_t)ss * M + m) * N + n]; });
+        float v = ordered_sum<8>(S, [&](int ss) {
+            return __hip_atomic_load(ws + ((size_t)ss * M + m) * N + n, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        });
         if (sx) v *= scale;
         if (bias) v += bf16_to_f32(bias[n]);
         store_out(out, (size_t)m * N + n, v, out_f32);

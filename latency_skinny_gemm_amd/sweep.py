@@ -52,10 +52,10 @@ def point_sets():
 
 def _tiled_reductions(skg, S):
     """Reductions tried for a tiled plan with S splits: the last arriver reads
-    S partial tiles in one workgroup, worth it only for few splits."""
+    S partial tiles in one workgroup, worth it only up to 16 splits."""
     if S == 1:
         return (skg.REDUCE_NONE,)
-    return (skg.REDUCE_KERNEL, skg.REDUCE_LAST) if S <= 8 else (skg.REDUCE_KERNEL,)
+    return (skg.REDUCE_KERNEL, skg.REDUCE_LAST) if S <= 16 else (skg.REDUCE_KERNEL,)
 
 
 def fp8_candidates(skg, M, N, K):
