@@ -30,6 +30,18 @@ int skinny_floor_empty(int grid, int threads, hipStream_t stream);
 int skinny_floor_read(const void *buf, int rows, int row_bytes, int threads, unsigned *sink,
                       hipStream_t stream);
 
+/* The operand intake of the bf16 dot-product plan (cols columns per
+ * workgroup, `threads` threads, `vecs` 16-byte vectors per thread per row;
+ * the plan's cols, threads and depth) with no arithmetic: ceil(N / cols)
+ * workgroups each load their cols rows of W[N, K] and all M rows of x[M, K]
+ * with the dot kernel's load pattern, all in flight at once, and fold them
+ * with xor.  Writes nothing unless the data hash to a fixed constant (then
+ * one word per workgroup to sink[ceil(N / cols)]).  1 <= M <= 16, K % 8 == 0,
+ * vecs * threads >= K / 8, x and W 16-byte aligned; an unbuilt (M, cols,
+ * vecs) or too many threads for it returns hipErrorInvalidValue. */
+int skinny_floor_intake(const void *x, const void *W, int M, int N, int K, int cols, int threads,
+                        int vecs, unsigned *sink, hipStream_t stream);
+
 /* Copies `bytes` (a multiple of 16, 16-byte aligned) from src to dst with
  * 16-byte loads and stores: the reference for hardware read/write byte
  * counters (it must read and write exactly `bytes`). */

@@ -164,7 +164,7 @@ def sweep_point_fp8(skg, torch, M, N, K, pool_bytes, reps, stream, log):
     results.sort(key=lambda r: r[0])
     _, best_modes, best = results[0]
     rec = {"dtype": "fp8", "M": M, "N": N, "K": K, "slots": slots, "tiled": "ring2",
-           "mx_scales": "per_slot", "dot_wave1": "direct",
+           "mx_scales": "per_slot", "dot_wave1": "direct", "dot_reduce": "scatter",
            "best_us": round(max(best_modes.values()), 3),
            "best_us_tensor": round(best_modes["tensor"], 3), "best_us_mx": round(best_modes["mx"], 3),
            "best": plan_dict(best),
@@ -287,6 +287,7 @@ def sweep_point(skg, torch, M, N, K, pool_bytes, reps, stream, log, kinds=None):
     results.sort(key=lambda r: r[0])
     best_us, best = results[0]
     rec = {"M": M, "N": N, "K": K, "slots": slots, "tiled": "ring2", "dot_wave1": "direct",
+           "dot_reduce": "scatter",
            "best_us": round(best_us, 3),
            "best": plan_dict(best),
            "candidates": [[round(us, 3), plan_dict(p)] for us, p in results]}
@@ -307,6 +308,10 @@ def run(args):
     pts = point_sets()[args.points]
     if args.M:
         pts = [p for p in pts if p[0] in args.M]
+    if args.N:
+        pts = [p for p in pts if p[1] in args.N]
+    if args.K:
+        pts = [p for p in pts if p[2] in args.K]
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         skg.reserve(128, 4096, 0, 64)
@@ -356,6 +361,9 @@ def emit_table(files, out_path=TABLE):
                 # so do one-wave dot timings from before its direct-store path
                 if plan["kind"] == 1 and plan["threads"] == 64 and r.get("dot_wave1") != "direct":
                     continue
+                # and dot timings from before its reduce-scatter
+                if plan["kind"] == 1 and r.get("dot_reduce") != "scatter":
+                    continue
                 ident = tuple(plan.get(f, 0) for f in ("kind", "threads", "cols", "splits", "depth",
                                                           "waves_m", "reduce", "flags"))
                 # FP8: one entry per scale mode, each from that mode's timing;
@@ -398,6 +406,8 @@ def main():
     ap.add_argument("--points", default="headline",
                     choices=("headline", "router", "decode", "all", "fp8", "large_bf16", "large_fp8"))
     ap.add_argument("--M", type=int, nargs="*", help="restrict to these M")
+    ap.add_argument("--N", type=int, nargs="*", help="restrict to these N")
+    ap.add_argument("--K", type=int, nargs="*", help="restrict to these K")
     ap.add_argument("--out", default="sweep.jsonl", help="JSON-lines log the sweep appends to")
     ap.add_argument("--pool-mb", type=int, default=512)
     ap.add_argument("--reps", type=int, default=5)

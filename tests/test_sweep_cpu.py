@@ -45,7 +45,7 @@ def test_emit_ranks_by_median_and_filters(lib, tmp_path):
     b = _plan(1, 256, depth=4, flags=1)   # T = 256, V = 4
     w1 = _plan(1, 64, depth=14, flags=1)  # one wave
     tiled = _plan(3, 256, cols=4, splits=4, depth=3, reduce=2, flags=2, waves_m=1)
-    base = {"M": M, "N": N, "K": K, "slots": 4}
+    base = {"M": M, "N": N, "K": K, "slots": 4, "dot_reduce": "scatter"}
     # b wins once by luck; a wins on the median of three logs
     logs = [
         _write(tmp_path / "l1.jsonl", [dict(base, candidates=[[4.0, a], [3.0, b]])]),
@@ -70,6 +70,12 @@ def test_emit_ranks_by_median_and_filters(lib, tmp_path):
     rows = _rows(out)
     assert "SKG_KIND_TILED, 256, 4, 4, 3, 1" in rows[("SKG_DTYPE_BF16", "7168", "256", "8")]
     assert "SKG_KIND_DOT, 64, 1, 1, 14" in rows[("SKG_DTYPE_BF16", "7168", "256", "1")]
+    # dot timings from before the reduce-scatter (no dot_reduce tag) are ignored
+    untagged = {k: v for k, v in base.items() if k != "dot_reduce"}
+    logs.append(_write(tmp_path / "l6.jsonl", [dict(untagged, M=2, candidates=[[0.5, b], [9.0, tiled]],
+                                                    tiled="ring2")]))
+    sweep.emit_table(logs, out_path=str(out))
+    assert "SKG_KIND_TILED" in _rows(out)[("SKG_DTYPE_BF16", "7168", "256", "2")]
 
 
 def test_emit_skips_plans_the_planner_rejects(lib, tmp_path):
@@ -77,7 +83,7 @@ def test_emit_skips_plans_the_planner_rejects(lib, tmp_path):
     bad = _plan(1, 256, cols=5, depth=1, flags=1)   # 5 columns: not built
     stale = _plan(1, 256, depth=3, flags=1)         # V is 1 at this K: completes differently
     good = _plan(1, 256, depth=1, flags=1)
-    log = _write(tmp_path / "l.jsonl", [{"M": M, "N": N, "K": K, "slots": 4,
+    log = _write(tmp_path / "l.jsonl", [{"M": M, "N": N, "K": K, "slots": 4, "dot_reduce": "scatter",
                                          "candidates": [[1.0, bad], [1.5, stale], [2.0, good]]}])
     out = tmp_path / "table.inc"
     sweep.emit_table([log], out_path=str(out))
@@ -90,6 +96,7 @@ def test_emit_fp8_entries_per_scale_mode(lib, tmp_path):
     d = _plan(1, 256, depth=1)
     s = _plan(2, 256, cols=1, splits=1, depth=2)
     rec = {"dtype": "fp8", "M": M, "N": N, "K": K, "slots": 4, "mx_scales": "per_slot",
+           "dot_reduce": "scatter",
            "candidates": [[9.0, {"tensor": 4.0, "mx": 5.0}, d], [9.0, {"tensor": 4.5, "mx": 4.5}, s]]}
     out = tmp_path / "table.inc"
     sweep.emit_table([_write(tmp_path / "f.jsonl", [rec])], out_path=str(out))
