@@ -16,10 +16,17 @@ value = algorithmic bytes of the step / time of the step, in GB/s, with
 bytes per call = N*K*2 + M*K*2 + M*N*2 (W, x, out).
 
 Also reported: per-M microseconds per call (graphs of one M over the whole
-pool), the empty-kernel and read-stream floors at the same shape, the
+pool), the empty-kernel and read-stream floors at the same shape and each
+M's operand-intake floor (the dot plan's loads with no arithmetic), the
 roofline line of the dominant kernel, and the CPU oracle's time on a
 bounded sample of the same workload (its outputs also checked against the
-GPU's).
+GPU's).  Then every other configuration, each with its own cold pool and
+read-stream floor: the small router GEMM (K = 2048, N = 256, M = 1), the
+router sweep at N = 384, the router shapes (4096, 256), (6144, 256) and
+(2880, 128) with and without bias, the dense decode linears with and
+without bias, FP8 K = N = 4096 in both scale modes, and the fp32-output and
+fused-quantisation variants; sampled outputs of every configuration are
+checked against the oracle.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu]
 """
@@ -30,6 +37,7 @@ import statistics
 import os
 import sys
 import time
+import zlib
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -90,13 +98,19 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 section")
-    ap.add_argument("--no-decode", action="store_true", help="skip the dense decode section")
+    ap.add_argument("--no-decode", action="store_true", help="skip the dense decode shapes")
+    ap.add_argument("--no-router-configs", action="store_true",
+                    help="skip the router shapes other than the headline one")
     ap.add_argument("--no-f3", action="store_true",
                     help="skip the fp32-output and fused-quantisation section")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="for rocprofv3 --pmc: the MFMA configurations (FP8 K = N = 4096 at "
                          "M >= 64, bf16 K = 7168, N = 4096 at M >= 128), a few cold calls each, "
                          "and exit")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="for rocprofv3 --pmc: the decode (K = 7168, N = 4096, M = 8 and 128) "
+                         "and FP8 (K = N = 4096, M = 16 and 128, both scale modes) calls, a few "
+                         "cold calls each, then a 64 MiB reference copy, and exit")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for rocprofv3 --pmc: launch each headline call a few times on cold "
                          "weights, then a 64 MiB reference copy, and exit")
@@ -135,13 +149,90 @@ PER_M_REPLAYS = 11  # timed graph replays per M: median, p10, p90
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it: the first processor's model
+    name with its family, model and stepping numbers, and the logical CPU
+    count the OS reports."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" not in line:
+                if fields:
+                    break  # end of the first processor's block
+                continue
+            k, v = (t.strip() for t in line.split(":", 1))
+            if k in ("model name", "cpu family", "model", "stepping", "vendor_id"):
+                fields.setdefault(k, v)
     except OSError:
-        pass
-    return None
+        return None
+    return {"model_name": fields.get("model name"), "vendor": fields.get("vendor_id"),
+            "family": fields.get("cpu family"), "model": fields.get("model"),
+            "stepping": fields.get("stepping"), "logical_cpus": os.cpu_count()}
+
+
+TRAFFIC_PROBE_CALLS = 4
+
+
+def traffic_probe(skg, torch, floors, stream, sptr):
+    """Eager launches for HBM byte counters of the tiled and FP8 plans:
+    TRAFFIC_PROBE_CALLS cold calls (each on its own W) of every
+    configuration below in the printed order, then one copy of COPY_BYTES
+    to scale the counters.  Every input is made before the first GEMM, so
+    the library's dispatches are exactly the printed calls."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(78)
+    n = TRAFFIC_PROBE_CALLS
+    KB, NB, K8, N8 = DECODE_K, 4096, 4096, 4096
+    WB = (torch.randn((n, NB, KB), generator=g, device=dev) * KB ** -0.5).to(torch.bfloat16)
+    W8 = torch.empty((2 * n, N8, K8), dtype=torch.float8_e4m3fn, device=dev)
+    for i in range(2 * n):
+        W8[i].copy_(torch.randn((N8, K8), generator=g, device=dev).to(torch.float8_e4m3fn))
+    XB = {M: torch.randn((M, KB), generator=g, device=dev).to(torch.bfloat16) for M in (8, 128)}
+    X8 = {M: torch.randn((M, K8), generator=g, device=dev).to(torch.float8_e4m3fn) for M in (16, 128)}
+    XE = {M: torch.randint(126, 129, (M, K8 // 32), generator=g, device=dev).to(torch.uint8)
+          for M in (16, 128)}
+    WE = torch.randint(126, 129, (N8, K8 // 32), generator=g, device=dev).to(torch.uint8)
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    out = torch.empty((128, 4096), dtype=torch.bfloat16, device=dev)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    order = []
+    with torch.cuda.stream(stream):
+        for M in (8, 128):
+            p = skg.plan(M, NB, KB)
+            for i in range(n):
+                rc = skg.lib().skinny_gemm_bf16(XB[M].data_ptr(), WB[i].data_ptr(), None, None,
+                                                out.data_ptr(), M, NB, KB, sptr)
+                if rc != 0:
+                    raise skg.SkinnyGemmError(rc, f"traffic probe bf16 M={M}")
+            order.append({"config": f"bf16_M{M}_N{NB}_K{KB}", "calls": n, **plan_brief(p),
+                          "algorithmic_bytes": 2 * NB * KB + 2 * M * KB + 2 * M * NB})
+        slot = 0
+        for M in (16, 128):
+            for mode in ("tensor", "mx"):
+                sc = skg.Fp8Scales()
+                if mode == "tensor":
+                    sc.mode, sc.sx, sc.sw = skg.FP8_PER_TENSOR, one.data_ptr(), one.data_ptr()
+                else:
+                    sc.mode, sc.x_e8m0, sc.w_e8m0 = skg.FP8_MX32, XE[M].data_ptr(), WE.data_ptr()
+                p = skg.plan(M, N8, K8, skg.DTYPE_FP8 if mode == "tensor" else skg.DTYPE_FP8_MX)
+                for _ in range(n):
+                    rc = skg.lib().skinny_gemm_fp8(X8[M].data_ptr(), W8[slot].data_ptr(), None,
+                                                   ctypes.byref(sc), out.data_ptr(), M, N8, K8, sptr)
+                    if rc != 0:
+                        raise skg.SkinnyGemmError(rc, f"traffic probe fp8 M={M} {mode}")
+                    slot = (slot + 1) % (2 * n)
+                extra = 8 if mode == "tensor" else (M + N8) * K8 // 32
+                order.append({"config": f"fp8_{mode}_M{M}_N{N8}_K{K8}", "calls": n, **plan_brief(p),
+                              "algorithmic_bytes": N8 * K8 + M * K8 + 2 * M * N8 + extra})
+        rc = floors.skinny_floor_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                      ctypes.c_size_t(COPY_BYTES), sptr)
+        if rc != 0:
+            raise RuntimeError(f"skinny_floor_copy failed: {rc}")
+    stream.synchronize()
+    print(json.dumps({"traffic_probe": order, "copy_bytes": COPY_BYTES}), flush=True)
+    return 0
 
 
 def mfma_probe(skg, torch, stream, sptr):
@@ -250,52 +341,137 @@ DECODE_K = 7168
 DECODE_N = (576, 2112, 4096)
 DECODE_M = (1, 8, 32, 64, 128)
 LARGE_M = (256, 512)  # the larger-M regime, at N = 4096 only
+SECTION_POOL = 512 << 20  # W bytes of a section's cold pool (> the 256 MB Infinity Cache)
+KIND_NAMES = {1: "dot", 2: "splitk", 3: "tiled"}
+
+# The bf16 configurations other than the headline shape, by (K, N): the
+# small router GEMM (K = 2048, N = 256, M = 1), the router sweep at N = 384
+# (M = 1..16), the tuned router shapes (4096, 256), (6144, 256) and the
+# non-tile-aligned (2880, 128) at M in {1, 3, 4, 5, 8, 9, 12, 16} with and
+# without bias, and the dense decode linears (K = 7168, N in {576, 2112,
+# 4096}, M in {1, 8, 32, 64, 128} with and without bias; M = 256 and 512 at
+# N = 4096).
+ROUTER_M = (1, 3, 4, 5, 8, 9, 12, 16)
+BF16_SHAPES = (
+    [("small_k2048_n256", 2048, 256, [(1, False)]),
+     ("router_k7168_n384", 7168, 384, [(M, False) for M in range(1, 17)])]
+    + [(f"router_k{K}_n{N}", K, N, [(M, b) for M in ROUTER_M for b in (False, True)])
+       for (K, N) in ((4096, 256), (6144, 256), (2880, 128))]
+    + [(f"decode_k{DECODE_K}_n{N}", DECODE_K, N,
+        [(M, b) for M in DECODE_M for b in (False, True)]
+        + ([(M, False) for M in LARGE_M] if N == 4096 else []))
+       for N in DECODE_N])
 
 
-def decode_section(skg, torch, stream, sptr, samples):
-    """bf16 dense decode linear, K = 7168, N in {576, 2112, 4096}, M in
-    {1, 8, 32, 64, 128} (and 256, 512 at N = 4096; the planner's plan, no
-    bias): microseconds per call
-    over a cold pool of >= 512 MB of distinct W, the algorithmic GB/s and
-    its fraction of 8 TB/s."""
+def plan_brief(p):
+    return {"kernel": KIND_NAMES[p.kind], "threads": p.threads, "cols": p.cols,
+            "splits": p.splits, "depth": p.depth,
+            "reduce": {0: "none", 1: "last", 2: "kernel"}[p.reduce]}
+
+
+def read_floor_us(torch, floors, stream, sptr, W, row_bytes, sink):
+    """The read-stream floor at one shape: a plain read of each pool slot's
+    W, timed like the GEMM (the same graph replay over the same cold pool),
+    two ways: one workgroup of 256 threads per row, and the same bytes read
+    flat in 32 KB per workgroup; every load in flight at once in both.
+    Returns (the faster, per-row, flat) microseconds per call."""
+    slots, rows = W.shape[0], W.shape[1]
+    nbytes = rows * row_bytes
+
+    def per_row():
+        for s in range(slots):
+            rc = floors.skinny_floor_read(ctypes.c_void_p(W[s].data_ptr()), rows, row_bytes, 256,
+                                          ctypes.c_void_p(sink.data_ptr()), sptr)
+            if rc != 0:
+                raise RuntimeError(f"skinny_floor_read failed: {rc}")
+
+    def flat():
+        for s in range(slots):
+            rc = floors.skinny_floor_read_flat(ctypes.c_void_p(W[s].data_ptr()),
+                                               ctypes.c_size_t(nbytes),
+                                               ctypes.c_void_p(sink.data_ptr()), sptr)
+            if rc != 0:
+                raise RuntimeError(f"skinny_floor_read_flat failed: {rc}")
+    t_rows = graph_times(torch, stream, per_row, slots)[0]
+    t_flat = graph_times(torch, stream, flat, slots)[0]
+    return min(t_rows, t_flat), t_rows, t_flat
+
+
+def intake_floor_us(torch, floors, stream, sptr, X, W, M, N, K, p, sink):
+    """The operand-intake floor of a dot-kernel plan: its W and x loads,
+    exactly as the plan issues them, with no arithmetic (skinny_floor_intake),
+    over the same cold pool; None when that plan's intake kernel is not
+    built."""
+    slots = W.shape[0]
+
+    def calls():
+        for s in range(slots):
+            rc = floors.skinny_floor_intake(ctypes.c_void_p(X[s].data_ptr()),
+                                            ctypes.c_void_p(W[s].data_ptr()), M, N, K, p.cols,
+                                            p.threads, p.depth, ctypes.c_void_p(sink.data_ptr()),
+                                            sptr)
+            if rc != 0:
+                raise RuntimeError(f"skinny_floor_intake failed: {rc}")
+    try:
+        return graph_times(torch, stream, calls, slots)[0]
+    except RuntimeError:
+        return None
+
+
+def bf16_shape_section(skg, torch, floors, stream, sptr, samples, K, N, points, seed):
+    """One bf16 shape (K, N) at the given (M, bias) points, each on the
+    planner's plan: microseconds per call (median, p10, p90 of graph
+    replays over a cold pool of >= 512 MB of distinct W, each slot with its
+    own x and bias), the algorithmic GB/s and its fraction of 8 TB/s, and
+    the fraction of the shape's read-stream floor; dot-kernel points also
+    give their operand-intake floor.  Bias ~ N(0, 0.1) bf16 (variance 0.1)."""
     dev = torch.device("cuda:0")
-    K = DECODE_K
     g = torch.Generator(device=dev)
-    g.manual_seed(11)
-    res = {}
-    for N in DECODE_N:
-        Ms = DECODE_M + (LARGE_M if N == 4096 else ())
-        slots = -(-(512 << 20) // (N * K * 2))
-        W = torch.empty((slots, N, K), dtype=torch.bfloat16, device=dev)
-        for i in range(slots):
-            W[i].copy_((torch.randn((N, K), generator=g, device=dev) * K ** -0.5).to(torch.bfloat16))
-        for M in Ms:
-            X = torch.randn((slots, M, K), generator=g, device=dev).to(torch.bfloat16)
-            O = torch.empty((slots, M, N), dtype=torch.bfloat16, device=dev)
-
-            def calls():
-                for s in range(slots):
-                    rc = skg.lib().skinny_gemm_bf16(X[s].data_ptr(), W[s].data_ptr(), None, None,
-                                                    O[s].data_ptr(), M, N, K, sptr)
-                    if rc != 0:
-                        raise skg.SkinnyGemmError(rc, f"skinny_gemm_bf16 M={M} N={N}")
-            us, p10, p90 = graph_times(torch, stream, calls, slots)
-            torch.cuda.synchronize()
-            rows, cols = sample_outputs(M, N)
-            samples.append({"key": f"decode_N{N}_M{M}", "kind": "bf16", "K": K,
-                            "x": X[0][rows].cpu(), "w": W[0][cols].cpu(),
-                            "out": O[0][rows][:, cols].cpu()})
-            byts = 2 * N * K + 2 * M * K + 2 * M * N
-            p = skg.plan(M, N, K)
-            res[f"N{N}_M{M}"] = {"us_per_call": round(us, 3), "p10_us": round(p10, 3),
-                                 "p90_us": round(p90, 3),
-                                 "GBps": round(byts / (us * 1e-6) / 1e9, 1),
-                                 "frac_of_8TBps": round(byts / (us * 1e-6) / (PEAK_GBS * 1e9), 4),
-                                 "TFLOPs": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1),
-                                 "kernel": {1: "dot", 2: "splitk", 3: "tiled"}[p.kind]}
-            del X, O
-        del W
-        torch.cuda.empty_cache()
+    g.manual_seed(seed)
+    slots = max(4, -(-SECTION_POOL // (N * K * 2)))
+    Mmax = max(M for M, _ in points)
+    W = torch.empty((slots, N, K), dtype=torch.bfloat16, device=dev)
+    for i in range(slots):
+        W[i].copy_((torch.randn((N, K), generator=g, device=dev) * K ** -0.5).to(torch.bfloat16))
+    X = torch.randn((slots, Mmax, K), generator=g, device=dev).to(torch.bfloat16)
+    B = (torch.randn((slots, N), generator=g, device=dev) * 0.1 ** 0.5).to(torch.bfloat16)
+    O = torch.empty((slots, Mmax, N), dtype=torch.bfloat16, device=dev)
+    sink = torch.zeros(max(N, 4096), dtype=torch.int32, device=dev)
+    t_read, t_rows, t_flat = read_floor_us(torch, floors, stream, sptr, W, 2 * K, sink)
+    res = {"read_stream_floor_us": round(t_read, 3), "read_per_row_us": round(t_rows, 3),
+           "read_flat_us": round(t_flat, 3), "W_bytes": 2 * N * K, "pool_slots": slots}
+    L = skg.lib()
+    for M, bias in points:
+        def calls(M=M, bias=bias):
+            for s in range(slots):
+                rc = L.skinny_gemm_bf16(X[s].data_ptr(), W[s].data_ptr(),
+                                        B[s].data_ptr() if bias else None, None, O[s].data_ptr(),
+                                        M, N, K, sptr)
+                if rc != 0:
+                    raise skg.SkinnyGemmError(rc, f"skinny_gemm_bf16 M={M} N={N} K={K}")
+        us, p10, p90 = graph_times(torch, stream, calls, slots)
+        torch.cuda.synchronize()
+        key = f"M{M}" + ("_bias" if bias else "")
+        rows, cols = sample_outputs(M, N)
+        samples.append({"key": f"bf16_K{K}_N{N}_{key}", "kind": "bf16", "K": K,
+                        "x": X[0][:M][rows].cpu(), "w": W[0][cols].cpu(),
+                        "b": B[0][cols].cpu() if bias else None,
+                        "out": O[0][:M][rows][:, cols].cpu()})
+        byts = 2 * N * K + 2 * M * K + 2 * M * N + (2 * N if bias else 0)
+        p = skg.plan(M, N, K)
+        e = {"us_per_call": round(us, 3), "p10_us": round(p10, 3), "p90_us": round(p90, 3),
+             "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+             "frac_of_8TBps": round(byts / (us * 1e-6) / (PEAK_GBS * 1e9), 4),
+             "of_read_floor": round(t_read / us, 3),
+             "TFLOPs": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1), **plan_brief(p)}
+        if p.kind == skg.KIND_DOT:
+            t_in = intake_floor_us(torch, floors, stream, sptr, X, W, M, N, K, p, sink)
+            if t_in is not None:
+                e["intake_floor_us"] = round(t_in, 3)
+                e["of_intake_floor"] = round(t_in / us, 3)
+        res[key] = e
+    del W, X, B, O
+    torch.cuda.empty_cache()
     return res
 
 
@@ -368,11 +544,12 @@ def f3_section(skg, torch, stream, sptr):
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 
 
-def fp8_section(skg, torch, stream, sptr, samples):
+def fp8_section(skg, torch, floors, stream, sptr, samples):
     """FP8 e4m3, K = N = 4096, M in {1, 16, 64, 128, 256, 512}, per-tensor and MX
     scales: microseconds per call over a cold pool of >= 512 MB of distinct
-    W, the achieved GB/s (W, x, out and scale bytes) and the MFMA rate
-    against the dense fp8 peak."""
+    W, the achieved GB/s (W, x, out and scale bytes), its fraction of the
+    read-stream floor of the same 16.8 MB, and the MFMA rate against the
+    dense fp8 peak."""
     K = N = 4096
     dev = torch.device("cuda:0")
     slots = -(-(512 << 20) // (N * K))
@@ -381,7 +558,10 @@ def fp8_section(skg, torch, stream, sptr, samples):
     W = torch.empty((slots, N, K), dtype=torch.float8_e4m3fn, device=dev)
     for i in range(slots):
         W[i].copy_(torch.randn((N, K), generator=g, device=dev).to(torch.float8_e4m3fn))
-    res = {}
+    sink = torch.zeros(N, dtype=torch.int32, device=dev)
+    t_read, t_rows, t_flat = read_floor_us(torch, floors, stream, sptr, W, K, sink)
+    res = {"read_stream_floor_us": round(t_read, 3), "read_per_row_us": round(t_rows, 3),
+           "read_flat_us": round(t_flat, 3), "W_bytes": N * K, "pool_slots": slots}
     for M in (1, 16, 64, 128, 256, 512):
         X = torch.randn((slots, M, K), generator=g, device=dev).to(torch.float8_e4m3fn)
         O = torch.empty((slots, M, N), dtype=torch.bfloat16, device=dev)
@@ -420,10 +600,11 @@ def fp8_section(skg, torch, stream, sptr, samples):
                                    "p90_us": round(p90, 3),
                                    "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                                    "frac_of_8TBps": round(byts / (us * 1e-6) / (PEAK_GBS * 1e9), 4),
+                                   "of_read_floor": round(t_read / us, 3),
                                    "TFLOPs": round(tflops, 1),
                                    "mfma_util": round(tflops / FP8_PEAK_TFLOPS, 4),
-                                   "kernel": {1: "dot", 2: "splitk", 3: "tiled"}[skg.plan(
-                                       M, N, K, skg.DTYPE_FP8 if mode == "tensor" else skg.DTYPE_FP8_MX).kind]}
+                                   **plan_brief(skg.plan(M, N, K, skg.DTYPE_FP8 if mode == "tensor"
+                                                         else skg.DTYPE_FP8_MX))}
         del X, O, XE, WE
     del W
     torch.cuda.empty_cache()
@@ -446,7 +627,9 @@ def check_samples(samples):
 
     for s in samples:
         if s["kind"] == "bf16":
-            ref = oracle.gemm_bf16(bits16(s["x"]), bits16(s["w"]), threads=16)
+            b = s.get("b")
+            ref = oracle.gemm_bf16(bits16(s["x"]), bits16(s["w"]), None if b is None else bits16(b),
+                                   threads=16)
         elif s["kind"] == "fp8_tensor":
             ref = oracle.gemm_fp8_tensor(bits8(s["x"]), bits8(s["w"]), 1.0, 1.0, threads=16)
         else:
@@ -479,8 +662,16 @@ def main():
     floors.skinny_floor_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     floors.skinny_floor_read.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_void_p, ctypes.c_void_p]
+    floors.skinny_floor_intake.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 6 + \
+        [ctypes.c_void_p, ctypes.c_void_p]
+    floors.skinny_floor_read_flat.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+    floors.skinny_floor_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_void_p]
     stream = torch.cuda.Stream()
     sptr = ctypes.c_void_p(stream.cuda_stream)
+    if args.traffic_probe:
+        return traffic_probe(skg, torch, floors, stream, sptr)
 
     # ---------------------------------------------------------------- pool
     w_bytes = N_DIM * K_DIM * 2
@@ -498,13 +689,10 @@ def main():
         X[i].copy_(torch.randn((Ms, K_DIM), generator=g, device=dev))
     torch.cuda.synchronize()
 
-    floors.skinny_floor_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                         ctypes.c_void_p]
     if args.pmc_probe:
         return pmc_probe(skg, torch, floors, stream, sptr, W, X, OUT, n_slots)
 
     plans = {M: skg.plan(M, N_DIM, K_DIM) for M in M_VALUES}
-    kind_name = {skg.KIND_DOT: "dot", skg.KIND_SPLITK: "splitk"}
 
     def launch(slot, M):
         rc = skg.lib().skinny_gemm_bf16(X[slot].data_ptr(), W[slot].data_ptr(), None, None,
@@ -592,8 +780,7 @@ def main():
                     "p90_us": round(ts[(9 * len(ts)) // 10], 3),
                     "GBps": round(call_bytes(M) / (us * 1e-6) / 1e9, 1),
                     "frac_of_8TBps": round(call_bytes(M) / (us * 1e-6) / (PEAK_GBS * 1e9), 4),
-                    "kernel": kind_name[plans[M].kind], "plan": {k: v for k, v in plans[M].as_dict().items()
-                                                                if k in ("threads", "cols", "splits", "depth", "reduce", "grid")}}
+                    **plan_brief(plans[M])}
         del gr
 
     # ---------------------------------------------------------------- floors
@@ -608,10 +795,25 @@ def main():
             floors.skinny_floor_read(ctypes.c_void_p(W[s].data_ptr()), N_DIM, K_DIM * 2, 256,
                                      ctypes.c_void_p(sink.data_ptr()), sptr)
 
+    def floor_read_flat():
+        for s in range(n_slots):
+            floors.skinny_floor_read_flat(ctypes.c_void_p(W[s].data_ptr()), ctypes.c_size_t(w_bytes),
+                                          ctypes.c_void_p(sink.data_ptr()), sptr)
+
     t_empty = statistics.median(replay_times(capture(floor_empty), PER_M_REPLAYS)) / n_slots * 1e6
-    t_read = statistics.median(replay_times(capture(floor_read), PER_M_REPLAYS)) / n_slots * 1e6
+    t_read_rows = statistics.median(replay_times(capture(floor_read), PER_M_REPLAYS)) / n_slots * 1e6
+    t_read_flat = statistics.median(replay_times(capture(floor_read_flat), PER_M_REPLAYS)) / n_slots * 1e6
+    t_read = min(t_read_rows, t_read_flat)
     for M in M_VALUES:  # context: the same bytes read by a plain stream at this size
         per_m[M]["of_read_floor"] = round(t_read / per_m[M]["us_per_call"], 3)
+    # the operand-intake floor of each M's dot plan: its loads alone
+    for M in M_VALUES:
+        if plans[M].kind != skg.KIND_DOT:
+            continue
+        t_in = intake_floor_us(torch, floors, stream, sptr, X, W, M, N_DIM, K_DIM, plans[M], sink)
+        if t_in is not None:
+            per_m[M]["intake_floor_us"] = round(t_in, 3)
+            per_m[M]["of_intake_floor"] = round(t_in / per_m[M]["us_per_call"], 3)
 
     # ---------------------------------------------------------------- determinism
     # every plan twice on the same inputs: the outputs must agree bit for bit
@@ -647,7 +849,11 @@ def main():
         import oracle
         from oracle import tolerance
 
-        threads = min(16, len(os.sched_getaffinity(0)))
+        # every CPU this process may run on, unless the host's OpenMP setting
+        # (the CPU share given to one GPU's jobs) is lower
+        affinity = len(os.sched_getaffinity(0))
+        share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+        threads = min(affinity, share) if share > 0 else affinity
         x0 = X[0].cpu()
         w0 = W[0].cpu()
         with torch.cuda.stream(stream):
@@ -688,11 +894,20 @@ def main():
                          f"{t_cpu / reps / len(M_VALUES) * 1e6:.0f} (mean over M)",
                "single_thread_value": round(step / statistics.median(one) / 1e9, 4),
                "single_thread_sample": "median of 3 passes over M=1..16, one thread",
-               "cpu_model": cpu_model()}
+               "affinity_cpus": affinity, "omp_num_threads": share or None,
+               "cpu": cpu_model()}
 
-    samples = []  # sampled outputs of the FP8 and decode sections, checked below
-    fp8 = None if args.no_fp8 else fp8_section(skg, torch, stream, sptr, samples)
-    decode = None if args.no_decode else decode_section(skg, torch, stream, sptr, samples)
+    samples = []  # sampled outputs of the other sections, checked below
+    fp8 = None if args.no_fp8 else fp8_section(skg, torch, floors, stream, sptr, samples)
+    configs = {}
+    for name, K, N, points in BF16_SHAPES:
+        if args.no_decode if name.startswith("decode") else args.no_router_configs:
+            continue
+        configs[name] = bf16_shape_section(skg, torch, floors, stream, sptr, samples, K, N, points,
+                                           seed=zlib.crc32(name.encode()))
+        # the launch floor does not depend on the shape (1 and 256 workgroups
+        # measure the same): the headline's empty kernel, beside each shape
+        configs[name]["empty_kernel_floor_us"] = round(t_empty, 3)
     f3 = None if args.no_f3 else f3_section(skg, torch, stream, sptr)
     # CPU-baseline leg, continued: the sections' sampled outputs against the oracle
     parity_sections = None
@@ -713,11 +928,13 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "floors": {"empty_kernel_us": round(t_empty, 3), "read_stream_us": round(t_read, 3),
+                   "read_per_row_us": round(t_read_rows, 3), "read_flat_us": round(t_read_flat, 3),
                    "read_stream_GBps": round(w_bytes / (t_read * 1e-6) / 1e9, 1),
-                   "shape": "256 workgroups x 256 threads; read: 256 rows x 14336 B"},
+                   "shape": "empty: 256 workgroups x 256 threads; read: 256 rows x 14336 B, "
+                            "or flat in 32 KB per workgroup (the faster is the floor)"},
         "per_m": per_m,
         "fp8_k4096_n4096": fp8,
-        "decode_bf16_k7168": decode,
+        "bf16_configs": configs,
         "fp32_out_and_fused_quant": f3,
         "parity": parity,
         "parity_sections": parity_sections,

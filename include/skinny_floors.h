@@ -30,6 +30,14 @@ int skinny_floor_empty(int grid, int threads, hipStream_t stream);
 int skinny_floor_read(const void *buf, int rows, int row_bytes, int threads, unsigned *sink,
                       hipStream_t stream);
 
+/* Reads `bytes` bytes (a multiple of 16, 16-byte aligned) from `buf` as one
+ * flat array: ceil(bytes / 32768) workgroups of 256 threads, each reading
+ * its 32 KB with every 16-byte load in flight at once.  Writes nothing
+ * unless the data hash to a fixed constant (then one word per workgroup to
+ * sink[ceil(bytes / 32768)]).  The read-stream floor for buffers whose rows
+ * are too short for one workgroup each. */
+int skinny_floor_read_flat(const void *buf, size_t bytes, unsigned *sink, hipStream_t stream);
+
 /* The operand intake of the bf16 dot-product plan (cols columns per
  * workgroup, `threads` threads, `vecs` 16-byte vectors per thread per row;
  * the plan's cols, threads and depth) with no arithmetic: ceil(N / cols)

@@ -30,6 +30,24 @@ __global__ void __launch_bounds__(1024)
     if (h == 0x9E3779B9u) sink[blockIdx.x] = h;
 }
 
+// A flat read of `bytes` bytes: workgroup b reads the 32 KB [32768 b,
+// 32768 (b + 1)) (the last one less), 256 threads with 8 loads of 16 bytes
+// each, every load issued before any is consumed.
+__global__ void __launch_bounds__(256)
+    read_flat_kernel(const uint8_t *__restrict__ buf, size_t bytes, unsigned *__restrict__ sink) {
+    const size_t base = (size_t)blockIdx.x * 32768;
+    const size_t left = bytes - base;
+    const skg::Rsrc r = skg::make_rsrc(buf + base, (unsigned)(left < 32768 ? left : 32768));
+    u32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] = skg::load16<skg::kCacheStream>(r, (unsigned)(threadIdx.x + i * 256) * 16u);
+    unsigned h = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+    if (h == 0x9E3779B9u) sink[blockIdx.x] = h;
+}
+
 __global__ void __launch_bounds__(256)
     copy_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst, size_t n) {
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -159,6 +177,17 @@ extern "C" int skinny_floor_read(const void *buf, int rows, int row_bytes, int t
         return (int)hipErrorInvalidValue;
     hipLaunchKernelGGL(read_kernel, dim3(rows), dim3(threads), 0, stream, (const uint8_t *)buf,
                        row_bytes, sink);
+    return (int)hipGetLastError();
+}
+
+extern "C" int skinny_floor_read_flat(const void *buf, size_t bytes, unsigned *sink,
+                                      hipStream_t stream) {
+    if (!buf || !sink || bytes < 16 || bytes % 16 || (uintptr_t)buf % 16 ||
+        bytes > ((size_t)1 << 40))
+        return (int)hipErrorInvalidValue;
+    const size_t grid = (bytes + 32767) / 32768;
+    hipLaunchKernelGGL(read_flat_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint8_t *)buf, bytes, sink);
     return (int)hipGetLastError();
 }
 
