@@ -342,7 +342,7 @@ DECODE_N = (576, 2112, 4096)
 DECODE_M = (1, 8, 32, 64, 128)
 LARGE_M = (256, 512)  # the larger-M regime, at N = 4096 only
 SECTION_POOL = 512 << 20  # W bytes of a section's cold pool (> the 256 MB Infinity Cache)
-KIND_NAMES = {1: "dot", 2: "splitk", 3: "tiled"}
+KIND_NAMES = {1: "dot", 2: "splitk", 3: "tiled", 4: "rows"}
 
 # The bf16 configurations other than the headline shape, by (K, N): the
 # small router GEMM (K = 2048, N = 256, M = 1), the router sweep at N = 384

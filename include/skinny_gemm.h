@@ -96,6 +96,11 @@ extern "C" {
 #define SKG_KIND_TILED 3  /* MFMA kernel with x and W tiles streamed into an LDS ring
                              (K % 32 == 0), K split
                              over workgroups (wide column tiles, larger M) */
+#define SKG_KIND_ROWS 4   /* bf16, M <= 64: MFMA kernel streaming whole row
+                             segments (1 KB, or 512 bytes with SKG_FLAG_ROWS_HALF)
+                             of x and W into an LDS ring; a workgroup owns 8 or 16
+                             columns and the whole K, its waves split the K steps
+                             (no cross-workgroup reduction) */
 
 #define SKG_REDUCE_NONE 0  /* splits == 1: no cross-workgroup reduction */
 #define SKG_REDUCE_LAST 1  /* the last workgroup to finish a tile reduces it */
@@ -107,6 +112,16 @@ extern "C" {
                           largest term) */
 #define SKG_FLAG_TILED_WIDE 2 /* TILED: LDS stages of four 32-wide K steps (256 bytes of
                                 each row) instead of two (128 bytes) */
+#define SKG_FLAG_DOT_XLDS 4 /* DOT (bf16, together with SKG_FLAG_DOT2): all M rows
+                              of x staged in LDS once per workgroup; each wave
+                              owns cols / (threads / 64) columns (1, 2 or 4) over
+                              the whole K, so `cols` may be up to 64 and no
+                              cross-wave reduction is needed.  Needs K = 512 * V
+                              with V in {4, 6, 8, 12, 14, 16} and M * K * 2 bytes
+                              of LDS (at most 160 KB - 256). */
+
+#define SKG_FLAG_ROWS_HALF 8 /* ROWS: stages of 256 K elements (512 bytes of each row)
+                               instead of 512; room in LDS for more rows of x */
 
 #define SKG_MAX_M 512 /* above 128 rows only tiled plans (K % 32, FP8 K % 128) */
 
@@ -131,14 +146,18 @@ typedef struct skinny_fp8_scales {
  * idea as a plain struct.  Fields marked (derived) are filled in by the
  * library from the others. */
 typedef struct SkgPlan {
-    int kind;     /* SKG_KIND_DOT, SKG_KIND_SPLITK or SKG_KIND_TILED */
-    int threads;  /* workgroup size, a multiple of 64, <= 1024 (TILED: 256) */
-    int cols;     /* DOT: output columns per workgroup (bf16: 1-4; FP8: 1, 2, 4);
+    int kind;     /* SKG_KIND_DOT, SKG_KIND_SPLITK, SKG_KIND_TILED or SKG_KIND_ROWS */
+    int threads;  /* workgroup size, a multiple of 64, <= 1024 (TILED: 256;
+                     ROWS: 256 or 512) */
+    int cols;     /* DOT: output columns per workgroup (bf16: 1-4; FP8: 1, 2, 4;
+                     with SKG_FLAG_DOT_XLDS: 1, 2 or 4 per wave);
                      SPLITK: 16-column blocks per workgroup (1, 2, 4);
-                     TILED: 16-column blocks per workgroup (1, 2, 4, 8, 16) */
-    int splits;   /* SPLITK, TILED: number of K chunks S (>= 1); DOT: 1 */
+                     TILED: 16-column blocks per workgroup (1, 2, 4, 8, 16);
+                     ROWS: output columns per workgroup (8, 16) */
+    int splits;   /* SPLITK, TILED: number of K chunks S (>= 1); DOT, ROWS: 1 */
     int depth;    /* SPLITK: 32-wide K steps a wave keeps in flight (1, 2, 4, 8);
                      TILED: stages of the LDS ring (2, 3, 4, 5, 6, 8);
+                     ROWS: stages of the LDS ring (3, 4, 5, 6);
                      DOT: 16-byte vectors per thread per column (derived) */
     int waves_m;  /* TILED: waves along M (1, 2, 4; the other 4/waves_m waves
                      split the columns); 0 = chosen by the library */

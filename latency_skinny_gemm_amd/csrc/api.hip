@@ -156,8 +156,9 @@ int acquire(hipStream_t stream, size_t floats, size_t tickets, float **ws, unsig
 
 int run_bf16(const void *x, const void *W, const void *bias, void *out, int out_f32, int M, int N,
              int K, const SkgPlan &p, hipStream_t stream) {
-    if (p.kind == SKG_KIND_DOT) {
-        int e = launch_dot(p, x, W, bias, out, out_f32, M, N, K, stream);
+    if (p.kind == SKG_KIND_DOT || p.kind == SKG_KIND_ROWS) {
+        int e = p.kind == SKG_KIND_DOT ? launch_dot(p, x, W, bias, out, out_f32, M, N, K, stream)
+                                       : launch_rows(p, x, W, bias, out, out_f32, M, N, K, stream);
         return e == (int)hipSuccess ? SKG_OK : SKG_ERR_HIP;
     }
     float *ws = nullptr;

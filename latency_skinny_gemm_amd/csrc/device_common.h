@@ -33,6 +33,39 @@ __device__ __forceinline__ u32x4 load16(Rsrc r, unsigned byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, POLICY);
 }
 
+// ---------------------------------------------------------------- LDS
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer straight into LDS at dst + 16 * lane
+// (dst wave-uniform; LDS-DMA, no VGPR round trip).  Kept out of the kernel
+// body: used there directly, the builtin made the host pass drop the
+// kernels' launch stubs.
+template <int POLICY>
+__device__ __forceinline__ void lds_load16(Rsrc r, unsigned char *dst, unsigned off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, off, 0, 0, POLICY);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8 = 0).  Vector memory
+// loads return in issue order, so vmcnt(N) means all but this wave's last
+// N loads have landed (in registers or, for LDS-DMA, in LDS).  Waiting for
+// lgkmcnt too means this wave's own LDS reads have returned, so a barrier
+// after it also orders them before later LDS writes by any wave.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
+}
+
+// s_barrier without a memory fence.  The asm statements keep the compiler
+// from moving LDS accesses across it; the hardware ordering comes from the
+// explicit vmcnt wait that precedes it.
+__device__ __forceinline__ void barrier_nofence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf16_lo(unsigned v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned v) { return __uint_as_float(v & 0xFFFF0000u); }

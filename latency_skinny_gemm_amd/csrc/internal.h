@@ -41,6 +41,56 @@ constexpr int dot_max_threads(int M, int C, int V, bool dot2) {
     return dot_regs(M, C, V, dot2) <= 96 ? 1024 : 512;
 }
 
+// DOT with x staged in LDS (SKG_FLAG_DOT_XLDS), K = 512 * V exactly: every
+// wave owns CW output columns over the whole K (64 lanes x V 16-byte
+// vectors per column), all
+// M rows of x sit in LDS, loaded once per workgroup; a workgroup of nw
+// waves covers CW * nw columns.  Registers: the CW * V W vectors in flight,
+// one step's M x vectors, CW * M accumulators and some addressing; the
+// same launch bounds as the plain dot kernel.  The whole x must fit the
+// LDS a workgroup may use, and the W loads of a thread must fit vmcnt's
+// 6 bits (the kernel waits for its x loads by counting them).
+constexpr int kXldsVecs[] = {4, 6, 8, 12, 14, 16};
+constexpr int xlds_regs(int M, int CW, int V) { return CW * V * 4 + 4 * M + CW * M + 16; }
+constexpr int xlds_max_threads(int M, int CW, int V) { return xlds_regs(M, CW, V) <= 96 ? 1024 : 512; }
+constexpr bool xlds_built(int M, int CW, int V) {
+    return (CW == 1 || CW == 2 || CW == 4) && xlds_regs(M, CW, V) <= kDotRegsMax && CW * V < 64;
+}
+constexpr long kXldsMaxLds = 160 * 1024 - 256;
+// LDS of one workgroup: the M x K8 16-byte chunks of x.
+constexpr long xlds_lds_bytes(int M, int K8) { return (long)M * K8 * 16; }
+
+// ROWS (MFMA, M <= 64): stages of KS = 512 (or 256 with SKG_FLAG_ROWS_HALF)
+// K elements; each of the R W rows and MP x rows of a stage (MP = M up to
+// 16 rows, else M rounded up to 24, 32, 48 or 64) is one LDS row of 2*KS
+// bytes, plus 1 KB that takes the padding loads.  A load instruction fills
+// 1 KB: one row (KS = 512) or two (KS = 256).  Wave w issues the W
+// instructions w, w+NW, ... and the x instructions likewise.  Built when
+// the ring fits the LDS a workgroup may use and the ring's vmcnt wait
+// (loads of NS-2 stages) fits its 6-bit field.
+constexpr int kRowsMaxM = 64;
+constexpr int rows_mp(int M) { return M <= 16 ? M : M <= 24 ? 24 : M <= 32 ? 32 : M <= 48 ? 48 : 64; }
+constexpr int rows_per_load(int KS) { return 1024 / (2 * KS); }
+constexpr int rows_w_loads(int NW, int R, int KS) {
+    return (R / rows_per_load(KS) + NW - 1) / NW;
+}
+constexpr int rows_x_loads(int MP, int NW, int KS) {
+    return ((MP + rows_per_load(KS) - 1) / rows_per_load(KS) + NW - 1) / NW;
+}
+constexpr int rows_stage_bytes(int MP, int R, int KS) {
+    return (R + (MP + rows_per_load(KS) - 1) / rows_per_load(KS) * rows_per_load(KS)) * 2 * KS +
+           1024;
+}
+constexpr long rows_lds_bytes(int MP, int NS, int R, int KS) {
+    return (long)NS * rows_stage_bytes(MP, R, KS);
+}
+constexpr bool rows_built(int MP, int NW, int NS, int R, int KS) {
+    return MP >= 1 && MP <= kRowsMaxM && MP == rows_mp(MP) && (NW == 4 || NW == 8) &&
+           (R == 8 || R == 16) && (KS == 512 || KS == 256) && NS >= 3 && NS <= 6 &&
+           rows_lds_bytes(MP, NS, R, KS) <= 160 * 1024 - 256 &&
+           (NS - 2) * (rows_w_loads(NW, R, KS) + rows_x_loads(MP, NW, KS)) < 64;
+}
+
 // SPLITK per-lane registers: two stages of D steps of (NB + MT) vectors and
 // NB*MT accumulators of 4 (those may live in AGPRs).  Above 224 the kernel
 // is bounded to 256 threads (one wave per SIMD); up to 96 it may run 1024
@@ -183,6 +233,8 @@ int tile_count(const SkgPlan &p, int N);
 // out_f32: 1 writes fp32 outputs, 0 bf16.
 int launch_dot(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
                int out_f32, int M, int N, int K, hipStream_t stream);
+int launch_rows(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
+                int out_f32, int M, int N, int K, hipStream_t stream);
 int launch_splitk(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
                   int out_f32, float *ws, unsigned *tickets, int M, int N, int K,
                   hipStream_t stream);

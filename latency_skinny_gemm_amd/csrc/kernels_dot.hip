@@ -22,8 +22,11 @@
 //    rounded once to bf16.
 // Every reduction order is fixed: the result is bitwise reproducible for a
 // given plan and input.
+#include <atomic>
+
 #include "device_common.h"
 #include "internal.h"
+#include "lds_limit.h"
 
 namespace skg {
 
@@ -120,6 +123,101 @@ __global__ void __launch_bounds__((W1 ? 64 : dot_max_threads(M, C, V, DOT2)))
     }
 }
 
+// The dot kernel with x in LDS (SKG_FLAG_DOT_XLDS), for K = 512 * V exactly
+// (every lane has V whole vectors of every row: no K tail).  A workgroup of
+// nw waves covers CW * nw consecutive columns; wave w owns CW of them over
+// the whole K, lane l the 16-byte vectors l, l + 64, ... (V of them) of
+// each.  Order of work:
+//  1. x (all M rows, in its own row-major layout) is copied to LDS by
+//     buffer-to-LDS loads, 16 bytes a lane, 1 KB a wave per pass;
+//  2. every W load of the wave (CW * V, streaming) is issued;
+//  3. s_waitcnt vmcnt(CW * V): loads complete in issue order, so this waits
+//     for the x loads only and leaves the W loads in flight; a barrier then
+//     makes every wave's part of x visible;
+//  4. the products: for each vector step, each row's x vector is read from
+//     LDS once and used for the CW columns, as the W vectors arrive;
+//  5. a wave reduce-scatter of the CW * M sums, and the owner lanes store.
+// x is read from L2 once per workgroup (not once per C columns), and no
+// cross-wave reduction is needed.  Lane l's sums and the reduction tree are
+// those of the one-wave dot kernel, so at equal V the bits are the same.
+template <int M, int CW, int V>
+__global__ void __launch_bounds__(xlds_max_threads(M, CW, V))
+    dotx_kernel(const uint16_t *x, const uint16_t *W, const uint16_t *__restrict__ bias,
+                void *__restrict__ out, int N, int K, int out_f32) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char xs[];
+    const int T = blockDim.x;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
+    const int nw = T >> 6;
+    const int n0 = (blockIdx.x * nw + wave) * CW;  // this wave's first column
+    const int ncols = n0 < N ? min(CW, N - n0) : 0;
+    const unsigned rowb = (unsigned)K * 2u;
+    constexpr int K8 = V * 64;                     // K / 8
+    const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
+    const Rsrc wr = make_rsrc(W + (size_t)(ncols ? n0 : 0) * K, (unsigned)ncols * rowb);
+
+    // 1. x -> LDS: wave w moves chunks q0 ... q0 + 63 for q0 = 64w, 64w + T,
+    // ... below M * K8 (both sides contiguous; M * K8 is a multiple of 64)
+#pragma unroll 1
+    for (int q0 = wave * 64; q0 < M * K8; q0 += T)
+        lds_load16<kCacheDefault>(xr, xs + (size_t)q0 * 16u, (unsigned)(q0 + lane) * 16u);
+    // The W loads must follow the x loads and precede the wait: the count
+    // in step 3 depends on it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. W, step-major (the order the products consume them); columns past
+    // N read zeros through the range check
+    u32x4 wv[V][CW];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int c = 0; c < CW; ++c)
+            wv[i][c] = load16<kCacheStream>(wr, (unsigned)(i * 64 + lane) * 16u + (unsigned)c * rowb);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. this wave's x loads are done once at most its CW*V W loads remain;
+    // then every wave's
+    wait_vmcnt_lds<CW * V>();
+    barrier_nofence();
+
+    // 4. products
+    float acc[CW][M];
+#pragma unroll
+    for (int c = 0; c < CW; ++c)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[c][m] = 0.0f;
+    const unsigned char *xl = xs + (size_t)lane * 16u;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const u32x4 xv = *reinterpret_cast<const u32x4 *>(xl + (size_t)(m * K8 + i * 64) * 16u);
+#pragma unroll
+            for (int c = 0; c < CW; ++c) acc[c][m] = dot8_dot2(xv, wv[i][c], acc[c][m]);
+        }
+
+    // 5. reduce-scatter over the wave; lane l owns index l >> (6 - L), c*M + m
+    constexpr int CM = CW * M;
+    constexpr int L = CM <= 1 ? 0 : CM <= 2 ? 1 : CM <= 4 ? 2 : CM <= 8 ? 3 : CM <= 16 ? 4 : CM <= 32 ? 5 : 6;
+    static_assert(CM <= 64, "one value index per lane at most");
+    float part[1 << L];
+#pragma unroll
+    for (int i = 0; i < (1 << L); ++i) part[i] = i < CM ? acc[i / M][i % M] : 0.0f;
+    const float total = wave_reduce_scatter<L>(part);
+    const int idx = lane >> (6 - L);
+    if ((lane & ((1 << (6 - L)) - 1)) == 0 && idx < CM) {
+        const int c = idx / M, m = idx - (idx / M) * M;
+        if (c < ncols) {
+            const int n = n0 + c;
+            float s = 0.0f + total;  // as the one-wave dot kernel: same bits
+            if (bias) s += bf16_to_f32(bias[n]);
+            store_out(out, (size_t)m * N + n, s, out_f32);
+        }
+    }
+}
+
 namespace {
 
 typedef int (*DotLaunch)(const SkgPlan &, const void *, const void *, const void *, void *, int,
@@ -200,11 +298,82 @@ DotLaunch pick(int M, int C, int V, bool dot2) {
     }
 }
 
+template <int M, int CW, int V>
+int launch_dotx_t(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
+                  int N, int K, int out_f32, hipStream_t stream) {
+    const int K8 = K / 8;
+    if (K8 != V * 64) return (int)hipErrorInvalidConfiguration;  // the kernel's contract
+    const size_t lds = (size_t)xlds_lds_bytes(M, K8);
+    static std::atomic<unsigned long long> lds_set{0};
+    if (lds > 64 * 1024) {
+        const hipError_t attr = allow_dynamic_lds(
+            reinterpret_cast<const void *>(&dotx_kernel<M, CW, V>), lds, lds_set);
+        if (attr != hipSuccess) return (int)attr;
+    }
+    hipLaunchKernelGGL((dotx_kernel<M, CW, V>), dim3(p.grid), dim3(p.threads), lds, stream,
+                       (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)bias, out, N, K,
+                       out_f32);
+    return (int)hipGetLastError();
+}
+
+template <int M, int CW, int V>
+constexpr DotLaunch dotx_entry() {
+    if constexpr (xlds_built(M, CW, V))
+        return &launch_dotx_t<M, CW, V>;
+    else
+        return nullptr;
+}
+
+template <int M, int CW>
+DotLaunch pickx_v(int V) {
+    switch (V) {
+    case 4: return dotx_entry<M, CW, 4>();
+    case 6: return dotx_entry<M, CW, 6>();
+    case 8: return dotx_entry<M, CW, 8>();
+    case 12: return dotx_entry<M, CW, 12>();
+    case 14: return dotx_entry<M, CW, 14>();
+    case 16: return dotx_entry<M, CW, 16>();
+    default: return nullptr;
+    }
+}
+
+template <int M>
+DotLaunch pickx_c(int CW, int V) {
+    if (CW == 1) return pickx_v<M, 1>(V);
+    if (CW == 2) return pickx_v<M, 2>(V);
+    if (CW == 4) return pickx_v<M, 4>(V);
+    return nullptr;
+}
+
+DotLaunch pickx(int M, int CW, int V) {
+    switch (M) {
+    case 1: return pickx_c<1>(CW, V);
+    case 2: return pickx_c<2>(CW, V);
+    case 3: return pickx_c<3>(CW, V);
+    case 4: return pickx_c<4>(CW, V);
+    case 5: return pickx_c<5>(CW, V);
+    case 6: return pickx_c<6>(CW, V);
+    case 7: return pickx_c<7>(CW, V);
+    case 8: return pickx_c<8>(CW, V);
+    case 9: return pickx_c<9>(CW, V);
+    case 10: return pickx_c<10>(CW, V);
+    case 11: return pickx_c<11>(CW, V);
+    case 12: return pickx_c<12>(CW, V);
+    case 13: return pickx_c<13>(CW, V);
+    case 14: return pickx_c<14>(CW, V);
+    case 15: return pickx_c<15>(CW, V);
+    case 16: return pickx_c<16>(CW, V);
+    default: return nullptr;
+    }
+}
+
 }  // namespace
 
 int launch_dot(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
                int out_f32, int M, int N, int K, hipStream_t stream) {
-    DotLaunch f = pick(M, p.cols, p.depth, (p.flags & SKG_FLAG_DOT2) != 0);
+    DotLaunch f = (p.flags & SKG_FLAG_DOT_XLDS)
+                      ? pickx(M, p.cols / (p.threads / 64), p.depth)
+                      : pick(M, p.cols, p.depth, (p.flags & SKG_FLAG_DOT2) != 0);
     if (!f) return (int)hipErrorInvalidConfiguration;
     return f(p, x, W, bias, out, N, K, out_f32, stream);
 }

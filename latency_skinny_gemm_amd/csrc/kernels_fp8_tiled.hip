@@ -30,27 +30,8 @@ namespace skg {
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lds() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
-}
-
-__device__ __forceinline__ void barrier_nofence() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Buffer-to-LDS loads of 16 or 4 bytes per lane (kept out of the kernel
-// body: used there directly, the builtin made the host pass drop the
-// kernels' launch stubs).
-template <int POLICY>
-__device__ __forceinline__ void lds_load16(Rsrc r, unsigned char *dst, unsigned off) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, off, 0, 0, POLICY);
-}
+// Buffer-to-LDS load of 4 bytes per lane (kept out of the kernel body for
+// the reason given at lds_load16).
 __device__ __forceinline__ void lds_load4(Rsrc r, unsigned char *dst, unsigned off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 4, off, 0, 0, 0);
 }

@@ -38,41 +38,12 @@ namespace skg {
 
 namespace {
 
-// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8 = 0).  Waiting for
-// lgkmcnt too means this wave's LDS reads of the slot that the next stage
-// overwrites have returned before the barrier that lets any wave refill it.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lds() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
-}
-
-// s_barrier without a memory fence.  The asm statements keep the compiler
-// from moving LDS accesses across it; the hardware ordering comes from the
-// explicit vmcnt wait that precedes it.
-__device__ __forceinline__ void barrier_nofence() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
 // Chunk swizzle of row r (0..15) in a block whose rows hold 4*U chunks of
 // 16 bytes: rows 64*U bytes apart share a 256-byte bank window 4/U at a
 // time, so the XOR key is the row's index among those that share it.
 template <int U>
 __device__ __forceinline__ int swz(int r) {
     return (r / (4 / U)) & (4 * U - 1);
-}
-
-// 16 bytes per lane from a buffer straight into LDS at dst + 16 * lane
-// (dst wave-uniform).  Kept out of the kernel body: used there directly,
-// the builtin made the host pass drop the kernels' launch stubs.
-template <int POLICY>
-__device__ __forceinline__ void lds_load16(Rsrc r, unsigned char *dst, unsigned off) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, off, 0, 0, POLICY);
 }
 
 }  // namespace

@@ -27,7 +27,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 TABLE = os.path.join(HERE, "csrc", "dispatch_table.inc")
 
-KIND_NAMES = {"dot": 1, "splitk": 2, "tiled": 3}
+KIND_NAMES = {"dot": 1, "splitk": 2, "tiled": 3, "rows": 4}
 DOT_THREADS = (64, 128, 192, 256, 320, 384, 448, 512, 640, 768, 896, 1024)
 SPLITS = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64)
 
@@ -172,7 +172,7 @@ def sweep_point_fp8(skg, torch, M, N, K, pool_bytes, reps, stream, log):
                           for t, pm, p in results]}
     log.write(json.dumps(rec) + "\n")
     log.flush()
-    kind = {1: "dot", 2: "splitk", 3: "tiled"}[best.kind]
+    kind = {1: "dot", 2: "splitk", 3: "tiled", 4: "rows"}[best.kind]
     print(f"FP8 M={M:3d} N={N:5d} K={K:5d}: best per-tensor {best_modes['tensor']:7.3f} us, "
           f"MX {best_modes['mx']:7.3f} us  {kind} {plan_dict(best)} ({len(results)} plans)", flush=True)
     return rec
@@ -198,6 +198,19 @@ def candidates(skg, M, N, K):
             for cols in (1, 2, 3, 4):
                 for T in DOT_THREADS:
                     add(skg.make_plan(skg.KIND_DOT, T, cols, flags=flags))
+        # x in LDS: waves of 1, 2 or 4 columns
+        for T in DOT_THREADS:
+            for cw in (1, 2, 4):
+                add(skg.make_plan(skg.KIND_DOT, T, cw * T // 64,
+                                  flags=skg.FLAG_DOT_XLDS | skg.FLAG_DOT2))
+    if M <= 64:
+        # whole-row MFMA ring: 8 or 16 columns, 4 or 8 waves, 3-6 stages of
+        # 512 or 256 K
+        for R in (8, 16):
+            for T in (256, 512):
+                for ns in (3, 4, 5, 6):
+                    for fl in (0, skg.FLAG_ROWS_HALF):
+                        add(skg.make_plan(skg.KIND_ROWS, T, R, depth=ns, flags=fl))
     ksteps = -(-K // 32)
     MT = -(-M // 16)
     for NB in (1, 2, 4):
@@ -293,7 +306,7 @@ def sweep_point(skg, torch, M, N, K, pool_bytes, reps, stream, log, kinds=None):
            "candidates": [[round(us, 3), plan_dict(p)] for us, p in results]}
     log.write(json.dumps(rec) + "\n")
     log.flush()
-    kind = {1: "dot", 2: "splitk", 3: "tiled"}[best.kind]
+    kind = {1: "dot", 2: "splitk", 3: "tiled", 4: "rows"}[best.kind]
     print(f"M={M:3d} N={N:5d} K={K:5d}: best {best_us:7.3f} us  {kind} {plan_dict(best)} "
           f"({len(results)} plans, slots={slots})", flush=True)
     return rec
@@ -382,7 +395,7 @@ def emit_table(files, out_path=TABLE):
                 best[key] = {"best_us": statistics.median(ts), "best": plan}
                 break
     names = {0: "SKG_REDUCE_NONE", 1: "SKG_REDUCE_LAST", 2: "SKG_REDUCE_KERNEL"}
-    kinds = {1: "SKG_KIND_DOT", 2: "SKG_KIND_SPLITK", 3: "SKG_KIND_TILED"}
+    kinds = {1: "SKG_KIND_DOT", 2: "SKG_KIND_SPLITK", 3: "SKG_KIND_TILED", 4: "SKG_KIND_ROWS"}
     lines = [
         "// dispatch_table.inc -- generated by latency_skinny_gemm_amd/sweep.py --emit-table",
         f"// from cold-weight graph-replay timings on one MI355X ({datetime.date.today()}).",

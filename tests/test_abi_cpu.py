@@ -550,7 +550,82 @@ def test_complete_drops_empty_splits(lib):
 # A model of the kernels' index arithmetic: every output written exactly
 # once, and every k of every output accumulated exactly once.
 
+def _check_xlds_coverage(p, M, N, K):
+    # waves of CW columns over the whole K: lane l takes vectors l + 64 i;
+    # x is copied to LDS by waves in 64-chunk runs q0 = 64 w + j T
+    T, C, V = p.threads, p.cols, p.depth
+    nw = T // 64
+    CW = C // nw
+    K8 = K // 8
+    assert C == CW * nw and CW in (1, 2, 4) and V * 64 == K8 and p.grid == -(-N // C)
+    cols = [n for b in range(p.grid) for w in range(nw) for c in range(CW)
+            if (n := (b * nw + w) * CW + c) < N]
+    assert sorted(cols) == list(range(N))
+    assert sorted(l + 64 * i for l in range(64) for i in range(V)) == list(range(K8))
+    chunks = sorted(q0 + l for w in range(nw) for q0 in range(64 * w, M * K8, T) for l in range(64))
+    assert chunks == list(range(M * K8)) and M * K8 * 16 <= 160 * 1024 - 256
+
+
+def _check_rows_coverage(p, M, N, K):
+    # whole-row MFMA ring: workgroup b owns columns R*b ..; stages of KS K
+    # walked in rotated order; a load instruction fills 1 KB: row j*RPL +
+    # p/CPR, position p%CPR holding chunk (p%CPR) ^ (LDS row % 16); wave w of
+    # NW issues instructions w + NW i of each block and multiplies MFMA steps
+    # w, w + NW, ... (32 K each, lane group g = l / 16 reads chunk 4u + g at
+    # position (4u + g) ^ (row % 16))
+    R, NW, NS = p.cols, p.threads // 64, p.depth
+    KS = 256 if p.flags & skg.FLAG_ROWS_HALF else 512
+    MP = M if M <= 16 else next(v for v in (24, 32, 48, 64) if v >= M)
+    CPR, RPL = KS // 8, 1024 // (2 * KS)
+    XR = -(-MP // RPL) * RPL
+    assert R in (8, 16) and NW in (4, 8) and 3 <= NS <= 6 and M <= 64 and p.splits == 1
+    assert p.grid == -(-N // R)
+    cols = sorted(n for b in range(p.grid) for c in range(R) if (n := b * R + c) < N)
+    assert cols == list(range(N))
+    wl, xl = R // RPL, XR // RPL
+    wpw, xpw = -(-wl // NW), -(-xl // NW)
+    stage = (R + XR) * 2 * KS + 1024
+    assert NS * stage <= 160 * 1024 - 256 and (NS - 2) * (wpw + xpw) < 64
+    assert NW * (-(-MP // 16)) * 16 * 17 * 4 <= NS * stage
+    # every (LDS row, chunk) of a stage is filled exactly once, from that row's chunk
+    for blk_rows, nl, npw in ((R, wl, wpw), (XR, xl, xpw)):
+        filled = {}
+        for w in range(NW):
+            for i in range(npw):
+                j = w + NW * i
+                if j >= nl:
+                    continue
+                for l in range(64):
+                    r, pos = j * RPL + l // CPR, l % CPR
+                    row = r if blk_rows == R else R + r
+                    filled[(r, pos ^ (row & 15))] = filled.get((r, pos ^ (row & 15)), 0) + 1
+        assert filled == {(r, c): 1 for r in range(blk_rows) for c in range(CPR)}
+    # fragment reads of a step land on the chunk the MFMA step needs, and the
+    # 16 rows of one lane group hit 16 distinct 16-byte bank groups
+    for u in range(KS // 32):
+        for g in range(4):
+            kc = 4 * u + g
+            banks = {(r * 2 * KS // 16 + (kc ^ (r & 15))) % 16 for r in range(16)}
+            assert len(banks) == 16 and all((kc ^ (r & 15)) < CPR for r in range(R + XR))
+    nst = -(-K // KS)
+    for b in {0, p.grid - 1, p.grid // 2}:
+        rot = b % nst
+        order = [(st + rot) % nst for st in range(nst)]
+        assert sorted(order) == list(range(nst))
+        steps = sorted(w + NW * q for w in range(NW) for q in range(KS // 32 // NW))
+        assert steps == list(range(KS // 32))
+        mult = sorted(KS * pos + 32 * u + 8 * g + e for pos in order for u in steps
+                      for g in range(4) for e in range(8))
+        assert mult == list(range(KS * nst))  # past K: zeros from the range check
+
+
 def _check_coverage(p, M, N, K):
+    if p.kind == skg.KIND_ROWS:
+        _check_rows_coverage(p, M, N, K)
+        return
+    if p.kind == skg.KIND_DOT and p.flags & skg.FLAG_DOT_XLDS:
+        _check_xlds_coverage(p, M, N, K)
+        return
     if p.kind == skg.KIND_DOT:
         T, C, V = p.threads, p.cols, p.depth
         K8 = K // 8
@@ -725,3 +800,84 @@ def test_tiled_rejects_bad_plans(lib):
     # whole 32-wide steps only
     with pytest.raises(skg.SkinnyGemmError):
         skg.plan_complete(64, 256, 2056, skg.make_plan(skg.KIND_TILED, 256, 4, 2, 4))
+
+
+# ------------------------------------------------------------------ x in LDS
+
+XLDS = skg.FLAG_DOT_XLDS | skg.FLAG_DOT2
+
+
+@pytest.mark.parametrize("M,N,K,T,C", [
+    (8, 4096, 7168, 512, 16), (1, 4096, 7168, 512, 16), (11, 2112, 7168, 512, 16),
+    (4, 300, 2048, 256, 16), (16, 37, 4096, 64, 1), (2, 1, 8192, 1024, 16),
+    (5, 1000, 3072, 128, 2), (3, 7, 6144, 256, 8)])
+def test_xlds_plans_cover(lib, M, N, K, T, C):
+    q = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_DOT, T, C, flags=XLDS))
+    assert (q.depth, q.splits, q.reduce, q.k_chunk) == (K // 512, 1, skg.REDUCE_NONE, K)
+    _check_coverage(q, M, N, K)
+
+
+@pytest.mark.parametrize("M,N,K,T,C,flags,dtype", [
+    (8, 4096, 7168, 512, 16, skg.FLAG_DOT_XLDS, skg.DTYPE_BF16),   # needs the dot instruction
+    (8, 4096, 2880, 512, 16, XLDS, skg.DTYPE_BF16),                # K not 512 V
+    (8, 4096, 5120, 512, 16, XLDS, skg.DTYPE_BF16),                # V = 10 not built
+    (12, 4096, 7168, 512, 16, XLDS, skg.DTYPE_BF16),               # x over the LDS bound
+    (8, 4096, 7168, 256, 12, XLDS, skg.DTYPE_BF16),                # 3 columns a wave
+    (8, 4096, 7168, 512, 12, XLDS, skg.DTYPE_BF16),                # cols not a multiple of waves
+    (8, 4096, 7168, 512, 4, XLDS, skg.DTYPE_BF16),                 # fewer cols than waves
+    (8, 4096, 7168, 256, 16, XLDS, skg.DTYPE_BF16),                # registers (4 x 14 vectors)
+    (8, 4096, 7168, 1024, 32, XLDS, skg.DTYPE_BF16),               # registers at 1024 threads
+    (17, 4096, 4096, 256, 4, XLDS, skg.DTYPE_BF16),                # M above the dot kernels
+    (8, 4096, 4096, 256, 4, XLDS, skg.DTYPE_FP8),                  # bf16 only
+    (8, 4096, 7168, 512, 16, XLDS | skg.FLAG_TILED_WIDE, skg.DTYPE_BF16),
+])
+def test_xlds_rejects(lib, M, N, K, T, C, flags, dtype):
+    with pytest.raises(skg.SkinnyGemmError) as e:
+        skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_DOT, T, C, flags=flags), dtype)
+    assert e.value.status == skg.ERR_INVALID_ARG
+
+
+def test_xlds_rejects_two_splits(lib):
+    with pytest.raises(skg.SkinnyGemmError):
+        skg.plan_complete(8, 4096, 7168, skg.make_plan(skg.KIND_DOT, 512, 16, splits=2, flags=XLDS))
+
+
+# ------------------------------------------------------------------ whole-row MFMA ring
+
+
+HALF = skg.FLAG_ROWS_HALF
+
+
+@pytest.mark.parametrize("M,N,K,T,R,NS,fl", [
+    (8, 4096, 7168, 256, 16, 4, 0), (8, 4096, 7168, 512, 16, 6, 0), (1, 2112, 7168, 256, 8, 3, 0),
+    (16, 100, 2880, 512, 8, 5, 0), (3, 7, 4104, 256, 16, 4, 0), (13, 4096, 4096, 512, 16, 3, 0),
+    (16, 1, 8, 256, 8, 3, 0), (32, 4096, 7168, 256, 16, 3, 0), (64, 4096, 7168, 256, 16, 3, HALF),
+    (17, 300, 2056, 512, 8, 6, HALF), (40, 33, 7168, 256, 8, 4, HALF), (5, 4096, 7168, 512, 16, 5, HALF)])
+def test_rows_plans_cover(lib, M, N, K, T, R, NS, fl):
+    q = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_ROWS, T, R, depth=NS, flags=fl))
+    assert (q.splits, q.reduce, q.k_chunk, q.m_tiles) == (1, skg.REDUCE_NONE, K, 1)
+    _check_coverage(q, M, N, K)
+
+
+@pytest.mark.parametrize("plan,M,dtype", [
+    (dict(threads=256, cols=16, depth=4), 65, skg.DTYPE_BF16),           # M > 64
+    (dict(threads=256, cols=16, depth=3), 64, skg.DTYPE_BF16),           # LDS: 64 rows of 1 KB
+    (dict(threads=256, cols=16, depth=4, flags=16), 8, skg.DTYPE_BF16),  # unknown flag
+    (dict(threads=128, cols=16, depth=4), 8, skg.DTYPE_BF16),            # 2 waves
+    (dict(threads=1024, cols=16, depth=4), 8, skg.DTYPE_BF16),           # 16 waves
+    (dict(threads=256, cols=4, depth=4), 8, skg.DTYPE_BF16),             # 4 columns
+    (dict(threads=256, cols=32, depth=4), 8, skg.DTYPE_BF16),
+    (dict(threads=256, cols=16, depth=2), 8, skg.DTYPE_BF16),            # ring of 2
+    (dict(threads=256, cols=16, depth=7), 8, skg.DTYPE_BF16),
+    (dict(threads=256, cols=16, depth=6), 16, skg.DTYPE_BF16),           # LDS: 6 x 33 rows
+    (dict(threads=256, cols=16, depth=4, splits=2), 8, skg.DTYPE_BF16),
+    (dict(threads=256, cols=16, depth=4, flags=skg.FLAG_DOT2), 8, skg.DTYPE_BF16),
+    (dict(threads=256, cols=16, depth=4, flags=skg.FLAG_TILED_WIDE), 8, skg.DTYPE_BF16),
+    (dict(threads=256, cols=16, depth=4, waves_m=1), 8, skg.DTYPE_BF16),
+    (dict(threads=256, cols=16, depth=4, reduce=skg.REDUCE_LAST), 8, skg.DTYPE_BF16),
+    (dict(threads=256, cols=16, depth=4), 8, skg.DTYPE_FP8),             # bf16 only
+])
+def test_rows_rejects(lib, plan, M, dtype):
+    with pytest.raises(skg.SkinnyGemmError) as e:
+        skg.plan_complete(M, 4096, 4096, skg.make_plan(skg.KIND_ROWS, **plan), dtype)
+    assert e.value.status == skg.ERR_INVALID_ARG

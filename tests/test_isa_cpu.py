@@ -1,0 +1,138 @@
+"""Instruction order of the dot kernel with x in LDS, checked in the built
+library.
+
+That kernel waits for its buffer-to-LDS copies of x by counting: after the
+copies each wave issues exactly CW * V loads of W, then s_waitcnt
+vmcnt(CW * V) (loads complete in issue order) and a barrier.  The count is
+only right while the compiler keeps that order.  This test disassembles the
+gfx950 code object of every instantiation in libskinny_gemm.so (our own
+build) and checks, between the last x copy and the first barrier after it:
+no branch, every W load issued before the first vmcnt wait, and that wait no
+larger than the loads issued after the last copy (the x copies have all
+landed when it returns).  It also checks that no instantiation touches
+scratch memory (register spills) and that the instantiations present are
+exactly those the register bound admits.
+"""
+import os
+import re
+import struct
+import subprocess
+import tempfile
+
+import pytest
+
+import latency_skinny_gemm_amd as skg
+from latency_skinny_gemm_amd import build as lib_build
+
+LLVM = "/opt/rocm/llvm/bin"
+MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
+NAME = re.compile(r"^[0-9a-f]+ <(_ZN3skg11dotx_kernelILi(\d+)ELi(\d+)ELi(\d+)E\S*)>:\s*$")
+
+
+def _gfx950_objects(fatbin):
+    """The gfx950 code objects of a .hip_fatbin section (one offload bundle
+    per compiled source: magic, entry count, then offset, size, triple)."""
+    out, i = [], fatbin.find(MAGIC)
+    while i >= 0:
+        (n,) = struct.unpack_from("<Q", fatbin, i + 24)
+        q = i + 32
+        for _ in range(n):
+            off, size, tl = struct.unpack_from("<QQQ", fatbin, q)
+            q += 24
+            triple = fatbin[q:q + tl].decode()
+            q += tl
+            if triple.endswith("gfx950"):
+                out.append(fatbin[i + off:i + off + size])
+        i = fatbin.find(MAGIC, i + 1)
+    return out
+
+
+@pytest.fixture(scope="module")
+def functions():
+    """{(M, CW, V): [(offset, text, branch target offset or None)]}"""
+    for tool in ("llvm-objcopy", "llvm-objdump"):
+        if not os.path.exists(os.path.join(LLVM, tool)):
+            pytest.skip(f"{tool} not installed")
+    if not os.path.exists(skg.library_path()):
+        lib_build.build()
+    with tempfile.TemporaryDirectory() as d:
+        fb = os.path.join(d, "fatbin")
+        subprocess.run([os.path.join(LLVM, "llvm-objcopy"), "--dump-section",
+                        f".hip_fatbin={fb}", skg.library_path()], check=True)
+        objs = [o for o in _gfx950_objects(open(fb, "rb").read()) if b"dotx_kernel" in o]
+        assert len(objs) == 1, "expected one code object holding the x-in-LDS dot kernels"
+        co = os.path.join(d, "dot.co")
+        open(co, "wb").write(objs[0])
+        dis = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", co],
+                             check=True, capture_output=True, text=True).stdout
+    funcs, cur, start = {}, None, 0
+    for line in dis.splitlines():
+        m = NAME.match(line)
+        if m:
+            cur = (int(m.group(2)), int(m.group(3)), int(m.group(4)))
+            start = int(line.split()[0], 16)
+            funcs[cur] = []
+            continue
+        if re.match(r"^[0-9a-f]+ <", line):
+            cur = None
+        elif cur is not None and line.startswith("\t"):
+            text, _, comment = line.partition("//")
+            addr = re.match(r"\s*([0-9A-Fa-f]+):", comment)
+            if addr is None:  # the "..." that stands for a run of zero words
+                continue
+            tgt = re.search(r"<[^>+]*\+0x([0-9a-f]+)>", comment)
+            funcs[cur].append((int(addr.group(1), 16) - start, text.strip(),
+                               int(tgt.group(1), 16) if tgt else None))
+    return funcs
+
+
+def _built(M, CW, V):
+    # the register bound of the kernel (CW * V W vectors, one step's x
+    # vectors, CW * M sums, addressing) and vmcnt's 6 bits
+    return CW in (1, 2, 4) and CW * V * 4 + 4 * M + CW * M + 16 <= 224 and CW * V < 64
+
+
+def test_instantiations_are_those_the_bound_admits(functions):
+    want = {(M, CW, V) for M in range(1, 17) for CW in (1, 2, 4) for V in (4, 6, 8, 12, 14, 16)
+            if _built(M, CW, V)}
+    assert set(functions) == want
+
+
+def _is_branch(text):
+    return text.startswith(("s_branch", "s_cbranch", "s_setpc", "s_swappc"))
+
+
+def test_w_loads_sit_between_x_copies_and_the_wait(functions):
+    for (M, CW, V), ins in sorted(functions.items()):
+        tag = f"dotx M={M} CW={CW} V={V}"
+        texts = [t for _, t, _ in ins]
+        offs = [o for o, _, _ in ins]
+        assert not any(t.startswith("scratch_") for t in texts), f"{tag}: spills to scratch"
+        copies = [k for k, t in enumerate(texts) if t.startswith("buffer_load") and t.endswith(" lds")]
+        assert copies, f"{tag}: no buffer-to-LDS copy"
+        s = copies[-1]
+        bar = next(k for k in range(s, len(texts)) if texts[k].startswith("s_barrier"))
+        wait, issued, first_w = None, 0, None
+        for k in range(s + 1, bar):
+            t = texts[k]
+            if t.startswith(("buffer_load", "global_load")):
+                issued += 1
+                first_w = k if first_w is None else first_w
+            m = re.match(r"s_waitcnt\b.*\bvmcnt\((\d+)\)", t)
+            if m:
+                wait = (k, int(m.group(1)))
+                break
+        assert wait is not None and first_w is not None, f"{tag}: no W loads and vmcnt wait"
+        # past the last copy only backward branches into the copy region
+        for k in range(s + 1, bar):
+            if _is_branch(texts[k]):
+                assert ins[k][2] is not None and ins[k][2] <= offs[s], \
+                    f"{tag}: branch at +{offs[k]:#x} out of the load sequence"
+        # no branch lands among the W loads or between the wait and the
+        # barrier: every path to the barrier issues all of them, then waits
+        for _, t, tgt in ins:
+            if tgt is not None and _is_branch(t):
+                assert not (offs[first_w] < tgt <= offs[bar]), \
+                    f"{tag}: branch into the load sequence at +{tgt:#x}"
+        assert wait[1] <= issued, f"{tag}: vmcnt({wait[1]}) with only {issued} loads after the copies"
+        assert issued == CW * V and wait[1] == CW * V, f"{tag}: {issued} loads, vmcnt({wait[1]})"

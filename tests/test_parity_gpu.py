@@ -65,6 +65,32 @@ def _kernel_plans(skg, M, N, K):
                     plans.append((f"dot_c{cols}_t64_f{flags}", p))
                 except skg.SkinnyGemmError:
                     pass
+    if M <= 16:
+        # x in LDS: the first multi-wave shape that fits, and one wave
+        xl = skg.FLAG_DOT_XLDS | skg.FLAG_DOT2
+        for group in (((512, 2), (256, 4), (512, 1), (256, 1)), ((64, 4), (64, 2), (64, 1))):
+            for threads, cw in group:
+                p = skg.make_plan(skg.KIND_DOT, threads, cols=cw * threads // 64, flags=xl)
+                try:
+                    skg.plan_complete(M, N, K, p)
+                except skg.SkinnyGemmError:
+                    continue
+                plans.append((f"dotx_cw{cw}_t{threads}", p))
+                break
+    if M <= 64:
+        # whole-row MFMA ring: the first of each pair that fits (16 or 8
+        # columns, 4 or 8 waves, stages of 512 or 256 K)
+        half = skg.FLAG_ROWS_HALF
+        for pair in (((256, 16, 4, 0), (256, 16, 3, half)), ((512, 8, 3, 0), (512, 8, 4, half)),
+                     ((512, 16, 6, half), (512, 16, 3, half)), ((256, 8, 5, half), (256, 8, 3, 0))):
+            for threads, cols, ns, fl in pair:
+                p = skg.make_plan(skg.KIND_ROWS, threads, cols=cols, depth=ns, flags=fl)
+                try:
+                    skg.plan_complete(M, N, K, p)
+                except skg.SkinnyGemmError:
+                    continue
+                plans.append((f"rows_t{threads}_c{cols}_ns{ns}_f{fl}", p))
+                break
     mt = (M + 15) // 16
     nb = 4 if mt >= 4 else (2 if mt >= 2 else 1)
     threads = 128 if nb * mt > 16 else 256
@@ -171,6 +197,24 @@ def test_all_ones_gives_K(skg, K):
     for name, plan in _kernel_plans(skg, 16, 256, K):
         out = _run(skg, xd, wd, None, plan)
         assert torch.all(out.float() == K), f"[{name}]"
+
+
+@pytest.mark.parametrize("M,N,K,T,CW", [(3, 300, 2048, 256, 2), (8, 77, 2048, 512, 1),
+                                        (1, 1000, 3072, 64, 4), (5, 130, 4096, 128, 2)])
+@pytest.mark.parametrize("bias", (False, True))
+def test_xlds_matches_one_wave_dot_bitwise(skg, M, N, K, T, CW, bias):
+    # equal V: each lane sums the same vectors in the same order and the
+    # wave's reduction tree is the same, so the bits must be the same; N
+    # ragged against the workgroup's columns
+    x, w, b = gen.bf16_inputs(M, N, K, bias, seed=1000 + M * 31 + N)
+    xd, wd, bd = _dev(x, w, b)
+    one = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_DOT, 64, 1, flags=skg.FLAG_DOT2))
+    xl = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_DOT, T, CW * T // 64,
+                                                  flags=skg.FLAG_DOT_XLDS | skg.FLAG_DOT2))
+    assert one.depth == xl.depth == K // 512
+    a = gen.bits16(_run(skg, xd, wd, bd, one))
+    c = gen.bits16(_run(skg, xd, wd, bd, xl))
+    assert np.array_equal(a, c), f"{np.count_nonzero(a != c)} of {a.size} differ"
 
 
 def test_runs_are_bitwise_deterministic(skg):
