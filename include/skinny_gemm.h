@@ -164,8 +164,12 @@ typedef struct SkgPlan {
     int reduce;   /* SKG_REDUCE_*; NONE iff splits == 1 */
     int flags;    /* SKG_FLAG_* */
     int k_chunk;  /* (derived) SPLITK, TILED: K elements per split, multiple of 32 */
-    int m_tiles;  /* (derived) SPLITK: ceil(M / 16); TILED: the power of two
-                     (1, 2, 4, 8) at or above ceil(M / 16) */
+    int m_tiles;  /* TILED: 16-row tiles per row block.  0 asks for the power of
+                     two (1, 2, 4, 8) at or above ceil(M / 16), capped at 8 (more
+                     rows: row blocks of 128); a smaller power of two splits the
+                     rows into ceil(M / (16 * m_tiles)) row blocks (wider,
+                     shorter tiles).  (derived) for the other kinds: SPLITK
+                     ceil(M / 16), DOT and ROWS 1 */
     int grid;     /* (derived) workgroups in the main launch */
     int from_table; /* (derived) 1 when the tuned table supplied the plan */
 } SkgPlan;

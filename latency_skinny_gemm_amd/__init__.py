@@ -361,10 +361,11 @@ def gemm_fp8_planned(xq, wq, p, sx=None, sw=None, xe=None, we=None, bias=None, o
     return out
 
 
-def make_plan(kind, threads, cols=1, splits=1, depth=0, reduce=REDUCE_NONE, flags=0, waves_m=0):
+def make_plan(kind, threads, cols=1, splits=1, depth=0, reduce=REDUCE_NONE, flags=0, waves_m=0,
+              m_tiles=0):
     p = SkgPlan()
     p.kind, p.threads, p.cols, p.splits, p.depth, p.reduce = kind, threads, cols, splits, depth, reduce
-    p.flags, p.waves_m = flags, waves_m
+    p.flags, p.waves_m, p.m_tiles = flags, waves_m, m_tiles
     return p
 
 

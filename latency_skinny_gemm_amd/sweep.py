@@ -50,6 +50,18 @@ def point_sets():
     }
 
 
+def _natural_mt(M):
+    mt = -(-M // 16)
+    return next((v for v in (1, 2, 4, 8) if v >= mt), 8)
+
+
+def _mt_requests(M):
+    """m_tiles a tiled plan may ask for at M rows: 0 (the rows' own power of
+    two, 8 above 128 rows) and each smaller power of two (more row blocks)."""
+    nat = _natural_mt(M)
+    return (0,) + tuple(v for v in (1, 2, 4) if v < nat)
+
+
 def _tiled_reductions(skg, S):
     """Reductions tried for a tiled plan with S splits: the last arriver reads
     S partial tiles in one workgroup, worth it only up to 16 splits."""
@@ -68,7 +80,7 @@ def fp8_candidates(skg, M, N, K):
         except skg.SkinnyGemmError:
             return
         key = (q.kind, q.threads, q.cols, q.splits, q.depth, q.waves_m, q.reduce, q.flags,
-               q.k_chunk)
+               q.k_chunk, q.m_tiles)
         if key not in seen:
             seen.add(key)
             out.append(q)
@@ -77,20 +89,22 @@ def fp8_candidates(skg, M, N, K):
         for T in DOT_THREADS:
             for C in (1, 2, 4):
                 add(skg.make_plan(skg.KIND_DOT, T, C))
-    # LDS-ring tiles (K % 128 == 0)
+    # LDS-ring tiles (K % 128 == 0), also in row blocks of fewer m-tiles
     if K % 128 == 0 and (M > 4 or N >= 1024):
-        for NB in (1, 2, 4, 8, 16):
-            groups = -(-N // (16 * NB))
-            for S in SPLITS:
-                if S > K // 128 or not (64 <= groups * S <= 2048):
-                    continue
-                for wm in (1, 2, 4):
-                    for ns, flags in ((2, 0), (3, 0), (4, 0), (5, 0), (6, 0), (8, 0),
-                                      (2, skg.FLAG_TILED_WIDE), (3, skg.FLAG_TILED_WIDE),
-                                      (4, skg.FLAG_TILED_WIDE), (5, skg.FLAG_TILED_WIDE)):
-                        for red in _tiled_reductions(skg, S):
-                            add(skg.make_plan(skg.KIND_TILED, 256, NB, S, ns, red, flags=flags,
-                                              waves_m=wm))
+        for mtr in _mt_requests(M):
+            MB = -(-M // (16 * (mtr or _natural_mt(M))))
+            for NB in (1, 2, 4, 8, 16):
+                groups = MB * -(-N // (16 * NB))
+                for S in SPLITS:
+                    if S > K // 128 or not (64 <= groups * S <= 2048):
+                        continue
+                    for wm in (1, 2, 4):
+                        for ns, flags in ((2, 0), (3, 0), (4, 0), (5, 0), (6, 0), (8, 0),
+                                          (2, skg.FLAG_TILED_WIDE), (3, skg.FLAG_TILED_WIDE),
+                                          (4, skg.FLAG_TILED_WIDE), (5, skg.FLAG_TILED_WIDE)):
+                            for red in _tiled_reductions(skg, S):
+                                add(skg.make_plan(skg.KIND_TILED, 256, NB, S, ns, red,
+                                                  flags=flags, waves_m=wm, m_tiles=mtr))
     ksteps = -(-K // 128)
     for NB in (1, 2, 4):
         groups = -(-N // (16 * NB))
@@ -188,7 +202,8 @@ def candidates(skg, M, N, K):
             q = skg.plan_complete(M, N, K, p)
         except skg.SkinnyGemmError:
             return
-        key = (q.kind, q.threads, q.cols, q.splits, q.depth, q.waves_m, q.reduce, q.flags, q.k_chunk)
+        key = (q.kind, q.threads, q.cols, q.splits, q.depth, q.waves_m, q.reduce, q.flags, q.k_chunk,
+               q.m_tiles)
         if key not in seen:
             seen.add(key)
             out.append(q)
@@ -230,25 +245,27 @@ def candidates(skg, M, N, K):
     # LDS-ring tiles (K % 32 == 0): worth it once a workgroup covers many
     # columns; stages and steps per stage cover 2-16 steps in flight
     if (M > 4 or N >= 1024) and K % 32 == 0:
-        for NB in (1, 2, 4, 8, 16):
-            groups = -(-N // (16 * NB))
-            for S in SPLITS:
-                if S > ksteps or not (64 <= groups * S <= 2048):
-                    continue
-                for wm in (1, 2, 4):
-                    for ns, flags in ((2, 0), (3, 0), (4, 0), (5, 0), (6, 0), (8, 0),
-                                      (2, skg.FLAG_TILED_WIDE), (3, skg.FLAG_TILED_WIDE),
-                                      (4, skg.FLAG_TILED_WIDE), (5, skg.FLAG_TILED_WIDE),
-                                      (6, skg.FLAG_TILED_WIDE)):
-                        for red in _tiled_reductions(skg, S):
-                            add(skg.make_plan(skg.KIND_TILED, 256, NB, S, ns, red, flags=flags,
-                                              waves_m=wm))
+        for mtr in _mt_requests(M):
+            MB = -(-M // (16 * (mtr or _natural_mt(M))))
+            for NB in (1, 2, 4, 8, 16):
+                groups = MB * -(-N // (16 * NB))
+                for S in SPLITS:
+                    if S > ksteps or not (64 <= groups * S <= 2048):
+                        continue
+                    for wm in (1, 2, 4):
+                        for ns, flags in ((2, 0), (3, 0), (4, 0), (5, 0), (6, 0), (8, 0),
+                                          (2, skg.FLAG_TILED_WIDE), (3, skg.FLAG_TILED_WIDE),
+                                          (4, skg.FLAG_TILED_WIDE), (5, skg.FLAG_TILED_WIDE),
+                                          (6, skg.FLAG_TILED_WIDE)):
+                            for red in _tiled_reductions(skg, S):
+                                add(skg.make_plan(skg.KIND_TILED, 256, NB, S, ns, red,
+                                                  flags=flags, waves_m=wm, m_tiles=mtr))
     return out
 
 
 def plan_dict(p):
     return {k: getattr(p, k) for k in ("kind", "threads", "cols", "splits", "depth", "waves_m",
-                                       "reduce", "flags", "k_chunk", "grid")}
+                                       "reduce", "flags", "k_chunk", "m_tiles", "grid")}
 
 
 def sweep_point(skg, torch, M, N, K, pool_bytes, reps, stream, log, kinds=None):
@@ -340,16 +357,26 @@ def run(args):
     print(f"swept {len(pts)} points in {time.time() - t0:.0f} s", flush=True)
 
 
+def _mt_request_of(plan, M):
+    """The m_tiles a recorded tiled plan asked for: 0 when it used the rows'
+    own power of two (records from before row blocks below 129 rows carry
+    none), else its m_tiles."""
+    mt = plan.get("m_tiles", 0)
+    return 0 if plan["kind"] != 3 or mt in (0, _natural_mt(M)) else mt
+
+
 def _still_valid(skg, dt, M, N, K, b):
     """True when the current planner accepts the swept plan unchanged."""
     p = skg.make_plan(b["kind"], b["threads"], b["cols"], b["splits"], b["depth"], b["reduce"],
-                      flags=b["flags"], waves_m=b.get("waves_m", 0))
+                      flags=b["flags"], waves_m=b.get("waves_m", 0),
+                      m_tiles=_mt_request_of(b, M))
     try:
         q = skg.plan_complete(M, N, K, p, {"fp8": skg.DTYPE_FP8, "fp8_mx": skg.DTYPE_FP8_MX}.get(
             dt, skg.DTYPE_BF16))
     except skg.SkinnyGemmError:
         return False
-    return (q.splits, q.depth, q.cols) == (b["splits"], b["depth"], b["cols"])
+    return (q.splits, q.depth, q.cols) == (b["splits"], b["depth"], b["cols"]) and \
+        (b["kind"] != 3 or q.m_tiles == (b.get("m_tiles") or q.m_tiles))
 
 
 def emit_table(files, out_path=TABLE):
@@ -379,6 +406,7 @@ def emit_table(files, out_path=TABLE):
                     continue
                 ident = tuple(plan.get(f, 0) for f in ("kind", "threads", "cols", "splits", "depth",
                                                           "waves_m", "reduce", "flags"))
+                ident += (_mt_request_of(plan, key[3]),)
                 # FP8: one entry per scale mode, each from that mode's timing;
                 # MX timings count only where the scale bytes were cold too
                 per_key = [(key, us)] if key[0] != "fp8" else [(key, c[1]["tensor"])]
@@ -399,16 +427,18 @@ def emit_table(files, out_path=TABLE):
     lines = [
         "// dispatch_table.inc -- generated by latency_skinny_gemm_amd/sweep.py --emit-table",
         f"// from cold-weight graph-replay timings on one MI355X ({datetime.date.today()}).",
-        "// {dtype, K, N, M, {kind, threads, cols, splits, depth, waves_m, reduce, flags}},  // us/call",
+        "// {dtype, K, N, M, {kind, threads, cols, splits, depth, waves_m, reduce, flags",
+        "//                   [, 0, m_tiles when a tiled plan asks for row blocks]}},  // us/call",
     ]
     dtypes = {"bf16": "SKG_DTYPE_BF16", "fp8": "SKG_DTYPE_FP8", "fp8_mx": "SKG_DTYPE_FP8_MX"}
     for key in sorted(best):
         dt, K, N, M = key
         b = best[key]["best"]
+        mtr = _mt_request_of(b, M)
         lines.append(
             f"{{{dtypes[dt]}, {K}, {N}, {M}, {{{kinds[b['kind']]}, {b['threads']}, {b['cols']}, "
-            f"{b['splits']}, {b['depth']}, {b.get('waves_m', 0)}, {names[b['reduce']]}, {b['flags']}}}}},"
-            f"  // {best[key]['best_us']:.3f}")
+            f"{b['splits']}, {b['depth']}, {b.get('waves_m', 0)}, {names[b['reduce']]}, {b['flags']}"
+            + (f", 0, {mtr}" if mtr else "") + f"}}}},  // {best[key]['best_us']:.3f}")
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote {len(best)} entries to {out_path}")

@@ -250,12 +250,15 @@ def _check_fp8_tiled_coverage(p, M, N, K):
     S, NB, NS, kc, WM = p.splits, p.cols, p.depth, p.k_chunk, p.waves_m
     U = 2 if p.flags & skg.FLAG_TILED_WIDE else 1
     WN = 4 // WM
-    MT = next((v for v in (1, 2, 4, 8) if v >= -(-M // 16)), 8)
-    assert p.m_tiles == MT and MT % WM == 0 and NB % WN == 0 and p.threads == 256
-    assert K % 128 == 0 and kc % 128 == 0 and (S - 1) * kc < K <= S * kc
+    natural = next((v for v in (1, 2, 4, 8) if v >= -(-M // 16)), 8)
+    MT = p.m_tiles  # the rows' own power of two, or a smaller one (row blocks)
+    assert MT in (1, 2, 4, 8) and MT <= natural and MT % WM == 0 and NB % WN == 0
+    assert p.threads == 256 and K % 128 == 0 and kc % 128 == 0 and (S - 1) * kc < K <= S * kc
     groups = -(-N // (16 * NB))
     MB = -(-M // (MT * 16))
-    assert MB == 1 or (MT == 8 and p.reduce != skg.REDUCE_LAST)
+    assert MB == 1 or S == 1 or p.reduce != skg.REDUCE_LAST
+    rows = sorted(mb * MT * 16 + r for mb in range(MB) for r in range(min(MT * 16, M - mb * MT * 16)))
+    assert rows == list(range(M))
     assert p.grid == MB * groups * S
     dec = [_tiled_position(b, MB, S, p.grid // MB) for b in range(p.grid)]
     assert sorted(dec) == sorted((mb, s, j) for mb in range(MB) for s in range(S) for j in range(groups))
@@ -672,14 +675,14 @@ def _check_tiled_coverage(p, M, N, K):
     S, NB, NS, kc, WM = p.splits, p.cols, p.depth, p.k_chunk, p.waves_m
     U = 4 if p.flags & skg.FLAG_TILED_WIDE else 2
     WN = 4 // WM
-    mt = -(-M // 16)
-    MT = next((v for v in (1, 2, 4, 8) if v >= mt), 8)
-    assert p.m_tiles == MT and MT % WM == 0 and NB % WN == 0
+    natural = next((v for v in (1, 2, 4, 8) if v >= -(-M // 16)), 8)
+    MT = p.m_tiles  # the rows' own power of two, or a smaller one (row blocks)
+    assert MT in (1, 2, 4, 8) and MT <= natural and MT % WM == 0 and NB % WN == 0
     MTW, NBW = MT // WM, NB // WN
     assert p.threads == 256 and K % 32 == 0
     groups = -(-N // (16 * NB))
-    MB = -(-M // (MT * 16))   # row blocks (only above 128 rows)
-    assert MB == 1 or (MT == 8 and p.reduce != skg.REDUCE_LAST)
+    MB = -(-M // (MT * 16))   # row blocks: above 128 rows, or fewer m-tiles asked for
+    assert MB == 1 or S == 1 or p.reduce != skg.REDUCE_LAST
     assert p.grid == MB * groups * S and kc % 32 == 0 and (S - 1) * kc < K <= S * kc
     # the grid's (mb, s, j) decode, and the row blocks of one (s, j) on one
     # XCD (ids 8 apart) whenever the (s, j) pairs come in whole groups of 8
@@ -880,4 +883,43 @@ def test_rows_plans_cover(lib, M, N, K, T, R, NS, fl):
 def test_rows_rejects(lib, plan, M, dtype):
     with pytest.raises(skg.SkinnyGemmError) as e:
         skg.plan_complete(M, 4096, 4096, skg.make_plan(skg.KIND_ROWS, **plan), dtype)
+    assert e.value.status == skg.ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ tiled row blocks below 129 rows
+
+
+@pytest.mark.parametrize("dtype,M,N,K,NB,mt,S", [
+    (skg.DTYPE_BF16, 128, 4096, 7168, 4, 2, 1), (skg.DTYPE_BF16, 100, 576, 7168, 2, 4, 2),
+    (skg.DTYPE_BF16, 32, 2112, 7168, 4, 1, 1), (skg.DTYPE_BF16, 17, 300, 1056, 4, 1, 3),
+    (skg.DTYPE_FP8, 128, 4096, 4096, 4, 2, 1), (skg.DTYPE_FP8, 128, 4096, 4096, 2, 4, 1),
+    (skg.DTYPE_FP8, 77, 1000, 4096, 4, 1, 2), (skg.DTYPE_FP8_MX, 64, 4096, 4096, 4, 2, 1),
+    (skg.DTYPE_BF16, 200, 4096, 7168, 4, 4, 1)])
+def test_tiled_row_blocks_below_129_rows(lib, dtype, M, N, K, NB, mt, S):
+    q = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_TILED, 256, NB, S, 3, m_tiles=mt), dtype)
+    MB = -(-M // (16 * mt))
+    assert q.m_tiles == mt and q.grid == MB * -(-N // (16 * NB)) * q.splits
+    assert q.splits == 1 or q.reduce == skg.REDUCE_KERNEL  # the last arriver needs one row block
+    # (above 128 rows the rows' own power of two is 8)
+    if dtype == skg.DTYPE_BF16:
+        _check_coverage(q, M, N, K)
+    else:
+        _check_fp8_tiled_coverage(q, M, N, K)
+    # 0 keeps the rows' own power of two; so does asking for exactly that
+    nat = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_TILED, 256, NB, S, 3), dtype)
+    assert nat.m_tiles == next((v for v in (1, 2, 4, 8) if v >= -(-M // 16)), 8)
+    again = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_TILED, 256, NB, S, 3,
+                                                     m_tiles=nat.m_tiles), dtype)
+    assert (again.m_tiles, again.grid) == (nat.m_tiles, nat.grid)
+
+
+@pytest.mark.parametrize("dtype", (skg.DTYPE_BF16, skg.DTYPE_FP8))
+@pytest.mark.parametrize("M,mt,reduce", [(16, 2, 0), (64, 8, 0), (128, 3, 0), (128, 16, 0),
+                                         (128, 2, skg.REDUCE_LAST), (200, 16, 0)])
+def test_tiled_row_block_requests_rejected(lib, dtype, M, mt, reduce):
+    # more tiles than the rows need (or than 8), not a power of two, a
+    # last-arriver reduction over several row blocks
+    p = skg.make_plan(skg.KIND_TILED, 256, 4, 2 if reduce else 1, 3, reduce, m_tiles=mt)
+    with pytest.raises(skg.SkinnyGemmError) as e:
+        skg.plan_complete(M, 4096, 4096, p, dtype)
     assert e.value.status == skg.ERR_INVALID_ARG

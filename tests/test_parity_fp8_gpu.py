@@ -69,6 +69,18 @@ def _plans(skg, M, N, K):
         except skg.SkinnyGemmError:
             continue
         plans.append((f"tiled_nb{NBt}_s{S}_ns{NS}_f{fl}_r{red}_wm{wm}", p))
+    # row blocks of fewer m-tiles than the rows need (wider, shorter tiles)
+    nat = 1 if M <= 16 else 2 if M <= 32 else 4 if M <= 64 else 8
+    for (mt, NBt, S, NS, fl, red) in ((nat // 2, 4, 1, 3, 0, skg.REDUCE_NONE),
+                                      (1, 4, 2, 2, wide, skg.REDUCE_KERNEL)):
+        if mt < 1 or mt >= nat:
+            continue
+        p = skg.make_plan(skg.KIND_TILED, 256, NBt, S, NS, red, flags=fl, m_tiles=mt)
+        try:
+            skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
+        except skg.SkinnyGemmError:
+            continue
+        plans.append((f"tiled_rows_mt{mt}_nb{NBt}_s{S}", p))
     return plans
 
 

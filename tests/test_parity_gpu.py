@@ -123,6 +123,19 @@ def _kernel_plans(skg, M, N, K):
         except skg.SkinnyGemmError:
             continue
         plans.append((f"tiled_nb{nbt}_s{S}_ns{ns}_f{fl}_r{red}_wm{wm}", p))
+    # row blocks of fewer m-tiles than the rows need (wider, shorter tiles)
+    nat = 1 if M <= 16 else 2 if M <= 32 else 4 if M <= 64 else 8
+    for (mt, nbt, S, ns, fl, red) in ((nat // 2, 4, 1, 3, 0, skg.REDUCE_NONE),
+                                      (1, 4, 3, 2, wide, skg.REDUCE_KERNEL)):
+        if mt < 1 or mt >= nat:
+            continue
+        p = skg.make_plan(skg.KIND_TILED, 256, cols=nbt, splits=S, depth=ns, reduce=red,
+                          flags=fl, m_tiles=mt)
+        try:
+            skg.plan_complete(M, N, K, p)
+        except skg.SkinnyGemmError:
+            continue
+        plans.append((f"tiled_rows_mt{mt}_nb{nbt}_s{S}", p))
     return plans
 
 
