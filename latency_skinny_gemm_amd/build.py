@@ -27,14 +27,16 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFOR
               "-I", "/opt/rocm/include", "-I", INCLUDE, "-I", CSRC]
 
 LIB_HIP = ["api.hip", "kernels_dot.hip", "kernels_splitk.hip", "kernels_tiled.hip",
-           "kernels_fp8.hip", "kernels_quant.hip", "kernels_fp8_tiled.hip", "kernels_rows.hip"]
+           "kernels_fp8.hip", "kernels_quant.hip", "kernels_fp8_tiled.hip", "kernels_rows.hip",
+           "kernels_fp8_rows.hip"]
 LIB_HOST = ["plan.cpp"]
 # Per-file flags.  The tiled kernels keep their accumulators in VGPRs: with the
 # compiler's default AGPR form, the loop-carried accumulators were copied
 # between AGPRs and VGPRs around every MFMA (resource report and assembly).
 EXTRA_FLAGS = {"kernels_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                "kernels_fp8_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-               "kernels_rows.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+               "kernels_rows.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "kernels_fp8_rows.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 FLOORS_HIP = ["floors.hip"]
 
 

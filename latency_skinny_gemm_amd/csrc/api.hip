@@ -370,7 +370,8 @@ extern "C" int skinny_gemm_fp8_planned(const void *x, const void *W, const void 
     rc = check_fp8(x, W, bias, scales, out, 0, 1, M, N, K);
     if (rc != SKG_OK) return rc;
     SkgPlan p = *plan;
-    rc = complete_plan(M, N, K, SKG_DTYPE_FP8, &p);
+    // validated for the scale mode it runs in (MX plans have their own limits)
+    rc = complete_plan(M, N, K, scales->mode == SKG_FP8_MX32 ? SKG_DTYPE_FP8_MX : SKG_DTYPE_FP8, &p);
     if (rc != SKG_OK) return rc;
     return run_fp8(x, W, bias, scales, out, 0, false, false, M, N, K, p, stream);
 }

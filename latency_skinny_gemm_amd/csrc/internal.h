@@ -91,6 +91,36 @@ constexpr bool rows_built(int MP, int NW, int NS, int R, int KS) {
            (NS - 2) * (rows_w_loads(NW, R, KS) + rows_x_loads(MP, NW, KS)) < 64;
 }
 
+// FP8 ROWS (M <= 32): the bf16 ring's layout with SB = 1024 (or 512) K per
+// stage, codes of R W rows and XR x rows (MP rounded to whole loads), the
+// padding KB, and for MX one KB block of scale bytes per 32 (or 64) rows of
+// each operand.  MP = the power of two at or above M.  MX needs K % 512 == 0.
+constexpr int kFp8RowsMaxM = 32;
+constexpr int kFp8RowsMxK = 512;
+constexpr int fp8_rows_mp(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : 32; }
+constexpr int fp8_rows_xr(int MP, int SB) { return (MP + 1024 / SB - 1) / (1024 / SB) * (1024 / SB); }
+constexpr int fp8_rows_scale_loads(int rows, int SB) { return (rows + 32768 / SB - 1) / (32768 / SB); }
+constexpr int fp8_rows_stage_bytes(int MP, int R, int SB, bool MX) {
+    return (R + fp8_rows_xr(MP, SB)) * SB + 1024 +
+           (MX ? (fp8_rows_scale_loads(R, SB) + fp8_rows_scale_loads(fp8_rows_xr(MP, SB), SB)) * 1024
+               : 0);
+}
+constexpr long fp8_rows_lds_bytes(int MP, int NS, int R, int SB, bool MX) {
+    return (long)NS * fp8_rows_stage_bytes(MP, R, SB, MX);
+}
+constexpr int fp8_rows_loads(int MP, int NW, int R, int SB, bool MX) {
+    return (R / (1024 / SB) + NW - 1) / NW + (fp8_rows_xr(MP, SB) / (1024 / SB) + NW - 1) / NW +
+           (MX ? 1 : 0);
+}
+constexpr bool fp8_rows_built(int MP, int NW, int NS, int R, int SB, bool MX) {
+    return MP >= 1 && MP <= kFp8RowsMaxM && MP == fp8_rows_mp(MP) && (NW == 4 || NW == 8) &&
+           (R == 8 || R == 16) && (SB == 1024 || SB == 512) && (SB / 128) % NW == 0 && NS >= 3 &&
+           NS <= 6 && fp8_rows_lds_bytes(MP, NS, R, SB, MX) <= 160 * 1024 - 256 &&
+           (NS - 2) * fp8_rows_loads(MP, NW, R, SB, MX) < 64 &&
+           (!MX || fp8_rows_scale_loads(R, SB) + fp8_rows_scale_loads(fp8_rows_xr(MP, SB), SB) <= NW) &&
+           NW * ((MP + 15) / 16) * 16 * 17 * 4 <= NS * fp8_rows_stage_bytes(MP, R, SB, MX);
+}
+
 // SPLITK per-lane registers: two stages of D steps of (NB + MT) vectors and
 // NB*MT accumulators of 4 (those may live in AGPRs).  Above 224 the kernel
 // is bounded to 256 threads (one wave per SIMD); up to 96 it may run 1024
@@ -250,6 +280,7 @@ int launch_fp8(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets,
                int K, hipStream_t stream);
 int launch_fp8_tiled(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets, int M,
                      int N, int K, hipStream_t stream);
+int launch_fp8_rows(const SkgPlan &p, const Fp8Args &a, int M, int N, int K, hipStream_t stream);
 // Whether the FP8 dot kernel that quantises bf16 x on load exists for (M, V)
 // and accepts workgroups of `threads` (its registers bound it lower than the
 // plain FP8 dot kernel).

@@ -535,6 +535,7 @@ int launch_fp8(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets,
     // quantises x first for every other plan)
     if (a.qx && (mx || p.kind != SKG_KIND_SPLITK)) return (int)hipErrorInvalidConfiguration;
     if (p.kind == SKG_KIND_TILED) return launch_fp8_tiled(p, a, ws, tickets, M, N, K, stream);
+    if (p.kind == SKG_KIND_ROWS) return launch_fp8_rows(p, a, M, N, K, stream);
     Fp8MfmaLaunch f = mx     ? fp8_mfma_mt<true, false>(p.m_tiles, p.cols, p.depth)
                       : a.qx ? fp8_mfma_mt<false, true>(p.m_tiles, p.cols, p.depth)
                              : fp8_mfma_mt<false, false>(p.m_tiles, p.cols, p.depth);

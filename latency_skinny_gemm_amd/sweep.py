@@ -89,6 +89,13 @@ def fp8_candidates(skg, M, N, K):
         for T in DOT_THREADS:
             for C in (1, 2, 4):
                 add(skg.make_plan(skg.KIND_DOT, T, C))
+    if M <= 32:
+        # whole-row ring: 8 or 16 columns, 4 or 8 waves, stages of 1024 or 512 K
+        for R in (8, 16):
+            for T in (256, 512):
+                for ns in (3, 4, 5, 6):
+                    for fl in (0, skg.FLAG_ROWS_HALF):
+                        add(skg.make_plan(skg.KIND_ROWS, T, R, depth=ns, flags=fl))
     # LDS-ring tiles (K % 128 == 0), also in row blocks of fewer m-tiles
     if K % 128 == 0 and (M > 4 or N >= 1024):
         for mtr in _mt_requests(M):

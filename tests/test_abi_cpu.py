@@ -208,14 +208,14 @@ def test_fp8_plans_valid_and_cover(lib, p):
     q = skg.plan(p.M, p.N, p.K, dt)
     again = skg.plan_complete(p.M, p.N, p.K, q, dt)
     assert (again.kind, again.grid, again.splits, again.k_chunk) == (q.kind, q.grid, q.splits, q.k_chunk)
-    _check_fp8_coverage(q, p.M, p.N, p.K)
+    _check_fp8_coverage(q, p.M, p.N, p.K, dt == skg.DTYPE_FP8_MX)
     if p.group.startswith("fp8_"):  # the swept FP8 points: one table entry per scale mode
         assert q.from_table == 1, p.key()
 
 
 def test_fp8_mx_planning_dtype(lib):
     # the same kernels and limits as per-tensor FP8, K % 32 == 0, and its own
-    # table entries (at M = 16 the two modes are fastest with different kernels)
+    # table entries (at M = 1 the two modes are fastest with different plans)
     with pytest.raises(skg.SkinnyGemmError) as e:
         skg.plan(4, 256, 4112, skg.DTYPE_FP8_MX)
     assert e.value.status == skg.ERR_UNSUPPORTED
@@ -227,10 +227,10 @@ def test_fp8_mx_planning_dtype(lib):
         b = skg.plan_complete(16, 4096, 4096, skg.make_plan(kind, T, NB, S, D, skg.REDUCE_KERNEL if S > 1
                                                             else skg.REDUCE_NONE), skg.DTYPE_FP8_MX)
         assert a.as_dict() == b.as_dict()
-    t = skg.plan(16, 4096, 4096, skg.DTYPE_FP8)
-    m = skg.plan(16, 4096, 4096, skg.DTYPE_FP8_MX)
+    t = skg.plan(1, 4096, 4096, skg.DTYPE_FP8)
+    m = skg.plan(1, 4096, 4096, skg.DTYPE_FP8_MX)
     assert t.from_table == m.from_table == 1
-    assert (t.kind, t.cols, t.splits) != (m.kind, m.cols, m.splits)
+    assert (t.kind, t.threads, t.depth) != (m.kind, m.threads, m.depth)
     # off the table both fall back to the same rule
     assert skg.plan(16, 4096, 2048, skg.DTYPE_FP8).as_dict() == \
         skg.plan(16, 4096, 2048, skg.DTYPE_FP8_MX).as_dict()
@@ -320,7 +320,57 @@ def _check_fp8_tiled_coverage(p, M, N, K):
     assert (NS - 2) * (XPW + WPW + 2) < 64
 
 
-def _check_fp8_coverage(p, M, N, K):
+def _check_fp8_rows_coverage(p, M, N, K, mx):
+    # the FP8 whole-row ring: stages of SB K (1 byte each); a load fills
+    # 1 KB (row j*RPL + p/CPR, position p%CPR holding chunk (p%CPR) ^ (LDS
+    # row % 16)); MX: wave w < WSL loads W scale rows RPS*w.., the next XSL
+    # waves the x ones (lane p: row p/CS, chunk p%CS); MFMA step u (128 K)
+    # reads chunks 8u + g and 8u + 4 + g and scale byte 4u + g
+    R, NW, NS = p.cols, p.threads // 64, p.depth
+    SB = 512 if p.flags & skg.FLAG_ROWS_HALF else 1024
+    MP = next(v for v in (1, 2, 4, 8, 16, 32) if v >= M)
+    CPR, RPL = SB // 16, 1024 // SB
+    XR = -(-MP // RPL) * RPL
+    SPR = SB // 32
+    CS = SPR // 16
+    RPS = 64 // CS
+    WSL, XSL = -(-R // RPS), -(-XR // RPS)
+    assert R in (8, 16) and NW in (4, 8) and 3 <= NS <= 6 and M <= 32 and p.splits == 1
+    assert (SB // 128) % NW == 0 and p.grid == -(-N // R)
+    assert sorted(n for b in range(p.grid) for c in range(R) if (n := b * R + c) < N) == list(range(N))
+    wl, xl = R // RPL, XR // RPL
+    lpw = -(-wl // NW) + -(-xl // NW) + 1  # the MX layout, which every plan must fit
+    stage = (R + XR) * SB + 1024 + (WSL + XSL) * 1024
+    assert NS * stage <= 160 * 1024 - 256 and (NS - 2) * lpw < 64 and WSL + XSL <= NW
+    for blk_rows, nl, base in ((R, wl, 0), (XR, xl, R)):
+        filled = {}
+        for j in range(nl):
+            for l in range(64):
+                r, pos = j * RPL + l // CPR, l % CPR
+                key = (r, pos ^ ((base + r) & 15))
+                filled[key] = filled.get(key, 0) + 1
+        assert filled == {(r, c): 1 for r in range(blk_rows) for c in range(CPR)}
+    # scale loads: every (row, 16-byte chunk) of each operand's stage scales once
+    for rows, nsl in ((R, WSL), (XR, XSL)):
+        got = sorted((i * RPS + l // CS, l % CS) for i in range(nsl) for l in range(64)
+                     if i * RPS + l // CS < rows)
+        assert got == [(r, c) for r in range(rows) for c in range(CS)]
+    # operand chunks of a 128-K step: lane group g takes bytes [16g, 16g+16)
+    # and [64+16g, 64+16g+16); every byte of the stage once over the steps
+    bytes_ = sorted(128 * u + 16 * c + e for u in range(SB // 128) for g in range(4)
+                    for c in (g, 4 + g) for e in range(16))
+    assert bytes_ == list(range(SB))
+    if mx:
+        assert K % 512 == 0
+    nst = -(-K // SB)
+    steps = sorted(w + NW * q for w in range(NW) for q in range(SB // 128 // NW))
+    assert steps == list(range(SB // 128)) and nst * SB >= K
+
+
+def _check_fp8_coverage(p, M, N, K, mx=False):
+    if p.kind == skg.KIND_ROWS:
+        _check_fp8_rows_coverage(p, M, N, K, mx)
+        return
     if p.kind == skg.KIND_TILED:
         _check_fp8_tiled_coverage(p, M, N, K)
         return
@@ -878,7 +928,7 @@ def test_rows_plans_cover(lib, M, N, K, T, R, NS, fl):
     (dict(threads=256, cols=16, depth=4, flags=skg.FLAG_TILED_WIDE), 8, skg.DTYPE_BF16),
     (dict(threads=256, cols=16, depth=4, waves_m=1), 8, skg.DTYPE_BF16),
     (dict(threads=256, cols=16, depth=4, reduce=skg.REDUCE_LAST), 8, skg.DTYPE_BF16),
-    (dict(threads=256, cols=16, depth=4), 8, skg.DTYPE_FP8),             # bf16 only
+    (dict(threads=256, cols=16, depth=4), 40, skg.DTYPE_FP8),            # FP8: M <= 32
 ])
 def test_rows_rejects(lib, plan, M, dtype):
     with pytest.raises(skg.SkinnyGemmError) as e:
@@ -922,4 +972,33 @@ def test_tiled_row_block_requests_rejected(lib, dtype, M, mt, reduce):
     p = skg.make_plan(skg.KIND_TILED, 256, 4, 2 if reduce else 1, 3, reduce, m_tiles=mt)
     with pytest.raises(skg.SkinnyGemmError) as e:
         skg.plan_complete(M, 4096, 4096, p, dtype)
+    assert e.value.status == skg.ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ FP8 whole-row ring
+
+
+@pytest.mark.parametrize("dtype,M,N,K,T,R,NS,fl", [
+    (skg.DTYPE_FP8, 16, 4096, 4096, 256, 16, 4, 0), (skg.DTYPE_FP8_MX, 16, 4096, 4096, 256, 16, 4, 0),
+    (skg.DTYPE_FP8, 1, 4096, 4096, 512, 16, 6, 0), (skg.DTYPE_FP8_MX, 32, 4096, 4096, 256, 16, 3, 8),
+    (skg.DTYPE_FP8, 5, 300, 4112, 256, 8, 5, 8), (skg.DTYPE_FP8, 13, 7, 16, 512, 16, 3, 0),
+    (skg.DTYPE_FP8_MX, 9, 1000, 2048, 256, 8, 5, 0)])
+def test_fp8_rows_plans_cover(lib, dtype, M, N, K, T, R, NS, fl):
+    q = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_ROWS, T, R, depth=NS, flags=fl), dtype)
+    assert (q.splits, q.reduce, q.k_chunk, q.m_tiles) == (1, skg.REDUCE_NONE, K, 1)
+    _check_fp8_coverage(q, M, N, K, dtype == skg.DTYPE_FP8_MX)
+
+
+@pytest.mark.parametrize("dtype,M,K,plan", [
+    (skg.DTYPE_FP8, 33, 4096, dict(threads=256, cols=16, depth=4)),             # M > 32
+    (skg.DTYPE_FP8_MX, 16, 4128, dict(threads=256, cols=16, depth=4)),          # MX: K % 512
+    (skg.DTYPE_FP8, 16, 4096, dict(threads=512, cols=16, depth=4, flags=8)),    # 4 steps, 8 waves
+    (skg.DTYPE_FP8, 32, 4096, dict(threads=256, cols=16, depth=4)),             # LDS (MX layout)
+    (skg.DTYPE_FP8, 16, 4096, dict(threads=256, cols=16, depth=4, flags=1)),
+    (skg.DTYPE_FP8, 16, 4096, dict(threads=256, cols=4, depth=4)),
+    (skg.DTYPE_FP8, 16, 4096, dict(threads=256, cols=16, depth=4, splits=2)),
+])
+def test_fp8_rows_rejects(lib, dtype, M, K, plan):
+    with pytest.raises(skg.SkinnyGemmError) as e:
+        skg.plan_complete(M, 4096, K, skg.make_plan(skg.KIND_ROWS, **plan), dtype)
     assert e.value.status == skg.ERR_INVALID_ARG

@@ -69,6 +69,18 @@ def _plans(skg, M, N, K):
         except skg.SkinnyGemmError:
             continue
         plans.append((f"tiled_nb{NBt}_s{S}_ns{NS}_f{fl}_r{red}_wm{wm}", p))
+    if M <= 32:
+        # whole-row ring: the first of each pair that fits
+        half = skg.FLAG_ROWS_HALF
+        for pair in (((256, 16, 4, 0), (256, 16, 3, half)), ((512, 8, 3, 0), (256, 8, 5, half))):
+            for T, R, NS, fl in pair:
+                p = skg.make_plan(skg.KIND_ROWS, T, R, depth=NS, flags=fl)
+                try:
+                    skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
+                except skg.SkinnyGemmError:
+                    continue
+                plans.append((f"rows_t{T}_c{R}_ns{NS}_f{fl}", p))
+                break
     # row blocks of fewer m-tiles than the rows need (wider, shorter tiles)
     nat = 1 if M <= 16 else 2 if M <= 32 else 4 if M <= 64 else 8
     for (mt, NBt, S, NS, fl, red) in ((nat // 2, 4, 1, 3, 0, skg.REDUCE_NONE),
