@@ -153,7 +153,8 @@ typedef struct SkgPlan {
                      with SKG_FLAG_DOT_XLDS: 1, 2 or 4 per wave);
                      SPLITK: 16-column blocks per workgroup (1, 2, 4);
                      TILED: 16-column blocks per workgroup (1, 2, 4, 8, 16);
-                     ROWS: output columns per workgroup (8, 16) */
+                     ROWS: output columns per workgroup (8, 16; bf16 up to 16
+                     rows also 10, 12) */
     int splits;   /* SPLITK, TILED: number of K chunks S (>= 1); DOT, ROWS: 1 */
     int depth;    /* SPLITK: 32-wide K steps a wave keeps in flight (1, 2, 4, 8);
                      TILED: stages of the LDS ring (2, 3, 4, 5, 6, 8);

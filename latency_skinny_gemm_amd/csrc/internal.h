@@ -61,7 +61,8 @@ constexpr long kXldsMaxLds = 160 * 1024 - 256;
 constexpr long xlds_lds_bytes(int M, int K8) { return (long)M * K8 * 16; }
 
 // ROWS (MFMA, M <= 64): stages of KS = 512 (or 256 with SKG_FLAG_ROWS_HALF)
-// K elements; each of the R W rows and MP x rows of a stage (MP = M up to
+// K elements; R = 8 or 16 columns per workgroup (also 10 or 12 up to 16
+// rows, to spread N over more CUs); each of the R W rows and MP x rows of a stage (MP = M up to
 // 16 rows, else M rounded up to 24, 32, 48 or 64) is one LDS row of 2*KS
 // bytes, plus 1 KB that takes the padding loads.  A load instruction fills
 // 1 KB: one row (KS = 512) or two (KS = 256).  Wave w issues the W
@@ -86,7 +87,8 @@ constexpr long rows_lds_bytes(int MP, int NS, int R, int KS) {
 }
 constexpr bool rows_built(int MP, int NW, int NS, int R, int KS) {
     return MP >= 1 && MP <= kRowsMaxM && MP == rows_mp(MP) && (NW == 4 || NW == 8) &&
-           (R == 8 || R == 16) && (KS == 512 || KS == 256) && NS >= 3 && NS <= 6 &&
+           (R == 8 || R == 16 || ((R == 10 || R == 12) && MP <= 16)) &&
+           (KS == 512 || KS == 256) && NS >= 3 && NS <= 6 &&
            rows_lds_bytes(MP, NS, R, KS) <= 160 * 1024 - 256 &&
            (NS - 2) * (rows_w_loads(NW, R, KS) + rows_x_loads(MP, NW, KS)) < 64;
 }

@@ -6,8 +6,9 @@
 // which needs a reduction across workgroups.  On gfx950 the dense decode
 // linear at small M can do without that:
 //  * workgroup b owns R consecutive output columns (R = 16, one MFMA tile
-//    width, or 8 for small N) and the whole K, so N = 4096 gives 256
-//    workgroups and nothing is reduced across workgroups;
+//    width, or 8, 10, 12 to spread a smaller N over more CUs) and the whole
+//    K, so N = 4096 gives 256 workgroups and nothing is reduced across
+//    workgroups;
 //  * a stage is KS = 512 (or 256) K elements: each of the R W rows and of
 //    the M x rows contributes one segment of 2*KS bytes, and one
 //    buffer-to-LDS load moves 1 KB (lane p: 16 bytes), so every load reads
@@ -225,10 +226,21 @@ RowsLaunch pick_ns(int NS) {
     }
 }
 
+template <int MP, int NW, int KS>
+RowsLaunch pick_r(int NS, int R) {
+    switch (R) {
+    case 8: return pick_ns<MP, NW, 8, KS>(NS);
+    case 10: return pick_ns<MP, NW, 10, KS>(NS);
+    case 12: return pick_ns<MP, NW, 12, KS>(NS);
+    case 16: return pick_ns<MP, NW, 16, KS>(NS);
+    default: return nullptr;
+    }
+}
+
 template <int MP, int KS>
 RowsLaunch pick_shape(int NW, int NS, int R) {
-    if (NW == 4) return R == 16 ? pick_ns<MP, 4, 16, KS>(NS) : R == 8 ? pick_ns<MP, 4, 8, KS>(NS) : nullptr;
-    if (NW == 8) return R == 16 ? pick_ns<MP, 8, 16, KS>(NS) : R == 8 ? pick_ns<MP, 8, 8, KS>(NS) : nullptr;
+    if (NW == 4) return pick_r<MP, 4, KS>(NS, R);
+    if (NW == 8) return pick_r<MP, 8, KS>(NS, R);
     return nullptr;
 }
 

@@ -226,9 +226,9 @@ def candidates(skg, M, N, K):
                 add(skg.make_plan(skg.KIND_DOT, T, cw * T // 64,
                                   flags=skg.FLAG_DOT_XLDS | skg.FLAG_DOT2))
     if M <= 64:
-        # whole-row MFMA ring: 8 or 16 columns, 4 or 8 waves, 3-6 stages of
-        # 512 or 256 K
-        for R in (8, 16):
+        # whole-row MFMA ring: 8, 10, 12 or 16 columns, 4 or 8 waves, 3-6
+        # stages of 512 or 256 K
+        for R in (8, 10, 12, 16):
             for T in (256, 512):
                 for ns in (3, 4, 5, 6):
                     for fl in (0, skg.FLAG_ROWS_HALF):

@@ -631,8 +631,8 @@ def _check_rows_coverage(p, M, N, K):
     MP = M if M <= 16 else next(v for v in (24, 32, 48, 64) if v >= M)
     CPR, RPL = KS // 8, 1024 // (2 * KS)
     XR = -(-MP // RPL) * RPL
-    assert R in (8, 16) and NW in (4, 8) and 3 <= NS <= 6 and M <= 64 and p.splits == 1
-    assert p.grid == -(-N // R)
+    assert (R in (8, 16) or (R in (10, 12) and M <= 16)) and NW in (4, 8) and 3 <= NS <= 6
+    assert M <= 64 and p.splits == 1 and p.grid == -(-N // R)
     cols = sorted(n for b in range(p.grid) for c in range(R) if (n := b * R + c) < N)
     assert cols == list(range(N))
     wl, xl = R // RPL, XR // RPL
@@ -905,7 +905,8 @@ HALF = skg.FLAG_ROWS_HALF
     (8, 4096, 7168, 256, 16, 4, 0), (8, 4096, 7168, 512, 16, 6, 0), (1, 2112, 7168, 256, 8, 3, 0),
     (16, 100, 2880, 512, 8, 5, 0), (3, 7, 4104, 256, 16, 4, 0), (13, 4096, 4096, 512, 16, 3, 0),
     (16, 1, 8, 256, 8, 3, 0), (32, 4096, 7168, 256, 16, 3, 0), (64, 4096, 7168, 256, 16, 3, HALF),
-    (17, 300, 2056, 512, 8, 6, HALF), (40, 33, 7168, 256, 8, 4, HALF), (5, 4096, 7168, 512, 16, 5, HALF)])
+    (17, 300, 2056, 512, 8, 6, HALF), (40, 33, 7168, 256, 8, 4, HALF), (5, 4096, 7168, 512, 16, 5, HALF),
+    (8, 2112, 7168, 256, 10, 5, HALF), (16, 2112, 7168, 512, 12, 3, 0), (3, 77, 2880, 256, 10, 4, 0)])
 def test_rows_plans_cover(lib, M, N, K, T, R, NS, fl):
     q = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_ROWS, T, R, depth=NS, flags=fl))
     assert (q.splits, q.reduce, q.k_chunk, q.m_tiles) == (1, skg.REDUCE_NONE, K, 1)
@@ -914,6 +915,8 @@ def test_rows_plans_cover(lib, M, N, K, T, R, NS, fl):
 
 @pytest.mark.parametrize("plan,M,dtype", [
     (dict(threads=256, cols=16, depth=4), 65, skg.DTYPE_BF16),           # M > 64
+    (dict(threads=256, cols=10, depth=4), 17, skg.DTYPE_BF16),           # 10 columns: M <= 16
+    (dict(threads=256, cols=9, depth=4), 8, skg.DTYPE_BF16),
     (dict(threads=256, cols=16, depth=3), 64, skg.DTYPE_BF16),           # LDS: 64 rows of 1 KB
     (dict(threads=256, cols=16, depth=4, flags=16), 8, skg.DTYPE_BF16),  # unknown flag
     (dict(threads=128, cols=16, depth=4), 8, skg.DTYPE_BF16),            # 2 waves

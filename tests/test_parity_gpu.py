@@ -82,7 +82,8 @@ def _kernel_plans(skg, M, N, K):
         # columns, 4 or 8 waves, stages of 512 or 256 K)
         half = skg.FLAG_ROWS_HALF
         for pair in (((256, 16, 4, 0), (256, 16, 3, half)), ((512, 8, 3, 0), (512, 8, 4, half)),
-                     ((512, 16, 6, half), (512, 16, 3, half)), ((256, 8, 5, half), (256, 8, 3, 0))):
+                     ((512, 16, 6, half), (512, 16, 3, half)), ((256, 8, 5, half), (256, 8, 3, 0)),
+                     ((256, 10, 5, half), (512, 12, 3, 0))):
             for threads, cols, ns, fl in pair:
                 p = skg.make_plan(skg.KIND_ROWS, threads, cols=cols, depth=ns, flags=fl)
                 try:
