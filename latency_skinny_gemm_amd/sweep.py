@@ -227,7 +227,9 @@ def candidates(skg, M, N, K):
                                   flags=skg.FLAG_DOT_XLDS | skg.FLAG_DOT2))
     if M <= 64:
         # whole-row MFMA ring: 8, 10, 12 or 16 columns, 4 or 8 waves, 3-6
-        # stages of 512 or 256 K
+        # stages of 512 or 256 K (fewer columns make stages too small to keep
+        # enough bytes in flight: 5.2 against 2.8 us for one column at the
+        # router's M = 1)
         for R in (8, 10, 12, 16):
             for T in (256, 512):
                 for ns in (3, 4, 5, 6):

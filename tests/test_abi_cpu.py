@@ -917,11 +917,12 @@ def test_rows_plans_cover(lib, M, N, K, T, R, NS, fl):
     (dict(threads=256, cols=16, depth=4), 65, skg.DTYPE_BF16),           # M > 64
     (dict(threads=256, cols=10, depth=4), 17, skg.DTYPE_BF16),           # 10 columns: M <= 16
     (dict(threads=256, cols=9, depth=4), 8, skg.DTYPE_BF16),
+    (dict(threads=256, cols=4, depth=4), 8, skg.DTYPE_BF16),
     (dict(threads=256, cols=16, depth=3), 64, skg.DTYPE_BF16),           # LDS: 64 rows of 1 KB
     (dict(threads=256, cols=16, depth=4, flags=16), 8, skg.DTYPE_BF16),  # unknown flag
     (dict(threads=128, cols=16, depth=4), 8, skg.DTYPE_BF16),            # 2 waves
     (dict(threads=1024, cols=16, depth=4), 8, skg.DTYPE_BF16),           # 16 waves
-    (dict(threads=256, cols=4, depth=4), 8, skg.DTYPE_BF16),             # 4 columns
+    (dict(threads=256, cols=2, depth=4), 8, skg.DTYPE_BF16),             # 2 columns
     (dict(threads=256, cols=32, depth=4), 8, skg.DTYPE_BF16),
     (dict(threads=256, cols=16, depth=2), 8, skg.DTYPE_BF16),            # ring of 2
     (dict(threads=256, cols=16, depth=7), 8, skg.DTYPE_BF16),
