@@ -505,16 +505,27 @@ def test_default_rule_details(lib):
     # past the x bound of the small-N rule: the tiled kernel
     assert skg.plan_on(16, 512, 7168, 255).kind == skg.KIND_TILED
     assert skg.plan_on(12, 512, 7168, 255).kind == skg.KIND_DOT
-    # FP8 from 5 to 16 rows: no K split with N >= 2048 (128 groups of 16
-    # columns fill half of 255 CUs), else tiled; above 16 rows tiled
+    # FP8 from 3 to 32 rows: the whole-row ring when its workgroups (8
+    # columns up to 8 rows, else 16) fill half the CUs and the MX layout
+    # fits; else from 5 to 16 rows split-K without a K split when its
+    # 16-column groups fill half the CUs, else tiled
     q = skg.plan_on(8, 2048, 4096, 255, skg.DTYPE_FP8)
-    assert (q.kind, q.splits, q.depth) == (skg.KIND_SPLITK, 1, 2)
-    assert skg.plan_on(12, 1024, 4096, 255, skg.DTYPE_FP8).kind == skg.KIND_TILED
-    assert skg.plan_on(24, 8192, 4096, 255, skg.DTYPE_FP8).kind == skg.KIND_TILED
+    assert (q.kind, q.cols, q.flags, q.grid) == (skg.KIND_ROWS, 8, skg.FLAG_ROWS_HALF, 256)
+    q = skg.plan_on(4, 4096, 4096, 255, skg.DTYPE_FP8_MX)
+    assert (q.kind, q.cols, q.flags) == (skg.KIND_ROWS, 8, 0)
+    q = skg.plan_on(24, 8192, 4096, 255, skg.DTYPE_FP8)
+    assert (q.kind, q.cols, q.depth) == (skg.KIND_ROWS, 16, 3)
+    assert skg.plan_on(12, 1024, 4096, 255, skg.DTYPE_FP8).kind == skg.KIND_TILED  # 64 groups
+    q = skg.plan_on(16, 4096, 4128, 255, skg.DTYPE_FP8_MX)  # MX ring needs K % 512 == 0
+    assert (q.kind, q.splits) == (skg.KIND_SPLITK, 1)
+    assert skg.plan_on(16, 4096, 4128, 255, skg.DTYPE_FP8).kind == skg.KIND_ROWS
+    assert skg.plan_on(33, 4096, 4096, 255, skg.DTYPE_FP8).kind == skg.KIND_TILED
     q = skg.plan_on(2, 4096, 4096, 255, skg.DTYPE_FP8)
     assert (q.kind, q.cols) == (skg.KIND_DOT, 1)
-    # FP8 K not a multiple of 128 above 16 rows: split-K
-    assert skg.plan_on(24, 4096, 4112, 255, skg.DTYPE_FP8).kind == skg.KIND_SPLITK
+    # FP8 K not a multiple of 128 above 16 rows: the ring takes any K,
+    # else split-K (the tiled kernel needs K % 128 == 0)
+    assert skg.plan_on(24, 4096, 4112, 255, skg.DTYPE_FP8).kind == skg.KIND_ROWS
+    assert skg.plan_on(24, 512, 4112, 255, skg.DTYPE_FP8).kind == skg.KIND_SPLITK
 
 
 def test_split_count_follows_cu_count(lib):

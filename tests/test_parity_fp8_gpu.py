@@ -271,30 +271,34 @@ def test_fp8_runs_bitwise_deterministic(skg):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{mode} [{name}]"
 
 
-# FP8 shapes off the dispatch table, one per branch of the default rule: the
-# dot kernel, split-K without a K split (N >= 2048), the tiled kernel (from 5
-# rows below N = 2048, and above 16 rows), split-K for K % 128 != 0
-FP8_DEFAULT_RULE_SHAPES = [(2, 1024, 1024), (8, 2048, 1024), (12, 1024, 2048), (24, 512, 1024),
-                           (24, 512, 1040)]
+# FP8 shapes off the dispatch table, one or more per branch of the default
+# rule at 256 CUs: the dot kernel (up to 2 rows, or up to 4 when the ring's
+# 8-column groups fill under half the CUs), the whole-row ring (3 to 32 rows
+# whose groups fill half the CUs, any K per tensor, MX with K % 512 == 0),
+# split-K without a K split (up to 16 rows, N >= 2048, ring refused), the
+# tiled kernel, split-K for K % 128 != 0
+FP8_DEFAULT_RULE_SHAPES = [
+    ((2, 1024, 1024, "fp8_tensor"), "dot"), ((4, 512, 1024, "fp8_tensor"), "dot"),
+    ((8, 2048, 1024, "fp8_tensor"), "rows"), ((24, 4096, 1040, "fp8_tensor"), "rows"),
+    ((32, 4096, 1024, "fp8_mx"), "rows"), ((16, 2048, 1056, "fp8_mx"), "splitk"),
+    ((12, 1024, 2048, "fp8_tensor"), "tiled"), ((24, 512, 1024, "fp8_tensor"), "tiled"),
+    ((24, 512, 1040, "fp8_tensor"), "splitk")]
 
 
-@pytest.mark.parametrize("shape", FP8_DEFAULT_RULE_SHAPES, ids=str)
-def test_fp8_default_rule_plans_within_tolerance(skg, shape):
-    M, N, K = shape
-    q = skg.plan(M, N, K, skg.DTYPE_FP8)
+@pytest.mark.parametrize("shape,kind", FP8_DEFAULT_RULE_SHAPES, ids=str)
+def test_fp8_default_rule_plans_within_tolerance(skg, shape, kind):
+    M, N, K, mode = shape
+    dt = skg.DTYPE_FP8 if mode == "fp8_tensor" else skg.DTYPE_FP8_MX
+    q = skg.plan(M, N, K, dt)
     assert q.from_table == 0
-    if M <= 4:
-        want = skg.KIND_DOT
-    elif M <= 16 and N >= 2048:
-        want = skg.KIND_SPLITK
-    else:
-        want = skg.KIND_TILED if K % 128 == 0 else skg.KIND_SPLITK
+    want = {"dot": skg.KIND_DOT, "rows": skg.KIND_ROWS, "splitk": skg.KIND_SPLITK,
+            "tiled": skg.KIND_TILED}[kind]
     assert q.kind == want, q
     if want == skg.KIND_SPLITK and M <= 16:
         assert q.splits == 1
-    xq, wq, s1, s2 = gen.fp8_inputs(M, N, K, "fp8_tensor", seed=M + N + K)
+    xq, wq, s1, s2 = gen.fp8_inputs(M, N, K, mode, seed=M + N + K)
     bias = (torch.randn(N, generator=torch.Generator().manual_seed(K)) * 0.5).to(torch.bfloat16)
-    ref = _oracle("fp8_tensor", xq, wq, s1, s2, bias)
-    out = _run(skg, None, xq.to(DEV), wq.to(DEV), bias.to(DEV), **_scales("fp8_tensor", s1, s2))
+    ref = _oracle(mode, xq, wq, s1, s2, bias)
+    out = _run(skg, None, xq.to(DEV), wq.to(DEV), bias.to(DEV), **_scales(mode, s1, s2))
     ok, msg = tolerance.check(out, ref, K)
     assert ok, f"{shape} plan {q}: {msg}"
