@@ -505,27 +505,42 @@ def test_default_rule_details(lib):
     # past the x bound of the small-N rule: the tiled kernel
     assert skg.plan_on(16, 512, 7168, 255).kind == skg.KIND_TILED
     assert skg.plan_on(12, 512, 7168, 255).kind == skg.KIND_DOT
-    # FP8 from 3 to 32 rows: the whole-row ring when its workgroups (8
-    # columns up to 8 rows, else 16) fill half the CUs and the MX layout
-    # fits; else from 5 to 16 rows split-K without a K split when its
-    # 16-column groups fill half the CUs, else tiled
-    q = skg.plan_on(8, 2048, 4096, 255, skg.DTYPE_FP8)
-    assert (q.kind, q.cols, q.flags, q.grid) == (skg.KIND_ROWS, 8, skg.FLAG_ROWS_HALF, 256)
-    q = skg.plan_on(4, 4096, 4096, 255, skg.DTYPE_FP8_MX)
-    assert (q.kind, q.cols, q.flags) == (skg.KIND_ROWS, 8, 0)
-    q = skg.plan_on(24, 8192, 4096, 255, skg.DTYPE_FP8)
-    assert (q.kind, q.cols, q.depth) == (skg.KIND_ROWS, 16, 3)
-    assert skg.plan_on(12, 1024, 4096, 255, skg.DTYPE_FP8).kind == skg.KIND_TILED  # 64 groups
-    q = skg.plan_on(16, 4096, 4128, 255, skg.DTYPE_FP8_MX)  # MX ring needs K % 512 == 0
-    assert (q.kind, q.splits) == (skg.KIND_SPLITK, 1)
-    assert skg.plan_on(16, 4096, 4128, 255, skg.DTYPE_FP8).kind == skg.KIND_ROWS
-    assert skg.plan_on(33, 4096, 4096, 255, skg.DTYPE_FP8).kind == skg.KIND_TILED
+    # FP8 from 3 to 32 rows: the whole-row ring when the 8-column groups
+    # reach a quarter of the CUs (all of them at 3-4 rows, else the dot
+    # kernel). Columns: the fewer on the busiest CU, on a tie 8 up to 8 rows
+    # with at most two groups per CU, else 16. Half-width stages with two
+    # groups per CU or above 8 rows; 3 stages with three groups per CU or
+    # two 16-column groups
+    def ring(M, N, K, dt=skg.DTYPE_FP8, cus=256):
+        q = skg.plan_on(M, N, K, cus, dt)
+        assert q.kind == skg.KIND_ROWS and q.threads == 256, q
+        return q.cols, q.depth, q.flags, q.grid
+    half = skg.FLAG_ROWS_HALF
+    assert ring(8, 4096, 4096) == (8, 4, half, 512)           # tie, two per CU
+    assert ring(4, 4096, 4096, skg.DTYPE_FP8_MX) == (8, 4, half, 512)
+    assert ring(4, 7168, 2048) == (16, 3, half, 448)          # tie, 896 groups of 8
+    assert ring(32, 4096, 4096) == (16, 4, half, 256)         # tie above 8 rows
+    assert ring(32, 2048, 7168) == (8, 4, half, 256)          # 16 columns idle half
+    assert ring(6, 5120, 3072) == (8, 3, half, 640)           # 3 groups per CU
+    assert ring(8, 1536, 4096) == (8, 4, 0, 192)              # one group per CU
+    assert ring(3, 2048, 7168) == (8, 4, 0, 256)
+    assert ring(8, 512, 4096) == (8, 4, 0, 64)                # a quarter of the CUs
+    assert ring(24, 8192, 4096) == (16, 3, half, 512)           # tie above 8 rows
+    assert ring(24, 8192, 4096, cus=255) == (8, 3, half, 1024)  # 40 columns against 48
+    q = skg.plan_on(4, 1024, 4096, 256, skg.DTYPE_FP8)        # 128 groups: dot
+    assert (q.kind, q.cols) == (skg.KIND_DOT, 1)
     q = skg.plan_on(2, 4096, 4096, 255, skg.DTYPE_FP8)
     assert (q.kind, q.cols) == (skg.KIND_DOT, 1)
-    # FP8 K not a multiple of 128 above 16 rows: the ring takes any K,
-    # else split-K (the tiled kernel needs K % 128 == 0)
-    assert skg.plan_on(24, 4096, 4112, 255, skg.DTYPE_FP8).kind == skg.KIND_ROWS
-    assert skg.plan_on(24, 512, 4112, 255, skg.DTYPE_FP8).kind == skg.KIND_SPLITK
+    assert skg.plan_on(33, 4096, 4096, 255, skg.DTYPE_FP8).kind == skg.KIND_TILED
+    # below a quarter of the CUs: from 5 rows tiled, split-K for K % 128 != 0
+    assert skg.plan_on(12, 256, 4096, 256, skg.DTYPE_FP8).kind == skg.KIND_TILED
+    assert skg.plan_on(24, 256, 4112, 256, skg.DTYPE_FP8).kind == skg.KIND_SPLITK
+    # the ring takes any K per tensor; MX needs K % 512 == 0, else from 5
+    # to 16 rows split-K without a K split where its 16-column groups fill
+    # half the CUs
+    assert skg.plan_on(16, 4096, 4128, 255, skg.DTYPE_FP8).kind == skg.KIND_ROWS
+    q = skg.plan_on(16, 4096, 4128, 255, skg.DTYPE_FP8_MX)
+    assert (q.kind, q.splits) == (skg.KIND_SPLITK, 1)
 
 
 def test_split_count_follows_cu_count(lib):

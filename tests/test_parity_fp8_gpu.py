@@ -272,17 +272,19 @@ def test_fp8_runs_bitwise_deterministic(skg):
 
 
 # FP8 shapes off the dispatch table, one or more per branch of the default
-# rule at 256 CUs: the dot kernel (up to 2 rows, or up to 4 when the ring's
-# 8-column groups fill under half the CUs), the whole-row ring (3 to 32 rows
-# whose groups fill half the CUs, any K per tensor, MX with K % 512 == 0),
-# split-K without a K split (up to 16 rows, N >= 2048, ring refused), the
-# tiled kernel, split-K for K % 128 != 0
+# rule at 256 CUs: the dot kernel (up to 2 rows, and 3-4 rows below a full
+# grid of 8-column groups), the whole-row ring (3 to 32 rows from N = 512:
+# 8 or 16 columns, full or half-width stages, 3 or 4 stages, any K per
+# tensor, MX with K % 512 == 0), split-K without a K split (up to 16 rows,
+# N >= 2048, ring refused), the tiled kernel and split-K for K % 128 != 0
+# below N = 512
 FP8_DEFAULT_RULE_SHAPES = [
-    ((2, 1024, 1024, "fp8_tensor"), "dot"), ((4, 512, 1024, "fp8_tensor"), "dot"),
-    ((8, 2048, 1024, "fp8_tensor"), "rows"), ((24, 4096, 1040, "fp8_tensor"), "rows"),
+    ((2, 1024, 1024, "fp8_tensor"), "dot"), ((4, 1024, 1024, "fp8_tensor"), "dot"),
+    ((8, 512, 1024, "fp8_tensor"), "rows"), ((24, 4096, 1040, "fp8_tensor"), "rows"),
+    ((4, 7168, 1024, "fp8_mx"), "rows"), ((6, 5120, 1024, "fp8_tensor"), "rows"),
     ((32, 4096, 1024, "fp8_mx"), "rows"), ((16, 2048, 1056, "fp8_mx"), "splitk"),
-    ((12, 1024, 2048, "fp8_tensor"), "tiled"), ((24, 512, 1024, "fp8_tensor"), "tiled"),
-    ((24, 512, 1040, "fp8_tensor"), "splitk")]
+    ((12, 256, 2048, "fp8_tensor"), "tiled"), ((24, 256, 1024, "fp8_tensor"), "tiled"),
+    ((24, 256, 1040, "fp8_tensor"), "splitk")]
 
 
 @pytest.mark.parametrize("shape,kind", FP8_DEFAULT_RULE_SHAPES, ids=str)
