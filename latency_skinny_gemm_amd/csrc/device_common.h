@@ -24,9 +24,13 @@ __device__ __forceinline__ Rsrc make_rsrc(const void *base, unsigned bytes) {
                                              0x00020000);
 }
 
-// cache-policy bits of the buffer instruction: bit 1 = nt (streaming)
+// cache-policy bits of the buffer instruction: bit 1 = nt (streaming),
+// bit 4 = sc1.  An sc1 access is what an agent-scope relaxed atomic load or
+// store of a dword compiles to on gfx950 (global_load/store_dword ... sc1):
+// a 16-byte sc1 access gives each of its dwords that same coherence.
 constexpr int kCacheDefault = 0;
 constexpr int kCacheStream = 2;
+constexpr int kCacheCoherent = 16;
 
 template <int POLICY>
 __device__ __forceinline__ u32x4 load16(Rsrc r, unsigned byte_off) {

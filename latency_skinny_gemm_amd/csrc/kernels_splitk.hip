@@ -140,7 +140,7 @@ __global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
     }
     if (S == 1 || reduce != SKG_REDUCE_LAST) return;
 
-    last_arriver_reduce(ws, tickets, bias, out, out_f32, M, N, S, j, col0, ncols, &is_last);
+    last_arriver_reduce<2, 4>(ws, tickets, bias, out, out_f32, M, N, S, j, col0, ncols, &is_last);
 }
 
 // Second-pass reduction: the same sum in the same order as the in-kernel

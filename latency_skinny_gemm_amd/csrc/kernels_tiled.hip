@@ -215,6 +215,7 @@ __global__ void __launch_bounds__(256)
     constexpr int C4 = NB * 4;  // 4-column groups per row
     const bool vec = (N & 3) == 0;  // 16-byte aligned workspace rows
     const bool coherent = reduce == SKG_REDUCE_LAST;  // partials read by the last arriver
+    const PartialsVec pv = partials_vec(ws, M, N, S);
     for (int e = t; e < Mb * C4; e += 256) {
         const int r = e / C4, c = (e % C4) * 4;
         if (c >= ncols) continue;
@@ -228,7 +229,7 @@ __global__ void __launch_bounds__(256)
                     store_out(out, m * N + n + q,
                               bias ? v[q] + bf16_to_f32(bias[n + q]) : v[q], out_f32);
         } else if (vec && c + 4 <= ncols) {
-            put_partial4(ws, ((size_t)s * M + m) * N + n, v, coherent);
+            put_partial4(ws, ((size_t)s * M + m) * N + n, v, coherent, pv);
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)

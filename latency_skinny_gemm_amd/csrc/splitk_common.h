@@ -43,9 +43,29 @@ __device__ __forceinline__ void put_partial(float *ws, size_t i, float v, bool c
         ws[i] = v;
 }
 
-// Four consecutive partials (ws + i 16-byte aligned).
-__device__ __forceinline__ void put_partial4(float *ws, size_t i, f32x4 v, bool coherent) {
-    if (coherent) {
+// The workspace ws[S][M][N] seen through one buffer resource, for 16-byte
+// coherent (sc1) accesses: usable when N % 4 == 0 (16-byte aligned rows)
+// and the S*M*N floats span less than 2^31 bytes (every byte offset is a
+// valid 32-bit buffer offset below kOOB).
+struct PartialsVec {
+    Rsrc r;
+    bool ok;
+};
+__device__ __forceinline__ PartialsVec partials_vec(float *ws, int M, int N, int S) {
+    const unsigned long long bytes = (unsigned long long)S * (unsigned)M * (unsigned)N * 4ull;
+    const bool ok = (N & 3) == 0 && bytes < 0x80000000ull;
+    return PartialsVec{make_rsrc(ws, ok ? (unsigned)bytes : 0u), ok};
+}
+
+// Four consecutive partials (ws + i 16-byte aligned).  Coherent: one
+// 16-byte sc1 store where the buffer view covers the workspace, else four
+// dword atomic stores (the same coherence per dword).
+__device__ __forceinline__ void put_partial4(float *ws, size_t i, f32x4 v, bool coherent,
+                                             const PartialsVec &pv) {
+    if (coherent && pv.ok) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), pv.r,
+                                               (unsigned)(i * 4u), 0, kCacheCoherent);
+    } else if (coherent) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             __hip_atomic_store(ws + i + q, v[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -68,6 +88,10 @@ __device__ __forceinline__ void put_partial4(float *ws, size_t i, f32x4 v, bool 
 // scale product when given (once), adds the bias and rounds once; it
 // re-arms the ticket (the next kernel on the stream sees the zero after
 // the kernel boundary).  No workgroup waits on another.
+// E and G size the batch of 16-byte partial loads each thread keeps in
+// flight (E * G loads, 4 * E * (G + 1) VGPRs): the kernels launched with up
+// to 1024 threads take a smaller batch than the 256-thread tiled kernels.
+template <int E = 8, int G = 4>
 __device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
                                                     unsigned *__restrict__ tickets,
                                                     const uint16_t *__restrict__ bias,
@@ -88,6 +112,62 @@ __device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
     __syncthreads();
     if (!*is_last) return;
     const float scale = sx ? sx[0] * sw[0] : 1.0f;  // FP8 per-tensor: applied once, here
+    const PartialsVec pv = partials_vec(ws, M, N, S);
+    if (pv.ok && ((col0 | ncols) & 3) == 0) {
+        // Four columns per item, 16-byte sc1 loads: each thread puts E items
+        // x G splits of loads in flight before adding any of them, so the
+        // tile costs about ceil(items / (E * threads)) * ceil(S / G) memory
+        // latencies.  Each column still adds its S partials in ascending s
+        // from 0.0f: the same bits as the loop below and the second kernel.
+        const int C4 = ncols >> 2, items = M * C4;
+        const unsigned plane = (unsigned)M * (unsigned)N * 4u;  // bytes per split
+        for (int e0 = threadIdx.x; e0 < items; e0 += E * (int)blockDim.x) {
+            unsigned off[E];
+#pragma unroll
+            for (int q = 0; q < E; ++q) {
+                const int e = e0 + q * (int)blockDim.x;
+                const int m = e / C4;
+                off[q] = e < items ? ((unsigned)m * (unsigned)N + (unsigned)(col0 + 4 * (e - m * C4))) * 4u
+                                   : kOOB;
+            }
+            f32x4 acc[E];
+#pragma unroll
+            for (int q = 0; q < E; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < S; s0 += G) {
+                f32x4 t[E][G];
+#pragma unroll
+                for (int q = 0; q < E; ++q)
+#pragma unroll
+                    for (int i = 0; i < G; ++i) {
+                        const bool live = off[q] != kOOB && s0 + i < S;
+                        t[q][i] = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       pv.r, live ? off[q] + (unsigned)(s0 + i) * plane : kOOB, 0,
+                                       kCacheCoherent));
+                    }
+#pragma unroll
+                for (int q = 0; q < E; ++q)
+#pragma unroll
+                    for (int i = 0; i < G; ++i)
+                        if (s0 + i < S) acc[q] += t[q][i];
+            }
+#pragma unroll
+            for (int q = 0; q < E; ++q) {
+                const int e = e0 + q * (int)blockDim.x;
+                if (e >= items) continue;
+                const int m = e / C4;
+                const int n = col0 + 4 * (e - m * C4);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    float v = acc[q][k];
+                    if (sx) v *= scale;
+                    if (bias) v += bf16_to_f32(bias[n + k]);
+                    store_out(out, (size_t)m * N + n + k, v, out_f32);
+                }
+            }
+        }
+        return;
+    }
     const int elems = M * ncols;
     for (int e = threadIdx.x; e < elems; e += blockDim.x) {
         const int m = e / ncols;

@@ -325,3 +325,29 @@ def test_ring_kernels_wait_for_their_stage(all_functions):
         seen[family] = seen.get(family, 0) + 1
         _check_ring(ins, ns, f"{family}<{', '.join(map(str, args))}>")
     assert set(seen) == {"rows_kernel", "fp8_rows_kernel", "tiled_kernel", "fp8_tiled_kernel"}, seen
+
+
+def test_no_kernel_uses_scratch():
+    # every kernel of the library keeps its state in registers and LDS: a
+    # register spill shows as a private segment in the code object metadata
+    for tool in ("llvm-objcopy", "llvm-readelf"):
+        if not os.path.exists(os.path.join(LLVM, tool)):
+            pytest.skip(f"{tool} not installed")
+    if not os.path.exists(skg.library_path()):
+        lib_build.build()
+    with tempfile.TemporaryDirectory() as d:
+        fb = os.path.join(d, "fatbin")
+        subprocess.run([os.path.join(LLVM, "llvm-objcopy"), "--dump-section",
+                        f".hip_fatbin={fb}", skg.library_path()], check=True)
+        kernels, spilled = 0, []
+        for n, co in enumerate(_gfx950_objects(open(fb, "rb").read())):
+            path = os.path.join(d, f"co{n}.o")
+            open(path, "wb").write(co)
+            notes = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", path],
+                                   check=True, capture_output=True, text=True).stdout
+            names = re.findall(r"\.symbol:\s+(\S+)", notes)
+            sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", notes)
+            assert len(names) == len(sizes), "one private segment size per kernel"
+            kernels += len(names)
+            spilled += [nm for nm, sz in zip(names, sizes) if int(sz) > 0]
+    assert kernels > 1000 and not spilled, spilled[:5]

@@ -304,3 +304,29 @@ def test_fp8_default_rule_plans_within_tolerance(skg, shape, kind):
     out = _run(skg, None, xq.to(DEV), wq.to(DEV), bias.to(DEV), **_scales(mode, s1, s2))
     ok, msg = tolerance.check(out, ref, K)
     assert ok, f"{shape} plan {q}: {msg}"
+
+
+@pytest.mark.parametrize("mode", ("fp8_tensor", "fp8_mx"))
+def test_fp8_reductions_agree_bitwise(skg, mode):
+    # last-arriver and second-kernel sums of the FP8 split-K and tiled
+    # kernels add the same partials in the same order (and apply the
+    # per-tensor scale product once, after the sum); N % 4 == 0 takes the
+    # 16-byte coherent partials, N = 130 the per-float ones
+    for (M, N, K) in ((16, 4096, 4096), (64, 1024, 2048), (7, 130, 2048), (128, 512, 4096)):
+        xq, wq, s1, s2 = gen.fp8_inputs(M, N, K, mode, seed=M + N)
+        xd, wd = xq.to(DEV), wq.to(DEV)
+        bias = (torch.randn(N, generator=torch.Generator().manual_seed(N)) * 0.5).to(torch.bfloat16).to(DEV)
+        dt = skg.DTYPE_FP8 if mode == "fp8_tensor" else skg.DTYPE_FP8_MX
+        for kind, T, cols, S, D, fl in ((skg.KIND_SPLITK, 256, 1, 4, 2, 0),
+                                        (skg.KIND_TILED, 256, 2, 4, 3, 0),
+                                        (skg.KIND_TILED, 256, 4, 2, 3, skg.FLAG_TILED_WIDE)):
+            outs = []
+            for red in (skg.REDUCE_LAST, skg.REDUCE_KERNEL):
+                try:
+                    plan = skg.plan_complete(M, N, K, skg.make_plan(kind, T, cols, S, D, red, flags=fl), dt)
+                except skg.SkinnyGemmError:
+                    break
+                outs.append(_run(skg, plan, xd, wd, bias, **_scales(mode, s1, s2)))
+            if len(outs) == 2:
+                assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), \
+                    (mode, M, N, K, kind, S)

@@ -243,16 +243,26 @@ def test_runs_are_bitwise_deterministic(skg):
 
 def test_reductions_agree_bitwise(skg):
     # the in-kernel last-arriver sum and the second-kernel sum add the same
-    # partials in the same order
-    for (M, N, K) in ((8, 256, 7168), (64, 576, 7168), (5, 100, 2880)):
+    # partials in the same order, on the split-K and the tiled kernels; N % 4
+    # == 0 takes the 16-byte coherent partials, N = 130 the per-float ones
+    for (M, N, K) in ((8, 256, 7168), (64, 576, 7168), (5, 100, 2880), (7, 130, 2880),
+                      (128, 1024, 2048), (33, 4096, 1024)):
         x, w, b = gen.bf16_inputs(M, N, K, True, seed=K + M)
         xd, wd, bd = _dev(x, w, b)
-        mt = (M + 15) // 16
-        outs = []
-        for red in (skg.REDUCE_LAST, skg.REDUCE_KERNEL):
-            plan = skg.make_plan(skg.KIND_SPLITK, 128, cols=1, splits=7, depth=2, reduce=red)
-            outs.append(_run(skg, xd, wd, bd, plan))
-        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), (M, N, K, mt)
+        for kind, T, cols, S, D, fl in ((skg.KIND_SPLITK, 128, 1, 7, 2, 0),
+                                        (skg.KIND_TILED, 256, 4, 4, 3, 0),
+                                        (skg.KIND_TILED, 256, 2, 3, 3, skg.FLAG_TILED_WIDE)):
+            outs = []
+            for red in (skg.REDUCE_LAST, skg.REDUCE_KERNEL):
+                plan = skg.make_plan(kind, T, cols=cols, splits=S, depth=D, reduce=red, flags=fl)
+                try:
+                    plan = skg.plan_complete(M, N, K, plan)
+                except skg.SkinnyGemmError:
+                    break
+                outs.append(_run(skg, xd, wd, bd, plan))
+            if len(outs) == 2:
+                assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), \
+                    (M, N, K, kind, S)
 
 
 def test_output_guard_bands_untouched(skg):
