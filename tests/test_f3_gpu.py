@@ -162,6 +162,14 @@ def _quant_plans(skg, M, N, K):
         plans.append(("tiled_s2", p))
     except skg.SkinnyGemmError:
         pass
+    # whole-row ring, quantising x from LDS (where its bf16 stages fit)
+    for (T, R, NS, fl) in ((256, 16, 4, skg.FLAG_ROWS_HALF), (256, 8, 4, 0), (512, 16, 3, 0)):
+        p = skg.make_plan(skg.KIND_ROWS, T, R, depth=NS, flags=fl)
+        try:
+            skg.plan_complete(M, N, K, p, skg.DTYPE_FP8)
+        except skg.SkinnyGemmError:
+            continue
+        plans.append((f"rows_t{T}_c{R}_ns{NS}_f{fl}", p))
     return plans
 
 
