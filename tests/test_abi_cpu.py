@@ -466,13 +466,16 @@ BF16 = [p for p in configs.all_points() if p.dtype == "bf16"]
 def test_default_rule_without_table(lib, p):
     # a made-up 200-CU device never uses the MI355X table: the pages' rule
     # (dot product for M <= 4 or K < 2048, here also up to 16 rows at
-    # N <= 512 with x of at most 192 KB), else the tiled kernel (split-K only
-    # where K is not a multiple of 32)
+    # N <= 512 with x of at most 192 KB), then the whole-row ring from 5 to
+    # 32 rows, else the tiled kernel (split-K only where K is not a multiple
+    # of 32)
     q = skg.plan_on(p.M, p.N, p.K, 200)
     if p.M > 128:
         want = skg.KIND_TILED  # above 128 rows only the tiled kernel runs
     elif p.M <= 4 or p.K < 2048 or (p.M <= 16 and p.N <= 512 and p.M * p.K <= 98304):
         want = skg.KIND_DOT
+    elif p.M <= 32 and 2 * -(-p.N // 8) >= 200 and p.M * p.K <= 114688:
+        want = skg.KIND_ROWS  # the whole-row ring: 8-column groups fill half the CUs, x <= 224 KB
     else:
         want = skg.KIND_TILED if p.K % 32 == 0 else skg.KIND_SPLITK
     assert q.kind == want and q.from_table == 0
@@ -504,6 +507,25 @@ def test_default_rule_details(lib):
     assert (q.kind, q.cols) == (skg.KIND_DOT, 1)  # 2 columns would leave 384 < 510 workgroups
     # past the x bound of the small-N rule: the tiled kernel
     assert skg.plan_on(16, 512, 7168, 255).kind == skg.KIND_TILED
+    # bf16 from 5 to 32 rows: the whole-row ring when its 8-column groups
+    # fill half the CUs and M * K <= 114688 (x <= 224 KB); columns 8, 12 (up
+    # to 16 rows) or 16, the fewest on the busiest CU (tie: 8 up to 8 rows,
+    # else the most); half-width stages with two groups per CU or above 16
+    # rows.  Off-table shapes at 256 CUs take the rule too.
+    def ring(M, N, K, cus):
+        q = skg.plan_on(M, N, K, cus)
+        assert q.kind == skg.KIND_ROWS and (q.threads, q.depth) == (256, 4) and q.from_table == 0, q
+        return q.cols, q.flags
+    half = skg.FLAG_ROWS_HALF
+    assert ring(8, 4096, 4096, 256) == (8, half)      # tie 8/16, two groups per CU
+    assert ring(16, 4096, 4096, 256) == (16, 0)       # tie above 8 rows, one per CU
+    assert ring(12, 3072, 5120, 256) == (12, 0)       # 12 columns fill the CUs once
+    assert ring(16, 4096, 7168, 256) == (16, 0)       # M * K = 114688: at the bound
+    assert ring(24, 2048, 4096, 256) == (8, half)     # above 16 rows: no 12, half-width
+    assert ring(8, 4096, 4096, 255) == (8, half)      # 24 columns on the busiest CU, as 12
+    assert skg.plan_on(20, 4096, 7168, 256).kind == skg.KIND_TILED  # x 280 KB
+    assert skg.plan_on(33, 4096, 2048, 256).kind == skg.KIND_TILED  # past 32 rows
+    assert skg.plan_on(8, 768, 4096, 256).kind == skg.KIND_TILED    # 96 groups of 8
     assert skg.plan_on(12, 512, 7168, 255).kind == skg.KIND_DOT
     # FP8 from 3 to 32 rows: the whole-row ring when the 8-column groups
     # reach a quarter of the CUs (all of them at 3-4 rows, else the dot
@@ -545,9 +567,10 @@ def test_default_rule_details(lib):
 
 def test_split_count_follows_cu_count(lib):
     # the default rule (no table below 256 CUs) sizes the grid to the device
+    # (40 rows: past the whole-row ring's 32)
     for K, kind in ((7168, skg.KIND_TILED), (7176, skg.KIND_SPLITK)):
-        small = skg.plan_on(16, 1024, K, 64)
-        big = skg.plan_on(16, 1024, K, 200)
+        small = skg.plan_on(40, 1024, K, 64)
+        big = skg.plan_on(40, 1024, K, 200)
         assert small.kind == big.kind == kind and small.from_table == big.from_table == 0
         assert small.splits < big.splits
         assert small.grid >= 48 and big.grid >= 150

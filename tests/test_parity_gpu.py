@@ -560,22 +560,27 @@ def test_binding_side_stream_matches_current_stream(skg):
     assert torch.equal(got32.view(torch.int32), ref32.view(torch.int32))
 
 
-# shapes off the dispatch table, one per branch of the default rule: the
-# dot kernel with 4 and with 1 column(s), the small-N dot kernel above 4
-# rows, the tiled kernel, and split-K for K not a multiple of 32
-DEFAULT_RULE_SHAPES = [(2, 2048, 1024), (3, 300, 2048), (12, 256, 3072), (6, 1536, 2048),
-                       (24, 640, 2048), (8, 700, 2056)]
+# shapes off the dispatch table, one or more per branch of the default rule
+# at 256 CUs: the dot kernel with 4 and with 1 column(s), the small-N dot
+# kernel above 4 rows, the whole-row ring (5 to 32 rows, 8-column groups
+# filling half the CUs, M * K <= 114688; ragged K, 12 columns, half-width
+# stages above 16 rows), the tiled kernel (too few groups, x past the bound,
+# past 32 rows), and split-K for K not a multiple of 32
+DEFAULT_RULE_SHAPES = [((2, 2048, 1024), "dot"), ((3, 300, 2048), "dot"), ((12, 256, 3072), "dot"),
+                       ((6, 1536, 2048), "rows"), ((16, 2048, 2056), "rows"),
+                       ((12, 3072, 2048), "rows"), ((32, 1024, 2048), "rows"),
+                       ((24, 640, 2048), "tiled"), ((18, 1024, 7168), "tiled"),
+                       ((40, 2048, 2048), "tiled"), ((8, 700, 2056), "splitk")]
 
 
-@pytest.mark.parametrize("shape", DEFAULT_RULE_SHAPES, ids=str)
-def test_default_rule_plans_within_tolerance(skg, shape):
+@pytest.mark.parametrize("shape,kind", DEFAULT_RULE_SHAPES, ids=str)
+def test_default_rule_plans_within_tolerance(skg, shape, kind):
     M, N, K = shape
     q = skg.plan(M, N, K)
     assert q.from_table == 0
-    if M <= 4 or (N <= 512 and M * K <= 98304):
-        assert q.kind == skg.KIND_DOT
-    else:
-        assert q.kind == (skg.KIND_TILED if K % 32 == 0 else skg.KIND_SPLITK)
+    want = {"dot": skg.KIND_DOT, "rows": skg.KIND_ROWS, "tiled": skg.KIND_TILED,
+            "splitk": skg.KIND_SPLITK}[kind]
+    assert q.kind == want, q
     x, w, b = gen.bf16_inputs(M, N, K, True, seed=M + N + K)
     ref = oracle.gemm_bf16(gen.bits16(x), gen.bits16(w), gen.bits16(b), threads=16)
     out = _run(skg, *_dev(x, w, b), None)
