@@ -217,15 +217,23 @@ constexpr bool fp8q_mfma_built(int MT, int NB, int D) {
 // accumulators and one stage's fragments fit 200 VGPRs, the ring fits
 // 144 KB and holds the epilogue tile, the vmcnt wait fits 6 bits, and each
 // operand's scales take at most one load per wave.
-constexpr int fp8_tiled_scale_bytes(int tiles, int U, bool mx) {
-    return mx ? (tiles * 16 * 4 * U + 255) / 256 * 256 : 0;
-}
-constexpr size_t fp8_tiled_stage_bytes(int MT, int NB, int U, bool mx) {
-    return (size_t)(MT + NB) * 2048 * U + fp8_tiled_scale_bytes(MT, U, mx) +
-           fp8_tiled_scale_bytes(NB, U, mx);
+constexpr size_t fp8_tiled_stage_bytes(int MT, int NB, int U) {
+    return (size_t)(MT + NB) * 2048 * U;
 }
 constexpr size_t fp8_tiled_lds_bytes(int MT, int NB, int NS, int U) {
-    return (size_t)NS * fp8_tiled_stage_bytes(MT, NB, U, true) + 1024;
+    return (size_t)NS * fp8_tiled_stage_bytes(MT, NB, U) + 1024;
+}
+// MX: the e8m0 bytes of a workgroup's K chunk (k_chunk / 32 per row) sit
+// after the ring, rows SR bytes apart with SR = 16 mod 32 (the 16 rows of one
+// fragment read then hit 16 different banks), x rows then W rows, each
+// area a whole number of KB.
+constexpr int fp8_tiled_scale_stride(int k_chunk) { return (k_chunk / 32 + 47) / 32 * 32 - 16; }
+constexpr size_t fp8_tiled_scale_area(int rows, int k_chunk) {
+    return ((size_t)rows * fp8_tiled_scale_stride(k_chunk) + 1023) / 1024 * 1024;
+}
+constexpr size_t fp8_tiled_mx_lds_bytes(int MT, int NB, int NS, int U, int k_chunk) {
+    return fp8_tiled_lds_bytes(MT, NB, NS, U) + fp8_tiled_scale_area(MT * 16, k_chunk) +
+           fp8_tiled_scale_area(NB * 16, k_chunk);
 }
 constexpr bool fp8_tiled_built(int MT, int NB, int WM, int NS, int U) {
     return (WM == 1 || WM == 2 || WM == 4) && MT % WM == 0 && NB % (4 / WM) == 0 &&

@@ -17,9 +17,14 @@
 //  * the MFMA operand of lane l (measured on the MI355X): row l % 16, the
 //    chunks at K offsets 16g and 64 + 16g of the step (g = l / 16), and the
 //    e8m0 byte of the step's 32-element block g;
-//  * MX mode streams the scale bytes of the stage into the ring as well
-//    (4 bytes per lane, rows x 4U bytes per operand); rows past M or N read
-//    zero codes and a zero exponent, which contribute exactly 0.
+//  * MX mode loads the e8m0 bytes of the workgroup's whole K chunk once,
+//    before the ring, in 16-byte pieces into an area after it (loads
+//    complete in issue order, so the wait for the first stage covers
+//    them).  Streaming 4 bytes of each row per stage cost 1.7 us at M = 128,
+//    K = N = 4096: every such load touched a cache line per two lanes.
+//    Rows past M or N read zero codes and a zero exponent, which contribute
+//    exactly 0; blocks past the chunk's end take exponent 127 (x 1) against
+//    their zero codes.
 #include "device_common.h"
 #include "internal.h"
 #include "lds_limit.h"
@@ -30,12 +35,6 @@ namespace skg {
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-// Buffer-to-LDS load of 4 bytes per lane (kept out of the kernel body for
-// the reason given at lds_load16).
-__device__ __forceinline__ void lds_load4(Rsrc r, unsigned char *dst, unsigned off) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 4, off, 0, 0, 0);
-}
-
 // chunk swizzle for rows of CPR 16-byte chunks (rows sharing a 256-byte
 // bank window get different keys)
 template <int CPR>
@@ -58,14 +57,11 @@ __global__ void __launch_bounds__(256)
     constexpr int NBW = NB / WN;
     constexpr int CPR = 8 * U;                 // 16-byte chunks per row and stage
     constexpr int BLKB = 16 * 128 * U;         // bytes per block
-    constexpr int XSB = fp8_tiled_scale_bytes(MT, U, MX);  // x scale bytes per stage
-    constexpr int WSB = fp8_tiled_scale_bytes(NB, U, MX);
-    constexpr int STAGE = (MT + NB) * BLKB + XSB + WSB;
+    constexpr int STAGE = (MT + NB) * BLKB;
     constexpr int XI = MT * 2 * U, WI = NB * 2 * U;   // data instructions per stage
     constexpr int XPW = (XI + 3) / 4, WPW = (WI + 3) / 4;
-    constexpr int BPW = XPW + WPW + (MX ? 2 : 0);
+    constexpr int BPW = XPW + WPW;
     static_assert(MT % WM == 0 && NB % WN == 0, "wave arrangement");
-    static_assert(!MX || (MT * U <= 16 && NB * U <= 16), "one scale load per wave and operand");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     __shared__ unsigned is_last;
     unsigned char *const pad = lds_raw + NS * STAGE;  // 1 KB that padding loads fill
@@ -114,16 +110,30 @@ __global__ void __launch_bounds__(256)
         woff[i] = (q < WI && row < ncols) ? (unsigned)row * rowb + (unsigned)c * 16u : kOOB;
         wstep[i] = c >> 3;
     }
-    // MX scale loads: instruction `wave` of each operand covers rows
-    // 64/U * wave .. (lane p: row p / U, dword p % U of the stage's 4U bytes)
-    const int srow_l = (64 / U) * wave + lane / U;
-    const int sdw = lane % U;
-    const bool xs_real = MX && wave * 256 < XSB;
-    const bool ws_real = MX && wave * 256 < WSB;
-    const unsigned xsoff =
-        (xs_real && srow_l < Mb) ? (unsigned)srow_l * srow + (unsigned)sdw * 4u : kOOB;
-    const unsigned wsoff =
-        (ws_real && srow_l < ncols) ? (unsigned)srow_l * srow + (unsigned)sdw * 4u : kOOB;
+    // MX: the chunk's scale bytes.  Slot q (16 bytes) of an area is piece
+    // q % (SR / 16) of row q / (SR / 16); the pieces past a row's k_chunk / 32
+    // bytes (the row's padding) load zeros.  Each area is a whole number of
+    // KB, so no instruction writes past its own.
+    const int kch = min(K, kbeg + k_chunk) - kbeg;  // this chunk's K
+    const int SR = fp8_tiled_scale_stride(k_chunk);
+    unsigned char *const xsa = pad + 1024;
+    unsigned char *const wsa = xsa + fp8_tiled_scale_area(MT * 16, k_chunk);
+    if constexpr (MX) {
+        const int spr = SR / 16;                  // slots per row
+        const int live = (k_chunk / 32 + 15) / 16;  // slots of a row that hold bytes
+        const unsigned kb = (unsigned)kbeg / 32u;
+        auto load_area = [&](Rsrc r, unsigned char *area, int rows, int real_rows) {
+            const int slots = rows * spr;
+            for (int b = wave * 64; b < slots; b += 256) {  // wave-uniform trip count
+                const int q = b + lane, row = q / spr, c = q - row * spr;
+                const bool ok = q < slots && c < live && row < real_rows;
+                lds_load16<kCacheDefault>(r, area + b * 16,
+                                          ok ? (unsigned)row * srow + kb + 16u * (unsigned)c : kOOB);
+            }
+        };
+        load_area(xer, xsa, MT * 16, Mb);
+        load_area(wer, wsa, NB * 16, ncols);
+    }
 
     const int rot = j % nstages;
     auto issue = [&](int slot, int stage) {
@@ -147,13 +157,6 @@ __global__ void __launch_bounds__(256)
                 q < WI ? base + (MT + q / (2 * U)) * BLKB + (q % (2 * U)) * 1024 : pad;
             lds_load16<kCacheStream>(wr, dst, live ? woff[i] + k0 : kOOB);
         }
-        if constexpr (MX) {
-            const bool live = pos * U + sdw < nsteps;
-            const unsigned kb = k0 >> 5;
-            unsigned char *sb = base + (MT + NB) * BLKB;
-            lds_load4(xer, xs_real ? sb + wave * 256 : pad, live ? xsoff + kb : kOOB);
-            lds_load4(wer, ws_real ? sb + XSB + wave * 256 : pad, live ? wsoff + kb : kOOB);
-        }
     };
 
     f32x4 acc[MTW][NBW];
@@ -163,7 +166,7 @@ __global__ void __launch_bounds__(256)
         for (int b = 0; b < NBW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int fr = lane & 15, fg = lane >> 4;
-    auto compute = [&](int slot) {
+    auto compute = [&](int slot, int pos) {
         const unsigned char *stg = lds_raw + slot * STAGE;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -171,6 +174,11 @@ __global__ void __launch_bounds__(256)
             const int o1 = fr * (CPR * 16) + (((8 * u + 4 + fg) ^ swz<CPR>(fr)) * 16);
             i32x8 af[MTW], bf[NBW];
             int as[MTW], bs[NBW];
+            // this lane's 32-element block of the chunk, and whether it lies
+            // inside the chunk's K
+            const int blk32 = 4 * (pos * U + u) + fg;
+            const bool sl = 32 * blk32 < kch;
+            const int sc = sl ? blk32 : 0;  // every scale read stays inside its row
 #pragma unroll
             for (int a = 0; a < MTW; ++a) {
                 const unsigned char *blk = stg + (wm * MTW + a) * BLKB;
@@ -178,9 +186,12 @@ __global__ void __launch_bounds__(256)
                 const u32x4 p1 = *reinterpret_cast<const u32x4 *>(blk + o1);
                 af[a] = i32x8{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w,
                               (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
-                as[a] = MX ? (int)stg[(MT + NB) * BLKB + ((wm * MTW + a) * 16 + fr) * 4 * U +
-                                      4 * u + fg]
-                           : 127;
+                if constexpr (MX) {
+                    const int v = xsa[((wm * MTW + a) * 16 + fr) * SR + sc];  // always in range
+                    as[a] = sl ? v : 127;
+                } else {
+                    as[a] = 127;
+                }
             }
 #pragma unroll
             for (int b = 0; b < NBW; ++b) {
@@ -189,9 +200,12 @@ __global__ void __launch_bounds__(256)
                 const u32x4 p1 = *reinterpret_cast<const u32x4 *>(blk + o1);
                 bf[b] = i32x8{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w,
                               (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
-                bs[b] = MX ? (int)stg[(MT + NB) * BLKB + XSB +
-                                      ((wn * NBW + b) * 16 + fr) * 4 * U + 4 * u + fg]
-                           : 127;
+                if constexpr (MX) {
+                    const int v = wsa[((wn * NBW + b) * 16 + fr) * SR + sc];
+                    bs[b] = sl ? v : 127;
+                } else {
+                    bs[b] = 127;
+                }
             }
 #pragma unroll
             for (int a = 0; a < MTW; ++a)
@@ -215,7 +229,8 @@ __global__ void __launch_bounds__(256)
         // in flight while they run.  The wait above still counts NS - 2
         // stages issued after the one it waits for.
         issue((st + NS - 1) % NS, st + NS - 1);
-        compute(st % NS);
+        const int cpos = st + rot < nstages ? st + rot : st + rot - nstages;  // as issue()
+        compute(st % NS, cpos);
     }
     wait_vmcnt_lds<0>();  // no load to LDS outlives the loop
 
@@ -274,11 +289,15 @@ typedef int (*Fp8TiledLaunch)(const SkgPlan &, const Fp8Args &, float *, unsigne
 template <int MT, int NB, int WM, int NS, int U, bool MX>
 int launch_fp8_tiled_t(const SkgPlan &p, const Fp8Args &a, float *ws, unsigned *tickets, int M,
                        int N, int K, hipStream_t stream) {
-    const size_t lds_bytes = fp8_tiled_lds_bytes(MT, NB, NS, U);
+    // MX adds the chunk's scale bytes (the planner checked the total); the
+    // limit is raised once per device to the most any chunk may take
+    const size_t lds_bytes = MX ? fp8_tiled_mx_lds_bytes(MT, NB, NS, U, p.k_chunk)
+                                : fp8_tiled_lds_bytes(MT, NB, NS, U);
+    if (lds_bytes > (size_t)kTiledMaxLds) return (int)hipErrorInvalidConfiguration;
     static std::atomic<unsigned long long> lds_set{0};  // devices whose limit is set
     const hipError_t attr = allow_dynamic_lds(
-        reinterpret_cast<const void *>(&fp8_tiled_kernel<MT, NB, WM, NS, U, MX>), lds_bytes,
-        lds_set);
+        reinterpret_cast<const void *>(&fp8_tiled_kernel<MT, NB, WM, NS, U, MX>),
+        MX ? (size_t)kTiledMaxLds : lds_bytes, lds_set);
     if (attr != hipSuccess) return (int)attr;
     hipLaunchKernelGGL((fp8_tiled_kernel<MT, NB, WM, NS, U, MX>), dim3(p.grid), dim3(256),
                        lds_bytes, stream, (const uint8_t *)a.x, (const uint8_t *)a.W,

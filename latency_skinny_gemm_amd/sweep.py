@@ -152,6 +152,14 @@ def sweep_point_fp8(skg, torch, M, N, K, pool_bytes, reps, stream, log):
     for p in fp8_candidates(skg, M, N, K):
         per_mode = {}
         for mname, sc in modes.items():
+            if mname == "mx":
+                # MX plans must also fit the scale bytes (tiled plans hold a
+                # K chunk's worth in LDS): the others time per-tensor only
+                try:
+                    skg.plan_complete(M, N, K, p, skg.DTYPE_FP8_MX)
+                except skg.SkinnyGemmError:
+                    per_mode[mname] = None
+                    continue
             def calls(p=p, sc=sc):
                 for s in range(slots):
                     rc = L.skinny_gemm_fp8_planned(X[s].data_ptr(), W[s].data_ptr(), None,
@@ -181,16 +189,19 @@ def sweep_point_fp8(skg, torch, M, N, K, pool_bytes, reps, stream, log):
                 del gr
             times.sort()
             per_mode[mname] = times[len(times) // 2]
-        results.append((per_mode["tensor"] + per_mode["mx"], per_mode, p))
+        results.append((per_mode["tensor"] + (per_mode["mx"] if per_mode["mx"] is not None
+                                               else float("inf")), per_mode, p))
     results.sort(key=lambda r: r[0])
     _, best_modes, best = results[0]
     rec = {"dtype": "fp8", "M": M, "N": N, "K": K, "slots": slots, "tiled": "ring2",
-           "mx_scales": "per_slot", "dot_wave1": "direct", "dot_reduce": "scatter",
+           "mx_scales": "per_slot", "mx_tiled": "chunk_scales", "dot_wave1": "direct",
+           "dot_reduce": "scatter",
            "best_us": round(max(best_modes.values()), 3),
            "best_us_tensor": round(best_modes["tensor"], 3), "best_us_mx": round(best_modes["mx"], 3),
            "best": plan_dict(best),
-           "candidates": [[round(t, 3), {k: round(v, 3) for k, v in pm.items()}, plan_dict(p)]
-                          for t, pm, p in results]}
+           "candidates": [[round(t, 3) if t != float("inf") else None,
+                           {k: (round(v, 3) if v is not None else None) for k, v in pm.items()},
+                           plan_dict(p)] for t, pm, p in results]}
     log.write(json.dumps(rec) + "\n")
     log.flush()
     kind = {1: "dot", 2: "splitk", 3: "tiled", 4: "rows"}[best.kind]
@@ -419,7 +430,11 @@ def emit_table(files, out_path=TABLE):
                 # FP8: one entry per scale mode, each from that mode's timing;
                 # MX timings count only where the scale bytes were cold too
                 per_key = [(key, us)] if key[0] != "fp8" else [(key, c[1]["tensor"])]
-                if key[0] == "fp8" and r.get("mx_scales") == "per_slot":
+                # (MX timings of tiled plans only since their scale bytes load
+                # once per K chunk)
+                if key[0] == "fp8" and r.get("mx_scales") == "per_slot" and \
+                        c[1].get("mx") is not None and \
+                        (plan["kind"] != 3 or r.get("mx_tiled") == "chunk_scales"):
                     per_key.append((("fp8_mx",) + key[1:], c[1]["mx"]))
                 for k, t in per_key:
                     timings.setdefault(k, {}).setdefault(ident, (plan, []))[1].append(t)

@@ -258,13 +258,21 @@ def _check_ring(ins, ns, tag):
                 loops.append((k - head, head, k, waits))
     assert loops, f"{tag}: no ring loop"
     _, head, back, waits = min(loops)
-    # inside the loop: no branch but the back-edge, no vector memory op but the
-    # ring's buffer-to-LDS loads
+    # inside the loop: no branch but the latch (the back-edge, which may be
+    # preceded by a conditional exit with only arithmetic after it), no
+    # vector memory op but the ring's buffer-to-LDS loads
     for j in range(head, back):
-        assert not _is_branch(texts[j]), f"{tag}: branch inside the ring loop at +{offs[j]:#x}"
+        if _is_branch(texts[j]):
+            exits = ins[j][2] is not None and ins[j][2] > offs[back]
+            plain = not any(_is_vmem(t) or _is_branch(t) or
+                            t.startswith(("ds_", "s_waitcnt", "s_barrier", "s_load", "s_buffer",
+                                          "s_store", "s_dcache"))
+                            for t in texts[j + 1:back])
+            assert exits and plain, f"{tag}: branch inside the ring loop at +{offs[j]:#x}"
         if _is_vmem(texts[j]):
             assert texts[j].startswith("buffer_load") and texts[j].endswith(" lds"), \
                 f"{tag}: '{texts[j]}' inside the ring loop"
+
     # each wait is followed, before the next wait or the back-edge, by the
     # stage's loads; all segments issue the same count, and nothing is issued
     # between the loop head and the first wait
@@ -294,6 +302,20 @@ def _check_ring(ins, ns, tag):
                 reach.add(a)
                 todo.append(a)
     assert 0 in reach, f"{tag}: the entry does not reach the ring loop"
+    # prologue blocks on a cycle among themselves: loops before the ring (the
+    # FP8 MX scale copies); the ring's own NS - 1 stages are straight-line
+    def on_cycle(a):
+        todo, seen_c = list(blocks[a][1]), set()
+        while todo:
+            b = todo.pop()
+            if b == a:
+                return True
+            if b in seen_c or b not in reach or b == head:
+                continue
+            seen_c.add(b)
+            todo.extend(blocks[b][1])
+        return False
+    cyclic = {a for a in reach if a != head and on_cycle(a)}
     seen, todo, arrive = set(), [(0, 0)], set()
     while todo:
         a, n = todo.pop()
@@ -305,11 +327,18 @@ def _check_ring(ins, ns, tag):
             arrive.add(n)
             continue
         end, succ = blocks[a]
+        m = n
         for j in range(a, end):
             if _is_vmem(texts[j]):
                 assert texts[j].startswith("buffer_load") and texts[j].endswith(" lds"), \
                     f"{tag}: '{texts[j]}' before the ring loop"
-        m = n + sum(1 for j in range(a, end) if _is_vmem(texts[j]))
+                if a not in cyclic:
+                    m += 1
+                else:
+                    # other copies to LDS (the MX scale bytes) must precede the
+                    # path's first ring load: the wait for the first stage
+                    # then covers them
+                    assert m == 0, f"{tag}: a copy to LDS after the ring's first load"
         for b in succ:
             if b in reach:  # other edges never reach the ring
                 todo.append((b, m))
