@@ -474,13 +474,19 @@ def test_default_rule_without_table(lib, p):
         want = skg.KIND_TILED  # above 128 rows only the tiled kernel runs
     elif p.M <= 4 or p.K < 2048 or (p.M <= 16 and p.N <= 512 and p.M * p.K <= 98304):
         want = skg.KIND_DOT
+    elif p.M <= 16 and p.N > 512 and 2 * -(-p.N // 8) < 200:
+        want = skg.KIND_DOT  # between N = 512 and the whole-row ring: 3 or 4 columns
     elif p.M <= 32 and 2 * -(-p.N // 8) >= 200 and p.M * p.K <= 114688:
         want = skg.KIND_ROWS  # the whole-row ring: 8-column groups fill half the CUs, x <= 224 KB
     else:
         want = skg.KIND_TILED if p.K % 32 == 0 else skg.KIND_SPLITK
     assert q.kind == want and q.from_table == 0
     _check_coverage(q, p.M, p.N, p.K)
-    if q.kind == skg.KIND_DOT:
+    if q.kind == skg.KIND_DOT and p.M >= 5 and p.N > 512 and p.K >= 2048:
+        # the band below the ring: 4 columns while N / 4 groups cover three
+        # quarters of the CUs, else 3
+        assert q.cols == (4 if 4 * -(-p.N // 4) >= 600 else 3), q
+    elif q.kind == skg.KIND_DOT:
         # the most columns per workgroup that leave two workgroups per CU
         c = next(c for c in (4, 2, 1) if c == 1 or -(-p.N // c) >= 400)
         assert q.cols == c, (q.cols, c)
@@ -525,7 +531,16 @@ def test_default_rule_details(lib):
     assert ring(8, 4096, 4096, 255) == (8, half)      # 24 columns on the busiest CU, as 12
     assert skg.plan_on(20, 4096, 7168, 256).kind == skg.KIND_TILED  # x 280 KB
     assert skg.plan_on(33, 4096, 2048, 256).kind == skg.KIND_TILED  # past 32 rows
-    assert skg.plan_on(8, 768, 4096, 256).kind == skg.KIND_TILED    # 96 groups of 8
+    # below that, from 5 to 16 rows above N = 512: the dot kernel with 4
+    # columns while N / 4 groups cover three quarters of the CUs, else 3,
+    # and one 16-byte vector of K per thread where the registers allow
+    q = skg.plan_on(8, 768, 4096, 256)
+    assert (q.kind, q.cols, q.threads, q.flags) == (skg.KIND_DOT, 4, 512, skg.FLAG_DOT2)
+    q = skg.plan_on(10, 704, 6144, 256)
+    assert (q.kind, q.cols, q.threads) == (skg.KIND_DOT, 3, 768)
+    q = skg.plan_on(12, 768, 7168, 256)
+    assert (q.kind, q.cols, q.threads) == (skg.KIND_DOT, 4, 448)  # two vectors: registers
+    assert skg.plan_on(24, 768, 4096, 256).kind == skg.KIND_TILED  # past 16 rows
     assert skg.plan_on(12, 512, 7168, 255).kind == skg.KIND_DOT
     # FP8 from 3 to 32 rows: the whole-row ring when the 8-column groups
     # reach a quarter of the CUs (all of them at 3-4 rows, else the dot

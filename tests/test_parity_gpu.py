@@ -562,15 +562,18 @@ def test_binding_side_stream_matches_current_stream(skg):
 
 # shapes off the dispatch table, one or more per branch of the default rule
 # at 256 CUs: the dot kernel with 4 and with 1 column(s), the small-N dot
-# kernel above 4 rows, the whole-row ring (5 to 32 rows, 8-column groups
+# kernel above 4 rows, the dot kernel with 3-4 columns between N = 512 and
+# the ring, the whole-row ring (5 to 32 rows, 8-column groups
 # filling half the CUs, M * K <= 114688; ragged K, 12 columns, half-width
 # stages above 16 rows), the tiled kernel (too few groups, x past the bound,
 # past 32 rows), and split-K for K not a multiple of 32
 DEFAULT_RULE_SHAPES = [((2, 2048, 1024), "dot"), ((3, 300, 2048), "dot"), ((12, 256, 3072), "dot"),
                        ((6, 1536, 2048), "rows"), ((16, 2048, 2056), "rows"),
                        ((12, 3072, 2048), "rows"), ((32, 1024, 2048), "rows"),
+                       ((8, 768, 4096), "dot"), ((10, 704, 6144), "dot"),
                        ((24, 640, 2048), "tiled"), ((18, 1024, 7168), "tiled"),
-                       ((40, 2048, 2048), "tiled"), ((8, 700, 2056), "splitk")]
+                       ((40, 2048, 2048), "tiled"), ((8, 700, 2056), "dot"),
+                       ((24, 640, 2056), "splitk")]
 
 
 @pytest.mark.parametrize("shape,kind", DEFAULT_RULE_SHAPES, ids=str)
