@@ -123,6 +123,12 @@ extern "C" {
 #define SKG_FLAG_ROWS_HALF 8 /* ROWS: stages of 256 K elements (512 bytes of each row)
                                instead of 512; room in LDS for more rows of x */
 
+#define SKG_FLAG_DOT_WFIRST 16 /* DOT (bf16, together with SKG_FLAG_DOT2, without
+                                 SKG_FLAG_DOT_XLDS): every W load is issued before
+                                 the first x load instead of in the compiler's
+                                 interleaved order.  Same arithmetic, same bits;
+                                 only the time differs, by shape. */
+
 #define SKG_MAX_M 512 /* above 128 rows only tiled plans (K % 32, FP8 K % 128) */
 
 /* FP8 scales (host struct; its pointers are DEVICE pointers).

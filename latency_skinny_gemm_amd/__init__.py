@@ -14,7 +14,7 @@ import torch
 __all__ = ["SkgPlan", "SkinnyGemmError", "gemm_bf16", "gemm_bf16_planned", "gemm_fp8",
            "gemm_fp8_planned", "plan", "plan_on",
            "plan_complete", "reserve", "release_all", "status_string", "library_path",
-           "KIND_DOT", "KIND_SPLITK", "KIND_TILED", "KIND_ROWS", "REDUCE_NONE", "REDUCE_LAST", "REDUCE_KERNEL", "FLAG_DOT2", "FLAG_TILED_WIDE", "FLAG_DOT_XLDS", "FLAG_ROWS_HALF",
+           "KIND_DOT", "KIND_SPLITK", "KIND_TILED", "KIND_ROWS", "REDUCE_NONE", "REDUCE_LAST", "REDUCE_KERNEL", "FLAG_DOT2", "FLAG_TILED_WIDE", "FLAG_DOT_XLDS", "FLAG_ROWS_HALF", "FLAG_DOT_WFIRST",
            "DTYPE_BF16", "DTYPE_FP8", "DTYPE_F32", "DTYPE_FP8_MX", "gemm_bf16_f32", "gemm_fp8_quant",
            "quant_e4m3"]
 
@@ -45,6 +45,7 @@ FLAG_DOT2 = 1
 FLAG_TILED_WIDE = 2
 FLAG_DOT_XLDS = 4
 FLAG_ROWS_HALF = 8
+FLAG_DOT_WFIRST = 16
 MAX_M = 512
 
 

@@ -84,6 +84,34 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// ---------------------------------------------------------------- epilogue operands
+// The bias does not depend on the main loop, so the kernels load it at the
+// start (the second-pass reduction also its FP8 per-tensor scales) and its
+// memory latency hides under the operand stream; loaded in the epilogue,
+// each value was one more round trip after the last product (0.1-0.6 us a
+// call, measured).  The loads go through buffer views: a null pointer gives
+// a zero-size view whose loads return 0 and touch no memory, and a column
+// n >= N, or live = false (kOOB), also returns 0 without touching memory.
+// In a ring kernel they are issued in the prologue, before the ring loop:
+// a load older than the ring's only makes the in-order vmcnt waits that
+// count the ring's loads stricter.
+// Callers keep testing the pointer before adding or multiplying: s + 0.0f
+// is not s when s = -0.0f.
+__device__ __forceinline__ Rsrc bias_rsrc(const uint16_t *bias, int N) {
+    return make_rsrc(bias, bias ? (unsigned)N * 2u : 0u);
+}
+// The bits are returned zero-extended in a dword: kept as 16-bit values,
+// the compiler packed pairs of them into one register right after the loads
+// and so waited for the loads there.
+__device__ __forceinline__ unsigned load_bias_bits(Rsrc br, int n, bool live = true) {
+    return __builtin_amdgcn_raw_buffer_load_b16(br, live ? (unsigned)n * 2u : kOOB, 0,
+                                                kCacheDefault);
+}
+__device__ __forceinline__ float load_scale(const float *p) {
+    return __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p, p ? 4u : 0u), 0u, 0, kCacheDefault));
+}
+
 // The final store of one output element: bf16 (one RNE rounding of the fp32
 // value) or, for fp32 outputs, the fp32 value itself.
 __device__ __forceinline__ void store_out(void *out, size_t i, float v, int out_f32) {

@@ -32,7 +32,19 @@ namespace skg {
 
 // W1: the workgroup is one wave (its own instantiation, so the multi-wave
 // kernels compile exactly as without it).
-template <int M, int C, int V, bool DOT2, bool W1>
+// WF (SKG_FLAG_DOT_WFIRST): the issue order of the loads.  Without it the
+// compiler orders them (it interleaves the W and x loads of successive
+// vectors and starts the first products while later x loads are still
+// being issued); with it every W load (the HBM stream, the longest latency)
+// and the bias load go first, pinned by a scheduling barrier, and the x
+// loads (from L2) and the products follow in the compiler's order.  Which
+// is faster depends on the shape (measured: W first gains up to 16 % at
+// 384 columns and 15-16 rows, and loses up to 7 % at 1-7 rows), so the
+// planner's table picks per shape.  The bias is loaded at the start with
+// WF and after the reductions without it: any other instruction in the
+// loads' scheduling region changed the compiler's order there (measured
+// 2-7 % slower at 5-12 rows).
+template <int M, int C, int V, bool DOT2, bool W1, bool WF>
 __global__ void __launch_bounds__((W1 ? 64 : dot_max_threads(M, C, V, DOT2)))
     dot_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
                const uint16_t *__restrict__ bias, void *__restrict__ out, int N, int K,
@@ -46,14 +58,32 @@ __global__ void __launch_bounds__((W1 ? 64 : dot_max_threads(M, C, V, DOT2)))
     const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
     const int K8 = K >> 3;
 
+    // The C*M sums end in a reduce-scatter over the wave (lane l ends with
+    // the total of index l >> (6 - L), index c*M + m) and then, across
+    // waves, in thread t < C*M.  So the thread that stores index i, and the
+    // bias column n0 + i / M it adds, are known from the start (WF loads it
+    // then).
+    constexpr int CM = C * M;
+    constexpr int L = CM <= 1 ? 0 : CM <= 2 ? 1 : CM <= 4 ? 2 : CM <= 8 ? 3 : CM <= 16 ? 4 : CM <= 32 ? 5 : 6;
+    static_assert(CM <= 64, "one value index per lane at most");
+    const int eidx = W1 ? (t & 63) >> (6 - L) : t;
+    auto load_bias = [&]() {
+        return load_bias_bits(bias_rsrc(bias, N), n0 + eidx / M, eidx < CM);
+    };
+
     u32x4 wv[C][V];
     u32x4 xv[M][V];
+    unsigned bb = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const int v = t + i * T;
         const unsigned off = v < K8 ? (unsigned)v * 16u : kOOB;
 #pragma unroll
         for (int c = 0; c < C; ++c) wv[c][i] = load16<kCacheStream>(wr, off + (unsigned)c * rowb);
+    }
+    if constexpr (WF) {
+        bb = load_bias();
+        __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = 0; i < V; ++i) {
@@ -80,9 +110,6 @@ __global__ void __launch_bounds__((W1 ? 64 : dot_max_threads(M, C, V, DOT2)))
     // Reduce-scatter the C*M per-lane sums over the wave (padded with zeros
     // to a power of two): lane l ends with the wave's total of index
     // l >> (6 - L), index c*M + m; the first lane of each index group owns it.
-    constexpr int CM = C * M;
-    constexpr int L = CM <= 1 ? 0 : CM <= 2 ? 1 : CM <= 4 ? 2 : CM <= 8 ? 3 : CM <= 16 ? 4 : CM <= 32 ? 5 : 6;
-    static_assert(CM <= 64, "one value index per lane at most");
     float part[1 << L];
 #pragma unroll
     for (int i = 0; i < (1 << L); ++i) part[i] = i < CM ? acc[i / M][i % M] : 0.0f;
@@ -103,7 +130,7 @@ __global__ void __launch_bounds__((W1 ? 64 : dot_max_threads(M, C, V, DOT2)))
             const int n = n0 + c;
             if (n < N) {
                 float s = 0.0f + total;
-                if (bias) s += bf16_to_f32(bias[n]);
+                if (bias) s += bf16_to_f32(WF ? bb : bias[n]);
                 store_out(out, (size_t)m * N + n, s, out_f32);
             }
         }
@@ -117,7 +144,7 @@ __global__ void __launch_bounds__((W1 ? 64 : dot_max_threads(M, C, V, DOT2)))
         const int n = n0 + c;
         float s = ordered_sum<8>(nw, [&](int w) { return red[w][t]; });
         if (n < N) {
-            if (bias) s += bf16_to_f32(bias[n]);
+            if (bias) s += bf16_to_f32(WF ? bb : bias[n]);
             store_out(out, (size_t)m * N + n, s, out_f32);
         }
     }
@@ -156,6 +183,15 @@ __global__ void __launch_bounds__(xlds_max_threads(M, CW, V))
     constexpr int K8 = V * 64;                     // K / 8
     const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
     const Rsrc wr = make_rsrc(W + (size_t)(ncols ? n0 : 0) * K, (unsigned)ncols * rowb);
+
+    // 0. the bias of the column this lane stores (index idx of step 5's
+    // reduce-scatter), ahead of every operand load (no load without a bias)
+    constexpr int CM = CW * M;
+    constexpr int L = CM <= 1 ? 0 : CM <= 2 ? 1 : CM <= 4 ? 2 : CM <= 8 ? 3 : CM <= 16 ? 4 : CM <= 32 ? 5 : 6;
+    static_assert(CM <= 64, "one value index per lane at most");
+    const int idx = lane >> (6 - L);
+    unsigned bb = 0;
+    if (bias) bb = load_bias_bits(bias_rsrc(bias, N), n0 + idx / M, idx < CM && idx / M < ncols);
 
     // 1. x -> LDS: wave w moves chunks q0 ... q0 + 63 for q0 = 64w, 64w + T,
     // ... below M * K8 (both sides contiguous; M * K8 is a multiple of 64)
@@ -199,20 +235,16 @@ __global__ void __launch_bounds__(xlds_max_threads(M, CW, V))
         }
 
     // 5. reduce-scatter over the wave; lane l owns index l >> (6 - L), c*M + m
-    constexpr int CM = CW * M;
-    constexpr int L = CM <= 1 ? 0 : CM <= 2 ? 1 : CM <= 4 ? 2 : CM <= 8 ? 3 : CM <= 16 ? 4 : CM <= 32 ? 5 : 6;
-    static_assert(CM <= 64, "one value index per lane at most");
     float part[1 << L];
 #pragma unroll
     for (int i = 0; i < (1 << L); ++i) part[i] = i < CM ? acc[i / M][i % M] : 0.0f;
     const float total = wave_reduce_scatter<L>(part);
-    const int idx = lane >> (6 - L);
     if ((lane & ((1 << (6 - L)) - 1)) == 0 && idx < CM) {
         const int c = idx / M, m = idx - (idx / M) * M;
         if (c < ncols) {
             const int n = n0 + c;
             float s = 0.0f + total;  // as the one-wave dot kernel: same bits
-            if (bias) s += bf16_to_f32(bias[n]);
+            if (bias) s += bf16_to_f32(bb);
             store_out(out, (size_t)m * N + n, s, out_f32);
         }
     }
@@ -223,77 +255,86 @@ namespace {
 typedef int (*DotLaunch)(const SkgPlan &, const void *, const void *, const void *, void *, int,
                          int, int, hipStream_t);
 
-template <int M, int C, int V, bool DOT2>
+template <int M, int C, int V, bool DOT2, bool WF>
 int launch_dot_t(const SkgPlan &p, const void *x, const void *W, const void *bias, void *out,
                  int N, int K, int out_f32, hipStream_t stream) {
     if constexpr (M <= kDotOneWaveMaxM) {
         if (p.threads == 64) {
-            hipLaunchKernelGGL((dot_kernel<M, C, V, DOT2, true>), dim3(p.grid), dim3(64), 0,
+            hipLaunchKernelGGL((dot_kernel<M, C, V, DOT2, true, WF>), dim3(p.grid), dim3(64), 0,
                                stream, (const uint16_t *)x, (const uint16_t *)W,
                                (const uint16_t *)bias, out, N, K, out_f32);
             return (int)hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((dot_kernel<M, C, V, DOT2, false>), dim3(p.grid), dim3(p.threads), 0, stream,
-                       (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)bias,
+    hipLaunchKernelGGL((dot_kernel<M, C, V, DOT2, false, WF>), dim3(p.grid), dim3(p.threads), 0,
+                       stream, (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)bias,
                        out, N, K, out_f32);
     return (int)hipGetLastError();
 }
 
 // Instantiated only where the per-thread registers fit (the planner applies
-// the same bound and never asks for the others).
-template <int M, int C, int V, bool DOT2>
+// the same bound and never asks for the others); the W-first order only
+// with the dot instruction (the planner rejects it without).
+template <int M, int C, int V, bool DOT2, bool WF>
 constexpr DotLaunch dot_entry() {
-    if constexpr (dot_regs(M, C, V, DOT2) <= kDotRegsMax)
-        return &launch_dot_t<M, C, V, DOT2>;
+    if constexpr (dot_regs(M, C, V, DOT2) <= kDotRegsMax && (DOT2 || !WF))
+        return &launch_dot_t<M, C, V, DOT2, WF>;
     else
         return nullptr;
 }
 
-template <int M, int C, bool DOT2>
+template <int M, int C, bool DOT2, bool WF>
 DotLaunch pick_v(int V) {
     switch (V) {
-    case 1: return dot_entry<M, C, 1, DOT2>();
-    case 2: return dot_entry<M, C, 2, DOT2>();
-    case 3: return dot_entry<M, C, 3, DOT2>();
-    case 4: return dot_entry<M, C, 4, DOT2>();
-    case 6: return dot_entry<M, C, 6, DOT2>();
-    case 7: return dot_entry<M, C, 7, DOT2>();
-    case 8: return dot_entry<M, C, 8, DOT2>();
-    case 12: return dot_entry<M, C, 12, DOT2>();
-    case 14: return dot_entry<M, C, 14, DOT2>();
-    case 16: return dot_entry<M, C, 16, DOT2>();
+    case 1: return dot_entry<M, C, 1, DOT2, WF>();
+    case 2: return dot_entry<M, C, 2, DOT2, WF>();
+    case 3: return dot_entry<M, C, 3, DOT2, WF>();
+    case 4: return dot_entry<M, C, 4, DOT2, WF>();
+    case 6: return dot_entry<M, C, 6, DOT2, WF>();
+    case 7: return dot_entry<M, C, 7, DOT2, WF>();
+    case 8: return dot_entry<M, C, 8, DOT2, WF>();
+    case 12: return dot_entry<M, C, 12, DOT2, WF>();
+    case 14: return dot_entry<M, C, 14, DOT2, WF>();
+    case 16: return dot_entry<M, C, 16, DOT2, WF>();
     default: return nullptr;
     }
 }
 
-template <int M>
-DotLaunch pick_c(int C, int V, bool dot2) {
-    if (C == 1) return dot2 ? pick_v<M, 1, true>(V) : pick_v<M, 1, false>(V);
-    if (C == 2) return dot2 ? pick_v<M, 2, true>(V) : pick_v<M, 2, false>(V);
-    if (C == 3) return dot2 ? pick_v<M, 3, true>(V) : pick_v<M, 3, false>(V);
-    if (C == 4) return dot2 ? pick_v<M, 4, true>(V) : pick_v<M, 4, false>(V);
-    return nullptr;
+template <int M, int C>
+DotLaunch pick_f(int V, bool dot2, bool wf) {
+    if (!dot2) return wf ? nullptr : pick_v<M, C, false, false>(V);
+    return wf ? pick_v<M, C, true, true>(V) : pick_v<M, C, true, false>(V);
 }
 
-DotLaunch pick(int M, int C, int V, bool dot2) {
+template <int M>
+DotLaunch pick_c(int C, int V, bool dot2, bool wf) {
+    switch (C) {
+    case 1: return pick_f<M, 1>(V, dot2, wf);
+    case 2: return pick_f<M, 2>(V, dot2, wf);
+    case 3: return pick_f<M, 3>(V, dot2, wf);
+    case 4: return pick_f<M, 4>(V, dot2, wf);
+    default: return nullptr;
+    }
+}
+
+DotLaunch pick(int M, int C, int V, bool dot2, bool wf) {
     switch (M) {
-    case 1: return pick_c<1>(C, V, dot2);
-    case 2: return pick_c<2>(C, V, dot2);
-    case 3: return pick_c<3>(C, V, dot2);
-    case 4: return pick_c<4>(C, V, dot2);
-    case 5: return pick_c<5>(C, V, dot2);
-    case 6: return pick_c<6>(C, V, dot2);
-    case 7: return pick_c<7>(C, V, dot2);
-    case 8: return pick_c<8>(C, V, dot2);
-    case 9: return pick_c<9>(C, V, dot2);
-    case 10: return pick_c<10>(C, V, dot2);
-    case 11: return pick_c<11>(C, V, dot2);
-    case 12: return pick_c<12>(C, V, dot2);
-    case 13: return pick_c<13>(C, V, dot2);
-    case 14: return pick_c<14>(C, V, dot2);
-    case 15: return pick_c<15>(C, V, dot2);
-    case 16: return pick_c<16>(C, V, dot2);
+    case 1: return pick_c<1>(C, V, dot2, wf);
+    case 2: return pick_c<2>(C, V, dot2, wf);
+    case 3: return pick_c<3>(C, V, dot2, wf);
+    case 4: return pick_c<4>(C, V, dot2, wf);
+    case 5: return pick_c<5>(C, V, dot2, wf);
+    case 6: return pick_c<6>(C, V, dot2, wf);
+    case 7: return pick_c<7>(C, V, dot2, wf);
+    case 8: return pick_c<8>(C, V, dot2, wf);
+    case 9: return pick_c<9>(C, V, dot2, wf);
+    case 10: return pick_c<10>(C, V, dot2, wf);
+    case 11: return pick_c<11>(C, V, dot2, wf);
+    case 12: return pick_c<12>(C, V, dot2, wf);
+    case 13: return pick_c<13>(C, V, dot2, wf);
+    case 14: return pick_c<14>(C, V, dot2, wf);
+    case 15: return pick_c<15>(C, V, dot2, wf);
+    case 16: return pick_c<16>(C, V, dot2, wf);
     default: return nullptr;
     }
 }
@@ -373,7 +414,8 @@ int launch_dot(const SkgPlan &p, const void *x, const void *W, const void *bias,
                int out_f32, int M, int N, int K, hipStream_t stream) {
     DotLaunch f = (p.flags & SKG_FLAG_DOT_XLDS)
                       ? pickx(M, p.cols / (p.threads / 64), p.depth)
-                      : pick(M, p.cols, p.depth, (p.flags & SKG_FLAG_DOT2) != 0);
+                      : pick(M, p.cols, p.depth, (p.flags & SKG_FLAG_DOT2) != 0,
+                             (p.flags & SKG_FLAG_DOT_WFIRST) != 0);
     if (!f) return (int)hipErrorInvalidConfiguration;
     return f(p, x, W, bias, out, N, K, out_f32, stream);
 }

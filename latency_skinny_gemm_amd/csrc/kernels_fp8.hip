@@ -383,7 +383,7 @@ __global__ void __launch_bounds__((QX ? 256 : fp8_mfma_max_threads(MT, NB, D, MX
     }
     if (S == 1 || reduce != SKG_REDUCE_LAST) return;
     last_arriver_reduce<2, 4>(ws, tickets, bias, out, out_f32, M, N, S, j, col0, ncols, &is_last,
-                        MX ? nullptr : sx, MX ? nullptr : sw);
+                              !MX, scale);
 }
 
 namespace {

@@ -72,6 +72,12 @@ __global__ void __launch_bounds__(NW * 64)
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
     const int n0 = blockIdx.x * R;
     const int ncols = min(R, N - n0);
+    // The epilogue's bias, loaded ahead of the ring: column n0 + t % R is
+    // the only one thread t stores (NW * 64 is a multiple of R).  Without a
+    // bias no load is issued.
+    static_assert((NW * 64) % R == 0, "a thread keeps its column");
+    unsigned bb = 0;
+    if (bias) bb = load_bias_bits(bias_rsrc(bias, N), n0 + t % R, t % R < ncols);
     const unsigned rowb = (unsigned)K;
     const Rsrc wr = make_rsrc(W + (size_t)n0 * K, (unsigned)ncols * rowb);
     const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
@@ -216,7 +222,7 @@ __global__ void __launch_bounds__(NW * 64)
         for (int w = 0; w < NW; ++w) s += red[((w * MT + m / 16) * 16 + m % 16) * 17 + c];
         if (!MX) s *= scale;
         const int n = n0 + c;
-        if (bias) s += bf16_to_f32(bias[n]);
+        if (bias) s += bf16_to_f32(bb);
         store_out(out, (size_t)m * N + n, s, out_f32);
     }
 }

@@ -89,6 +89,19 @@ __global__ void __launch_bounds__(256)
     const int nsteps = (min(K, kbeg + k_chunk) - kbeg) >> 7;  // K, k_chunk: multiples of 128
     const int nstages = (nsteps + U - 1) / U;
 
+    // The epilogue's bias (S == 1), loaded now: thread t stores columns
+    // col0 + 4 * (t % C4) + 0..3 of its rows.  Without a bias no load is
+    // issued (the extra loads cost about 1 % at these shapes).
+    constexpr int C4 = NB * 4;  // 4-column groups per row
+    static_assert(256 % C4 == 0, "a thread keeps its column group");
+    unsigned bb[4] = {0, 0, 0, 0};
+    if (bias && S == 1) {
+        const Rsrc br = bias_rsrc(bias, N);
+        const int c = (t % C4) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bb[q] = load_bias_bits(br, col0 + c + q);
+    }
+
     // data loads: instruction q fills part q % (2U) of block q / (2U)
     unsigned xoff[XPW], woff[WPW];
     int xstep[XPW], wstep[WPW];
@@ -249,7 +262,6 @@ __global__ void __launch_bounds__(256)
                     acc[a][b][i];
     __syncthreads();
     const float scale = MX ? 1.0f : sx[0] * sw[0];
-    constexpr int C4 = NB * 4;
     const bool vec = (N & 3) == 0;
     const bool coherent = reduce == SKG_REDUCE_LAST;  // partials read by the last arriver
     const PartialsVec pv = partials_vec(ws, M, N, S);
@@ -264,7 +276,7 @@ __global__ void __launch_bounds__(256)
             for (int q = 0; q < 4; ++q)
                 if (c + q < ncols) {
                     float o = MX ? v[q] : v[q] * scale;
-                    if (bias) o += bf16_to_f32(bias[n + q]);
+                    if (bias) o += bf16_to_f32(bb[q]);
                     store_out(out, m * N + n + q, o, out_f32);
                 }
         } else if (vec && c + 4 <= ncols) {
@@ -277,8 +289,8 @@ __global__ void __launch_bounds__(256)
     }
     // (the planner gives REDUCE_LAST only with one row block)
     if (S == 1 || reduce != SKG_REDUCE_LAST) return;
-    last_arriver_reduce(ws, tickets, bias, out, out_f32, M, N, S, j, col0, ncols, &is_last,
-                        MX ? nullptr : sx, MX ? nullptr : sw);
+    last_arriver_reduce(ws, tickets, bias, out, out_f32, M, N, S, j, col0, ncols, &is_last, !MX,
+                        scale);
 }
 
 namespace {

@@ -66,6 +66,12 @@ __global__ void __launch_bounds__(NW * 64)
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
     const int n0 = blockIdx.x * R;
     const int ncols = min(R, N - n0);
+    // The bias of the epilogue's first column for thread t, n0 + t % R,
+    // loaded ahead of the ring (the only column it stores when NW * 64 is a
+    // multiple of R or M * R <= NW * 64).  Without a bias no load is issued.
+    const Rsrc br = bias_rsrc(bias, N);
+    unsigned bb = 0;
+    if (bias) bb = load_bias_bits(br, n0 + t % R, t % R < ncols);
     const unsigned rowb = (unsigned)K * 2u;
     const Rsrc wr = make_rsrc(W + (size_t)n0 * K, (unsigned)ncols * rowb);
     const Rsrc xr = make_rsrc(x, (unsigned)M * rowb);
@@ -181,7 +187,8 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
         for (int w = 0; w < NW; ++w) s += red[((w * MT + m / 16) * 16 + m % 16) * 17 + c];
         const int n = n0 + c;
-        if (bias) s += bf16_to_f32(bias[n]);
+        const unsigned b = ((NW * 64) % R == 0 || e == t) ? bb : load_bias_bits(br, n);
+        if (bias) s += bf16_to_f32(b);
         store_out(out, (size_t)m * N + n, s, out_f32);
     }
 }

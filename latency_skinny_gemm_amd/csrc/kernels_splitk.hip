@@ -61,6 +61,17 @@ __global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
     const unsigned r16 = (unsigned)(lane & 15);
     const int kq = (lane >> 4) * 8;
 
+    // (S == 1) the bias of the lane's column in each of the NB column
+    // blocks, loaded ahead of the operand stream for the epilogue
+    unsigned bb[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) bb[nb] = 0;
+    if (bias && S == 1) {
+        const Rsrc br = bias_rsrc(bias, N);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) bb[nb] = load_bias_bits(br, col0 + nb * 16 + (lane & 15));
+    }
+
     f32x4 acc[NB][MT];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -131,7 +142,10 @@ __global__ void __launch_bounds__((splitk_max_threads(MT, NB, D)))
         const int m = mt * 16 + (lane >> 4) * 4 + i;
         if (m < M && n < N) {
             if (S == 1) {
-                if (bias) v += bf16_to_f32(bias[n]);
+                unsigned b = bb[0];  // bb[nb], without indexing registers at run time
+#pragma unroll
+                for (int k = 1; k < NB; ++k) b = nb == k ? bb[k] : b;
+                if (bias) v += bf16_to_f32(b);
                 store_out(out, (size_t)m * N + n, v, out_f32);
             } else {
                 put_partial(ws, ((size_t)s * M + m) * N + n, v, reduce == SKG_REDUCE_LAST);
@@ -153,9 +167,18 @@ __global__ void __launch_bounds__(256)
     if (e >= M * N) return;
     const int m = e / N;
     const int n = e - m * N;
+    // bias and scales first: their loads overlap the partials' loads (none
+    // is issued for a null pointer)
+    unsigned bb = 0;
+    if (bias) bb = load_bias_bits(bias_rsrc(bias, N), n);
+    float sxv = 1.0f, swv = 1.0f;
+    if (sx) {
+        sxv = load_scale(sx);
+        swv = load_scale(sw);
+    }
     float v = ordered_sum<8>(S, [&](int ss) { return ws[((size_t)ss * M + m) * N + n]; });
-    if (sx) v *= sx[0] * sw[0];  // FP8 per-tensor scale product, applied once
-    if (bias) v += bf16_to_f32(bias[n]);
+    if (sx) v *= sxv * swv;  // FP8 per-tensor scale product, applied once
+    if (bias) v += bf16_to_f32(bb);
     store_out(out, e, v, out_f32);
 }
 
@@ -170,6 +193,21 @@ __global__ void __launch_bounds__(256)
     const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (e >= M * N) return;
     const size_t plane = (size_t)M * N;
+    const int n = e % N;
+    // bias and scales first: their loads overlap the partials' loads
+    // instead of following them one round trip each (none is issued for a
+    // null pointer)
+    unsigned bb[4] = {0, 0, 0, 0};
+    if (bias) {
+        const Rsrc br = bias_rsrc(bias, N);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bb[q] = load_bias_bits(br, n + q);
+    }
+    float sxv = 1.0f, swv = 1.0f;
+    if (sx) {
+        sxv = load_scale(sx);
+        swv = load_scale(sw);
+    }
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     for (int i0 = 0; i0 < S; i0 += 8) {
         f32x4 t[8];
@@ -181,13 +219,12 @@ __global__ void __launch_bounds__(256)
         for (int i = 0; i < 8; ++i)
             if (i0 + i < S) v += t[i];
     }
-    const int n = e % N;
-    const float scale = sx ? sx[0] * sw[0] : 1.0f;
+    const float scale = sxv * swv;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         float r = v[q];
         if (sx) r *= scale;
-        if (bias) r += bf16_to_f32(bias[n + q]);
+        if (bias) r += bf16_to_f32(bb[q]);
         store_out(out, e + q, r, out_f32);
     }
 }

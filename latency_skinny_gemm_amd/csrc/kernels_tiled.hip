@@ -83,6 +83,19 @@ __global__ void __launch_bounds__(256)
     const int nsteps = (min(K, kbeg + k_chunk) - kbeg) >> 5;  // K, k_chunk: multiples of 32
     const int nstages = (nsteps + U - 1) / U;
 
+    // The epilogue's bias (S == 1), loaded now: thread t stores columns
+    // col0 + 4 * (t % C4) + 0..3 of its rows.  Without a bias no load is
+    // issued (the extra loads cost about 1 % at these shapes).
+    constexpr int C4 = NB * 4;  // 4-column groups per row
+    static_assert(256 % C4 == 0, "a thread keeps its column group");
+    unsigned bb[4] = {0, 0, 0, 0};
+    if (bias && S == 1) {
+        const Rsrc br = bias_rsrc(bias, N);
+        const int c = (t % C4) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bb[q] = load_bias_bits(br, col0 + c + q);
+    }
+
     // Stage layout: MT x-blocks then NB W-blocks; a block is 16 rows of the
     // stage's 64*U bytes (U steps), U KB, row-major.  Inside a row the
     // 16-byte chunk c sits at position c ^ swz(r), so the 16 rows that one
@@ -212,7 +225,6 @@ __global__ void __launch_bounds__(256)
                 tile[((wm * MTW + a) * 16 + (lane >> 4) * 4 + i) * TS + (wn * NBW + b) * 16 +
                      (lane & 15)] = acc[a][b][i];
     __syncthreads();
-    constexpr int C4 = NB * 4;  // 4-column groups per row
     const bool vec = (N & 3) == 0;  // 16-byte aligned workspace rows
     const bool coherent = reduce == SKG_REDUCE_LAST;  // partials read by the last arriver
     const PartialsVec pv = partials_vec(ws, M, N, S);
@@ -226,8 +238,8 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 if (c + q < ncols)
-                    store_out(out, m * N + n + q,
-                              bias ? v[q] + bf16_to_f32(bias[n + q]) : v[q], out_f32);
+                    store_out(out, m * N + n + q, bias ? v[q] + bf16_to_f32(bb[q]) : v[q],
+                              out_f32);
         } else if (vec && c + 4 <= ncols) {
             put_partial4(ws, ((size_t)s * M + m) * N + n, v, coherent, pv);
         } else {

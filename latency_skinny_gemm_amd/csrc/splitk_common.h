@@ -85,7 +85,8 @@ __device__ __forceinline__ void put_partial4(float *ws, size_t i, f32x4 v, bool 
 // fence writes back or invalidates an L2: the ordering comes from the
 // explicit wait, the barrier and the atomic, all at device scope.  That
 // workgroup sums the S partials in ascending s, applies the FP8 per-tensor
-// scale product when given (once), adds the bias and rounds once; it
+// scale product when `scaled` (once; the caller loaded the scales at its
+// start), adds the bias and rounds once; it
 // re-arms the ticket (the next kernel on the stream sees the zero after
 // the kernel boundary).  No workgroup waits on another.
 // E and G size the batch of 16-byte partial loads each thread keeps in
@@ -97,9 +98,8 @@ __device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
                                                     const uint16_t *__restrict__ bias,
                                                     void *__restrict__ out, int out_f32, int M, int N,
                                                     int S, int j, int col0, int ncols,
-                                                    unsigned *is_last,
-                                                    const float *__restrict__ sx = nullptr,
-                                                    const float *__restrict__ sw = nullptr) {
+                                                    unsigned *is_last, bool scaled = false,
+                                                    float scale = 1.0f) {
     wait_all_memory();
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -111,8 +111,8 @@ __device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
     }
     __syncthreads();
     if (!*is_last) return;
-    const float scale = sx ? sx[0] * sw[0] : 1.0f;  // FP8 per-tensor: applied once, here
     const PartialsVec pv = partials_vec(ws, M, N, S);
+    const Rsrc br = bias_rsrc(bias, N);
     if (pv.ok && ((col0 | ncols) & 3) == 0) {
         // Four columns per item, 16-byte sc1 loads: each thread puts E items
         // x G splits of loads in flight before adding any of them, so the
@@ -129,6 +129,16 @@ __device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
                 const int m = e / C4;
                 off[q] = e < items ? ((unsigned)m * (unsigned)N + (unsigned)(col0 + 4 * (e - m * C4))) * 4u
                                    : kOOB;
+            }
+            // the items' bias values go out ahead of their partials
+            unsigned bb[E][4];
+#pragma unroll
+            for (int q = 0; q < E; ++q) {
+                const int e = e0 + q * (int)blockDim.x;
+                const int m = e / C4;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    bb[q][k] = load_bias_bits(br, col0 + 4 * (e - m * C4) + k, e < items);
             }
             f32x4 acc[E];
 #pragma unroll
@@ -160,8 +170,8 @@ __device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     float v = acc[q][k];
-                    if (sx) v *= scale;
-                    if (bias) v += bf16_to_f32(bias[n + k]);
+                    if (scaled) v *= scale;
+                    if (bias) v += bf16_to_f32(bb[q][k]);
                     store_out(out, (size_t)m * N + n + k, v, out_f32);
                 }
             }
@@ -172,12 +182,13 @@ __device__ __forceinline__ void last_arriver_reduce(float *__restrict__ ws,
     for (int e = threadIdx.x; e < elems; e += blockDim.x) {
         const int m = e / ncols;
         const int n = col0 + (e - m * ncols);
+        const unsigned bb = load_bias_bits(br, n);  // ahead of the partials
         float v = ordered_sum<8>(S, [&](int ss) {
             return __hip_atomic_load(ws + ((size_t)ss * M + m) * N + n, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
         });
-        if (sx) v *= scale;
-        if (bias) v += bf16_to_f32(bias[n]);
+        if (scaled) v *= scale;
+        if (bias) v += bf16_to_f32(bb);
         store_out(out, (size_t)m * N + n, v, out_f32);
     }
 }

@@ -227,7 +227,7 @@ def candidates(skg, M, N, K):
             out.append(q)
 
     if M <= 16:
-        for flags in (0, skg.FLAG_DOT2):
+        for flags in (0, skg.FLAG_DOT2, skg.FLAG_DOT2 | skg.FLAG_DOT_WFIRST):
             for cols in (1, 2, 3, 4):
                 for T in DOT_THREADS:
                     add(skg.make_plan(skg.KIND_DOT, T, cols, flags=flags))

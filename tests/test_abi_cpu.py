@@ -959,6 +959,53 @@ def test_xlds_rejects_two_splits(lib):
         skg.plan_complete(8, 4096, 7168, skg.make_plan(skg.KIND_DOT, 512, 16, splits=2, flags=XLDS))
 
 
+# ------------------------------------------------------------------ W-first load order
+
+WFIRST = skg.FLAG_DOT2 | skg.FLAG_DOT_WFIRST
+PLAN_FIELDS = ("kind", "threads", "cols", "splits", "depth", "waves_m", "reduce", "k_chunk",
+               "m_tiles", "grid")
+
+
+@pytest.mark.parametrize("M,N,K,T,C", [
+    (8, 256, 7168, 448, 1), (16, 384, 7168, 448, 2), (1, 256, 7168, 64, 1), (3, 128, 2880, 192, 1),
+    (13, 1000, 4096, 256, 3), (2, 7, 2048, 1024, 4)])
+def test_wfirst_plans_match_dot2(lib, M, N, K, T, C):
+    # the same geometry as the dot plan without it: only the load order differs
+    q = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_DOT, T, C, flags=WFIRST))
+    r = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_DOT, T, C, flags=skg.FLAG_DOT2))
+    assert q.flags == WFIRST
+    assert [getattr(q, f) for f in PLAN_FIELDS] == [getattr(r, f) for f in PLAN_FIELDS]
+    _check_coverage(q, M, N, K)
+
+
+@pytest.mark.parametrize("kind,M,N,K,plan,good,bad,dtype", [
+    (skg.KIND_DOT, 8, 256, 7168, dict(threads=448), 0, skg.FLAG_DOT_WFIRST,   # needs dot2
+     skg.DTYPE_BF16),
+    (skg.KIND_DOT, 8, 4096, 7168, dict(threads=512, cols=16), XLDS,          # not with x in LDS
+     XLDS | skg.FLAG_DOT_WFIRST, skg.DTYPE_BF16),
+    (skg.KIND_DOT, 8, 256, 4096, dict(threads=256), 0, WFIRST, skg.DTYPE_FP8),  # bf16 only
+    (skg.KIND_DOT, 8, 256, 4096, dict(threads=256), 0, WFIRST, skg.DTYPE_FP8_MX),
+    (skg.KIND_ROWS, 8, 4096, 7168, dict(threads=256, cols=16, depth=4), 0, skg.FLAG_DOT_WFIRST,
+     skg.DTYPE_BF16),
+    (skg.KIND_TILED, 64, 4096, 7168, dict(threads=256, cols=4, splits=2, depth=4), 0,
+     skg.FLAG_DOT_WFIRST, skg.DTYPE_BF16),
+    (skg.KIND_SPLITK, 8, 4096, 7168, dict(threads=256, cols=1, splits=4, depth=2,
+                                          reduce=skg.REDUCE_KERNEL), 0, skg.FLAG_DOT_WFIRST,
+     skg.DTYPE_BF16),
+])
+def test_wfirst_rejects(lib, kind, M, N, K, plan, good, bad, dtype):
+    # the plan is valid without the flag and invalid with it
+    skg.plan_complete(M, N, K, skg.make_plan(kind, flags=good, **plan), dtype)
+    with pytest.raises(skg.SkinnyGemmError) as e:
+        skg.plan_complete(M, N, K, skg.make_plan(kind, flags=bad, **plan), dtype)
+    assert e.value.status == skg.ERR_INVALID_ARG
+
+
+def test_wfirst_rejects_above_16_rows(lib):
+    with pytest.raises(skg.SkinnyGemmError):
+        skg.plan_complete(17, 256, 7168, skg.make_plan(skg.KIND_DOT, 448, 1, flags=WFIRST))
+
+
 # ------------------------------------------------------------------ whole-row MFMA ring
 
 
@@ -983,7 +1030,7 @@ def test_rows_plans_cover(lib, M, N, K, T, R, NS, fl):
     (dict(threads=256, cols=9, depth=4), 8, skg.DTYPE_BF16),
     (dict(threads=256, cols=4, depth=4), 8, skg.DTYPE_BF16),
     (dict(threads=256, cols=16, depth=3), 64, skg.DTYPE_BF16),           # LDS: 64 rows of 1 KB
-    (dict(threads=256, cols=16, depth=4, flags=16), 8, skg.DTYPE_BF16),  # unknown flag
+    (dict(threads=256, cols=16, depth=4, flags=16), 8, skg.DTYPE_BF16),  # a dot flag
     (dict(threads=128, cols=16, depth=4), 8, skg.DTYPE_BF16),            # 2 waves
     (dict(threads=1024, cols=16, depth=4), 8, skg.DTYPE_BF16),           # 16 waves
     (dict(threads=256, cols=2, depth=4), 8, skg.DTYPE_BF16),             # 2 columns

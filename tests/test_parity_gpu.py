@@ -49,7 +49,7 @@ def _kernel_plans(skg, M, N, K):
     """The library's plan plus one explicit plan per kernel / reduction."""
     plans = [("default", None)]
     if M <= 16:
-        for flags in (0, skg.FLAG_DOT2):
+        for flags in (0, skg.FLAG_DOT2, skg.FLAG_DOT2 | skg.FLAG_DOT_WFIRST):
             for cols in (1, 2, 3, 4):
                 for threads in range(256, 1025, 64):  # the smallest workgroup that fits
                     p = skg.make_plan(skg.KIND_DOT, threads, cols=cols, flags=flags)
