@@ -490,6 +490,9 @@ def test_default_rule_without_table(lib, p):
         # the most columns per workgroup that leave two workgroups per CU
         c = next(c for c in (4, 2, 1) if c == 1 or -(-p.N // c) >= 400)
         assert q.cols == c, (q.cols, c)
+    if q.kind == skg.KIND_DOT:
+        # the dot instruction, and the W-first load order from 8 rows
+        assert q.flags == skg.FLAG_DOT2 | (skg.FLAG_DOT_WFIRST if p.M >= 8 else 0)
 
 
 @pytest.mark.parametrize("p", BF16, ids=lambda p: p.key())
@@ -502,11 +505,16 @@ def test_library_plan_is_valid_and_covers(lib, p):
 
 
 def test_default_rule_details(lib):
-    # bf16 dot plans: the dot instruction, two vectors per thread above 4
-    # rows, and 4 (else 2) columns while two workgroups per CU remain
+    # bf16 dot plans: the dot instruction (W first from 8 rows), two vectors
+    # per thread above 4 rows, and 4 (else 2) columns while two workgroups
+    # per CU remain
+    wfirst = skg.FLAG_DOT2 | skg.FLAG_DOT_WFIRST
     q = skg.plan_on(12, 256, 6144, 255)
-    assert (q.kind, q.flags, q.depth, q.cols) == (skg.KIND_DOT, skg.FLAG_DOT2, 2, 1)
+    assert (q.kind, q.flags, q.depth, q.cols) == (skg.KIND_DOT, wfirst, 2, 1)
     assert q.threads == 384
+    assert skg.plan_on(7, 256, 6144, 255).flags == skg.FLAG_DOT2
+    assert skg.plan_on(8, 256, 6144, 255).flags == wfirst
+    assert skg.plan_on(4, 4096, 7168, 255).flags == skg.FLAG_DOT2
     q = skg.plan_on(2, 4096, 7168, 255)
     assert (q.kind, q.cols) == (skg.KIND_DOT, 4) and q.grid == 1024
     q = skg.plan_on(2, 768, 7168, 255)
@@ -535,7 +543,8 @@ def test_default_rule_details(lib):
     # columns while N / 4 groups cover three quarters of the CUs, else 3,
     # and one 16-byte vector of K per thread where the registers allow
     q = skg.plan_on(8, 768, 4096, 256)
-    assert (q.kind, q.cols, q.threads, q.flags) == (skg.KIND_DOT, 4, 512, skg.FLAG_DOT2)
+    assert (q.kind, q.cols, q.threads, q.flags) == (skg.KIND_DOT, 4, 512, wfirst)
+    assert skg.plan_on(6, 640, 3072, 256).flags == skg.FLAG_DOT2
     q = skg.plan_on(10, 704, 6144, 256)
     assert (q.kind, q.cols, q.threads) == (skg.KIND_DOT, 3, 768)
     q = skg.plan_on(12, 768, 7168, 256)
