@@ -231,6 +231,22 @@ def test_xlds_matches_one_wave_dot_bitwise(skg, M, N, K, T, CW, bias):
     assert np.array_equal(a, c), f"{np.count_nonzero(a != c)} of {a.size} differ"
 
 
+@pytest.mark.parametrize("M,N,K,T,C", [(8, 256, 7168, 448, 1), (16, 384, 7168, 448, 2),
+                                       (3, 130, 2880, 192, 1), (12, 1000, 4096, 256, 3),
+                                       (1, 77, 2048, 64, 2), (5, 256, 6144, 1024, 4)])
+@pytest.mark.parametrize("bias", (False, True))
+def test_wfirst_matches_dot_bitwise(skg, M, N, K, T, C, bias):
+    # the W-first load order changes no arithmetic: the same plan with and
+    # without it gives the same bits (N ragged against the columns)
+    x, w, b = gen.bf16_inputs(M, N, K, bias, seed=2000 + M * 37 + N)
+    xd, wd, bd = _dev(x, w, b)
+    outs = []
+    for fl in (skg.FLAG_DOT2, skg.FLAG_DOT2 | skg.FLAG_DOT_WFIRST):
+        plan = skg.plan_complete(M, N, K, skg.make_plan(skg.KIND_DOT, T, C, flags=fl))
+        outs.append(gen.bits16(_run(skg, xd, wd, bd, plan)))
+    assert np.array_equal(outs[0], outs[1]), f"{np.count_nonzero(outs[0] != outs[1])} differ"
+
+
 def test_runs_are_bitwise_deterministic(skg):
     p = configs.Point("det", "bf16", 12, 384, 7168, True)
     x, w, b, _ = _ref_point(p)
