@@ -85,8 +85,8 @@ __device__ __forceinline__ void put_partial4(float *ws, size_t i, f32x4 v, bool 
 // fence writes back or invalidates an L2: the ordering comes from the
 // explicit wait, the barrier and the atomic, all at device scope.  That
 // workgroup sums the S partials in ascending s, applies the FP8 per-tensor
-// scale product when `scaled` (once; the caller loaded the scales at its
-// start), adds the bias and rounds once; it
+// scale product `scale` when `scaled` (once; the caller computes it),
+// adds the bias and rounds once; it
 // re-arms the ticket (the next kernel on the stream sees the zero after
 // the kernel boundary).  No workgroup waits on another.
 // E and G size the batch of 16-byte partial loads each thread keeps in
